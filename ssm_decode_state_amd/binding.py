@@ -1,0 +1,240 @@
+"""Thin ctypes binding of the ReplaySSM C ABI (include/ssm_replay.h).
+
+Argument marshalling only: every function here has the name of the C entry point it calls, turns
+torch tensors into device pointers and the current HIP stream into a hipStream_t, and raises
+SSMError on a non-zero status. All computation happens in the HIP library; there is no fallback
+path, and importing this module fails loudly when libssm_replay.so has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Mapping, Optional
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libssm_replay.so")
+
+SSM_OK, SSM_E_ARG, SSM_E_SHAPE, SSM_E_ALIGN, SSM_E_STATE, SSM_E_CAPACITY, SSM_E_UNSUPPORTED, \
+    SSM_E_HIP = 0, -1, -2, -3, -4, -5, -6, -7
+SSM_MAMBA2, SSM_GDN = 0, 1
+SSM_IN_F32, SSM_IN_BF16 = 0, 1
+SSM_RC_NONE, SSM_RC_FP8_ROW, SSM_RC_FP4_B16 = 0, 1, 2
+SSM_FLUSH_IF_FULL, SSM_FLUSH_ALL = 0, 1
+
+
+class SSMError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__("%s failed: %s (%d)" % (fn, _lib.ssm_status_string(status).decode(),
+                                                 status))
+
+
+class ssm_config(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("batch", ctypes.c_int32), ("heads", ctypes.c_int32),
+                ("groups", ctypes.c_int32), ("dim_p", ctypes.c_int32), ("dim_n", ctypes.c_int32),
+                ("window", ctypes.c_int32), ("max_draft", ctypes.c_int32),
+                ("in_dtype", ctypes.c_int32), ("readcopy", ctypes.c_int32),
+                ("gdn_scale", ctypes.c_float)]
+
+
+class ssm_layout(ctypes.Structure):
+    _fields_ = [("total_bytes", ctypes.c_uint64), ("ring_cap", ctypes.c_int32),
+                ("reserved", ctypes.c_int32), ("off_ckpt", ctypes.c_uint64),
+                ("off_rc_codes", ctypes.c_uint64), ("off_rc_scale", ctypes.c_uint64),
+                ("off_rc_tscale", ctypes.c_uint64), ("off_ring", ctypes.c_uint64 * 5),
+                ("off_ptr", ctypes.c_uint64)]
+
+
+class ssm_state(ctypes.Structure):
+    _fields_ = [("magic", ctypes.c_uint32), ("pending", ctypes.c_int32),
+                ("count_lo", ctypes.c_int32), ("count_hi", ctypes.c_int32),
+                ("cfg", ssm_config), ("lay", ssm_layout), ("mem", ctypes.c_void_p),
+                ("A", ctypes.c_void_p), ("D", ctypes.c_void_p)]
+
+
+class ssm_m2_in(ctypes.Structure):
+    _fields_ = [("x", ctypes.c_void_p), ("B", ctypes.c_void_p), ("C", ctypes.c_void_p),
+                ("dt", ctypes.c_void_p)]
+
+
+class ssm_gdn_in(ctypes.Structure):
+    _fields_ = [("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("beta", ctypes.c_void_p), ("g", ctypes.c_void_p)]
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError("libssm_replay.so is not built (run __graft_entry__.build() or "
+                           "python -m ssm_decode_state_amd.build); there is no fallback path")
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp, i32, st = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32
+    P = ctypes.POINTER
+    sig = {
+        "ssm_abi_version": ([], i32),
+        "ssm_status_string": ([st], ctypes.c_char_p),
+        "ssm_layout_query": ([P(ssm_config), P(ssm_layout)], st),
+        "ssm_ckpt_init": ([P(ssm_state), P(ssm_config), vp, ctypes.c_uint64, vp, vp, vp, vp], st),
+        "ssm_replay_decode": ([P(ssm_state), vp, vp, vp], st),
+        "ssm_flush": ([P(ssm_state), i32, vp], st),
+        "ssm_spec_append": ([P(ssm_state), i32, vp, vp, vp], st),
+        "ssm_spec_rollback": ([P(ssm_state), vp, vp], st),
+        "ssm_ckpt_export": ([P(ssm_state), vp, vp], st),
+        "ssm_conventional_step": ([P(ssm_config), vp, vp, vp, vp, vp, vp], st),
+        "ssm_tiles_pack": ([P(ssm_config), vp, vp, vp], st),
+        "ssm_tiles_unpack": ([P(ssm_config), vp, vp, vp], st),
+        "ssm_debug_codec": ([i32, vp, vp, ctypes.c_int64, vp], st),
+    }
+    for name, (args, res) in sig.items():
+        f = getattr(lib, name)
+        f.argtypes = args
+        f.restype = res
+    return lib
+
+
+_lib = _load()
+EXPORTS = ("ssm_abi_version", "ssm_status_string", "ssm_layout_query", "ssm_ckpt_init",
+           "ssm_replay_decode", "ssm_flush", "ssm_spec_append", "ssm_spec_rollback",
+           "ssm_ckpt_export", "ssm_conventional_step", "ssm_tiles_pack", "ssm_tiles_unpack",
+           "ssm_debug_codec")
+
+
+def _st(st):
+    """Accept either an ssm_state or a State that owns one."""
+    return st.st if isinstance(st, State) else st
+
+
+def _check(fn: str, status: int) -> None:
+    if status != SSM_OK:
+        raise SSMError(fn, status)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to the ReplaySSM ABI must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def make_config(kind: int, batch: int, heads: int, groups: int, dim_p: int, dim_n: int,
+                window: int, max_draft: int = 1, in_dtype: int = SSM_IN_BF16,
+                readcopy: int = SSM_RC_NONE, gdn_scale: float = 1.0) -> ssm_config:
+    return ssm_config(kind, batch, heads, groups, dim_p, dim_n, window, max_draft, in_dtype,
+                      readcopy, gdn_scale)
+
+
+def _inputs(cfg: ssm_config, inp: Mapping[str, torch.Tensor]):
+    if cfg.kind == SSM_MAMBA2:
+        return ssm_m2_in(inp["x"].data_ptr(), inp["B"].data_ptr(), inp["C"].data_ptr(),
+                         inp["dt"].data_ptr())
+    return ssm_gdn_in(inp["q"].data_ptr(), inp["k"].data_ptr(), inp["v"].data_ptr(),
+                      inp["beta"].data_ptr(), inp["g"].data_ptr())
+
+
+def ssm_abi_version() -> int:
+    return _lib.ssm_abi_version()
+
+
+def ssm_status_string(status: int) -> str:
+    return _lib.ssm_status_string(status).decode()
+
+
+def ssm_layout_query(cfg: ssm_config) -> ssm_layout:
+    lay = ssm_layout()
+    _check("ssm_layout_query", _lib.ssm_layout_query(ctypes.byref(cfg), ctypes.byref(lay)))
+    return lay
+
+
+def ssm_ckpt_init(st: ssm_state, cfg: ssm_config, mem: torch.Tensor, h0: Optional[torch.Tensor],
+                  A: Optional[torch.Tensor], D: Optional[torch.Tensor], stream=None) -> None:
+    _check("ssm_ckpt_init", _lib.ssm_ckpt_init(
+        ctypes.byref(st), ctypes.byref(cfg), _ptr(mem), mem.numel() * mem.element_size(),
+        _ptr(h0), _ptr(A), _ptr(D), _stream(stream)))
+
+
+def ssm_replay_decode(st: ssm_state, inputs: Mapping[str, torch.Tensor], y: torch.Tensor,
+                      stream=None) -> None:
+    st = _st(st)
+    inp = _inputs(st.cfg, inputs)
+    _check("ssm_replay_decode", _lib.ssm_replay_decode(ctypes.byref(st), ctypes.byref(inp),
+                                                       _ptr(y), _stream(stream)))
+
+
+def ssm_flush(st: ssm_state, mode: int, stream=None) -> None:
+    st = _st(st)
+    _check("ssm_flush", _lib.ssm_flush(ctypes.byref(st), mode, _stream(stream)))
+
+
+def ssm_spec_append(st: ssm_state, ndraft: int, inputs: Mapping[str, torch.Tensor],
+                    y: torch.Tensor, stream=None) -> None:
+    st = _st(st)
+    inp = _inputs(st.cfg, inputs)
+    _check("ssm_spec_append", _lib.ssm_spec_append(ctypes.byref(st), ndraft, ctypes.byref(inp),
+                                                   _ptr(y), _stream(stream)))
+
+
+def ssm_spec_rollback(st: ssm_state, n_accept: torch.Tensor, stream=None) -> None:
+    if n_accept.dtype != torch.int32:
+        raise ValueError("n_accept must be int32")
+    st = _st(st)
+    _check("ssm_spec_rollback", _lib.ssm_spec_rollback(ctypes.byref(st), _ptr(n_accept),
+                                                       _stream(stream)))
+
+
+def ssm_ckpt_export(st: ssm_state, h_out: torch.Tensor, stream=None) -> None:
+    st = _st(st)
+    _check("ssm_ckpt_export", _lib.ssm_ckpt_export(ctypes.byref(st), _ptr(h_out),
+                                                   _stream(stream)))
+
+
+def ssm_conventional_step(cfg: ssm_config, h: torch.Tensor, inputs: Mapping[str, torch.Tensor],
+                          A: Optional[torch.Tensor], D: Optional[torch.Tensor], y: torch.Tensor,
+                          stream=None) -> None:
+    inp = _inputs(cfg, inputs)
+    _check("ssm_conventional_step", _lib.ssm_conventional_step(
+        ctypes.byref(cfg), _ptr(h), ctypes.byref(inp), _ptr(A), _ptr(D), _ptr(y),
+        _stream(stream)))
+
+
+def ssm_tiles_pack(cfg: ssm_config, natural: torch.Tensor, tiles: torch.Tensor,
+                   stream=None) -> None:
+    _check("ssm_tiles_pack", _lib.ssm_tiles_pack(ctypes.byref(cfg), _ptr(natural), _ptr(tiles),
+                                                 _stream(stream)))
+
+
+def ssm_tiles_unpack(cfg: ssm_config, tiles: torch.Tensor, natural: torch.Tensor,
+                     stream=None) -> None:
+    _check("ssm_tiles_unpack", _lib.ssm_tiles_unpack(ctypes.byref(cfg), _ptr(tiles),
+                                                     _ptr(natural), _stream(stream)))
+
+
+def ssm_debug_codec(op: int, inp: torch.Tensor, out: torch.Tensor, stream=None) -> None:
+    _check("ssm_debug_codec", _lib.ssm_debug_codec(op, _ptr(inp), _ptr(out), inp.numel(),
+                                                   _stream(stream)))
+
+
+class State:
+    """Owner of one layer's device memory and its ssm_state (keeps the borrowed tensors alive)."""
+
+    def __init__(self, cfg: ssm_config, h0: Optional[torch.Tensor] = None,
+                 A: Optional[torch.Tensor] = None, D: Optional[torch.Tensor] = None,
+                 device: str = "cuda", stream=None):
+        self.cfg = cfg
+        self.layout = ssm_layout_query(cfg)
+        self.mem = torch.empty(max(1, self.layout.total_bytes), dtype=torch.uint8, device=device)
+        self.A, self.D = A, D
+        self.st = ssm_state()
+        ssm_ckpt_init(self.st, cfg, self.mem, h0, A, D, stream)
+
+    def region(self, offset: int, nbytes: int) -> torch.Tensor:
+        """Raw bytes of a region of the state memory (a view, for inspection in tests)."""
+        return self.mem[offset:offset + nbytes]

@@ -1,0 +1,770 @@
+// m2_kernels.hip -- Mamba-2 ReplaySSM kernels for gfx950 (wave64).
+//
+// Pages: "ReplaySSM: Rethinking State Storage for Faster Hybrid-Model Decoding" -- the deskofai.com
+// news article (paragraphs counted from the first body paragraph) and the nexus-ai-blog.com
+// explainer (cited by section heading). The Mamba-2 recurrence is the published one (Dao & Gu,
+// "Transformers are SSMs", 2024): h_t = exp(dt_t A) h_{t-1} + dt_t x_t B_t^T, y_t = h_t C_t + D x_t.
+//
+// Work decomposition. One wavefront owns one (sequence, head) pair; four heads per 256-thread
+// workgroup. The P x N fp32 checkpoint tile is stored "quad-interleaved": element (p, n) at float
+// ((n/4)*P + p)*4 + n%4. For P = 64 lane p therefore holds row p and every 16-byte load of the
+// wave covers 1 KiB of contiguous memory; the row dot products h[p,:] . C need no cross-lane
+// reduction. For P < 64 the wave holds 64/P copies of the rows, each lane group taking every
+// (64/P)-th quad, and the groups are summed with shuffles at the end.
+#include "ssm_device.hpp"
+#include "ssm_kernels.hpp"
+
+namespace ssm {
+
+template <int P, int N> struct M2Geo {
+    static_assert(P == 16 || P == 32 || P == 64, "Mamba-2 tile rows: 16, 32 or 64");
+    static_assert(N == 16 || N == 32 || N == 64 || N == 128, "Mamba-2 tile columns: 16..128");
+    static constexpr int kNQ = N / 4;     // 16-byte quads per row
+    static constexpr int kGrp = 64 / P;   // lane groups (copies of the rows) per wave
+    static constexpr int kQPL = kNQ / kGrp;  // quads per lane
+    static_assert(kNQ % kGrp == 0, "N too small for P");
+    static constexpr int kSeg = N / 4;    // B.C dot: elements per lane segment (4 segments)
+};
+
+constexpr int kHeadsPerBlock = 4;
+constexpr int kMaxEntries = 64;  // ring entries a wave can address (cap <= 63)
+
+// Ring slot of entry e (0-based after the checkpoint): (start + e) mod cap for start < cap and
+// e < cap, without an integer division (keeps the address arithmetic branch-free).
+__device__ __forceinline__ int ring_slot(int start, int e, int cap) {
+    const int s = start + e;
+    return s >= cap ? s - cap : s;
+}
+
+// ---------------------------------------------------------------------------------------------
+// Read copy (news, para 4: a low-precision copy of the checkpoint serves the reads while the
+// recurrence keeps the fp32 checkpoint). Only P = 64 tiles, where lane p owns row p:
+//   fp8 row copy: s = amax_row / 448 (1 if zero), code = RNE_sat_e4m3(h * (1/s)), value*s.
+//   fp4 copy (NVFP4 reading): s_t = amax_tile / 2688 (1 if zero); per 16-element block
+//     s_b = value(RNE_sat_e4m3(amax_blk / (6 s_t))), S = s_b s_t,
+//     code = RNE_sat_e2m1(h * (1/S)) (all zero when S == 0), value*S.
+// Codes: fp8 byte at ((n/16)*P + p)*16 + n%16 of the head's code block; fp4 nibble of byte
+// ((n/32)*P + p)*16 + (n%32)/2, low nibble = even n. Block scales [p][N/16]; row/tile scales fp32.
+// ---------------------------------------------------------------------------------------------
+template <int P, int N, int MAXQ, int RC>
+__device__ __forceinline__ void rc_row_dots(const M2Args& a, long head, int row, int nq,
+                                            const float* s_c /* [MAXQ][N] */, float (&acc)[MAXQ]) {
+    static_assert(P == 64, "read copy needs P == 64");
+    if constexpr (RC == 1) {
+        const u32x4_t* codes = reinterpret_cast<const u32x4_t*>(a.rc_codes + head * (long)(P * N));
+        u32x4_t u[N / 16];
+#pragma unroll
+        for (int k = 0; k < N / 16; ++k) u[k] = __builtin_nontemporal_load(codes + k * P + row);
+        const float s = static_cast<const float*>(a.rc_scale)[head * P + row];
+#pragma unroll
+        for (int k = 0; k < N / 16; ++k) {
+            const uint32_t w[4] = {u[k].x, u[k].y, u[k].z, u[k].w};
+            float v[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) v[i] = e4m3_decode((w[i / 4] >> (8 * (i % 4))) & 0xff);
+#pragma unroll
+            for (int j = 0; j < MAXQ; ++j) {
+                if (j >= nq) break;
+                float d = 0.f;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) d += v[i] * s_c[j * N + 16 * k + i];
+                acc[j] += d;
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < MAXQ; ++j) acc[j] *= s;
+    } else {
+        const u32x4_t* codes = reinterpret_cast<const u32x4_t*>(a.rc_codes + head * (long)(P * N / 2));
+        u32x4_t u[N / 32];
+#pragma unroll
+        for (int k = 0; k < N / 32; ++k) u[k] = __builtin_nontemporal_load(codes + k * P + row);
+        const uint8_t* sbp = static_cast<const uint8_t*>(a.rc_scale) + (head * P + row) * (N / 16);
+        uint32_t sbw[(N / 16 + 3) / 4];
+        if constexpr (N / 16 >= 8) {
+            const uint2 t = *reinterpret_cast<const uint2*>(sbp);
+            sbw[0] = t.x; sbw[1] = t.y;
+        } else {
+            sbw[0] = *reinterpret_cast<const uint32_t*>(sbp);
+        }
+        const float st = a.rc_tscale[head];
+#pragma unroll
+        for (int k = 0; k < N / 32; ++k) {
+            const uint32_t w[4] = {u[k].x, u[k].y, u[k].z, u[k].w};
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                const int blk = 2 * k + half;
+                const float S = e4m3_decode((sbw[blk / 4] >> (8 * (blk % 4))) & 0xff) * st;
+                float v[16];
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int e = 16 * half + i;  // element within the 32-element unit
+                    v[i] = e2m1_decode((w[e / 8] >> (4 * (e % 8))) & 0xf);
+                }
+#pragma unroll
+                for (int j = 0; j < MAXQ; ++j) {
+                    if (j >= nq) break;
+                    float d = 0.f;
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) d += v[i] * s_c[j * N + 16 * blk + i];
+                    acc[j] += S * d;
+                }
+            }
+        }
+    }
+}
+
+template <int P, int N, int RC>
+__device__ __forceinline__ void rc_write(const M2Args& a, long head, int row,
+                                         const float4 (&hv)[N / 4]) {
+    static_assert(P == 64, "read copy needs P == 64");
+    float amax = 0.f;
+#pragma unroll
+    for (int q = 0; q < N / 4; ++q)
+        amax = fmaxf(amax, fmaxf(fmaxf(fabsf(hv[q].x), fabsf(hv[q].y)),
+                                 fmaxf(fabsf(hv[q].z), fabsf(hv[q].w))));
+    if constexpr (RC == 1) {
+        const float s = amax > 0.f ? amax / 448.f : 1.f;
+        const float inv = 1.f / s;
+        uint4* codes = reinterpret_cast<uint4*>(a.rc_codes + head * (long)(P * N));
+#pragma unroll
+        for (int k = 0; k < N / 16; ++k) {
+            uint32_t w[4];
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq) {
+                const float4 v = hv[4 * k + qq];
+                w[qq] = e4m3_encode(v.x * inv) | (e4m3_encode(v.y * inv) << 8) |
+                        (e4m3_encode(v.z * inv) << 16) | (e4m3_encode(v.w * inv) << 24);
+            }
+            codes[k * P + row] = make_uint4(w[0], w[1], w[2], w[3]);
+        }
+        static_cast<float*>(a.rc_scale)[head * P + row] = s;
+    } else {
+        const float amax_t = xor_reduce_max<1, 32>(amax);
+        const float st = amax_t > 0.f ? amax_t / 2688.f : 1.f;
+        const float d6 = 6.f * st;
+        uint4* codes = reinterpret_cast<uint4*>(a.rc_codes + head * (long)(P * N / 2));
+        uint32_t sbw[(N / 16 + 3) / 4];
+#pragma unroll
+        for (int i = 0; i < (N / 16 + 3) / 4; ++i) sbw[i] = 0;
+#pragma unroll
+        for (int k = 0; k < N / 32; ++k) {
+            uint32_t w[4] = {0, 0, 0, 0};
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                const int blk = 2 * k + half;
+                float ab = 0.f;
+#pragma unroll
+                for (int qq = 0; qq < 4; ++qq) {
+                    const float4 v = hv[4 * blk + qq];
+                    ab = fmaxf(ab, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+                }
+                const uint32_t sb = e4m3_encode(ab / d6);
+                sbw[blk / 4] |= sb << (8 * (blk % 4));
+                const float S = e4m3_decode(sb) * st;
+                const float inv = S > 0.f ? 1.f / S : 0.f;
+#pragma unroll
+                for (int qq = 0; qq < 4; ++qq) {
+                    const float4 v = hv[4 * blk + qq];
+                    const float f[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int e = 16 * half + 4 * qq + i;  // element within the 32-unit
+                        const uint32_t c = S > 0.f ? e2m1_encode(f[i] * inv) : 0u;
+                        w[e / 8] |= c << (4 * (e % 8));
+                    }
+                }
+            }
+            codes[k * P + row] = make_uint4(w[0], w[1], w[2], w[3]);
+        }
+        uint8_t* sbp = static_cast<uint8_t*>(a.rc_scale) + (head * P + row) * (N / 16);
+        if constexpr (N / 16 >= 8) *reinterpret_cast<uint2*>(sbp) = make_uint2(sbw[0], sbw[1]);
+        else *reinterpret_cast<uint32_t*>(sbp) = sbw[0];
+        if (row == 0) a.rc_tscale[head] = st;
+    }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Replay decode / speculative verify.
+//
+// For each query token j (entry index kq_j - 1 after the checkpoint, 0-based) the output is
+//   y_j = e^{s0_j} h_c C_j + sum_{e < kq_j} e^{s_{e,j}} dt_e (B_e . C_j) x_e + D x_{kq_j - 1}
+// with s_{e,j} = A * sum_{m = e+1 .. kq_j - 1} dt_m and s0_j = A * sum_{m < kq_j} dt_m
+// (news, para 2: outputs from checkpoint + buffered inputs, no state write).
+// Entries e < count come from the ring; entries count .. count+ntok-1 are this call's tokens,
+// read from the caller's input and appended to the ring (news, para 3).
+// COMMIT: decode (count += ntok at the end); otherwise the tokens stay pending drafts.
+//
+// Memory order matters here: the vector-memory counter retires in order, so every small load
+// (pointers, dt, B segments, x rows, C) is issued BEFORE the checkpoint stream; the coefficient
+// work then only waits for those, and the 32 KiB tile keeps streaming underneath it.
+// MAXE bounds the entries a call can see (count + ntok <= MAXE).
+// ---------------------------------------------------------------------------------------------
+template <int P, int N, typename TIN, int RC, int MAXQ, int MAXE, bool COMMIT>
+__global__ __launch_bounds__(256) void m2_replay_kernel(M2Args a) {
+    using G = M2Geo<P, N>;
+    constexpr int kEPC = 16 / (int)sizeof(TIN);          // elements per 16-byte chunk
+    constexpr int kCPR = P / kEPC;                       // chunks per x row
+    constexpr int kXL = (MAXE * kCPR + 63) / 64;         // x-row chunks per lane
+    constexpr int kBC = MAXE / 16;                       // 16-entry chunks of B segments
+    constexpr int kCE = N >= 64 ? N / 64 : 1;            // C elements per lane
+    static_assert(MAXE % 16 == 0 && MAXE <= 64, "MAXE");
+    __shared__ float s_c[kHeadsPerBlock][MAXQ][N];
+    __shared__ u32x4_t s_x[kHeadsPerBlock][MAXE * kCPR];
+    __shared__ float s_w[kHeadsPerBlock][MAXE][MAXQ];
+
+    const int wave = uniform(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int h = blockIdx.x * kHeadsPerBlock + wave;
+    if (h >= a.heads) return;  // whole wave; no block-level barriers below
+    const int b = blockIdx.y;
+    const int head = b * a.heads + h;
+    const int hpg = a.heads / a.groups;
+    const int grp = h / hpg;
+    const int bg = b * a.groups + grp;
+    const int cap = a.cap, nq = a.ntok;
+    const int H = a.heads, Gn = a.groups;
+
+    const int2 pt = *reinterpret_cast<const int2*>(a.ptr + 2 * head);
+    const int start = uniform(pt.x);
+    const int count = uniform(pt.y);
+    const int kmax = count + nq;
+    const float A = a.A[h];
+    const float D = a.D[h];
+    const int row = lane % P, gq = lane / P;
+
+    const TIN* inx = static_cast<const TIN*>(a.in_x);
+    const TIN* inB = static_cast<const TIN*>(a.in_B);
+    const TIN* inC = static_cast<const TIN*>(a.in_C);
+    TIN* rx = static_cast<TIN*>(a.ring_x);
+    TIN* rB = static_cast<TIN*>(a.ring_B);
+    TIN* rC = static_cast<TIN*>(a.ring_C);
+
+    // ---- 1. small loads (branch-free: invalid entries read a valid row and are masked later) -
+    const long tok0 = (long)b * nq;  // this sequence's first token in the call's inputs
+    // C of each query: lane holds elements n = lane + 64 i (N >= 64) or n = lane (N < 64)
+    TIN craw[MAXQ][kCE];
+#pragma unroll
+    for (int j = 0; j < MAXQ; ++j) {
+        const int jj = j < nq ? j : 0;
+#pragma unroll
+        for (int i = 0; i < kCE; ++i) {
+            const int n = (lane + 64 * i) % N;
+            craw[j][i] = inC[((tok0 + jj) * Gn + grp) * N + n];
+        }
+    }
+    // dt of entry e = lane
+    const float* dsrc = lane < count ? a.ring_dt + head * cap + ring_slot(start, min(lane, cap - 1), cap)
+                                     : a.in_dt + (tok0 + min(max(lane - count, 0), nq - 1)) * H + h;
+    float dte = *dsrc;
+    dte = lane < kmax ? dte : 0.f;
+    // B segments: lane (ei, sg) holds entry e = 16c + ei, elements [sg*kSeg, sg*kSeg + kSeg)
+    const int ei = lane & 15, sg = lane >> 4;
+    constexpr int kSW = G::kSeg * (int)sizeof(TIN) / 4;  // 32-bit words per segment
+    uint32_t braw[kBC][kSW];
+#pragma unroll
+    for (int c = 0; c < kBC; ++c) {
+        const int e = 16 * c + ei;
+        const TIN* src = e < count ? rB + ((long)bg * cap + ring_slot(start, min(e, cap - 1), cap)) * N
+                                   : inB + ((tok0 + min(max(e - count, 0), nq - 1)) * Gn + grp) * N;
+        const uint32_t* w = reinterpret_cast<const uint32_t*>(src + sg * G::kSeg);
+        if constexpr (kSW % 4 == 0) {
+#pragma unroll
+            for (int u = 0; u < kSW / 4; ++u) {
+                const u32x4_t t = reinterpret_cast<const u32x4_t*>(w)[u];
+                braw[c][4 * u] = t.x; braw[c][4 * u + 1] = t.y;
+                braw[c][4 * u + 2] = t.z; braw[c][4 * u + 3] = t.w;
+            }
+        } else {
+#pragma unroll
+            for (int u = 0; u < kSW / 2; ++u) {
+                const uint2 t = reinterpret_cast<const uint2*>(w)[u];
+                braw[c][2 * u] = t.x; braw[c][2 * u + 1] = t.y;
+            }
+        }
+    }
+    // x rows of every entry, in 16-byte chunks: chunk idx -> (row e = idx / kCPR, part idx % kCPR)
+    u32x4_t xraw[kXL];
+#pragma unroll
+    for (int i = 0; i < kXL; ++i) {
+        const int idx = lane + 64 * i;
+        const int e = idx / kCPR, part = idx % kCPR;
+        const TIN* src = e < count ? rx + ((long)head * cap + ring_slot(start, min(e, cap - 1), cap)) * P
+                                   : inx + ((tok0 + min(max(e - count, 0), nq - 1)) * H + h) * P;
+        xraw[i] = *reinterpret_cast<const u32x4_t*>(src + part * kEPC);
+    }
+
+    // ---- 2. the checkpoint stream (explainer, "Why Decoding, Not Prefill, Is the Hard Part":
+    //         decode time goes to reading the state) ----------------------------------------
+    float4 hv[G::kQPL];
+    const float4* tile = reinterpret_cast<const float4*>(a.ckpt) + (long)head * (P * N / 4);
+    if constexpr (RC == 0) {
+#pragma unroll
+        for (int j = 0; j < G::kQPL; ++j) hv[j] = ld_stream(tile + (gq + G::kGrp * j) * P + row);
+    }
+    asm volatile("" ::: "memory");  // keep every staging store below the stream issue
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- 3. stage C and x rows in LDS; append this call's tokens to the rings ---------------
+    // (every staging store is unconditional so that no load can be sunk past the stream)
+#pragma unroll
+    for (int j = 0; j < MAXQ; ++j) {
+#pragma unroll
+        for (int i = 0; i < kCE; ++i) s_c[wave][j][(lane + 64 * i) % N] = to_f32<TIN>(craw[j][i]);
+    }
+#pragma unroll
+    for (int i = 0; i < kXL; ++i) {
+        const int idx = lane + 64 * i;
+        if (kXL * 64 == MAXE * kCPR || idx < MAXE * kCPR) s_x[wave][idx] = xraw[i];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < kXL; ++i) {
+        const int idx = lane + 64 * i;
+        const int e = idx / kCPR, part = idx % kCPR;
+        if (e >= count && e < kmax)  // this call's token: append its x row
+            *reinterpret_cast<u32x4_t*>(rx + ((long)head * cap + ring_slot(start, e, cap)) * P + part * kEPC) =
+                xraw[i];
+    }
+    if (lane >= count && lane < kmax) a.ring_dt[head * cap + ring_slot(start, lane, cap)] = dte;
+    if (h % hpg == 0) {  // the group's first head writes the shared B and C entries
+#pragma unroll
+        for (int c = 0; c < kBC; ++c) {
+            const int e = 16 * c + ei;
+            if (e >= count && e < kmax) {
+                uint32_t* w = reinterpret_cast<uint32_t*>(rB + ((long)bg * cap + ring_slot(start, e, cap)) * N +
+                                                          sg * G::kSeg);
+                if constexpr (kSW % 4 == 0) {
+#pragma unroll
+                    for (int u = 0; u < kSW / 4; ++u)
+                        reinterpret_cast<u32x4_t*>(w)[u] = u32x4_t{braw[c][4 * u], braw[c][4 * u + 1],
+                                                                   braw[c][4 * u + 2], braw[c][4 * u + 3]};
+                } else {
+#pragma unroll
+                    for (int u = 0; u < kSW / 2; ++u)
+                        reinterpret_cast<uint2*>(w)[u] = make_uint2(braw[c][2 * u], braw[c][2 * u + 1]);
+                }
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < MAXQ; ++j) {
+            if (j >= nq) break;
+            const int slot = ring_slot(start, count + j, cap);
+#pragma unroll
+            for (int i = 0; i < kCE; ++i) {
+                const int n = lane + 64 * i;
+                if (n < N) rC[((long)bg * cap + slot) * N + n] = craw[j][i];
+            }
+        }
+    }
+    wave_sync();
+
+    // ---- 4. replay weights w_{e,j} and checkpoint decays e^{s0_j} ---------------------------
+    float s0[MAXQ];
+#pragma unroll
+    for (int j = 0; j < MAXQ; ++j) {
+        s0[j] = 0.f;
+        if (j >= nq) continue;
+        float tot = 0.f;
+        for (int m = 0; m < count + j + 1; ++m) tot += readlane(dte, m);
+        s0[j] = expf(A * tot);
+    }
+#pragma unroll
+    for (int c = 0; c < kBC; ++c) {
+        const int e = 16 * c + ei;
+        if (16 * c >= kmax) break;
+        float bf[G::kSeg];
+        if constexpr (sizeof(TIN) == 2) {
+#pragma unroll
+            for (int u = 0; u < kSW; ++u) {
+                bf[2 * u] = __uint_as_float(braw[c][u] << 16);
+                bf[2 * u + 1] = __uint_as_float(braw[c][u] & 0xffff0000u);
+            }
+        } else {
+#pragma unroll
+            for (int u = 0; u < kSW; ++u) bf[u] = __uint_as_float(braw[c][u]);
+        }
+        const float dt_e = __shfl(dte, e & 63, 64);
+#pragma unroll
+        for (int j = 0; j < MAXQ; ++j) {
+            if (j >= nq) break;
+            const float* cj = &s_c[wave][j][sg * G::kSeg];
+            float d = 0.f;
+#pragma unroll
+            for (int i = 0; i < G::kSeg; ++i) d += bf[i] * cj[i];
+            d = xor_reduce_sum<16, 32>(d);
+            const int kq = count + j + 1;
+            float suf = 0.f;  // sum of dt over entries e+1 .. kq-1
+            for (int m = 0; m < kq; ++m) {
+                const float dm = readlane(dte, m);
+                suf += (m > e) ? dm : 0.f;
+            }
+            const float w = (e < kq) ? expf(A * suf) * dt_e * d : 0.f;
+            if (sg == 0) s_w[wave][e][j] = w;
+        }
+    }
+    wave_sync();
+
+    // ---- 5. buffered-input and skip terms (LDS only) -----------------------------------------
+    float out[MAXQ];
+#pragma unroll
+    for (int j = 0; j < MAXQ; ++j) out[j] = 0.f;
+    const TIN* sx = reinterpret_cast<const TIN*>(&s_x[wave][0]);
+    for (int e = 0; e < kmax; ++e) {
+        const float xe = to_f32<TIN>(sx[e * P + row]);
+#pragma unroll
+        for (int j = 0; j < MAXQ; ++j) {
+            if (j >= nq) break;
+            out[j] += s_w[wave][e][j] * xe;
+            if (e == count + j) out[j] += D * xe;
+        }
+    }
+
+    // ---- 6. checkpoint row dots h_c[p,:] . C_j -------------------------------------------------
+    float acc[MAXQ];
+#pragma unroll
+    for (int j = 0; j < MAXQ; ++j) acc[j] = 0.f;
+    if constexpr (RC == 0) {
+#pragma unroll
+        for (int jq = 0; jq < G::kQPL; ++jq) {
+            const int q = gq + G::kGrp * jq;
+#pragma unroll
+            for (int j = 0; j < MAXQ; ++j) {
+                if (j >= nq) break;
+                const float4 c4 = *reinterpret_cast<const float4*>(&s_c[wave][j][4 * q]);
+                acc[j] += hv[jq].x * c4.x + hv[jq].y * c4.y + hv[jq].z * c4.z + hv[jq].w * c4.w;
+            }
+        }
+    } else {
+        rc_row_dots<P, N, MAXQ, RC>(a, head, row, nq, &s_c[wave][0][0], acc);
+    }
+    if constexpr (G::kGrp > 1) {
+#pragma unroll
+        for (int j = 0; j < MAXQ; ++j) acc[j] = xor_reduce_sum<P, 32>(acc[j]);
+    }
+    if (gq == 0) {
+#pragma unroll
+        for (int j = 0; j < MAXQ; ++j) {
+            if (j >= nq) break;
+            a.y[(((long)b * nq + j) * H + h) * P + row] = s0[j] * acc[j] + out[j];
+        }
+    }
+    if constexpr (COMMIT) {
+        if (lane == 0) a.ptr[2 * head + 1] = count + nq;
+    }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Flush: fold the oldest nfold committed entries into the checkpoint (news, para 3):
+//   h_c <- e^{s0} h_c + sum_{e < nfold} e^{s_e} dt_e x_e B_e^T,  s_e = A sum_{m=e+1..nfold-1} dt_m
+// nfold = L when count >= L (mode IF_FULL), = count (mode ALL), else nothing is folded. Then
+// start += nfold, count -= nfold, and the read copy (if any) is rewritten from the new h_c
+// (news, para 4: the low-precision copy is for reads only; the recurrence never sees it).
+// With rewrite_only the checkpoint is untouched and only the read copy is written (init).
+// Entries are folded in chunks of 16; the first chunk's B and x rows are fetched before the
+// checkpoint tile for the same in-order-counter reason as in the replay kernel.
+// ---------------------------------------------------------------------------------------------
+template <int P, int N, typename TIN, int RC>
+__global__ __launch_bounds__(256) void m2_flush_kernel(M2Args a, int mode_all, int rewrite_only) {
+    using G = M2Geo<P, N>;
+    constexpr int kEPC = 16 / (int)sizeof(TIN);
+    constexpr int kBCR = N / kEPC;                 // 16-byte chunks per B row
+    constexpr int kBL = (16 * kBCR + 63) / 64;     // B chunks per lane (16 rows)
+    constexpr int kXCR = P / kEPC;                 // chunks per x row
+    constexpr int kXL = (16 * kXCR + 63) / 64;
+    __shared__ float s_b[kHeadsPerBlock][16][N];
+    __shared__ u32x4_t s_x[kHeadsPerBlock][16 * kXCR];
+
+    const int wave = uniform(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int h = blockIdx.x * kHeadsPerBlock + wave;
+    if (h >= a.heads) return;
+    const int b = blockIdx.y;
+    const int head = b * a.heads + h;
+    const int grp = h / (a.heads / a.groups);
+    const int bg = b * a.groups + grp;
+    const int cap = a.cap;
+    const int2 pt = *reinterpret_cast<const int2*>(a.ptr + 2 * head);
+    const int start = uniform(pt.x);
+    const int count = uniform(pt.y);
+    const int nfold = rewrite_only ? 0 : (mode_all ? count : (count >= a.window ? a.window : 0));
+    if (nfold == 0 && !rewrite_only) return;
+    const int row = lane % P, gq = lane / P;
+    const TIN* rx = static_cast<const TIN*>(a.ring_x);
+    const TIN* rB = static_cast<const TIN*>(a.ring_B);
+
+    float dte = a.ring_dt[head * cap + ring_slot(start, min(lane, cap - 1), cap)];
+    dte = lane < nfold ? dte : 0.f;
+    const float A = a.A[h];
+
+    // chunk loader: B rows and x rows of entries c0 .. c0+15 into registers
+    u32x4_t braw[kBL], xraw[kXL];
+    auto fetch = [&](int c0) {  // branch-free: rows past nfold re-read the last folded row
+#pragma unroll
+        for (int i = 0; i < kBL; ++i) {
+            const int idx = (lane + 64 * i) % (16 * kBCR);
+            const int e = min(c0 + idx / kBCR, nfold - 1), part = idx % kBCR;
+            braw[i] = *reinterpret_cast<const u32x4_t*>(rB + ((long)bg * cap + ring_slot(start, e, cap)) * N +
+                                                      part * kEPC);
+        }
+#pragma unroll
+        for (int i = 0; i < kXL; ++i) {
+            const int idx = (lane + 64 * i) % (16 * kXCR);
+            const int e = min(c0 + idx / kXCR, nfold - 1), part = idx % kXCR;
+            xraw[i] = *reinterpret_cast<const u32x4_t*>(rx + ((long)head * cap + ring_slot(start, e, cap)) * P +
+                                                      part * kEPC);
+        }
+    };
+    if (nfold > 0) fetch(0);
+
+    float4 hv[G::kQPL];
+    float4* tile = reinterpret_cast<float4*>(a.ckpt) + (long)head * (P * N / 4);
+#pragma unroll
+    for (int j = 0; j < G::kQPL; ++j) hv[j] = ld_stream(tile + (gq + G::kGrp * j) * P + row);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+
+    if (nfold > 0) {
+        // u_e = e^{s_e} dt_e in lane e; e^{s0} uniform
+        float suf = 0.f, tot = 0.f;
+        for (int m = 0; m < nfold; ++m) {
+            const float dm = readlane(dte, m);
+            tot += dm;
+            suf += (m > lane) ? dm : 0.f;
+        }
+        const float ue = expf(A * suf) * dte;
+        const float e0 = expf(A * tot);
+        bool first = true;
+        for (int c0 = 0; c0 < nfold; c0 += 16) {
+            const int nc = min(16, nfold - c0);
+            if (c0 > 0) fetch(c0);
+            // stage the chunk: B rows as fp32, x rows raw
+#pragma unroll
+            for (int i = 0; i < kBL; ++i) {
+                const int idx = lane + 64 * i;
+                if (idx < 16 * kBCR) {
+                    float f[kEPC];
+                    Unit<TIN>::unpack(make_uint4(braw[i].x, braw[i].y, braw[i].z, braw[i].w), f);
+                    const int r = idx / kBCR, part = idx % kBCR;
+#pragma unroll
+                    for (int k = 0; k < kEPC; ++k) s_b[wave][r][part * kEPC + k] = f[k];
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < kXL; ++i) {
+                const int idx = lane + 64 * i;
+                if (idx < 16 * kXCR) s_x[wave][idx] = xraw[i];
+            }
+            wave_sync();
+            if (first) {
+#pragma unroll
+                for (int j = 0; j < G::kQPL; ++j) {
+                    hv[j].x *= e0; hv[j].y *= e0; hv[j].z *= e0; hv[j].w *= e0;
+                }
+                first = false;
+            }
+            const TIN* sx = reinterpret_cast<const TIN*>(&s_x[wave][0]);
+            float ax[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                ax[i] = (i < nc) ? readlane(ue, c0 + i) * to_f32<TIN>(sx[i * P + row]) : 0.f;
+#pragma unroll
+            for (int j = 0; j < G::kQPL; ++j) {
+                const int q = gq + G::kGrp * j;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    if (i >= nc) break;
+                    const float4 b4 = *reinterpret_cast<const float4*>(&s_b[wave][i][4 * q]);
+                    hv[j].x += ax[i] * b4.x; hv[j].y += ax[i] * b4.y;
+                    hv[j].z += ax[i] * b4.z; hv[j].w += ax[i] * b4.w;
+                }
+            }
+            wave_sync();
+        }
+#pragma unroll
+        for (int j = 0; j < G::kQPL; ++j) st_stream(hv[j], tile + (gq + G::kGrp * j) * P + row);
+    }
+    if constexpr (RC != 0) rc_write<P, N, RC>(a, head, row, hv);  // P == 64: kQPL == N/4
+    if (nfold > 0 && lane == 0) {
+        a.ptr[2 * head] = ring_slot(start, nfold, cap);
+        a.ptr[2 * head + 1] = count - nfold;
+    }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Conventional step (the comparison point; news, para 3 -- the full state rewritten per token):
+//   h <- exp(dt A) h + dt x B^T (in place), y = h C + D x.
+// ---------------------------------------------------------------------------------------------
+template <int P, int N, typename TIN>
+__global__ __launch_bounds__(256) void m2_conv_kernel(M2ConvArgs a) {
+    using G = M2Geo<P, N>;
+    constexpr int kCE = N >= 64 ? N / 64 : 1;
+    __shared__ float s_bc[kHeadsPerBlock][2][N];
+    const int wave = uniform(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int h = blockIdx.x * kHeadsPerBlock + wave;
+    if (h >= a.heads) return;
+    const int b = blockIdx.y;
+    const int head = b * a.heads + h;
+    const int grp = h / (a.heads / a.groups);
+    const int row = lane % P, gq = lane / P;
+
+    const TIN* inB = static_cast<const TIN*>(a.in_B) + ((long)b * a.groups + grp) * N;
+    const TIN* inC = static_cast<const TIN*>(a.in_C) + ((long)b * a.groups + grp) * N;
+    TIN braw[kCE], craw[kCE];
+#pragma unroll
+    for (int i = 0; i < kCE; ++i) {
+        const int n = (lane + 64 * i) % N;
+        braw[i] = inB[n];
+        craw[i] = inC[n];
+    }
+    const float dt = a.in_dt[head];
+    const TIN xraw = static_cast<const TIN*>(a.in_x)[(long)head * P + row];
+    const float A = a.A[h], D = a.D[h];
+
+    float4 hv[G::kQPL];
+    float4* tile = reinterpret_cast<float4*>(a.h) + (long)head * (P * N / 4);
+#pragma unroll
+    for (int j = 0; j < G::kQPL; ++j) hv[j] = ld_stream(tile + (gq + G::kGrp * j) * P + row);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+
+#pragma unroll
+    for (int i = 0; i < kCE; ++i) {
+        const int n = (lane + 64 * i) % N;
+        s_bc[wave][0][n] = to_f32<TIN>(braw[i]);
+        s_bc[wave][1][n] = to_f32<TIN>(craw[i]);
+    }
+    const float decay = expf(dt * A);
+    const float x = to_f32<TIN>(xraw);
+    const float dx = dt * x;
+    wave_sync();
+    float acc = 0.f;
+#pragma unroll
+    for (int j = 0; j < G::kQPL; ++j) {
+        const int q = gq + G::kGrp * j;
+        const float4 b4 = *reinterpret_cast<const float4*>(&s_bc[wave][0][4 * q]);
+        const float4 c4 = *reinterpret_cast<const float4*>(&s_bc[wave][1][4 * q]);
+        hv[j].x = decay * hv[j].x + dx * b4.x;
+        hv[j].y = decay * hv[j].y + dx * b4.y;
+        hv[j].z = decay * hv[j].z + dx * b4.z;
+        hv[j].w = decay * hv[j].w + dx * b4.w;
+        acc += hv[j].x * c4.x + hv[j].y * c4.y + hv[j].z * c4.z + hv[j].w * c4.w;
+        st_stream(hv[j], tile + q * P + row);
+    }
+    if constexpr (G::kGrp > 1) acc = xor_reduce_sum<P, 32>(acc);
+    if (gq == 0) a.y[(long)head * P + row] = acc + D * x;
+}
+
+// ---------------------------------------------------------------------------------------------
+// Instantiation tables. Grid: (ceil(H / 4), batch); one wavefront per head.
+// ---------------------------------------------------------------------------------------------
+static dim3 head_grid(int batch, int heads) {
+    return dim3((unsigned)((heads + kHeadsPerBlock - 1) / kHeadsPerBlock), (unsigned)batch);
+}
+
+template <int P, int N, typename TIN, int RC>
+static hipError_t launch_replay_pn(const M2Args& a, bool spec, int maxe, hipStream_t s) {
+    const dim3 grid = head_grid(a.batch, a.heads), block(256);
+    if (spec) {
+        if (maxe <= 32)
+            hipLaunchKernelGGL((m2_replay_kernel<P, N, TIN, RC, 8, 32, false>), grid, block, 0, s, a);
+        else
+            hipLaunchKernelGGL((m2_replay_kernel<P, N, TIN, RC, 8, 64, false>), grid, block, 0, s, a);
+    } else {
+        if (maxe <= 16)
+            hipLaunchKernelGGL((m2_replay_kernel<P, N, TIN, RC, 1, 16, true>), grid, block, 0, s, a);
+        else
+            hipLaunchKernelGGL((m2_replay_kernel<P, N, TIN, RC, 1, 32, true>), grid, block, 0, s, a);
+    }
+    return hipGetLastError();
+}
+template <int P, int N, typename TIN, int RC>
+static hipError_t launch_flush_pn(const M2Args& a, int mode_all, int rewrite_only, hipStream_t s) {
+    hipLaunchKernelGGL((m2_flush_kernel<P, N, TIN, RC>), head_grid(a.batch, a.heads), dim3(256), 0,
+                       s, a, mode_all, rewrite_only);
+    return hipGetLastError();
+}
+template <int P, int N, typename TIN>
+static hipError_t launch_conv_pn(const M2ConvArgs& a, hipStream_t s) {
+    hipLaunchKernelGGL((m2_conv_kernel<P, N, TIN>), head_grid(a.batch, a.heads), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+#ifdef SSM_SINGLE_SHAPE  // faster builds when inspecting the serving-shape kernels
+#define SSM_M2_SHAPES(X, ...) X(64, 128, __VA_ARGS__)
+#else
+#define SSM_M2_SHAPES(X, ...)                                                                   \
+    X(16, 16, __VA_ARGS__) X(16, 32, __VA_ARGS__) X(16, 64, __VA_ARGS__)                       \
+    X(16, 128, __VA_ARGS__) X(32, 32, __VA_ARGS__) X(32, 64, __VA_ARGS__)                      \
+    X(32, 128, __VA_ARGS__) X(64, 16, __VA_ARGS__) X(64, 32, __VA_ARGS__)                      \
+    X(64, 64, __VA_ARGS__) X(64, 128, __VA_ARGS__)
+#endif
+
+template <typename TIN, int RC>
+static hipError_t dispatch_replay(const M2Args& a, int P, int N, bool spec, int maxe,
+                                  hipStream_t s) {
+#define X(PP, NN, ...) \
+    if (P == PP && N == NN) return launch_replay_pn<PP, NN, TIN, RC>(a, spec, maxe, s);
+    if constexpr (RC == 0) {
+        SSM_M2_SHAPES(X, 0)
+    } else {
+        if (P == 64 && N == 64) return launch_replay_pn<64, 64, TIN, RC>(a, spec, maxe, s);
+        if (P == 64 && N == 128) return launch_replay_pn<64, 128, TIN, RC>(a, spec, maxe, s);
+    }
+#undef X
+    return hipErrorNotSupported;
+}
+template <typename TIN, int RC>
+static hipError_t dispatch_flush(const M2Args& a, int P, int N, int mode_all, int rewrite_only,
+                                 hipStream_t s) {
+#define X(PP, NN, ...) \
+    if (P == PP && N == NN) return launch_flush_pn<PP, NN, TIN, RC>(a, mode_all, rewrite_only, s);
+    if constexpr (RC == 0) {
+        SSM_M2_SHAPES(X, 0)
+    } else {
+        if (P == 64 && N == 64) return launch_flush_pn<64, 64, TIN, RC>(a, mode_all, rewrite_only, s);
+        if (P == 64 && N == 128)
+            return launch_flush_pn<64, 128, TIN, RC>(a, mode_all, rewrite_only, s);
+    }
+#undef X
+    return hipErrorNotSupported;
+}
+
+hipError_t m2_launch_replay(const M2Args& a, int P, int N, int bf16, int rc, bool spec, int maxe,
+                            hipStream_t s) {
+    if (maxe > 64) return hipErrorNotSupported;
+    if (bf16) {
+        if (rc == 0) return dispatch_replay<bf16_t, 0>(a, P, N, spec, maxe, s);
+        if (rc == 1) return dispatch_replay<bf16_t, 1>(a, P, N, spec, maxe, s);
+        return dispatch_replay<bf16_t, 2>(a, P, N, spec, maxe, s);
+    }
+    if (rc == 0) return dispatch_replay<float, 0>(a, P, N, spec, maxe, s);
+    if (rc == 1) return dispatch_replay<float, 1>(a, P, N, spec, maxe, s);
+    return dispatch_replay<float, 2>(a, P, N, spec, maxe, s);
+}
+
+hipError_t m2_launch_flush(const M2Args& a, int P, int N, int bf16, int rc, int mode_all,
+                           int rewrite_only, hipStream_t s) {
+    if (bf16) {
+        if (rc == 0) return dispatch_flush<bf16_t, 0>(a, P, N, mode_all, rewrite_only, s);
+        if (rc == 1) return dispatch_flush<bf16_t, 1>(a, P, N, mode_all, rewrite_only, s);
+        return dispatch_flush<bf16_t, 2>(a, P, N, mode_all, rewrite_only, s);
+    }
+    if (rc == 0) return dispatch_flush<float, 0>(a, P, N, mode_all, rewrite_only, s);
+    if (rc == 1) return dispatch_flush<float, 1>(a, P, N, mode_all, rewrite_only, s);
+    return dispatch_flush<float, 2>(a, P, N, mode_all, rewrite_only, s);
+}
+
+hipError_t m2_launch_conv(const M2ConvArgs& a, int P, int N, int bf16, hipStream_t s) {
+#define X(PP, NN, T) \
+    if (P == PP && N == NN) return launch_conv_pn<PP, NN, T>(a, s);
+    if (bf16) {
+        SSM_M2_SHAPES(X, bf16_t)
+    } else {
+        SSM_M2_SHAPES(X, float)
+    }
+#undef X
+    return hipErrorNotSupported;
+}
+
+}  // namespace ssm

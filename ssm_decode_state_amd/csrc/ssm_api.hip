@@ -1,0 +1,427 @@
+// ssm_api.hip -- the C ABI (include/ssm_replay.h): validation, state layout, host-side pointer
+// bounds, and kernel launches. All checks run on the host before anything is enqueued.
+#include "../../include/ssm_replay.h"
+
+#include <math.h>
+#include <string.h>
+
+#include "ssm_kernels.hpp"
+
+namespace {
+
+constexpr uint32_t kMagic = 0x524d5353u;  // "SSMR"
+constexpr uint64_t kAlign = 256;
+
+uint64_t align_up(uint64_t v) { return (v + kAlign - 1) & ~(kAlign - 1); }
+bool is_pow2_dim(int v) { return v == 16 || v == 32 || v == 64 || v == 128; }
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+ssm_status check_config(const ssm_config* c) {
+    if (!c) return SSM_E_ARG;
+    if (c->kind != SSM_MAMBA2 && c->kind != SSM_GDN) return SSM_E_ARG;
+    if (c->in_dtype != SSM_IN_F32 && c->in_dtype != SSM_IN_BF16) return SSM_E_ARG;
+    if (c->readcopy < SSM_RC_NONE || c->readcopy > SSM_RC_FP4_B16) return SSM_E_ARG;
+    if (c->batch < 0 || c->heads < 1 || c->groups < 1) return SSM_E_SHAPE;
+    if ((int64_t)c->batch * c->heads > (int64_t)1 << 30) return SSM_E_SHAPE;
+    if (c->heads % c->groups != 0) return SSM_E_SHAPE;
+    if (c->window < 1 || c->window > 32) return SSM_E_SHAPE;
+    if (c->max_draft < 1 || c->max_draft > 8 || c->max_draft > c->window) return SSM_E_SHAPE;
+    if (!is_pow2_dim(c->dim_p) || !is_pow2_dim(c->dim_n)) return SSM_E_SHAPE;
+    if (c->kind == SSM_MAMBA2) {
+        if (c->dim_p > 64) return SSM_E_SHAPE;           // one wavefront per head tile
+        if (c->dim_n < 64 / c->dim_p * 4) return SSM_E_SHAPE;  // every lane group owns a quad
+        if (c->readcopy != SSM_RC_NONE && c->dim_p != 64) return SSM_E_UNSUPPORTED;
+        if (c->readcopy == SSM_RC_FP8_ROW && c->dim_n % 16) return SSM_E_SHAPE;
+        if (c->readcopy == SSM_RC_FP4_B16 && c->dim_n % 32) return SSM_E_SHAPE;
+    } else {
+        if (c->groups != c->heads) return SSM_E_SHAPE;
+        if (c->readcopy != SSM_RC_NONE) return SSM_E_UNSUPPORTED;
+        if (!isfinite(c->gdn_scale)) return SSM_E_ARG;
+    }
+    return SSM_OK;
+}
+
+void compute_layout(const ssm_config* c, ssm_layout* L) {
+    memset(L, 0, sizeof(*L));
+    const uint64_t B = (uint64_t)c->batch, H = (uint64_t)c->heads, G = (uint64_t)c->groups;
+    const uint64_t P = (uint64_t)c->dim_p, N = (uint64_t)c->dim_n;
+    const uint64_t cap = (uint64_t)(c->window + c->max_draft - 1);
+    const uint64_t esz = c->in_dtype == SSM_IN_BF16 ? 2 : 4;
+    L->ring_cap = (int32_t)cap;
+    uint64_t off = 0;
+    auto take = [&](uint64_t bytes) { const uint64_t o = off; off = align_up(off + bytes); return o; };
+    L->off_ckpt = take(B * H * P * N * 4);
+    if (c->readcopy == SSM_RC_FP8_ROW) {
+        L->off_rc_codes = take(B * H * P * N);
+        L->off_rc_scale = take(B * H * P * 4);
+        L->off_rc_tscale = take(0);
+    } else if (c->readcopy == SSM_RC_FP4_B16) {
+        L->off_rc_codes = take(B * H * P * N / 2);
+        L->off_rc_scale = take(B * H * P * (N / 16));
+        L->off_rc_tscale = take(B * H * 4);
+    } else {
+        L->off_rc_codes = L->off_rc_scale = L->off_rc_tscale = take(0);
+    }
+    if (c->kind == SSM_MAMBA2) {
+        L->off_ring[0] = take(B * H * cap * P * esz);  // x
+        L->off_ring[1] = take(B * G * cap * N * esz);  // B
+        L->off_ring[2] = take(B * G * cap * N * esz);  // C
+        L->off_ring[3] = take(B * H * cap * 4);        // dt
+        L->off_ring[4] = take(0);
+    } else {
+        L->off_ring[0] = take(B * H * cap * N * esz);  // q  (dk)
+        L->off_ring[1] = take(B * H * cap * N * esz);  // k  (dk)
+        L->off_ring[2] = take(B * H * cap * P * esz);  // v  (dv)
+        L->off_ring[3] = take(B * H * cap * 4);        // beta
+        L->off_ring[4] = take(B * H * cap * 4);        // g
+    }
+    L->off_ptr = take(B * H * 2 * 4);
+    L->total_bytes = off;
+}
+
+ssm_status check_state(const ssm_state* st) {
+    if (!st || st->magic != kMagic || !st->mem) return SSM_E_STATE;
+    return SSM_OK;
+}
+
+ssm_status hip_status(hipError_t e) { return e == hipSuccess ? SSM_OK : SSM_E_HIP; }
+
+template <typename T> T* at(const ssm_state* st, uint64_t off) {
+    return reinterpret_cast<T*>(static_cast<char*>(st->mem) + off);
+}
+
+ssm::M2Args m2_args(const ssm_state* st) {
+    ssm::M2Args a;
+    memset(&a, 0, sizeof(a));
+    const ssm_layout& L = st->lay;
+    a.ckpt = at<float>(st, L.off_ckpt);
+    a.rc_codes = at<uint8_t>(st, L.off_rc_codes);
+    a.rc_scale = at<void>(st, L.off_rc_scale);
+    a.rc_tscale = at<float>(st, L.off_rc_tscale);
+    a.ring_x = at<void>(st, L.off_ring[0]);
+    a.ring_B = at<void>(st, L.off_ring[1]);
+    a.ring_C = at<void>(st, L.off_ring[2]);
+    a.ring_dt = at<float>(st, L.off_ring[3]);
+    a.ptr = at<int>(st, L.off_ptr);
+    a.A = st->A;
+    a.D = st->D;
+    a.batch = st->cfg.batch;
+    a.heads = st->cfg.heads;
+    a.groups = st->cfg.groups;
+    a.cap = L.ring_cap;
+    a.window = st->cfg.window;
+    return a;
+}
+
+ssm::GdnArgs gdn_args(const ssm_state* st) {
+    ssm::GdnArgs a;
+    memset(&a, 0, sizeof(a));
+    const ssm_layout& L = st->lay;
+    a.ckpt = at<float>(st, L.off_ckpt);
+    a.ring_q = at<void>(st, L.off_ring[0]);
+    a.ring_k = at<void>(st, L.off_ring[1]);
+    a.ring_v = at<void>(st, L.off_ring[2]);
+    a.ring_beta = at<float>(st, L.off_ring[3]);
+    a.ring_g = at<float>(st, L.off_ring[4]);
+    a.ptr = at<int>(st, L.off_ptr);
+    a.scale = st->cfg.gdn_scale;
+    a.batch = st->cfg.batch;
+    a.heads = st->cfg.heads;
+    a.cap = L.ring_cap;
+    a.window = st->cfg.window;
+    return a;
+}
+
+ssm_status check_inputs(const ssm_config& c, const void* in) {
+    if (!in) return SSM_E_ARG;
+    if (c.kind == SSM_MAMBA2) {
+        const ssm_m2_in* m = static_cast<const ssm_m2_in*>(in);
+        if (!m->x || !m->B || !m->C || !m->dt) return SSM_E_ARG;
+        if (!aligned16(m->x) || !aligned16(m->B) || !aligned16(m->C) || !aligned16(m->dt))
+            return SSM_E_ALIGN;
+    } else {
+        const ssm_gdn_in* g = static_cast<const ssm_gdn_in*>(in);
+        if (!g->q || !g->k || !g->v || !g->beta || !g->g) return SSM_E_ARG;
+        if (!aligned16(g->q) || !aligned16(g->k) || !aligned16(g->v) || !aligned16(g->beta) ||
+            !aligned16(g->g))
+            return SSM_E_ALIGN;
+    }
+    return SSM_OK;
+}
+
+// Host bounds on the committed counts after a fold of L entries from every sequence with
+// count >= L (the device predicate of SSM_FLUSH_IF_FULL).
+void fold_bounds(ssm_state* st) {
+    const int L = st->cfg.window;
+    if (st->count_hi < L) return;
+    if (st->count_lo >= L) {
+        st->count_lo -= L;
+        st->count_hi -= L;
+    } else {
+        st->count_lo = 0;
+        st->count_hi = (st->count_hi - L > L - 1) ? st->count_hi - L : L - 1;
+    }
+}
+
+ssm_status launch_flush(ssm_state* st, int mode_all, hipStream_t s) {
+    if (st->cfg.batch == 0) return SSM_OK;
+    hipError_t e;
+    if (st->cfg.kind == SSM_MAMBA2) {
+        ssm::M2Args a = m2_args(st);
+        e = ssm::m2_launch_flush(a, st->cfg.dim_p, st->cfg.dim_n, st->cfg.in_dtype, st->cfg.readcopy,
+                                 mode_all, 0, s);
+    } else {
+        ssm::GdnArgs a = gdn_args(st);
+        e = ssm::gdn_launch_flush(a, st->cfg.dim_p, st->cfg.dim_n, st->cfg.in_dtype, mode_all, s);
+    }
+    if (e == hipErrorNotSupported) return SSM_E_UNSUPPORTED;
+    return hip_status(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t ssm_abi_version(void) { return SSM_ABI_VERSION; }
+
+const char* ssm_status_string(ssm_status s) {
+    switch (s) {
+        case SSM_OK: return "ok";
+        case SSM_E_ARG: return "invalid argument";
+        case SSM_E_SHAPE: return "unsupported or inconsistent shape";
+        case SSM_E_ALIGN: return "device pointer not 16-byte aligned";
+        case SSM_E_STATE: return "invalid state for this call";
+        case SSM_E_CAPACITY: return "ring capacity exceeded";
+        case SSM_E_UNSUPPORTED: return "not supported by this build";
+        case SSM_E_HIP: return "HIP launch failed";
+        default: return "unknown status";
+    }
+}
+
+ssm_status ssm_layout_query(const ssm_config* cfg, ssm_layout* out) {
+    if (!out) return SSM_E_ARG;
+    const ssm_status s = check_config(cfg);
+    if (s != SSM_OK) return s;
+    compute_layout(cfg, out);
+    return SSM_OK;
+}
+
+ssm_status ssm_ckpt_init(ssm_state* st, const ssm_config* cfg, void* mem, uint64_t mem_bytes,
+                         const float* h0, const float* A, const float* D, void* stream) {
+    if (!st) return SSM_E_ARG;
+    ssm_status s = check_config(cfg);
+    if (s != SSM_OK) return s;
+    ssm_layout lay;
+    compute_layout(cfg, &lay);
+    if (!mem || mem_bytes < lay.total_bytes) return SSM_E_ARG;
+    if (((uintptr_t)mem & (kAlign - 1)) != 0) return SSM_E_ALIGN;
+    if (h0 && !aligned16(h0)) return SSM_E_ALIGN;
+    if (cfg->kind == SSM_MAMBA2) {
+        if (!A || !D) return SSM_E_ARG;
+        if (!aligned16(A) || !aligned16(D)) return SSM_E_ALIGN;
+    }
+    memset(st, 0, sizeof(*st));
+    st->cfg = *cfg;
+    st->lay = lay;
+    st->mem = mem;
+    st->A = cfg->kind == SSM_MAMBA2 ? A : nullptr;
+    st->D = cfg->kind == SSM_MAMBA2 ? D : nullptr;
+    st->magic = kMagic;
+    const hipStream_t hs = as_stream(stream);
+    const long nheads = (long)cfg->batch * cfg->heads;
+    if (nheads == 0) return SSM_OK;
+    float* ck = at<float>(st, lay.off_ckpt);
+    hipError_t e;
+    if (h0) {
+        e = ssm::launch_pack(h0, ck, nheads, cfg->dim_p, cfg->dim_n, 0, hs);
+    } else {
+        e = ssm::launch_fill_i32(reinterpret_cast<int*>(ck), 0, nheads * cfg->dim_p * cfg->dim_n, hs);
+    }
+    if (e != hipSuccess) return SSM_E_HIP;
+    e = ssm::launch_fill_i32(at<int>(st, lay.off_ptr), 0, nheads * 2, hs);
+    if (e != hipSuccess) return SSM_E_HIP;
+    if (cfg->kind == SSM_MAMBA2 && cfg->readcopy != SSM_RC_NONE) {
+        ssm::M2Args a = m2_args(st);
+        e = ssm::m2_launch_flush(a, cfg->dim_p, cfg->dim_n, cfg->in_dtype, cfg->readcopy, 0, 1, hs);
+        if (e != hipSuccess) return SSM_E_HIP;
+    }
+    return SSM_OK;
+}
+
+ssm_status ssm_replay_decode(ssm_state* st, const void* in, float* y, void* stream) {
+    ssm_status s = check_state(st);
+    if (s != SSM_OK) return s;
+    if (st->pending) return SSM_E_STATE;
+    if (!y) return SSM_E_ARG;
+    if (!aligned16(y)) return SSM_E_ALIGN;
+    s = check_inputs(st->cfg, in);
+    if (s != SSM_OK) return s;
+    if (st->count_hi + 1 > st->lay.ring_cap) return SSM_E_CAPACITY;
+    const hipStream_t hs = as_stream(stream);
+    hipError_t e = hipSuccess;
+    if (st->cfg.batch == 0) {
+        // no sequences: nothing to launch, the host bounds still advance
+    } else if (st->cfg.kind == SSM_MAMBA2) {
+        ssm::M2Args a = m2_args(st);
+        const ssm_m2_in* m = static_cast<const ssm_m2_in*>(in);
+        a.in_x = m->x; a.in_B = m->B; a.in_C = m->C; a.in_dt = m->dt;
+        a.y = y;
+        a.ntok = 1;
+        e = ssm::m2_launch_replay(a, st->cfg.dim_p, st->cfg.dim_n, st->cfg.in_dtype,
+                                  st->cfg.readcopy, false, st->count_hi + 1, hs);
+    } else {
+        ssm::GdnArgs a = gdn_args(st);
+        const ssm_gdn_in* g = static_cast<const ssm_gdn_in*>(in);
+        a.in_q = g->q; a.in_k = g->k; a.in_v = g->v; a.in_beta = g->beta; a.in_g = g->g;
+        a.o = y;
+        a.ntok = 1;
+        e = ssm::gdn_launch_replay(a, st->cfg.dim_p, st->cfg.dim_n, st->cfg.in_dtype, hs);
+    }
+    if (e == hipErrorNotSupported) return SSM_E_UNSUPPORTED;
+    if (e != hipSuccess) return SSM_E_HIP;
+    st->count_lo += 1;
+    st->count_hi += 1;
+    if (st->count_hi >= st->cfg.window) {
+        s = launch_flush(st, 0, hs);
+        if (s != SSM_OK) return s;
+        fold_bounds(st);
+    }
+    return SSM_OK;
+}
+
+ssm_status ssm_flush(ssm_state* st, int32_t mode, void* stream) {
+    ssm_status s = check_state(st);
+    if (s != SSM_OK) return s;
+    if (mode != SSM_FLUSH_IF_FULL && mode != SSM_FLUSH_ALL) return SSM_E_ARG;
+    if (st->pending) return SSM_E_STATE;
+    const hipStream_t hs = as_stream(stream);
+    if (mode == SSM_FLUSH_IF_FULL) {
+        if (st->count_hi < st->cfg.window) return SSM_OK;  // no sequence can be full
+        s = launch_flush(st, 0, hs);
+        if (s == SSM_OK) fold_bounds(st);
+        return s;
+    }
+    if (st->count_hi == 0) return SSM_OK;
+    s = launch_flush(st, 1, hs);
+    if (s == SSM_OK) st->count_lo = st->count_hi = 0;
+    return s;
+}
+
+ssm_status ssm_spec_append(ssm_state* st, int32_t ndraft, const void* in, float* y, void* stream) {
+    ssm_status s = check_state(st);
+    if (s != SSM_OK) return s;
+    if (st->pending) return SSM_E_STATE;
+    if (st->cfg.kind != SSM_MAMBA2) return SSM_E_UNSUPPORTED;
+    if (ndraft < 1) return SSM_E_ARG;
+    if (ndraft > st->cfg.max_draft) return SSM_E_CAPACITY;
+    if (!y) return SSM_E_ARG;
+    if (!aligned16(y)) return SSM_E_ALIGN;
+    s = check_inputs(st->cfg, in);
+    if (s != SSM_OK) return s;
+    if (st->count_hi + ndraft > st->lay.ring_cap) return SSM_E_CAPACITY;
+    if (st->cfg.batch > 0) {
+        ssm::M2Args a = m2_args(st);
+        const ssm_m2_in* m = static_cast<const ssm_m2_in*>(in);
+        a.in_x = m->x; a.in_B = m->B; a.in_C = m->C; a.in_dt = m->dt;
+        a.y = y;
+        a.ntok = ndraft;
+        const hipError_t e = ssm::m2_launch_replay(a, st->cfg.dim_p, st->cfg.dim_n,
+                                                   st->cfg.in_dtype, st->cfg.readcopy, true,
+                                                   st->count_hi + ndraft, as_stream(stream));
+        if (e != hipSuccess) return SSM_E_HIP;
+    }
+    st->pending = ndraft;
+    return SSM_OK;
+}
+
+ssm_status ssm_spec_rollback(ssm_state* st, const int32_t* n_accept, void* stream) {
+    ssm_status s = check_state(st);
+    if (s != SSM_OK) return s;
+    if (!st->pending) return SSM_E_STATE;
+    if (!n_accept) return SSM_E_ARG;
+    if (((uintptr_t)n_accept & 3u) != 0) return SSM_E_ALIGN;
+    const hipStream_t hs = as_stream(stream);
+    const hipError_t e = ssm::launch_commit(at<int>(st, st->lay.off_ptr), n_accept, st->cfg.batch,
+                                            st->cfg.heads, st->pending, hs);
+    if (e != hipSuccess) return SSM_E_HIP;
+    st->count_hi += st->pending;
+    st->pending = 0;
+    // a flush fires whenever a sequence's committed count reaches L
+    if (st->count_hi >= st->cfg.window) {
+        s = launch_flush(st, 0, hs);
+        if (s != SSM_OK) return s;
+        fold_bounds(st);
+    }
+    return SSM_OK;
+}
+
+ssm_status ssm_ckpt_export(const ssm_state* st, float* h_out, void* stream) {
+    ssm_status s = check_state(st);
+    if (s != SSM_OK) return s;
+    if (!h_out) return SSM_E_ARG;
+    if (!aligned16(h_out)) return SSM_E_ALIGN;
+    const long nheads = (long)st->cfg.batch * st->cfg.heads;
+    return hip_status(ssm::launch_pack(at<float>(st, st->lay.off_ckpt), h_out, nheads,
+                                       st->cfg.dim_p, st->cfg.dim_n, 1, as_stream(stream)));
+}
+
+ssm_status ssm_conventional_step(const ssm_config* cfg, float* h, const void* in, const float* A,
+                                 const float* D, float* y, void* stream) {
+    ssm_config c;
+    if (!cfg) return SSM_E_ARG;
+    c = *cfg;
+    c.readcopy = SSM_RC_NONE;  // the conventional step reads and writes the fp32 state itself
+    ssm_status s = check_config(&c);
+    if (s != SSM_OK) return s;
+    if (!h || !y) return SSM_E_ARG;
+    if (!aligned16(h) || !aligned16(y)) return SSM_E_ALIGN;
+    s = check_inputs(c, in);
+    if (s != SSM_OK) return s;
+    if (c.batch == 0) return SSM_OK;
+    hipError_t e;
+    if (c.kind == SSM_MAMBA2) {
+        if (!A || !D) return SSM_E_ARG;
+        if (!aligned16(A) || !aligned16(D)) return SSM_E_ALIGN;
+        const ssm_m2_in* m = static_cast<const ssm_m2_in*>(in);
+        ssm::M2ConvArgs a{h, m->x, m->B, m->C, m->dt, A, D, y, c.batch, c.heads, c.groups};
+        e = ssm::m2_launch_conv(a, c.dim_p, c.dim_n, c.in_dtype, as_stream(stream));
+    } else {
+        const ssm_gdn_in* g = static_cast<const ssm_gdn_in*>(in);
+        ssm::GdnConvArgs a{h, g->q, g->k, g->v, g->beta, g->g, y, c.gdn_scale, c.batch, c.heads};
+        e = ssm::gdn_launch_conv(a, c.dim_p, c.dim_n, c.in_dtype, as_stream(stream));
+    }
+    if (e == hipErrorNotSupported) return SSM_E_UNSUPPORTED;
+    return hip_status(e);
+}
+
+static ssm_status pack_common(const ssm_config* cfg, const float* src, float* dst, int unpack,
+                              void* stream) {
+    ssm_config c;
+    if (!cfg) return SSM_E_ARG;
+    c = *cfg;
+    c.readcopy = SSM_RC_NONE;
+    const ssm_status s = check_config(&c);
+    if (s != SSM_OK) return s;
+    if (!src || !dst) return SSM_E_ARG;
+    if (!aligned16(src) || !aligned16(dst)) return SSM_E_ALIGN;
+    return hip_status(ssm::launch_pack(src, dst, (long)c.batch * c.heads, c.dim_p, c.dim_n, unpack,
+                                       as_stream(stream)));
+}
+
+ssm_status ssm_tiles_pack(const ssm_config* cfg, const float* natural, float* tiles, void* stream) {
+    return pack_common(cfg, natural, tiles, 0, stream);
+}
+
+ssm_status ssm_tiles_unpack(const ssm_config* cfg, const float* tiles, float* natural,
+                            void* stream) {
+    return pack_common(cfg, tiles, natural, 1, stream);
+}
+
+ssm_status ssm_debug_codec(int32_t op, const void* in, void* out, int64_t n, void* stream) {
+    if (op < 0 || op > 3 || n < 0) return SSM_E_ARG;
+    if (n > 0 && (!in || !out)) return SSM_E_ARG;
+    return hip_status(ssm::launch_codec(op, in, out, (long)n, as_stream(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,207 @@
+// ssm_device.hpp -- device helpers shared by the gfx950 kernels of the ReplaySSM library.
+//
+// Wave64 throughout (CDNA4). Nothing here depends on a particular layer type.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ssm {
+
+typedef uint16_t bf16_t;  // storage of bfloat16 inputs (upper half of an fp32)
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+
+// Streaming (non-temporal) 16-byte accesses for data touched once per launch.
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ float4 ld_stream(const float4* p) {
+    const f32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p));
+    return make_float4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint4 ld_stream(const uint4* p) {
+    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void st_stream(float4 v, float4* p) {
+    const f32x4_t t = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(t, reinterpret_cast<f32x4_t*>(p));
+}
+
+// Unpack one 16-byte unit of T (fp32 or bf16 bits) into floats.
+template <typename T> struct Unit;
+template <> struct Unit<float> {
+    static constexpr int kElems = 4;
+    __device__ __forceinline__ static void unpack(uint4 u, float* d) {
+        d[0] = __uint_as_float(u.x); d[1] = __uint_as_float(u.y);
+        d[2] = __uint_as_float(u.z); d[3] = __uint_as_float(u.w);
+    }
+};
+template <> struct Unit<bf16_t> {
+    static constexpr int kElems = 8;
+    __device__ __forceinline__ static void unpack(uint4 u, float* d) {
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            d[2 * i] = __uint_as_float(w[i] << 16);
+            d[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+        }
+    }
+};
+
+template <typename T> __device__ __forceinline__ float to_f32(T v);
+template <> __device__ __forceinline__ float to_f32<float>(float v) { return v; }
+template <> __device__ __forceinline__ float to_f32<bf16_t>(bf16_t v) { return bf16_to_f32(v); }
+
+// Load E contiguous elements of T starting at src (aligned to the access width) as floats, using
+// the widest access the byte count allows.
+template <typename T, int E>
+__device__ __forceinline__ void load_row(const T* __restrict__ src, float (&d)[E]) {
+    constexpr int kBytes = E * (int)sizeof(T);
+    if constexpr (kBytes % 16 == 0) {
+        const uint4* s = reinterpret_cast<const uint4*>(src);
+#pragma unroll
+        for (int u = 0; u < kBytes / 16; ++u) Unit<T>::unpack(s[u], d + u * Unit<T>::kElems);
+    } else {
+#pragma unroll
+        for (int i = 0; i < E; ++i) d[i] = to_f32<T>(src[i]);
+    }
+}
+
+// Load E contiguous elements of T as raw bits (no conversion) with the widest access possible.
+template <typename T, int E>
+__device__ __forceinline__ void load_raw(const T* __restrict__ src, T (&d)[E]) {
+    constexpr int kBytes = E * (int)sizeof(T);
+    if constexpr (kBytes % 16 == 0) {
+#pragma unroll
+        for (int u = 0; u < kBytes / 16; ++u) {
+            const uint4 t = reinterpret_cast<const uint4*>(src)[u];
+            __builtin_memcpy(&d[u * (16 / sizeof(T))], &t, 16);
+        }
+    } else if constexpr (kBytes % 8 == 0) {
+#pragma unroll
+        for (int u = 0; u < kBytes / 8; ++u) {
+            const uint2 t = reinterpret_cast<const uint2*>(src)[u];
+            __builtin_memcpy(&d[u * (8 / sizeof(T))], &t, 8);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < E; ++i) d[i] = src[i];
+    }
+}
+
+// Store E raw elements of T with the widest access possible.
+template <typename T, int E>
+__device__ __forceinline__ void store_raw(T* __restrict__ dst, const T (&d)[E]) {
+    constexpr int kBytes = E * (int)sizeof(T);
+    if constexpr (kBytes % 16 == 0) {
+#pragma unroll
+        for (int u = 0; u < kBytes / 16; ++u) {
+            uint4 t;
+            __builtin_memcpy(&t, &d[u * (16 / sizeof(T))], 16);
+            reinterpret_cast<uint4*>(dst)[u] = t;
+        }
+    } else if constexpr (kBytes % 8 == 0) {
+#pragma unroll
+        for (int u = 0; u < kBytes / 8; ++u) {
+            uint2 t;
+            __builtin_memcpy(&t, &d[u * (8 / sizeof(T))], 8);
+            reinterpret_cast<uint2*>(dst)[u] = t;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < E; ++i) dst[i] = d[i];
+    }
+}
+
+// Copy E contiguous elements of T (raw bits) from src to dst with the widest access possible.
+template <typename T, int E>
+__device__ __forceinline__ void copy_row(T* __restrict__ dst, const T* __restrict__ src) {
+    constexpr int kBytes = E * (int)sizeof(T);
+    if constexpr (kBytes % 16 == 0) {
+#pragma unroll
+        for (int u = 0; u < kBytes / 16; ++u)
+            reinterpret_cast<uint4*>(dst)[u] = reinterpret_cast<const uint4*>(src)[u];
+    } else {
+#pragma unroll
+        for (int i = 0; i < E; ++i) dst[i] = src[i];
+    }
+}
+
+// Wave-local ordering point for LDS written by some lanes and read by others of the same wave:
+// the LDS unit executes one wave's operations in order, so a compiler-level barrier with
+// wavefront-scope fences is enough.
+__device__ __forceinline__ void wave_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ float shfl_xor(float v, int m) { return __shfl_xor(v, m, 64); }
+
+// Sum over lanes that differ only in the bits of `lo..hi` (masks lo, 2lo, ..., hi).
+template <int LO, int HI>
+__device__ __forceinline__ float xor_reduce_sum(float v) {
+#pragma unroll
+    for (int m = LO; m <= HI; m <<= 1) v += shfl_xor(v, m);
+    return v;
+}
+template <int LO, int HI>
+__device__ __forceinline__ float xor_reduce_max(float v) {
+#pragma unroll
+    for (int m = LO; m <= HI; m <<= 1) v = fmaxf(v, shfl_xor(v, m));
+    return v;
+}
+
+__device__ __forceinline__ float readlane(float v, int lane) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// ---------------------------------------------------------------------------------------------
+// OCP low-precision codecs, written from the format definitions (OCP OFP8 E4M3: bias 7, three
+// mantissa bits, max 448, no infinity; OCP MX E2M1: bias 1, one mantissa bit, max 6).
+// Encoding: round to nearest, ties to even, saturating at the largest finite magnitude; the code's
+// sign bit is the sign bit of the fp32 input.
+// ---------------------------------------------------------------------------------------------
+
+// Magnitude code of |v| on a grid with MB mantissa bits, minimum normal exponent EMIN and largest
+// magnitude code MAXC. |v| * 2^k scalings are exact, and rintf rounds half to even.
+template <int MB, int EMIN, int MAXC>
+__device__ __forceinline__ uint32_t encode_mag(float a) {
+    // a >= 0, finite. Saturate first: every value above the largest finite rounds to it.
+    const float amax = __uint_as_float(((uint32_t)(((MAXC >> MB) + EMIN - 1) + 127) << 23) |
+                                       ((uint32_t)(MAXC & ((1 << MB) - 1)) << (23 - MB)));
+    if (a >= amax) return MAXC;
+    int e = (int)((__float_as_uint(a) >> 23) & 0xff) - 127;  // floor(log2 a) for normal a
+    if (e < EMIN) e = EMIN;                                  // subnormal range: quantum 2^(EMIN-MB)
+    const float q = ldexpf(a, MB - e);                       // a / 2^(e-MB), exact
+    const uint32_t n = (uint32_t)rintf(q);                   // in [0, 2^(MB+1)]
+    // code = (biased exponent << MB) + mantissa; for the subnormal range the biased exponent is 0
+    // and n < 2^MB, and n == 2^(MB+1) rolls over into the next binade correctly.
+    const uint32_t be = (uint32_t)(e - EMIN);  // 0 for the lowest binade (normal or subnormal)
+    return (be << MB) + n;
+}
+
+__device__ __forceinline__ uint32_t e4m3_encode(float v) {
+    const uint32_t s = (__float_as_uint(v) >> 31) << 7;
+    return s | encode_mag<3, -6, 0x7E>(fabsf(v));
+}
+__device__ __forceinline__ uint32_t e2m1_encode(float v) {
+    const uint32_t s = (__float_as_uint(v) >> 31) << 3;
+    return s | encode_mag<1, 0, 0x7>(fabsf(v));
+}
+
+// Software decode of an E4M3 code (no NaN codes are ever written).
+__device__ __forceinline__ float e4m3_decode(uint32_t c) {
+    const uint32_t e = (c >> 3) & 0xF, m = c & 7;
+    const float mag = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0.001953125f;
+    return (c & 0x80) ? -mag : mag;
+}
+// Software decode of an E2M1 code.
+__device__ __forceinline__ float e2m1_decode(uint32_t c) {
+    const uint32_t twice = (0xC8643210u >> ((c & 7) * 4)) & 0xF;  // 2*|value|: 0,1,2,3,4,6,8,12
+    const float mag = (float)twice * 0.5f;
+    return (c & 8) ? -mag : mag;
+}
+
+}  // namespace ssm

@@ -1,0 +1,94 @@
+// ssm_kernels.hpp -- kernel argument blocks and launcher entry points (internal to the library).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ssm {
+
+// Everything a Mamba-2 replay / verify / flush launch touches. Device pointers into one state's
+// memory (see the layout in ssm_replay.h) plus this call's inputs and outputs.
+struct M2Args {
+    float* ckpt;        // fp32 checkpoint tiles
+    uint8_t* rc_codes;  // read-copy codes
+    void* rc_scale;     // fp8: fp32 row scales; fp4: E4M3 block-scale codes
+    float* rc_tscale;   // fp4: fp32 tile scales
+    void* ring_x;
+    void* ring_B;
+    void* ring_C;
+    float* ring_dt;
+    int* ptr;           // int32 [batch][heads][2] = {start, count}
+    const void* in_x;   // this call's tokens, [batch][ntok][...]
+    const void* in_B;
+    const void* in_C;
+    const float* in_dt;
+    const float* A;
+    const float* D;
+    float* y;           // [batch][ntok][H][P]
+    int batch, heads, groups, cap, ntok, window;
+};
+
+struct M2ConvArgs {
+    float* h;  // tiles, updated in place
+    const void* in_x;
+    const void* in_B;
+    const void* in_C;
+    const float* in_dt;
+    const float* A;
+    const float* D;
+    float* y;
+    int batch, heads, groups;
+};
+
+// Gated DeltaNet launches.
+struct GdnArgs {
+    float* ckpt;
+    void* ring_q;
+    void* ring_k;
+    void* ring_v;
+    float* ring_beta;
+    float* ring_g;
+    int* ptr;
+    const void* in_q;
+    const void* in_k;
+    const void* in_v;
+    const float* in_beta;
+    const float* in_g;
+    float* o;
+    float scale;
+    int batch, heads, cap, ntok, window;
+};
+
+struct GdnConvArgs {
+    float* S;
+    const void* in_q;
+    const void* in_k;
+    const void* in_v;
+    const float* in_beta;
+    const float* in_g;
+    float* o;
+    float scale;
+    int batch, heads;
+};
+
+// maxe: upper bound on count + ntok over all sequences (<= 64).
+hipError_t m2_launch_replay(const M2Args& a, int P, int N, int bf16, int rc, bool spec, int maxe,
+                            hipStream_t s);
+hipError_t m2_launch_flush(const M2Args& a, int P, int N, int bf16, int rc, int mode_all,
+                           int rewrite_only, hipStream_t s);
+hipError_t m2_launch_conv(const M2ConvArgs& a, int P, int N, int bf16, hipStream_t s);
+
+hipError_t gdn_launch_replay(const GdnArgs& a, int dv, int dk, int bf16, hipStream_t s);
+hipError_t gdn_launch_flush(const GdnArgs& a, int dv, int dk, int bf16, int mode_all,
+                            hipStream_t s);
+hipError_t gdn_launch_conv(const GdnConvArgs& a, int dv, int dk, int bf16, hipStream_t s);
+
+// Pointer commit after a speculative round: count += min(n_accept[b], pending) for every head.
+hipError_t launch_commit(int* ptr, const int32_t* n_accept, int batch, int heads, int pending,
+                         hipStream_t s);
+hipError_t launch_fill_i32(int* p, int value, long n, hipStream_t s);
+// Natural [heads][P][N] -> quad-interleaved tiles (unpack = 0) or back (unpack = 1).
+hipError_t launch_pack(const float* src, float* dst, long nheads, int P, int N, int unpack,
+                       hipStream_t s);
+hipError_t launch_codec(int op, const void* in, void* out, long n, hipStream_t s);
+
+}  // namespace ssm

@@ -1,0 +1,203 @@
+"""C ABI checks that need no GPU: the library loads, exports every entry point the header
+declares, computes layouts, and rejects bad arguments on the host before any HIP call.
+
+States with batch = 0 are fully valid and every call on them is a no-op, so the state-machine
+errors (pending drafts, capacity, rollback without drafts) can be driven without a device; fake
+device addresses are never dereferenced because validation fails (or there is no work) first.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ssm_replay.h")
+
+bd = pytest.importorskip("ssm_decode_state_amd.binding",
+                         reason="libssm_replay.so not built (run __graft_entry__.build())")
+
+FAKE = 0x7F0000000000  # 256-byte aligned, never dereferenced
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ssm_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    names = header_functions()
+    assert len(names) >= 12
+    lib = ctypes.CDLL(bd._LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(bd.EXPORTS)
+
+
+def test_abi_version_and_status_strings():
+    assert bd.ssm_abi_version() == 1
+    for s in range(-7, 1):
+        assert bd.ssm_status_string(s) not in ("", "unknown status")
+    assert bd.ssm_status_string(-99) == "unknown status"
+
+
+def cfg(**kw):
+    base = dict(kind=bd.SSM_MAMBA2, batch=256, heads=128, groups=128, dim_p=64, dim_n=128,
+                window=16, max_draft=1, in_dtype=bd.SSM_IN_BF16, readcopy=bd.SSM_RC_NONE)
+    base.update(kw)
+    return bd.make_config(**base)
+
+
+def test_layout_serving_shape():
+    lay = bd.ssm_layout_query(cfg())
+    assert lay.ring_cap == 16
+    assert lay.off_ckpt == 0
+    ck = 256 * 128 * 64 * 128 * 4
+    assert lay.off_ring[0] >= ck
+    offs = [lay.off_ckpt, lay.off_rc_codes, lay.off_ring[0], lay.off_ring[1], lay.off_ring[2],
+            lay.off_ring[3], lay.off_ptr]
+    assert all(o % 256 == 0 for o in offs)
+    assert offs == sorted(offs)
+    assert lay.total_bytes >= lay.off_ptr + 256 * 128 * 8
+    spec = bd.ssm_layout_query(cfg(max_draft=4))
+    assert spec.ring_cap == 19
+
+
+def test_layout_read_copies():
+    f8 = bd.ssm_layout_query(cfg(readcopy=bd.SSM_RC_FP8_ROW))
+    assert f8.off_rc_scale - f8.off_rc_codes == 256 * 128 * 64 * 128
+    f4 = bd.ssm_layout_query(cfg(readcopy=bd.SSM_RC_FP4_B16))
+    assert f4.off_rc_scale - f4.off_rc_codes == 256 * 128 * 64 * 64
+    assert f4.off_rc_tscale - f4.off_rc_scale == 256 * 128 * 64 * 8
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(kind=5), bd.SSM_E_ARG),
+    (dict(in_dtype=7), bd.SSM_E_ARG),
+    (dict(readcopy=3), bd.SSM_E_ARG),
+    (dict(heads=6, groups=4), bd.SSM_E_SHAPE),
+    (dict(dim_p=48), bd.SSM_E_SHAPE),
+    (dict(dim_p=128), bd.SSM_E_SHAPE),
+    (dict(dim_n=8), bd.SSM_E_SHAPE),
+    (dict(window=0), bd.SSM_E_SHAPE),
+    (dict(window=33), bd.SSM_E_SHAPE),
+    (dict(max_draft=0), bd.SSM_E_SHAPE),
+    (dict(max_draft=9, window=16), bd.SSM_E_SHAPE),
+    (dict(max_draft=5, window=4), bd.SSM_E_SHAPE),
+    (dict(batch=-1), bd.SSM_E_SHAPE),
+    (dict(readcopy=bd.SSM_RC_FP8_ROW, dim_p=32, dim_n=64), bd.SSM_E_UNSUPPORTED),
+    (dict(kind=bd.SSM_GDN, groups=64), bd.SSM_E_SHAPE),
+    (dict(kind=bd.SSM_GDN, readcopy=bd.SSM_RC_FP8_ROW), bd.SSM_E_UNSUPPORTED),
+])
+def test_bad_configs_rejected(kw, status):
+    with pytest.raises(bd.SSMError) as ei:
+        bd.ssm_layout_query(cfg(**kw))
+    assert ei.value.status == status
+
+
+def raw(fn, *args):
+    return getattr(bd._lib, fn)(*args)
+
+
+def empty_state(**kw):
+    c = cfg(batch=0, **kw)
+    st = bd.ssm_state()
+    s = raw("ssm_ckpt_init", ctypes.byref(st), ctypes.byref(c), ctypes.c_void_p(FAKE),
+            1 << 40, None, ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE), None)
+    assert s == bd.SSM_OK
+    return st
+
+
+def m2_in(addr=FAKE):
+    return bd.ssm_m2_in(addr, addr, addr, addr)
+
+
+def test_init_validation():
+    c = cfg()
+    st = bd.ssm_state()
+    v = ctypes.c_void_p
+    assert raw("ssm_ckpt_init", None, ctypes.byref(c), v(FAKE), 1 << 40, None, v(FAKE),
+               v(FAKE), None) == bd.SSM_E_ARG
+    assert raw("ssm_ckpt_init", ctypes.byref(st), ctypes.byref(c), None, 1 << 40, None, v(FAKE),
+               v(FAKE), None) == bd.SSM_E_ARG
+    assert raw("ssm_ckpt_init", ctypes.byref(st), ctypes.byref(c), v(FAKE), 1024, None, v(FAKE),
+               v(FAKE), None) == bd.SSM_E_ARG  # too small
+    assert raw("ssm_ckpt_init", ctypes.byref(st), ctypes.byref(c), v(FAKE + 16), 1 << 40, None,
+               v(FAKE), v(FAKE), None) == bd.SSM_E_ALIGN
+    assert raw("ssm_ckpt_init", ctypes.byref(st), ctypes.byref(c), v(FAKE), 1 << 40, v(FAKE + 4),
+               v(FAKE), v(FAKE), None) == bd.SSM_E_ALIGN
+    assert raw("ssm_ckpt_init", ctypes.byref(st), ctypes.byref(c), v(FAKE), 1 << 40, None,
+               None, v(FAKE), None) == bd.SSM_E_ARG  # Mamba-2 needs A and D
+
+
+def test_bad_magic_rejected():
+    st = bd.ssm_state()
+    y = ctypes.c_void_p(FAKE)
+    assert raw("ssm_replay_decode", ctypes.byref(st), ctypes.byref(m2_in()), y, None) == bd.SSM_E_STATE
+    assert raw("ssm_flush", ctypes.byref(st), 0, None) == bd.SSM_E_STATE
+    assert raw("ssm_spec_rollback", ctypes.byref(st), y, None) == bd.SSM_E_STATE
+
+
+def test_state_machine_errors_without_device():
+    st = empty_state(max_draft=4)
+    y = ctypes.c_void_p(FAKE)
+    assert st.count_hi == 0 and st.pending == 0
+    # rollback without drafts
+    assert raw("ssm_spec_rollback", ctypes.byref(st), y, None) == bd.SSM_E_STATE
+    # too many drafts
+    assert raw("ssm_spec_append", ctypes.byref(st), 5, ctypes.byref(m2_in()), y, None) == \
+        bd.SSM_E_CAPACITY
+    assert raw("ssm_spec_append", ctypes.byref(st), 0, ctypes.byref(m2_in()), y, None) == bd.SSM_E_ARG
+    # misaligned inputs / outputs
+    assert raw("ssm_spec_append", ctypes.byref(st), 2, ctypes.byref(m2_in(FAKE + 2)), y, None) == \
+        bd.SSM_E_ALIGN
+    assert raw("ssm_spec_append", ctypes.byref(st), 2, ctypes.byref(m2_in()),
+               ctypes.c_void_p(FAKE + 8), None) == bd.SSM_E_ALIGN
+    assert raw("ssm_spec_append", ctypes.byref(st), 2, None, y, None) == bd.SSM_E_ARG
+    # a valid append on an empty batch: drafts now pending
+    assert raw("ssm_spec_append", ctypes.byref(st), 3, ctypes.byref(m2_in()), y, None) == bd.SSM_OK
+    assert st.pending == 3
+    assert raw("ssm_replay_decode", ctypes.byref(st), ctypes.byref(m2_in()), y, None) == bd.SSM_E_STATE
+    assert raw("ssm_flush", ctypes.byref(st), 0, None) == bd.SSM_E_STATE
+    assert raw("ssm_spec_append", ctypes.byref(st), 1, ctypes.byref(m2_in()), y, None) == bd.SSM_E_STATE
+    assert raw("ssm_flush", ctypes.byref(st), 7, None) == bd.SSM_E_ARG
+    assert raw("ssm_spec_rollback", ctypes.byref(st), None, None) == bd.SSM_E_ARG
+    assert raw("ssm_spec_rollback", ctypes.byref(st), y, None) == bd.SSM_OK
+    assert st.pending == 0 and st.count_hi == 3
+    # decodes advance the host bound; the L-th folds
+    for _ in range(12):
+        assert raw("ssm_replay_decode", ctypes.byref(st), ctypes.byref(m2_in()), y, None) == bd.SSM_OK
+    assert st.count_hi == 15
+    assert raw("ssm_replay_decode", ctypes.byref(st), ctypes.byref(m2_in()), y, None) == bd.SSM_OK
+    assert (st.count_lo, st.count_hi) == (0, 15)  # lo < L <= hi before the fold
+    assert raw("ssm_flush", ctypes.byref(st), bd.SSM_FLUSH_ALL, None) == bd.SSM_OK
+    assert (st.count_lo, st.count_hi) == (0, 0)
+
+
+def test_capacity_bound_after_rollback():
+    st = empty_state(max_draft=4, window=4)  # cap = 7
+    y = ctypes.c_void_p(FAKE)
+    for _ in range(3):
+        assert raw("ssm_replay_decode", ctypes.byref(st), ctypes.byref(m2_in()), y, None) == bd.SSM_OK
+    assert (st.count_lo, st.count_hi) == (3, 3)
+    assert raw("ssm_spec_append", ctypes.byref(st), 4, ctypes.byref(m2_in()), y, None) == bd.SSM_OK
+    assert raw("ssm_spec_rollback", ctypes.byref(st), y, None) == bd.SSM_OK
+    # counts in [3, 7] before the automatic fold -> [0, 3] after it
+    assert (st.count_lo, st.count_hi) == (0, 3)
+
+
+def test_conventional_and_pack_validation():
+    c = cfg()
+    v = ctypes.c_void_p
+    assert raw("ssm_conventional_step", ctypes.byref(c), None, ctypes.byref(m2_in()), v(FAKE),
+               v(FAKE), v(FAKE), None) == bd.SSM_E_ARG
+    assert raw("ssm_conventional_step", ctypes.byref(c), v(FAKE + 4), ctypes.byref(m2_in()),
+               v(FAKE), v(FAKE), v(FAKE), None) == bd.SSM_E_ALIGN
+    assert raw("ssm_conventional_step", ctypes.byref(c), v(FAKE), ctypes.byref(m2_in()), None,
+               v(FAKE), v(FAKE), None) == bd.SSM_E_ARG
+    bad = cfg(dim_p=48)
+    assert raw("ssm_tiles_pack", ctypes.byref(bad), v(FAKE), v(FAKE), None) == bd.SSM_E_SHAPE
+    assert raw("ssm_tiles_unpack", ctypes.byref(c), None, v(FAKE), None) == bd.SSM_E_ARG
+    assert raw("ssm_debug_codec", 9, v(FAKE), v(FAKE), 4, None) == bd.SSM_E_ARG
+    assert raw("ssm_debug_codec", 0, None, None, 0, None) == bd.SSM_OK  # empty: nothing to do
