@@ -137,6 +137,44 @@ def token_inputs(shape: Shape, seed: int, tag: str, index: int, ntok: int = 1,
             "beta": beta.to(torch.float32), "g": gl.to(torch.float32)}
 
 
+def token_inputs_device(shape: Shape, seed: int, tag: str, index: int, ntok: int = 1,
+                        layer: int = 0, device="cuda") -> Dict[str, torch.Tensor]:
+    """Same distributions as token_inputs, drawn on the device with a seeded device generator
+    (used where only throughput matters and hundreds of steps of inputs must be resident in HBM
+    quickly; the values differ from the host stream, so parity tests use token_inputs)."""
+    g = torch.Generator(device=device).manual_seed(derive_seed(seed, tag, layer, index, "dev"))
+    bsz, H = shape.batch, shape.heads
+    dt_ = shape.in_dtype
+    kw = dict(generator=g, device=device)
+    if shape.kind == MAMBA2:
+        G, P, N = shape.groups, shape.dim_p, shape.dim_n
+        sN = math.sqrt(1.0 / N)
+        x = torch.randn(bsz, ntok, H, P, **kw).to(dt_)
+        Bm = (torch.randn(bsz, ntok, G, N, **kw) * sN).to(dt_)
+        Cm = (torch.randn(bsz, ntok, G, N, **kw) * sN).to(dt_)
+        z = torch.randn(bsz, ntok, H, dtype=torch.float64, **kw) * math.sqrt(0.5) - 2.0
+        return {"x": x, "B": Bm, "C": Cm, "dt": _softplus64(z).to(torch.float32)}
+    dv, dk = shape.dim_p, shape.dim_n
+    q = torch.randn(bsz, ntok, H, dk, dtype=torch.float64, **kw)
+    k = torch.randn(bsz, ntok, H, dk, dtype=torch.float64, **kw)
+    q = q / q.norm(dim=-1, keepdim=True)
+    k = k / k.norm(dim=-1, keepdim=True)
+    v = torch.randn(bsz, ntok, H, dv, **kw)
+    beta = torch.sigmoid(torch.randn(bsz, ntok, H, dtype=torch.float64, **kw))
+    gl = -_softplus64(torch.randn(bsz, ntok, H, dtype=torch.float64, **kw))
+    return {"q": q.to(torch.float32).to(dt_), "k": k.to(torch.float32).to(dt_), "v": v.to(dt_),
+            "beta": beta.to(torch.float32), "g": gl.to(torch.float32)}
+
+
+def initial_state_device(shape: Shape, seed: int, std: float, layer: int = 0,
+                         device="cuda") -> torch.Tensor:
+    """Prefilled checkpoint drawn on the device (same distribution as initial_state)."""
+    g = torch.Generator(device=device).manual_seed(derive_seed(seed, "h0dev", layer))
+    out = torch.randn(shape.batch, shape.heads, shape.dim_p, shape.dim_n, generator=g,
+                      device=device)
+    return out.mul_(std)
+
+
 def accept_counts(batch: int, ndraft: int, seed: int, round_index: int) -> torch.Tensor:
     """Per-sequence accepted draft counts, uniform over {0, ..., ndraft}, int32 [batch]."""
     g = _gen(seed, "accept", round_index)
