@@ -1,11 +1,540 @@
-// gdn_kernels.hip -- Gated DeltaNet ReplaySSM kernels for gfx950 (not yet implemented).
+// gdn_kernels.hip -- Gated DeltaNet ReplaySSM kernels for gfx950 (wave64).
+//
+// Pages: "ReplaySSM: Rethinking State Storage for Faster Hybrid-Model Decoding" (news article, paras
+// 2-3: checkpoint plus buffered inputs, outputs without a state write, fold when the buffer fills;
+// the layer type is named in para 7 and in the feed excerpt). The recurrence is the published gated
+// delta rule (Yang, Kautz & Hatamizadeh, 2025), per head with S in R^{dv x dk}, alpha = exp(g):
+//   S_t = alpha_t S_{t-1} + beta_t (v_t - alpha_t S_{t-1} k_t) k_t^T,   o_t = scale S_t q_t.
+//
+// Work decomposition: one workgroup of dv/64 wavefronts (two for dv = 128) per (sequence, head).
+// The checkpoint uses the same quad-interleaved tile as Mamba-2 (element (p, n) at float
+// ((n/4)*dv + p)*4 + n%4), so in replay and in the conventional step lane p of wave w owns row
+// p = 64w + lane and every row product with a dk-vector runs inside one lane. The flush holds the
+// tile in fp32 MFMA accumulator order instead (16x16 blocks: lane l owns row 16*pb + l%16 and the
+// quad 4*nb + l/16), which is the same memory layout read with a different lane map.
 #include "ssm_device.hpp"
 #include "ssm_kernels.hpp"
 
 namespace ssm {
 
-hipError_t gdn_launch_replay(const GdnArgs&, int, int, int, hipStream_t) { return hipErrorNotSupported; }
-hipError_t gdn_launch_flush(const GdnArgs&, int, int, int, int, hipStream_t) { return hipErrorNotSupported; }
-hipError_t gdn_launch_conv(const GdnConvArgs&, int, int, int, hipStream_t) { return hipErrorNotSupported; }
+namespace {
+
+__device__ __forceinline__ int ring_slot(int start, int e, int cap) {
+    const int s = start + e;
+    return s >= cap ? s - cap : s;
+}
+
+// Sum over all 64 lanes, result in every lane.
+__device__ __forceinline__ float wave_sum(float v) { return xor_reduce_sum<1, 32>(v); }
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+constexpr int kMaxWin = 32;  // largest window (entries a decode call can see)
+
+}  // namespace
+
+// ---------------------------------------------------------------------------------------------
+// Replay decode (one query). With entries 1..k after the checkpoint (entry k = this token):
+//   r <- q_k, acc <- 0; for i = k..1: c_i = beta_i (k_i . r), acc += c_i v_i, r <- alpha_i (r - c_i k_i)
+//   o = scale (S_c r + acc)
+// which is the delta-rule recurrence unrolled k times (each step maps the query through
+// alpha_i (I - beta_i k_i k_i^T) and emits beta_i (k_i . r) v_i).
+// ---------------------------------------------------------------------------------------------
+template <int DV, int DK, typename TIN, int MAXW>
+__global__ __launch_bounds__(64 * (DV >= 64 ? DV / 64 : 1))
+__attribute__((amdgpu_waves_per_eu(2))) void gdn_replay_kernel(GdnArgs a) {
+    static_assert(DV >= 64 && DK >= 64, "replay tile: dv, dk >= 64");
+    constexpr int kW = DV / 64;                   // wavefronts per head
+    constexpr int kRows = 64;                     // rows per wave
+    constexpr int kNQ = DK / 4;
+    constexpr int kE = DK / 64;                   // key elements per lane in the sweep
+    constexpr int kEPC = 16 / (int)sizeof(TIN);
+    constexpr int kVC = kRows / kEPC;             // 16-byte chunks of a wave's v slice
+    constexpr int kVL = (MAXW * kVC + 63) / 64;
+    __shared__ __attribute__((aligned(16))) float s_r[kW][DK];
+    __shared__ __attribute__((aligned(16))) u32x4_t s_v[kW][MAXW * kVC];
+
+    const int wave = uniform(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int h = blockIdx.x, b = blockIdx.y;
+    const int H = a.heads;
+    const int head = b * H + h;
+    const int cap = a.cap;
+    const int2 pt = *reinterpret_cast<const int2*>(a.ptr + 2 * head);
+    const int start = uniform(pt.x), count = uniform(pt.y);
+    const int kmax = count + 1;
+    const long tok = (long)b * H + h;  // this token's row in the [batch][1][H] inputs
+    const TIN* rq = static_cast<const TIN*>(a.ring_q);
+    const TIN* rk = static_cast<const TIN*>(a.ring_k);
+    const TIN* rv = static_cast<const TIN*>(a.ring_v);
+    const TIN* inq = static_cast<const TIN*>(a.in_q);
+    const TIN* ink = static_cast<const TIN*>(a.in_k);
+    const TIN* inv = static_cast<const TIN*>(a.in_v);
+    const int row = wave * kRows + lane;
+
+    // ---- small loads first (in-order memory counter) ------------------------------------------
+    const int el = lane;  // lane's key elements: [el*kE, el*kE + kE)
+    float be = 0.f, ge = 0.f;  // beta, g of entry e = lane
+    {
+        const bool ring = lane < count;
+        const int s = ring_slot(start, min(lane, cap - 1), cap);
+        const float* pb = ring ? a.ring_beta + (long)head * cap + s : a.in_beta + tok;
+        const float* pg = ring ? a.ring_g + (long)head * cap + s : a.in_g + tok;
+        be = *pb;
+        ge = *pg;
+        be = lane < kmax ? be : 0.f;
+        ge = lane < kmax ? ge : 0.f;
+    }
+    TIN kraw[MAXW][kE];  // keys of the buffered entries (entry `count` = this token)
+#pragma unroll
+    for (int e = 0; e < MAXW; ++e) {
+        const TIN* src = e < count ? rk + ((long)head * cap + ring_slot(start, min(e, cap - 1), cap)) * DK
+                                   : ink + tok * DK;
+        load_raw<TIN, kE>(src + el * kE, kraw[e]);
+    }
+    TIN qraw[kE], kcur[kE];
+    load_raw<TIN, kE>(inq + tok * DK + el * kE, qraw);
+    load_raw<TIN, kE>(ink + tok * DK + el * kE, kcur);
+    u32x4_t vraw[kVL];
+#pragma unroll
+    for (int i = 0; i < kVL; ++i) {
+        const int idx = (lane + 64 * i) % (MAXW * kVC);
+        const int e = idx / kVC, part = idx % kVC;
+        const TIN* src = e < count ? rv + ((long)head * cap + ring_slot(start, min(e, cap - 1), cap)) * DV
+                                   : inv + tok * DV;
+        vraw[i] = *reinterpret_cast<const u32x4_t*>(src + wave * kRows + part * kEPC);
+    }
+
+    // ---- the checkpoint rows of this wave ------------------------------------------------------
+    float4 hv[kNQ];
+    const float4* tile = reinterpret_cast<const float4*>(a.ckpt) + (long)head * (DV * DK / 4);
+#pragma unroll
+    for (int q = 0; q < kNQ; ++q) hv[q] = ld_stream(tile + q * DV + row);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- stage v rows, append this token to the rings -------------------------------------------
+#pragma unroll
+    for (int i = 0; i < kVL; ++i) {
+        const int idx = lane + 64 * i;
+        if (idx < MAXW * kVC) s_v[wave][idx] = vraw[i];
+    }
+    {
+        const int slot = ring_slot(start, count, cap);
+        const long rbase = (long)head * cap + slot;
+#pragma unroll
+        for (int i = 0; i < kVL; ++i) {
+            const int idx = lane + 64 * i;
+            const int e = idx / kVC, part = idx % kVC;
+            if (e == count && idx < MAXW * kVC)
+                *reinterpret_cast<u32x4_t*>(static_cast<TIN*>(a.ring_v) + rbase * DV + wave * kRows +
+                                            part * kEPC) = vraw[i];
+        }
+        if (wave == 0) {
+            store_raw<TIN, kE>(static_cast<TIN*>(a.ring_q) + rbase * DK + el * kE, qraw);
+            store_raw<TIN, kE>(static_cast<TIN*>(a.ring_k) + rbase * DK + el * kE, kcur);
+            if (lane == count) {
+                a.ring_beta[rbase] = be;
+                a.ring_g[rbase] = ge;
+            }
+        }
+    }
+
+    // ---- backward sweep over the buffered entries ----------------------------------------------
+    float r[kE];
+#pragma unroll
+    for (int j = 0; j < kE; ++j) r[j] = to_f32<TIN>(qraw[j]);
+    float cvals[MAXW];
+#pragma unroll
+    for (int e = MAXW - 1; e >= 0; --e) {
+        cvals[e] = 0.f;
+        if (e < kmax) {
+            float kv[kE];
+#pragma unroll
+            for (int j = 0; j < kE; ++j) kv[j] = to_f32<TIN>(e == count ? kcur[j] : kraw[e][j]);
+            float d = 0.f;
+#pragma unroll
+            for (int j = 0; j < kE; ++j) d += kv[j] * r[j];
+            d = wave_sum(d);
+            const float c = readlane(be, e) * d;
+            const float al = expf(readlane(ge, e));
+#pragma unroll
+            for (int j = 0; j < kE; ++j) r[j] = al * (r[j] - c * kv[j]);
+            cvals[e] = c;
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < kE; ++j) s_r[wave][el * kE + j] = r[j];
+    wave_sync();
+
+    // ---- value terms and the checkpoint row product --------------------------------------------
+    const TIN* sv = reinterpret_cast<const TIN*>(&s_v[wave][0]);
+    float acc = 0.f;
+#pragma unroll
+    for (int e = 0; e < MAXW; ++e)
+        if (e < kmax) acc += cvals[e] * to_f32<TIN>(sv[e * kRows + lane]);
+    float dot = 0.f;
+#pragma unroll
+    for (int q = 0; q < kNQ; ++q) {
+        const float4 r4 = *reinterpret_cast<const float4*>(&s_r[wave][4 * q]);
+        dot += hv[q].x * r4.x + hv[q].y * r4.y + hv[q].z * r4.z + hv[q].w * r4.w;
+    }
+    a.o[tok * DV + row] = a.scale * (dot + acc);
+    if constexpr (kW > 1) __builtin_amdgcn_s_barrier();  // every wave has read the pointers
+    if (wave == 0 && lane == 0) a.ptr[2 * head + 1] = count + 1;
+}
+
+// ---------------------------------------------------------------------------------------------
+// Conventional step (comparison point; the full state rewritten every token):
+//   S <- alpha S + beta (v - alpha S k) k^T (in place),  o = scale S q.
+// ---------------------------------------------------------------------------------------------
+template <int DV, int DK, typename TIN>
+__global__ __launch_bounds__(64 * (DV >= 64 ? DV / 64 : 1))
+__attribute__((amdgpu_waves_per_eu(2))) void gdn_conv_kernel(GdnConvArgs a) {
+    constexpr int kW = DV >= 64 ? DV / 64 : 1;
+    constexpr int kRows = DV >= 64 ? 64 : DV;
+    constexpr int kNQ = DK / 4;
+    constexpr int kCE = DK >= 64 ? DK / 64 : 1;
+    __shared__ __attribute__((aligned(16))) float s_kq[kW][2][DK];
+    const int wave = uniform(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int h = blockIdx.x, b = blockIdx.y;
+    const long head = (long)b * a.heads + h;
+    const int row = wave * kRows + (lane % kRows);
+    const TIN* ink = static_cast<const TIN*>(a.in_k) + head * DK;
+    const TIN* inq = static_cast<const TIN*>(a.in_q) + head * DK;
+    TIN kraw[kCE], qraw[kCE];
+#pragma unroll
+    for (int i = 0; i < kCE; ++i) {
+        const int n = (lane + 64 * i) % DK;
+        kraw[i] = ink[n];
+        qraw[i] = inq[n];
+    }
+    const float v = to_f32<TIN>(static_cast<const TIN*>(a.in_v)[head * DV + row]);
+    const float beta = a.in_beta[head];
+    const float alpha = expf(a.in_g[head]);
+    float4 hv[kNQ];
+    float4* tile = reinterpret_cast<float4*>(a.S) + head * (DV * DK / 4);
+#pragma unroll
+    for (int q = 0; q < kNQ; ++q) hv[q] = ld_stream(tile + q * DV + row);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < kCE; ++i) {
+        const int n = (lane + 64 * i) % DK;
+        s_kq[wave][0][n] = to_f32<TIN>(kraw[i]);
+        s_kq[wave][1][n] = to_f32<TIN>(qraw[i]);
+    }
+    wave_sync();
+    float sk = 0.f;
+#pragma unroll
+    for (int q = 0; q < kNQ; ++q) {
+        const float4 k4 = *reinterpret_cast<const float4*>(&s_kq[wave][0][4 * q]);
+        sk += hv[q].x * k4.x + hv[q].y * k4.y + hv[q].z * k4.z + hv[q].w * k4.w;
+    }
+    const float u = beta * (v - alpha * sk);
+    asm volatile("" ::: "memory");  // re-read k below rather than keeping 32 quads of it live
+    float o = 0.f;
+#pragma unroll
+    for (int q = 0; q < kNQ; ++q) {
+        const float4 k4 = *reinterpret_cast<const float4*>(&s_kq[wave][0][4 * q]);
+        const float4 q4 = *reinterpret_cast<const float4*>(&s_kq[wave][1][4 * q]);
+        hv[q].x = alpha * hv[q].x + u * k4.x;
+        hv[q].y = alpha * hv[q].y + u * k4.y;
+        hv[q].z = alpha * hv[q].z + u * k4.z;
+        hv[q].w = alpha * hv[q].w + u * k4.w;
+        o += hv[q].x * q4.x + hv[q].y * q4.y + hv[q].z * q4.z + hv[q].w * q4.w;
+        st_stream(hv[q], tile + q * DV + row);
+    }
+    if (lane < kRows) a.o[head * DV + row] = a.scale * o;
+}
+
+// ---------------------------------------------------------------------------------------------
+// Flush in UT/WY form (news para 3: fold the buffer into the checkpoint in one pass). For a chunk
+// of (up to) 16 entries, with G_t the running sum of g (log of the cumulative decay gamma_t):
+//   Lm[t][i] = beta_t exp(G_t - G_i) (k_t . k_i)   (i < t; decay as a partial sum of g)
+//   W_t = beta_t gamma_t k_t - sum_{i<t} Lm[t][i] W_i       (forward substitution, dk-vectors)
+//   U_t = beta_t v_t     - sum_{i<t} Lm[t][i] U_i       (forward substitution, dv-vectors)
+//   Delta_t = U_t - S W_t,   S <- gamma_L S + sum_t (gamma_L / gamma_t) Delta_t k_t^T
+// The Gram matrix K K^T and the two dv x dk x 16 contractions run on fp32 MFMA
+// (v_mfma_f32_16x16x4f32): A[m][k] from lane l = (m = l%16, k = l/16), B[k][c] from lane l =
+// (k = l/16, c = l%16), D[m][c] in lane l at register r = (m = 4(l/16) + r, c = l%16).
+// Entries past the fold count are zero rows (beta = g = 0, k = v = 0), which leave S unchanged.
+// Requires DV % 64 == 0 and DK % 16 == 0 (one wave per 64 rows).
+// ---------------------------------------------------------------------------------------------
+template <int DV, int DK, typename TIN>
+__global__ __launch_bounds__(DV)
+__attribute__((amdgpu_waves_per_eu(2))) void gdn_flush_kernel(GdnArgs a, int mode_all) {
+    static_assert(DV % 64 == 0 && DK % 16 == 0, "flush tile shape");
+    constexpr int kW = DV / 64;
+    constexpr int kPB = 4;            // 16-row blocks per wave
+    constexpr int kNB = DK / 16;      // 16-column blocks
+    constexpr int kKP = DK + 4;       // padded LDS row strides (bank spread)
+    constexpr int kVP = 64 + 4;
+    constexpr int kEPC = 16 / (int)sizeof(TIN);
+    constexpr int kKC = DK / kEPC, kVC = 64 / kEPC;   // 16-byte chunks per k row / per v slice
+    constexpr int kKL = (16 * kKC + 63) / 64, kVL = (16 * kVC + 63) / 64;
+    __shared__ __attribute__((aligned(16))) float s_k[kW][16][kKP];     // K chunk (fp32)
+    __shared__ __attribute__((aligned(16))) float s_w[kW][16][kKP];     // -W
+    __shared__ __attribute__((aligned(16))) float s_v[kW][16][kVP];     // this wave's v slice, then U ([t][p]), then Delta'^T
+    __shared__ __attribute__((aligned(16))) float s_l[kW][16][17];      // Lm
+    __shared__ __attribute__((aligned(16))) float s_d[kW][64][17];      // Delta' as [p][t] (transpose buffer)
+
+    const int wave = uniform(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int h = blockIdx.x, b = blockIdx.y;
+    const int head = b * a.heads + h;
+    const int cap = a.cap;
+    const int2 pt = *reinterpret_cast<const int2*>(a.ptr + 2 * head);
+    const int start = uniform(pt.x), count = uniform(pt.y);
+    const int nfold = mode_all ? count : (count >= a.window ? a.window : 0);
+    if (nfold == 0) return;  // uniform over the workgroup
+    const TIN* rk = static_cast<const TIN*>(a.ring_k);
+    const TIN* rv = static_cast<const TIN*>(a.ring_v);
+    const int li = lane & 15, lg = lane >> 4;
+    const int p_base = wave * 64;
+
+    // chunk loader (branch-free: entries past nfold read the last folded entry, zeroed later)
+    u32x4_t kraw[kKL], vraw[kVL];
+    float be = 0.f, ge = 0.f;
+    auto fetch = [&](int c0) {
+#pragma unroll
+        for (int i = 0; i < kKL; ++i) {
+            const int idx = (lane + 64 * i) % (16 * kKC);
+            const int e = min(c0 + idx / kKC, nfold - 1), part = idx % kKC;
+            kraw[i] = *reinterpret_cast<const u32x4_t*>(
+                rk + ((long)head * cap + ring_slot(start, e, cap)) * DK + part * kEPC);
+        }
+#pragma unroll
+        for (int i = 0; i < kVL; ++i) {
+            const int idx = (lane + 64 * i) % (16 * kVC);
+            const int e = min(c0 + idx / kVC, nfold - 1), part = idx % kVC;
+            vraw[i] = *reinterpret_cast<const u32x4_t*>(
+                rv + ((long)head * cap + ring_slot(start, e, cap)) * DV + p_base + part * kEPC);
+        }
+        const int e = min(c0 + li, nfold - 1);
+        const long s = (long)head * cap + ring_slot(start, e, cap);
+        be = a.ring_beta[s];
+        ge = a.ring_g[s];
+        be = (c0 + li < nfold) ? be : 0.f;  // lanes 16..63 mirror lanes 0..15
+        ge = (c0 + li < nfold) ? ge : 0.f;
+    };
+    fetch(0);
+
+    // the tile in accumulator order: block (pb, nb) of lane l = row p_base + 16pb + l%16,
+    // columns 16nb + 4(l/16) .. +3
+    f32x4 S[kPB][kNB];
+    const float4* tile = reinterpret_cast<const float4*>(a.ckpt) + (long)head * (DV * DK / 4);
+#pragma unroll
+    for (int pb = 0; pb < kPB; ++pb)
+#pragma unroll
+        for (int nb = 0; nb < kNB; ++nb) {
+            const float4 t = ld_stream(tile + (4 * nb + lg) * DV + p_base + 16 * pb + li);
+            S[pb][nb] = f32x4{t.x, t.y, t.z, t.w};
+        }
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+
+    for (int c0 = 0; c0 < nfold; c0 += 16) {
+        if (c0 > 0) fetch(c0);
+        const int nc = min(16, nfold - c0);
+        // stage K and V (entries >= nc as zeros)
+#pragma unroll
+        for (int i = 0; i < kKL; ++i) {
+            const int idx = lane + 64 * i;
+            if (idx < 16 * kKC) {
+                const int e = idx / kKC, part = idx % kKC;
+                float f[kEPC];
+                Unit<TIN>::unpack(make_uint4(kraw[i].x, kraw[i].y, kraw[i].z, kraw[i].w), f);
+#pragma unroll
+                for (int j = 0; j < kEPC; ++j) s_k[wave][e][part * kEPC + j] = e < nc ? f[j] : 0.f;
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < kVL; ++i) {
+            const int idx = lane + 64 * i;
+            if (idx < 16 * kVC) {
+                const int e = idx / kVC, part = idx % kVC;
+                float f[kEPC];
+                Unit<TIN>::unpack(make_uint4(vraw[i].x, vraw[i].y, vraw[i].z, vraw[i].w), f);
+#pragma unroll
+                for (int j = 0; j < kEPC; ++j) s_v[wave][e][part * kEPC + j] = e < nc ? f[j] : 0.f;
+            }
+        }
+        wave_sync();
+
+        // Gram matrix K K^T on MFMA: lane l supplies K[l%16][n0 + l/16] as both operands
+        f32x4 gram = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int n0 = 0; n0 < DK; n0 += 4) {
+            const float kk = s_k[wave][li][n0 + lg];
+            gram = mfma4(kk, kk, gram);
+        }
+        // Lm[t][i] for t = 4lg + r, i = li (t varies across lanes: beta_t by a per-lane shuffle)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int t = 4 * lg + r, i = li;
+            float part = 0.f;  // sum_{m=i+1..t} g_m
+#pragma unroll
+            for (int m = 0; m < 16; ++m) part += (m > i && m <= t) ? readlane(ge, m) : 0.f;
+            const float bt = __shfl(be, t, 64);
+            const float lm = (i < t) ? bt * expf(part) * gram[r] : 0.f;
+            s_l[wave][t][i] = lm;
+        }
+        wave_sync();
+
+        // forward substitution for W (lane owns columns n = lane + 64 j) and U (lane owns row
+        // p_base + lane); W is stored negated for the MFMA below, U as [t][p]
+        constexpr int kWE = DK / 64 > 0 ? DK / 64 : 1;
+        float w[16][kWE], u[16];
+        float gcum = 0.f;
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+            gcum += readlane(ge, t);
+            const float bt = readlane(be, t);
+            const float bg = bt * expf(gcum);
+#pragma unroll
+            for (int j = 0; j < kWE; ++j) {
+                const int n = lane + 64 * j;
+                float s = n < DK ? bg * s_k[wave][t][n] : 0.f;
+#pragma unroll
+                for (int i = 0; i < t; ++i) s -= s_l[wave][t][i] * w[i][j];
+                w[t][j] = s;
+            }
+            float su = bt * s_v[wave][t][lane];
+#pragma unroll
+            for (int i = 0; i < t; ++i) su -= s_l[wave][t][i] * u[i];
+            u[t] = su;
+            asm volatile("" ::: "memory");  // one row of Lm live at a time
+        }
+        const float gL = gcum;  // log gamma_L (zero-padded entries add nothing)
+        wave_sync();
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+#pragma unroll
+            for (int j = 0; j < kWE; ++j) {
+                const int n = lane + 64 * j;
+                if (n < DK) s_w[wave][t][n] = -w[t][j];
+            }
+            s_v[wave][t][lane] = u[t];  // U as [t][p - p_base]
+        }
+        wave_sync();
+
+        asm volatile("" ::: "memory");
+        // Delta^T[p][t] = U^T[p][t] - sum_n S[p][n] W[t][n]   (D layout: p = 4lg + r, t = li)
+        f32x4 wop[kNB];  // B operand: -W[t = li][16nb + 4lg + r]
+#pragma unroll
+        for (int nb = 0; nb < kNB; ++nb)
+            wop[nb] = *reinterpret_cast<const f32x4*>(&s_w[wave][li][16 * nb + 4 * lg]);
+        float tail = 0.f;  // log(gamma_L / gamma_t) for t = li
+#pragma unroll
+        for (int m = 0; m < 16; ++m) tail += (m > li) ? readlane(ge, m) : 0.f;
+        const float dscale = expf(tail);
+        f32x4 delta[kPB];
+#pragma unroll
+        for (int pb = 0; pb < kPB; ++pb) {
+            f32x4 acc;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[r] = s_v[wave][li][16 * pb + 4 * lg + r];
+#pragma unroll
+            for (int nb = 0; nb < kNB; ++nb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc = mfma4(S[pb][nb][r], wop[nb][r], acc);
+            delta[pb] = acc * dscale;  // Delta'[p][t] = (gamma_L / gamma_t) Delta[p][t]
+        }
+        wave_sync();
+        // transpose Delta' through LDS ([p][t])
+#pragma unroll
+        for (int pb = 0; pb < kPB; ++pb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) s_d[wave][16 * pb + 4 * lg + r][li] = delta[pb][r];
+        wave_sync();
+
+        asm volatile("" ::: "memory");
+        // S <- gamma_L S + sum_t K^T[n][t] Delta'^T[t][p]   (D rows = n, columns = p)
+        const float gammaL = expf(gL);
+#pragma unroll
+        for (int pb = 0; pb < kPB; ++pb) {
+            float dop[4];  // B operand: Delta'[p = 16pb + li][t = 4tg + lg]
+#pragma unroll
+            for (int tg = 0; tg < 4; ++tg) dop[tg] = s_d[wave][16 * pb + li][4 * tg + lg];
+#pragma unroll
+            for (int nb = 0; nb < kNB; ++nb) {
+                f32x4 acc = S[pb][nb] * gammaL;
+#pragma unroll
+                for (int tg = 0; tg < 4; ++tg)
+                    acc = mfma4(s_k[wave][4 * tg + lg][16 * nb + li], dop[tg], acc);
+                S[pb][nb] = acc;
+            }
+        }
+        wave_sync();
+    }
+
+    float4* wtile = reinterpret_cast<float4*>(a.ckpt) + (long)head * (DV * DK / 4);
+#pragma unroll
+    for (int pb = 0; pb < kPB; ++pb)
+#pragma unroll
+        for (int nb = 0; nb < kNB; ++nb)
+            st_stream(make_float4(S[pb][nb][0], S[pb][nb][1], S[pb][nb][2], S[pb][nb][3]),
+                      wtile + (4 * nb + lg) * DV + p_base + 16 * pb + li);
+    if constexpr (kW > 1) __builtin_amdgcn_s_barrier();  // every wave has read the pointers
+    if (wave == 0 && lane == 0) {
+        a.ptr[2 * head] = ring_slot(start, nfold, cap);
+        a.ptr[2 * head + 1] = count - nfold;
+    }
+}
+
+// ---------------------------------------------------------------------------------------------
+#define SSM_GDN_SHAPES(X, T) X(64, 64, T) X(64, 128, T) X(128, 64, T) X(128, 128, T)
+
+template <int DV, int DK, typename TIN>
+static hipError_t launch_replay_dd(const GdnArgs& a, hipStream_t s) {
+    if (a.window <= 16)
+        hipLaunchKernelGGL((gdn_replay_kernel<DV, DK, TIN, 16>), dim3(a.heads, a.batch), dim3(DV), 0,
+                           s, a);
+    else
+        hipLaunchKernelGGL((gdn_replay_kernel<DV, DK, TIN, 32>), dim3(a.heads, a.batch), dim3(DV), 0,
+                           s, a);
+    return hipGetLastError();
+}
+template <int DV, int DK, typename TIN>
+static hipError_t launch_flush_dd(const GdnArgs& a, int mode_all, hipStream_t s) {
+    hipLaunchKernelGGL((gdn_flush_kernel<DV, DK, TIN>), dim3(a.heads, a.batch), dim3(DV), 0, s, a,
+                       mode_all);
+    return hipGetLastError();
+}
+template <int DV, int DK, typename TIN>
+static hipError_t launch_conv_dd(const GdnConvArgs& a, hipStream_t s) {
+    hipLaunchKernelGGL((gdn_conv_kernel<DV, DK, TIN>), dim3(a.heads, a.batch), dim3(DV), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t gdn_launch_replay(const GdnArgs& a, int dv, int dk, int bf16, hipStream_t s) {
+    if (a.window > kMaxWin) return hipErrorNotSupported;
+#define X(V, K, T) \
+    if (dv == V && dk == K) return launch_replay_dd<V, K, T>(a, s);
+    if (bf16) { SSM_GDN_SHAPES(X, bf16_t) } else { SSM_GDN_SHAPES(X, float) }
+#undef X
+    return hipErrorNotSupported;
+}
+hipError_t gdn_launch_flush(const GdnArgs& a, int dv, int dk, int bf16, int mode_all,
+                            hipStream_t s) {
+#define X(V, K, T) \
+    if (dv == V && dk == K) return launch_flush_dd<V, K, T>(a, mode_all, s);
+    if (bf16) { SSM_GDN_SHAPES(X, bf16_t) } else { SSM_GDN_SHAPES(X, float) }
+#undef X
+    return hipErrorNotSupported;
+}
+hipError_t gdn_launch_conv(const GdnConvArgs& a, int dv, int dk, int bf16, hipStream_t s) {
+#define X(V, K, T) \
+    if (dv == V && dk == K) return launch_conv_dd<V, K, T>(a, s);
+    if (bf16) { SSM_GDN_SHAPES(X, bf16_t) } else { SSM_GDN_SHAPES(X, float) }
+#undef X
+    return hipErrorNotSupported;
+}
 
 }  // namespace ssm

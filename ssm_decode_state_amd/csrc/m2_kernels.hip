@@ -208,9 +208,9 @@ __global__ __launch_bounds__(256) void m2_replay_kernel(M2Args a) {
     constexpr int kBC = MAXE / 16;                       // 16-entry chunks of B segments
     constexpr int kCE = N >= 64 ? N / 64 : 1;            // C elements per lane
     static_assert(MAXE % 16 == 0 && MAXE <= 64, "MAXE");
-    __shared__ float s_c[kHeadsPerBlock][MAXQ][N];
-    __shared__ u32x4_t s_x[kHeadsPerBlock][MAXE * kCPR];
-    __shared__ float s_w[kHeadsPerBlock][MAXE][MAXQ];
+    __shared__ __attribute__((aligned(16))) float s_c[kHeadsPerBlock][MAXQ][N];
+    __shared__ __attribute__((aligned(16))) u32x4_t s_x[kHeadsPerBlock][MAXE * kCPR];
+    __shared__ __attribute__((aligned(16))) float s_w[kHeadsPerBlock][MAXE][MAXQ];
 
     const int wave = uniform(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
@@ -471,8 +471,8 @@ __global__ __launch_bounds__(256) void m2_flush_kernel(M2Args a, int mode_all, i
     constexpr int kBL = (16 * kBCR + 63) / 64;     // B chunks per lane (16 rows)
     constexpr int kXCR = P / kEPC;                 // chunks per x row
     constexpr int kXL = (16 * kXCR + 63) / 64;
-    __shared__ float s_b[kHeadsPerBlock][16][N];
-    __shared__ u32x4_t s_x[kHeadsPerBlock][16 * kXCR];
+    __shared__ __attribute__((aligned(16))) float s_b[kHeadsPerBlock][16][N];
+    __shared__ __attribute__((aligned(16))) u32x4_t s_x[kHeadsPerBlock][16 * kXCR];
 
     const int wave = uniform(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
@@ -598,7 +598,7 @@ template <int P, int N, typename TIN>
 __global__ __launch_bounds__(256) void m2_conv_kernel(M2ConvArgs a) {
     using G = M2Geo<P, N>;
     constexpr int kCE = N >= 64 ? N / 64 : 1;
-    __shared__ float s_bc[kHeadsPerBlock][2][N];
+    __shared__ __attribute__((aligned(16))) float s_bc[kHeadsPerBlock][2][N];
     const int wave = uniform(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int h = blockIdx.x * kHeadsPerBlock + wave;

@@ -36,6 +36,7 @@ ssm_status check_config(const ssm_config* c) {
         if (c->readcopy == SSM_RC_FP4_B16 && c->dim_n % 32) return SSM_E_SHAPE;
     } else {
         if (c->groups != c->heads) return SSM_E_SHAPE;
+        if (c->dim_p < 64 || c->dim_n < 64) return SSM_E_SHAPE;  // dv, dk in {64, 128}
         if (c->readcopy != SSM_RC_NONE) return SSM_E_UNSUPPORTED;
         if (!isfinite(c->gdn_scale)) return SSM_E_ARG;
     }

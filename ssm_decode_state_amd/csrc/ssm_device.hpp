@@ -83,6 +83,12 @@ __device__ __forceinline__ void load_raw(const T* __restrict__ src, T (&d)[E]) {
             const uint2 t = reinterpret_cast<const uint2*>(src)[u];
             __builtin_memcpy(&d[u * (8 / sizeof(T))], &t, 8);
         }
+    } else if constexpr (kBytes % 4 == 0) {
+#pragma unroll
+        for (int u = 0; u < kBytes / 4; ++u) {
+            const uint32_t t = reinterpret_cast<const uint32_t*>(src)[u];
+            __builtin_memcpy(&d[u * (4 / sizeof(T))], &t, 4);
+        }
     } else {
 #pragma unroll
         for (int i = 0; i < E; ++i) d[i] = src[i];
@@ -106,6 +112,13 @@ __device__ __forceinline__ void store_raw(T* __restrict__ dst, const T (&d)[E]) 
             uint2 t;
             __builtin_memcpy(&t, &d[u * (8 / sizeof(T))], 8);
             reinterpret_cast<uint2*>(dst)[u] = t;
+        }
+    } else if constexpr (kBytes % 4 == 0) {
+#pragma unroll
+        for (int u = 0; u < kBytes / 4; ++u) {
+            uint32_t t;
+            __builtin_memcpy(&t, &d[u * (4 / sizeof(T))], 4);
+            reinterpret_cast<uint32_t*>(dst)[u] = t;
         }
     } else {
 #pragma unroll
@@ -152,6 +165,9 @@ __device__ __forceinline__ float xor_reduce_max(float v) {
     return v;
 }
 
+// Value of v in lane `lane`. The index MUST be wave-uniform: a per-lane index is silently
+// replaced by the first active lane's (v_readlane takes a scalar lane select). Use __shfl for
+// per-lane indices.
 __device__ __forceinline__ float readlane(float v, int lane) {
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
 }

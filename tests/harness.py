@@ -80,3 +80,29 @@ def m2_oracle(A, D, h0, tokens: M2Tokens, pairs, snap_after=()):
 
 def to_dev(d, dev):
     return {k: v.to(dev, non_blocking=True).contiguous() for k, v in d.items()}
+
+
+class GdnTokens:
+    """Per-step GDN inputs and per-head gathers for the oracle."""
+
+    def __init__(self, shape: synth.Shape, seed: int, tag: str = "decode"):
+        self.shape, self.seed, self.tag = shape, seed, tag
+        self.steps = []
+
+    def draw(self, index: int):
+        d = synth.token_inputs(self.shape, self.seed, self.tag, index)
+        self.steps.append(d)
+        return d
+
+    def head_inputs(self, pairs):
+        out = []
+        for key in ("q", "k", "v", "beta", "g"):
+            out.append(synth.to_f64(torch.stack(
+                [torch.cat([d[key][b, :, h] for d in self.steps], 0) for (b, h) in pairs])))
+        return out
+
+
+def gdn_oracle(S0, tokens: GdnTokens, pairs, scale=1.0, snap_after=()):
+    q, k, v, beta, g = tokens.head_inputs(pairs)
+    S0p = None if S0 is None else np.stack([S0[b, h].double().numpy() for (b, h) in pairs])
+    return oracle.gdn_sequential(S0p, q, k, v, beta, g, scale=scale, snap_after=snap_after)

@@ -1,0 +1,115 @@
+"""GPU parity of the Gated DeltaNet replay path (backward-sweep replay, UT/WY flush on MFMA,
+conventional step) against the fp64 oracle's sequential gated delta rule."""
+import numpy as np
+import pytest
+import torch
+
+from harness import GdnTokens, assert_close, gdn_oracle, sample_pairs, to_dev
+from ssm_decode_state_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():
+    pytest.skip("needs a GPU", allow_module_level=True)
+bd = pytest.importorskip("ssm_decode_state_amd.binding")
+DEV = torch.device("cuda:0")
+
+
+def tiles_of(st, pairs):
+    c = st.cfg
+    P, N = c.dim_p, c.dim_n
+    ck = st.region(st.layout.off_ckpt, c.batch * c.heads * P * N * 4).view(torch.float32)
+    ck = ck.view(c.batch * c.heads, N // 4, P, 4)
+    idx = torch.tensor([b * c.heads + h for (b, h) in pairs], device=DEV)
+    return ck.index_select(0, idx).permute(0, 2, 1, 3).reshape(len(pairs), P, N).cpu().double().numpy()
+
+
+def run_gdn(shape, seed, T, s0_std, pairs, scale=1.0):
+    S0 = synth.initial_state(shape, seed, s0_std) if s0_std else None
+    cfg = bd.make_config(bd.SSM_GDN, shape.batch, shape.heads, shape.heads, shape.dim_p,
+                         shape.dim_n, shape.window, 1,
+                         bd.SSM_IN_BF16 if shape.in_bf16 else bd.SSM_IN_F32, 0, scale)
+    st = bd.State(cfg, None if S0 is None else S0.to(DEV), None, None)
+    tok = GdnTokens(shape, seed)
+    bi = torch.tensor([b for (b, _) in pairs], device=DEV)
+    hi = torch.tensor([h for (_, h) in pairs], device=DEV)
+    o = torch.empty(shape.batch, shape.heads, shape.dim_p, device=DEV)
+    os_, cks = [], []
+    L = shape.window
+    for t in range(T):
+        bd.ssm_replay_decode(st, to_dev(tok.draw(t), DEV), o)
+        os_.append(o[bi, hi].clone())
+        if (t + 1) % L == 0:
+            cks.append(tiles_of(st, pairs))
+    torch.cuda.synchronize()
+    snaps = list(range(L, T + 1, L))
+    oo, _, osn = gdn_oracle(S0, tok, pairs, scale, snaps)
+    go = torch.stack(os_, 1).cpu().double().numpy()
+    return go, (np.stack(cks, 1) if cks else None), oo, osn, st, S0, tok
+
+
+def _gshape(B, H, dv, dk, L, bf16=True):
+    return synth.Shape(synth.GDN, B, H, H, dv, dk, L, 1, in_bf16=bf16)
+
+
+@pytest.mark.parametrize("B,H,dv,dk,L,bf16,T", [
+    (2, 3, 64, 64, 4, True, 21),
+    (1, 2, 128, 128, 16, False, 37),
+    (2, 2, 128, 64, 8, True, 19),
+    (1, 3, 64, 128, 32, True, 70),
+    (2, 2, 128, 128, 1, True, 5),
+])
+def test_gdn_decode_shapes(B, H, dv, dk, L, bf16, T):
+    shape = _gshape(B, H, dv, dk, L, bf16)
+    pairs = [(b, h) for b in range(B) for h in range(H)]
+    go, gck, oo, osn, *_ = run_gdn(shape, 70 + T, T, 0.3162, pairs, scale=0.5 if L == 8 else 1.0)
+    assert_close(go, oo, (-1,), "GDN replay outputs")
+    if gck is not None:
+        assert_close(gck, osn, (-2, -1), "GDN flushed checkpoints")
+
+
+def test_gdn_serving_batch_sampled_heads():
+    w = synth.WORKLOADS["gdn_b256"]
+    shape = w["shape"]
+    pairs = sample_pairs(shape.batch, shape.heads, 24)
+    go, gck, oo, osn, *_ = run_gdn(shape, w["seed"], w["steps"], w["h0_std"], pairs)
+    assert_close(go, oo, (-1,), "GDN replay outputs")
+    assert_close(gck, osn, (-2, -1), "GDN flushed checkpoints")
+
+
+def test_gdn_flush_all_and_export():
+    shape = _gshape(2, 2, 128, 128, 16)
+    pairs = [(b, h) for b in range(2) for h in range(2)]
+    go, gck, oo, osn, st, S0, tok = run_gdn(shape, 81, 21, 0.3162, pairs)
+    bd.ssm_flush(st, bd.SSM_FLUSH_ALL)
+    out = torch.empty(2, 2, 128, 128, device=DEV)
+    bd.ssm_ckpt_export(st, out)
+    torch.cuda.synchronize()
+    _, ST, _ = gdn_oracle(S0, tok, pairs)
+    assert_close(out.cpu().double().numpy().reshape(4, 128, 128), ST, (-2, -1),
+                 "GDN checkpoint after flush(ALL) of 5 entries")
+
+
+@pytest.mark.parametrize("B,H,dv,dk,bf16", [(2, 3, 64, 128, False), (256, 32, 128, 128, True)])
+def test_gdn_conventional_step(B, H, dv, dk, bf16):
+    shape = _gshape(B, H, dv, dk, 16, bf16)
+    S0 = synth.initial_state(shape, 90, 0.3162)
+    cfg = bd.make_config(bd.SSM_GDN, B, H, H, dv, dk, 16, 1,
+                         bd.SSM_IN_BF16 if bf16 else bd.SSM_IN_F32)
+    tiles = torch.empty(B * H * dv * dk, device=DEV)
+    bd.ssm_tiles_pack(cfg, S0.to(DEV).contiguous(), tiles)
+    pairs = sample_pairs(B, H, 16) if B * H > 64 else [(b, h) for b in range(B) for h in range(H)]
+    bi = torch.tensor([b for (b, _) in pairs], device=DEV)
+    hi = torch.tensor([h for (_, h) in pairs], device=DEV)
+    tok = GdnTokens(shape, 90)
+    o = torch.empty(B, H, dv, device=DEV)
+    os_ = []
+    for t in range(7):
+        bd.ssm_conventional_step(cfg, tiles, to_dev(tok.draw(t), DEV), None, None, o)
+        os_.append(o[bi, hi].clone())
+    nat = torch.empty(B, H, dv, dk, device=DEV)
+    bd.ssm_tiles_unpack(cfg, tiles, nat)
+    torch.cuda.synchronize()
+    oo, ST, _ = gdn_oracle(S0, tok, pairs)
+    assert_close(torch.stack(os_, 1).cpu().double().numpy(), oo, (-1,), "GDN conventional outputs")
+    assert_close(nat[bi, hi].cpu().double().numpy(), ST, (-2, -1), "GDN conventional state")
