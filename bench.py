@@ -52,6 +52,202 @@ def m2_conv_bytes_per_head(P, N, esz=2):
     return 2 * P * N * 4 + P * esz + 2 * N * esz + 4 + P * 4
 
 
+def m2_verify_bytes_per_head(P, N, kc, S, esz=2):
+    """One speculative verify launch for one head: checkpoint read once, kc committed entries
+    (x, B, dt), S drafts read and appended (x, B, C, dt), S outputs, pointers."""
+    entry_rd = P * esz + N * esz + 4
+    token = P * esz + 2 * N * esz + 4
+    return P * N * 4 + kc * entry_rd + 2 * S * token + S * P * 4 + 8
+
+
+def m2_rc_replay_bytes_per_head(P, N, k, rc, esz=2):
+    """Replay launch reading the low-precision copy instead of the fp32 checkpoint."""
+    copy = P * N + P * 4 if rc == 1 else P * N // 2 + P * (N // 16) + 4
+    return m2_replay_bytes_per_head(P, N, k, esz) - P * N * 4 + copy
+
+
+def gdn_replay_bytes_per_head(dv, dk, k, esz=2):
+    """GDN replay for one head at count k: state read + k-1 older entries (k, v, beta, g) + this
+    token read and appended (q, k, v, beta, g) + o written + pointers."""
+    entry_rd = dk * esz + dv * esz + 8
+    token = 2 * dk * esz + dv * esz + 8
+    return dv * dk * 4 + (k - 1) * entry_rd + 2 * token + dv * 4 + 12
+
+
+def gdn_conv_bytes_per_head(dv, dk, esz=2):
+    return 2 * dv * dk * 4 + 2 * dk * esz + dv * esz + 8 + dv * 4
+
+
+def timed_calls(n, fn):
+    """Run fn(i) for i < n with a HIP-event pair around each call on the current stream; returns
+    (wall seconds, per-call milliseconds)."""
+    import torch
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(n)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(n):
+        ev[i][0].record()
+        fn(i)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return wall, [a.elapsed_time(b) for a, b in ev]
+
+
+def bench_spec(dev, rounds=64, warm=16, pool=16):
+    """Speculative decoding on the serving shapes: each round appends 4 drafts per sequence and
+    verifies them in one replay call, then accepts U{0..4} per sequence and rolls back by moving
+    pointers (a fold fires whenever a sequence reaches L)."""
+    import torch
+    from ssm_decode_state_amd import binding as bd
+    from ssm_decode_state_amd import synth
+    w = synth.WORKLOADS["m2_b256_spec"]
+    shape = w["shape"]
+    Bn, H, P, N, L, S = shape.batch, shape.heads, shape.dim_p, shape.dim_n, shape.window, w["ndraft"]
+    A, D = synth.head_constants(shape, w["seed"])
+    h0 = synth.initial_state_device(shape, w["seed"], w["h0_std"])
+    cfg = bd.make_config(bd.SSM_MAMBA2, Bn, H, shape.groups, P, N, L, S, bd.SSM_IN_BF16)
+    st = bd.State(cfg, h0, A.to(dev), D.to(dev))
+    del h0
+    drafts = [synth.token_inputs_device(shape, w["seed"], "bench-draft", i, ntok=S)
+              for i in range(pool)]
+    accs = [synth.accept_counts(Bn, S, w["accept_seed"], r) for r in range(warm + rounds)]
+    accs_d = [a.to(dev) for a in accs]
+    y = torch.empty(Bn, S, H, P, device=dev)
+    counts = [0] * Bn  # host model of the committed counts, for the byte accounting
+
+    def advance(r):
+        for b in range(Bn):
+            counts[b] += int(accs[r][b])
+            if counts[b] >= L:
+                counts[b] -= L
+
+    for r in range(warm):
+        bd.ssm_spec_append(st, S, drafts[r % pool], y)
+        bd.ssm_spec_rollback(st, accs_d[r])
+        advance(r)
+    ver_bytes = 0.0
+    for r in range(warm, warm + rounds):
+        ver_bytes += H * sum(m2_verify_bytes_per_head(P, N, c, S) for c in counts)
+        advance(r)
+    # events are created up front: creating them inside the timed loop makes it host-bound
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(rounds)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(rounds):
+        r = warm + i
+        ev[i][0].record()
+        bd.ssm_spec_append(st, S, drafts[r % pool], y)
+        ev[i][1].record()
+        bd.ssm_spec_rollback(st, accs_d[r])
+        ev[i][2].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ver = sum(e[0].elapsed_time(e[1]) for e in ev)
+    rb = sum(e[1].elapsed_time(e[2]) for e in ev)
+    accepted = sum(int(accs[r].sum()) for r in range(warm, warm + rounds))
+    gbs = ver_bytes / (ver * 1e-3) / 1e9
+    return {"workload": "mamba2_spec_b256_4drafts", "accepted_tokens_per_s": accepted / wall,
+            "unit": "accepted tokens/s/layer", "rounds": rounds, "mean_accept": accepted / (Bn * rounds),
+            "verify_avg_us": ver / rounds * 1e3, "verify_achieved_gbs": gbs,
+            "verify_frac": gbs / HBM_PEAK_GBS,
+            "rollback_and_fold_avg_us": rb / rounds * 1e3, "ms_per_round": wall / rounds * 1e3}
+
+
+def bench_readcopy(dev, rc, steps=128, warm=16, layers=4, pool=16):
+    """Decode with the fp8 or fp4 read copy on `layers` rotated layer instances (the fp4 copy of
+    one layer fits the 256 MB last-level cache, so each step reads a different layer)."""
+    import torch
+    from ssm_decode_state_amd import binding as bd
+    from ssm_decode_state_amd import synth
+    w = synth.WORKLOADS["m2_b256_readcopy"]
+    shape = w["shape"]
+    Bn, H, P, N, L = shape.batch, shape.heads, shape.dim_p, shape.dim_n, shape.window
+    cfg = bd.make_config(bd.SSM_MAMBA2, Bn, H, shape.groups, P, N, L, 1, bd.SSM_IN_BF16, rc)
+    sts = []
+    for layer in range(layers):
+        A, D = synth.head_constants(shape, w["seed"], layer)
+        h0 = synth.initial_state_device(shape, w["seed"], w["h0_std"], layer)
+        sts.append(bd.State(cfg, h0, A.to(dev), D.to(dev)))
+        del h0
+    inputs = [synth.token_inputs_device(shape, w["seed"], "bench-rc", i) for i in range(pool)]
+    y = torch.empty(Bn, H, P, device=dev)
+    # every layer steps once per `layers` calls, so each layer's window advances in lock step
+    n_warm, n = warm * layers, steps * layers
+    for i in range(n_warm):
+        bd.ssm_replay_decode(sts[i % layers], inputs[i % pool], y)
+    wall, ms = timed_calls(n, lambda i: bd.ssm_replay_decode(sts[i % layers],
+                                                             inputs[(n_warm + i) % pool], y))
+    heads = Bn * H
+    rep_b = rep_ms = 0.0
+    flush_ms = []
+    for i, m in enumerate(ms):
+        k = ((n_warm + i) // layers) % L + 1
+        if k == L:
+            flush_ms.append(m)
+            continue
+        rep_b += heads * m2_rc_replay_bytes_per_head(P, N, k, rc)
+        rep_ms += m
+    gbs = rep_b / (rep_ms * 1e-3) / 1e9
+    return {"workload": "mamba2_readcopy_%s_b256" % ("fp8row" if rc == 1 else "fp4b16"),
+            "tokens_per_s": Bn * n / wall, "unit": "tokens/s/layer", "layers_rotated": layers,
+            "ms_per_step": wall / n * 1e3, "replay_avg_us": rep_ms / (n - len(flush_ms)) * 1e3,
+            "replay_achieved_gbs": gbs, "replay_frac": gbs / HBM_PEAK_GBS,
+            "fold_step_avg_us": sum(flush_ms) / max(len(flush_ms), 1) * 1e3}
+
+
+def bench_gdn(dev, steps=128, warm=16, layers=2, pool=16):
+    """Gated DeltaNet layer at B=256, H=32, dv=dk=128, L=16 on `layers` rotated layer instances:
+    replay path vs the conventional read-modify-write step."""
+    import torch
+    from ssm_decode_state_amd import binding as bd
+    from ssm_decode_state_amd import synth
+    w = synth.WORKLOADS["gdn_b256"]
+    shape = w["shape"]
+    Bn, H, dv, dk, L = shape.batch, shape.heads, shape.dim_p, shape.dim_n, shape.window
+    cfg = bd.make_config(bd.SSM_GDN, Bn, H, H, dv, dk, L, 1, bd.SSM_IN_BF16)
+    sts, convs = [], []
+    for layer in range(layers):
+        s0 = synth.initial_state_device(shape, w["seed"], w["h0_std"], layer)
+        sts.append(bd.State(cfg, s0, None, None))
+        t = torch.empty(Bn * H * dv * dk, device=dev)
+        bd.ssm_tiles_pack(cfg, s0, t)
+        convs.append(t)
+        del s0
+    inputs = [synth.token_inputs_device(shape, w["seed"], "bench-gdn", i) for i in range(pool)]
+    o = torch.empty(Bn, H, dv, device=dev)
+    n_warm, n = warm * layers, steps * layers
+    for i in range(n_warm):
+        bd.ssm_replay_decode(sts[i % layers], inputs[i % pool], o)
+    wall, ms = timed_calls(n, lambda i: bd.ssm_replay_decode(sts[i % layers],
+                                                             inputs[(n_warm + i) % pool], o))
+    heads = Bn * H
+    rep_b = rep_ms = 0.0
+    fold = []
+    for i, m in enumerate(ms):
+        k = ((n_warm + i) // layers) % L + 1
+        if k == L:
+            fold.append(m)
+            continue
+        rep_b += heads * gdn_replay_bytes_per_head(dv, dk, k)
+        rep_ms += m
+    gbs = rep_b / (rep_ms * 1e-3) / 1e9
+    for i in range(n_warm):
+        bd.ssm_conventional_step(cfg, convs[i % layers], inputs[i % pool], None, None, o)
+    cwall, cms = timed_calls(n, lambda i: bd.ssm_conventional_step(
+        cfg, convs[i % layers], inputs[(n_warm + i) % pool], None, None, o))
+    cgbs = heads * gdn_conv_bytes_per_head(dv, dk) / (sum(cms) / n * 1e-3) / 1e9
+    return {"workload": "gdn_replay_decode_b256", "tokens_per_s": Bn * n / wall,
+            "unit": "tokens/s/layer", "layers_rotated": layers, "ms_per_step": wall / n * 1e3,
+            "replay_avg_us": rep_ms / (n - len(fold)) * 1e3, "replay_achieved_gbs": gbs,
+            "replay_frac": gbs / HBM_PEAK_GBS,
+            "fold_step_avg_us": sum(fold) / max(len(fold), 1) * 1e3,
+            "conventional": {"tokens_per_s": Bn * n / cwall, "avg_us": sum(cms) / n * 1e3,
+                             "achieved_gbs": cgbs, "frac": cgbs / HBM_PEAK_GBS},
+            "speedup_vs_conventional": (Bn * n / wall) / (Bn * n / cwall)}
+
+
 def cpu_baseline(seconds_target: float = 10.0):
     """The fp64 oracle (sequential recurrence, OpenMP over heads) on a bounded sample of the
     serving workload: S sequences x all 128 heads x 16 tokens, S sized for ~seconds_target of
@@ -85,15 +281,19 @@ def cpu_baseline(seconds_target: float = 10.0):
     t0 = time.perf_counter()
     oracle.m2_sequential(*args)
     t_cal = time.perf_counter() - t0
-    nseq = int(max(1, min(full.batch, round(cal * seconds_target / max(t_cal, 1e-3)))))
+    want = cal * seconds_target / max(t_cal, 1e-3)  # sequences x 16 tokens for the target time
+    nseq = int(max(1, min(full.batch, round(want))))
+    reps = int(max(1, round(want / nseq)))  # beyond the full batch: repeat the same sample
     args = sample(nseq)
     t0 = time.perf_counter()
-    oracle.m2_sequential(*args)
+    for _ in range(reps):
+        oracle.m2_sequential(*args)
     el = time.perf_counter() - t0
-    return {"value": nseq * T / el, "unit": "tokens/s/layer", "cores": oracle.num_threads(),
+    return {"value": reps * nseq * T / el, "unit": "tokens/s/layer", "cores": oracle.num_threads(),
             "kind": "oracle",
-            "sample": "%d of 256 sequences x 128 heads x %d tokens of the serving workload, fp64 "
-                      "sequential recurrence (C, OpenMP over heads), %.1f s" % (nseq, T, el)}
+            "sample": "%d of 256 sequences x 128 heads x %d tokens of the serving workload, run %d "
+                      "time(s); fp64 sequential recurrence (C, OpenMP over heads), %.1f s"
+                      % (nseq, T, reps, el)}
 
 
 def torch_cat(ts):
@@ -110,6 +310,8 @@ def main():
     ap.add_argument("--skip-conv", action="store_true", help="skip the conventional comparison")
     ap.add_argument("--copy-ref", type=int, default=0,
                     help="also run a plain copy of this many MiB (reference for HBM counters)")
+    ap.add_argument("--workloads", default="all",
+                    help="comma list of extra workloads: spec, fp8, fp4, gdn; 'all' or 'none'")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -217,7 +419,6 @@ def main():
                                "ms_per_step": t_conv / K * 1e3, "avg_launch_us": conv_ms * 1e3,
                                "achieved_gbs": conv_gbs, "frac": conv_gbs / HBM_PEAK_GBS}
         out["speedup_vs_conventional"] = out["value"] / out["conventional"]["value"]
-        del tiles
 
     if args.copy_ref:
         n = args.copy_ref * (1 << 20) // 4
@@ -232,6 +433,27 @@ def main():
         torch.cuda.synchronize()
         out["copy_ref"] = {"bytes_read": 4 * n, "bytes_written": 4 * n, "launches": 5,
                            "avg_us": e0.elapsed_time(e1) / 5 * 1e3}
+
+    extra = ({"spec", "fp8", "fp4", "gdn"} if args.workloads == "all" else
+             set() if args.workloads == "none" else set(args.workloads.split(",")))
+    if extra:
+        del inputs, st, h0
+        if not args.skip_conv:
+            del tiles
+        torch.cuda.empty_cache()
+        out["workloads"] = {}
+        if "spec" in extra:
+            out["workloads"]["spec"] = bench_spec(dev)
+            torch.cuda.empty_cache()
+        if "fp8" in extra:
+            out["workloads"]["readcopy_fp8"] = bench_readcopy(dev, 1)
+            torch.cuda.empty_cache()
+        if "fp4" in extra:
+            out["workloads"]["readcopy_fp4"] = bench_readcopy(dev, 2)
+            torch.cuda.empty_cache()
+        if "gdn" in extra:
+            out["workloads"]["gdn"] = bench_gdn(dev)
+            torch.cuda.empty_cache()
 
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline()
