@@ -27,12 +27,6 @@ __device__ __forceinline__ int ring_slot(int start, int e, int cap) {
 // Sum over all 64 lanes, result in every lane.
 __device__ __forceinline__ float wave_sum(float v) { return xor_reduce_sum<1, 32>(v); }
 
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-}
-
 constexpr int kMaxWin = 32;  // largest window (entries a decode call can see)
 
 }  // namespace

@@ -113,76 +113,6 @@ __device__ __forceinline__ void rc_row_dots(const M2Args& a, long head, int row,
     }
 }
 
-template <int P, int N, int RC>
-__device__ __forceinline__ void rc_write(const M2Args& a, long head, int row,
-                                         const float4 (&hv)[N / 4]) {
-    static_assert(P == 64, "read copy needs P == 64");
-    float amax = 0.f;
-#pragma unroll
-    for (int q = 0; q < N / 4; ++q)
-        amax = fmaxf(amax, fmaxf(fmaxf(fabsf(hv[q].x), fabsf(hv[q].y)),
-                                 fmaxf(fabsf(hv[q].z), fabsf(hv[q].w))));
-    if constexpr (RC == 1) {
-        const float s = amax > 0.f ? amax / 448.f : 1.f;
-        const float inv = 1.f / s;
-        uint4* codes = reinterpret_cast<uint4*>(a.rc_codes + head * (long)(P * N));
-#pragma unroll
-        for (int k = 0; k < N / 16; ++k) {
-            uint32_t w[4];
-#pragma unroll
-            for (int qq = 0; qq < 4; ++qq) {
-                const float4 v = hv[4 * k + qq];
-                w[qq] = e4m3_encode(v.x * inv) | (e4m3_encode(v.y * inv) << 8) |
-                        (e4m3_encode(v.z * inv) << 16) | (e4m3_encode(v.w * inv) << 24);
-            }
-            codes[k * P + row] = make_uint4(w[0], w[1], w[2], w[3]);
-        }
-        static_cast<float*>(a.rc_scale)[head * P + row] = s;
-    } else {
-        const float amax_t = xor_reduce_max<1, 32>(amax);
-        const float st = amax_t > 0.f ? amax_t / 2688.f : 1.f;
-        const float d6 = 6.f * st;
-        uint4* codes = reinterpret_cast<uint4*>(a.rc_codes + head * (long)(P * N / 2));
-        uint32_t sbw[(N / 16 + 3) / 4];
-#pragma unroll
-        for (int i = 0; i < (N / 16 + 3) / 4; ++i) sbw[i] = 0;
-#pragma unroll
-        for (int k = 0; k < N / 32; ++k) {
-            uint32_t w[4] = {0, 0, 0, 0};
-#pragma unroll
-            for (int half = 0; half < 2; ++half) {
-                const int blk = 2 * k + half;
-                float ab = 0.f;
-#pragma unroll
-                for (int qq = 0; qq < 4; ++qq) {
-                    const float4 v = hv[4 * blk + qq];
-                    ab = fmaxf(ab, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
-                }
-                const uint32_t sb = e4m3_encode(ab / d6);
-                sbw[blk / 4] |= sb << (8 * (blk % 4));
-                const float S = e4m3_decode(sb) * st;
-                const float inv = S > 0.f ? 1.f / S : 0.f;
-#pragma unroll
-                for (int qq = 0; qq < 4; ++qq) {
-                    const float4 v = hv[4 * blk + qq];
-                    const float f[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int e = 16 * half + 4 * qq + i;  // element within the 32-unit
-                        const uint32_t c = S > 0.f ? e2m1_encode(f[i] * inv) : 0u;
-                        w[e / 8] |= c << (4 * (e % 8));
-                    }
-                }
-            }
-            codes[k * P + row] = make_uint4(w[0], w[1], w[2], w[3]);
-        }
-        uint8_t* sbp = static_cast<uint8_t*>(a.rc_scale) + (head * P + row) * (N / 16);
-        if constexpr (N / 16 >= 8) *reinterpret_cast<uint2*>(sbp) = make_uint2(sbw[0], sbw[1]);
-        else *reinterpret_cast<uint32_t*>(sbp) = sbw[0];
-        if (row == 0) a.rc_tscale[head] = st;
-    }
-}
-
 // ---------------------------------------------------------------------------------------------
 // Replay decode / speculative verify.
 //
@@ -454,99 +384,204 @@ __global__ __launch_bounds__(256) void m2_replay_kernel(M2Args a) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// Flush: fold the oldest nfold committed entries into the checkpoint (news, para 3):
+// Fold (flush): fold the oldest nfold committed entries into the checkpoint (news, para 3):
 //   h_c <- e^{s0} h_c + sum_{e < nfold} e^{s_e} dt_e x_e B_e^T,  s_e = A sum_{m=e+1..nfold-1} dt_m
-// nfold = L when count >= L (mode IF_FULL), = count (mode ALL), else nothing is folded. Then
-// start += nfold, count -= nfold, and the read copy (if any) is rewritten from the new h_c
-// (news, para 4: the low-precision copy is for reads only; the recurrence never sees it).
-// With rewrite_only the checkpoint is untouched and only the read copy is written (init).
-// Entries are folded in chunks of 16; the first chunk's B and x rows are fetched before the
-// checkpoint tile for the same in-order-counter reason as in the replay kernel.
+// a rank-nfold update, run on fp32 MFMA (v_mfma_f32_16x16x4f32) with the tile held in accumulator
+// order: lane l owns row 16 pb + l%16 and the quad 4 nb + l/16 of every 16x16 block (pb, nb), so
+// D[n][p] += sum_k B_k[n] a_k[p] with A = B-ring values and B = a_k[p] = e^{s_k} dt_k x_k[p].
+// Not FUSED: nfold = L when count >= L (IF_FULL), = count (ALL), else nothing; rewrite_only
+//   only rewrites the read copy (init). start += nfold, count -= nfold.
+// FUSED: the L-th token of a lock-step decode (count == L-1 for every sequence): the token's own
+//   inputs come from the caller and are folded with the L-1 buffered entries at once, its output
+//   is y = h_new C + D x (the recurrence's own form), and the ring is left empty. This saves the
+//   separate replay pass over the checkpoint on that step.
+// The read copy (news, para 4) is rewritten from the new fp32 checkpoint in the same pass.
 // ---------------------------------------------------------------------------------------------
-template <int P, int N, typename TIN, int RC>
-__global__ __launch_bounds__(256) void m2_flush_kernel(M2Args a, int mode_all, int rewrite_only) {
-    using G = M2Geo<P, N>;
+template <int P, int N, int RC>
+__device__ __forceinline__ void rc_write_blocks(const M2Args& a, int head, int li, int lg,
+                                                const f32x4 (&hb)[P / 16][N / 16]) {
+    static_assert(P == 64, "read copy needs P == 64");
+    constexpr int kPB = P / 16, kNB = N / 16;
+    if constexpr (RC == 1) {
+        uint8_t* codes = a.rc_codes + (long)head * (P * N);
+#pragma unroll
+        for (int pb = 0; pb < kPB; ++pb) {
+            float amax = 0.f;
+#pragma unroll
+            for (int nb = 0; nb < kNB; ++nb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) amax = fmaxf(amax, fabsf(hb[pb][nb][r]));
+            amax = xor_reduce_max<16, 32>(amax);  // the row is spread over lanes li + 16 lg
+            const float sc = amax > 0.f ? amax / 448.f : 1.f;
+            const float inv = 1.f / sc;
+            const int p = 16 * pb + li;
+#pragma unroll
+            for (int nb = 0; nb < kNB; ++nb) {
+                const uint32_t w = e4m3_encode(hb[pb][nb][0] * inv) | (e4m3_encode(hb[pb][nb][1] * inv) << 8) |
+                                   (e4m3_encode(hb[pb][nb][2] * inv) << 16) |
+                                   (e4m3_encode(hb[pb][nb][3] * inv) << 24);
+                *reinterpret_cast<uint32_t*>(codes + ((long)nb * P + p) * 16 + 4 * lg) = w;
+            }
+            if (lg == 0) static_cast<float*>(a.rc_scale)[(long)head * P + p] = sc;
+        }
+    } else {
+        float amax = 0.f;
+#pragma unroll
+        for (int pb = 0; pb < kPB; ++pb)
+#pragma unroll
+            for (int nb = 0; nb < kNB; ++nb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) amax = fmaxf(amax, fabsf(hb[pb][nb][r]));
+        const float amax_t = xor_reduce_max<1, 32>(amax);
+        const float st = amax_t > 0.f ? amax_t / 2688.f : 1.f;
+        const float d6 = 6.f * st;
+        uint8_t* codes = a.rc_codes + (long)head * (P * N / 2);
+        uint8_t* sbp = static_cast<uint8_t*>(a.rc_scale) + (long)head * P * (N / 16);
+#pragma unroll
+        for (int pb = 0; pb < kPB; ++pb) {
+            const int p = 16 * pb + li;
+#pragma unroll
+            for (int nb = 0; nb < kNB; ++nb) {
+                float ab = fmaxf(fmaxf(fabsf(hb[pb][nb][0]), fabsf(hb[pb][nb][1])),
+                                 fmaxf(fabsf(hb[pb][nb][2]), fabsf(hb[pb][nb][3])));
+                ab = xor_reduce_max<16, 32>(ab);  // the 16-element block spans lanes li + 16 lg
+                const uint32_t sb = e4m3_encode(ab / d6);
+                const float S = e4m3_decode(sb) * st;
+                const float inv = S > 0.f ? 1.f / S : 0.f;
+                uint32_t c = 0;
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    c |= (S > 0.f ? e2m1_encode(hb[pb][nb][r] * inv) : 0u) << (4 * r);
+                *reinterpret_cast<uint16_t*>(codes + ((long)(nb / 2) * P + p) * 16 + 8 * (nb % 2) + 2 * lg) =
+                    (uint16_t)c;
+                if (lg == 0) sbp[p * (N / 16) + nb] = (uint8_t)sb;
+            }
+        }
+        if (threadIdx.x % 64 == 0) a.rc_tscale[head] = st;
+    }
+}
+
+template <int P, int N, typename TIN, int RC, bool FUSED>
+__global__ __launch_bounds__(256)
+__attribute__((amdgpu_waves_per_eu(2))) void m2_fold_kernel(M2Args a, int mode_all, int rewrite_only) {
+    constexpr int kPB = P / 16, kNB = N / 16;
     constexpr int kEPC = 16 / (int)sizeof(TIN);
     constexpr int kBCR = N / kEPC;                 // 16-byte chunks per B row
     constexpr int kBL = (16 * kBCR + 63) / 64;     // B chunks per lane (16 rows)
     constexpr int kXCR = P / kEPC;                 // chunks per x row
     constexpr int kXL = (16 * kXCR + 63) / 64;
-    __shared__ __attribute__((aligned(16))) float s_b[kHeadsPerBlock][16][N];
+    constexpr int kBP = N + 16;                    // padded LDS row: the 4 rows an MFMA reads
+    constexpr int kCE = N >= 64 ? N / 64 : 1;      //   land in disjoint banks
+    __shared__ __attribute__((aligned(16))) float s_b[kHeadsPerBlock][16][kBP];
     __shared__ __attribute__((aligned(16))) u32x4_t s_x[kHeadsPerBlock][16 * kXCR];
+    __shared__ __attribute__((aligned(16))) float s_c[kHeadsPerBlock][FUSED ? N : 4];
 
     const int wave = uniform(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int h = blockIdx.x * kHeadsPerBlock + wave;
     if (h >= a.heads) return;
     const int b = blockIdx.y;
-    const int head = b * a.heads + h;
-    const int grp = h / (a.heads / a.groups);
+    const int H = a.heads;
+    const int head = b * H + h;
+    const int grp = h / (H / a.groups);
     const int bg = b * a.groups + grp;
     const int cap = a.cap;
     const int2 pt = *reinterpret_cast<const int2*>(a.ptr + 2 * head);
     const int start = uniform(pt.x);
     const int count = uniform(pt.y);
-    const int nfold = rewrite_only ? 0 : (mode_all ? count : (count >= a.window ? a.window : 0));
-    if (nfold == 0 && !rewrite_only) return;
-    const int row = lane % P, gq = lane / P;
+    int nfold, nring;
+    if constexpr (FUSED) {
+        nfold = count + 1;  // the buffered entries and this token
+        nring = count;
+    } else {
+        nfold = rewrite_only ? 0 : (mode_all ? count : (count >= a.window ? a.window : 0));
+        if (nfold == 0 && !rewrite_only) return;
+        nring = nfold;
+    }
+    const int li = lane & 15, lg = lane >> 4;
     const TIN* rx = static_cast<const TIN*>(a.ring_x);
     const TIN* rB = static_cast<const TIN*>(a.ring_B);
+    const long tok = (long)b * H + h;  // FUSED: this token's row of the [batch][1][H] inputs
 
-    float dte = a.ring_dt[head * cap + ring_slot(start, min(lane, cap - 1), cap)];
-    dte = lane < nfold ? dte : 0.f;
-    const float A = a.A[h];
-
-    // chunk loader: B rows and x rows of entries c0 .. c0+15 into registers
+    // entry e's rows: ring slot for e < nring, the caller's token otherwise (FUSED), clamped to a
+    // folded entry past nfold (those rows are zeroed in LDS)
+    auto brow = [&](int e) -> const TIN* {
+        if (FUSED && e >= nring)
+            return static_cast<const TIN*>(a.in_B) + ((long)b * a.groups + grp) * N;
+        return rB + ((long)bg * cap + ring_slot(start, min(e, max(nring - 1, 0)), cap)) * N;
+    };
+    auto xrow = [&](int e) -> const TIN* {
+        if (FUSED && e >= nring) return static_cast<const TIN*>(a.in_x) + tok * P;
+        return rx + ((long)head * cap + ring_slot(start, min(e, max(nring - 1, 0)), cap)) * P;
+    };
     u32x4_t braw[kBL], xraw[kXL];
-    auto fetch = [&](int c0) {  // branch-free: rows past nfold re-read the last folded row
+    auto fetch = [&](int c0) {
 #pragma unroll
         for (int i = 0; i < kBL; ++i) {
             const int idx = (lane + 64 * i) % (16 * kBCR);
-            const int e = min(c0 + idx / kBCR, nfold - 1), part = idx % kBCR;
-            braw[i] = *reinterpret_cast<const u32x4_t*>(rB + ((long)bg * cap + ring_slot(start, e, cap)) * N +
-                                                      part * kEPC);
+            braw[i] = *reinterpret_cast<const u32x4_t*>(brow(c0 + idx / kBCR) + (idx % kBCR) * kEPC);
         }
 #pragma unroll
         for (int i = 0; i < kXL; ++i) {
             const int idx = (lane + 64 * i) % (16 * kXCR);
-            const int e = min(c0 + idx / kXCR, nfold - 1), part = idx % kXCR;
-            xraw[i] = *reinterpret_cast<const u32x4_t*>(rx + ((long)head * cap + ring_slot(start, e, cap)) * P +
-                                                      part * kEPC);
+            xraw[i] = *reinterpret_cast<const u32x4_t*>(xrow(c0 + idx / kXCR) + (idx % kXCR) * kEPC);
         }
     };
+    float dte;
+    {
+        const float* src = (FUSED && lane >= nring)
+                               ? a.in_dt + tok
+                               : a.ring_dt + (long)head * cap + ring_slot(start, min(lane, cap - 1), cap);
+        dte = *src;
+        dte = lane < nfold ? dte : 0.f;
+    }
+    const float A = a.A[h];  // before the stream: a later load would wait for all of it
+    const float D = FUSED ? a.D[h] : 0.f;
+    TIN craw[kCE];
+    if constexpr (FUSED) {
+        const TIN* inC = static_cast<const TIN*>(a.in_C) + ((long)b * a.groups + grp) * N;
+#pragma unroll
+        for (int i = 0; i < kCE; ++i) craw[i] = inC[(lane + 64 * i) % N];
+    }
     if (nfold > 0) fetch(0);
 
-    float4 hv[G::kQPL];
+    f32x4 hb[kPB][kNB];
     float4* tile = reinterpret_cast<float4*>(a.ckpt) + (long)head * (P * N / 4);
 #pragma unroll
-    for (int j = 0; j < G::kQPL; ++j) hv[j] = ld_stream(tile + (gq + G::kGrp * j) * P + row);
+    for (int pb = 0; pb < kPB; ++pb)
+#pragma unroll
+        for (int nb = 0; nb < kNB; ++nb) {
+            const float4 t = ld_stream(tile + (4 * nb + lg) * P + 16 * pb + li);
+            hb[pb][nb] = f32x4{t.x, t.y, t.z, t.w};
+        }
     asm volatile("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
 
     if (nfold > 0) {
-        // u_e = e^{s_e} dt_e in lane e; e^{s0} uniform
-        float suf = 0.f, tot = 0.f;
+        float suf = 0.f, tot = 0.f;  // suffix sum of dt after lane's entry; total
         for (int m = 0; m < nfold; ++m) {
             const float dm = readlane(dte, m);
             tot += dm;
             suf += (m > lane) ? dm : 0.f;
         }
-        const float ue = expf(A * suf) * dte;
+        const float ue = expf(A * suf) * dte;  // zero past nfold
         const float e0 = expf(A * tot);
-        bool first = true;
+        if constexpr (FUSED) {
+#pragma unroll
+            for (int i = 0; i < kCE; ++i) s_c[wave][(lane + 64 * i) % N] = to_f32<TIN>(craw[i]);
+        }
         for (int c0 = 0; c0 < nfold; c0 += 16) {
-            const int nc = min(16, nfold - c0);
             if (c0 > 0) fetch(c0);
-            // stage the chunk: B rows as fp32, x rows raw
+            const int nc = min(16, nfold - c0);
 #pragma unroll
             for (int i = 0; i < kBL; ++i) {
                 const int idx = lane + 64 * i;
                 if (idx < 16 * kBCR) {
+                    const int r = idx / kBCR, part = idx % kBCR;
                     float f[kEPC];
                     Unit<TIN>::unpack(make_uint4(braw[i].x, braw[i].y, braw[i].z, braw[i].w), f);
-                    const int r = idx / kBCR, part = idx % kBCR;
 #pragma unroll
-                    for (int k = 0; k < kEPC; ++k) s_b[wave][r][part * kEPC + k] = f[k];
+                    for (int k = 0; k < kEPC; ++k) s_b[wave][r][part * kEPC + k] = r < nc ? f[k] : 0.f;
                 }
             }
 #pragma unroll
@@ -555,38 +590,59 @@ __global__ __launch_bounds__(256) void m2_flush_kernel(M2Args a, int mode_all, i
                 if (idx < 16 * kXCR) s_x[wave][idx] = xraw[i];
             }
             wave_sync();
-            if (first) {
+            if (c0 == 0) {  // decay of the old checkpoint, applied once the staging is done
 #pragma unroll
-                for (int j = 0; j < G::kQPL; ++j) {
-                    hv[j].x *= e0; hv[j].y *= e0; hv[j].z *= e0; hv[j].w *= e0;
-                }
-                first = false;
+                for (int pb = 0; pb < kPB; ++pb)
+#pragma unroll
+                    for (int nb = 0; nb < kNB; ++nb) hb[pb][nb] *= e0;
             }
             const TIN* sx = reinterpret_cast<const TIN*>(&s_x[wave][0]);
-            float ax[16];
 #pragma unroll
-            for (int i = 0; i < 16; ++i)
-                ax[i] = (i < nc) ? readlane(ue, c0 + i) * to_f32<TIN>(sx[i * P + row]) : 0.f;
+            for (int g = 0; g < 4; ++g) {
+                if (4 * g >= nc) break;
+                const int ek = 4 * g + lg;                       // this lane's k-slot entry
+                const float uk = __shfl(ue, (c0 + ek) & 63, 64);  // per-lane entry: shuffle
+                float aop[kPB], bop[kNB];
 #pragma unroll
-            for (int j = 0; j < G::kQPL; ++j) {
-                const int q = gq + G::kGrp * j;
+                for (int pb = 0; pb < kPB; ++pb) aop[pb] = uk * to_f32<TIN>(sx[ek * P + 16 * pb + li]);
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    if (i >= nc) break;
-                    const float4 b4 = *reinterpret_cast<const float4*>(&s_b[wave][i][4 * q]);
-                    hv[j].x += ax[i] * b4.x; hv[j].y += ax[i] * b4.y;
-                    hv[j].z += ax[i] * b4.z; hv[j].w += ax[i] * b4.w;
-                }
+                for (int nb = 0; nb < kNB; ++nb) bop[nb] = s_b[wave][ek][16 * nb + li];
+#pragma unroll
+                for (int pb = 0; pb < kPB; ++pb)
+#pragma unroll
+                    for (int nb = 0; nb < kNB; ++nb) hb[pb][nb] = mfma4(bop[nb], aop[pb], hb[pb][nb]);
             }
             wave_sync();
         }
 #pragma unroll
-        for (int j = 0; j < G::kQPL; ++j) st_stream(hv[j], tile + (gq + G::kGrp * j) * P + row);
+        for (int pb = 0; pb < kPB; ++pb)
+#pragma unroll
+            for (int nb = 0; nb < kNB; ++nb)
+                st_stream(make_float4(hb[pb][nb][0], hb[pb][nb][1], hb[pb][nb][2], hb[pb][nb][3]),
+                          tile + (4 * nb + lg) * P + 16 * pb + li);
     }
-    if constexpr (RC != 0) rc_write<P, N, RC>(a, head, row, hv);  // P == 64: kQPL == N/4
+    if constexpr (FUSED) {  // output from the new state: y = h C + D x
+        const TIN* xin = static_cast<const TIN*>(a.in_x) + tok * P;
+#pragma unroll
+        for (int pb = 0; pb < kPB; ++pb) {
+            float part = 0.f;
+#pragma unroll
+            for (int nb = 0; nb < kNB; ++nb) {
+                const float4 c4 = *reinterpret_cast<const float4*>(&s_c[wave][16 * nb + 4 * lg]);
+                part += hb[pb][nb][0] * c4.x + hb[pb][nb][1] * c4.y + hb[pb][nb][2] * c4.z +
+                        hb[pb][nb][3] * c4.w;
+            }
+            part = xor_reduce_sum<16, 32>(part);
+            if (lg == 0) {
+                const int p = 16 * pb + li;
+                a.y[tok * P + p] = part + D * to_f32<TIN>(xin[p]);
+            }
+        }
+    }
+    if constexpr (RC != 0) rc_write_blocks<P, N, RC>(a, head, li, lg, hb);
     if (nfold > 0 && lane == 0) {
         a.ptr[2 * head] = ring_slot(start, nfold, cap);
-        a.ptr[2 * head + 1] = count - nfold;
+        a.ptr[2 * head + 1] = (FUSED ? count + 1 : count) - nfold;
     }
 }
 
@@ -680,8 +736,12 @@ static hipError_t launch_replay_pn(const M2Args& a, bool spec, int maxe, hipStre
 }
 template <int P, int N, typename TIN, int RC>
 static hipError_t launch_flush_pn(const M2Args& a, int mode_all, int rewrite_only, hipStream_t s) {
-    hipLaunchKernelGGL((m2_flush_kernel<P, N, TIN, RC>), head_grid(a.batch, a.heads), dim3(256), 0,
-                       s, a, mode_all, rewrite_only);
+    if (mode_all == 2)  // fused decode + fold of the L-th lock-step token
+        hipLaunchKernelGGL((m2_fold_kernel<P, N, TIN, RC, true>), head_grid(a.batch, a.heads),
+                           dim3(256), 0, s, a, 0, 0);
+    else
+        hipLaunchKernelGGL((m2_fold_kernel<P, N, TIN, RC, false>), head_grid(a.batch, a.heads),
+                           dim3(256), 0, s, a, mode_all, rewrite_only);
     return hipGetLastError();
 }
 template <int P, int N, typename TIN>

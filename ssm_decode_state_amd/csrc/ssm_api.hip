@@ -269,6 +269,16 @@ ssm_status ssm_replay_decode(ssm_state* st, const void* in, float* y, void* stre
         a.in_x = m->x; a.in_B = m->B; a.in_C = m->C; a.in_dt = m->dt;
         a.y = y;
         a.ntok = 1;
+        const int L = st->cfg.window;
+        if (st->count_lo == L - 1 && st->count_hi == L - 1) {
+            // lock step and this token completes every window: one pass folds the window and
+            // emits the output from the new checkpoint (no replay pass, no ring append)
+            e = ssm::m2_launch_flush(a, st->cfg.dim_p, st->cfg.dim_n, st->cfg.in_dtype,
+                                     st->cfg.readcopy, 2, 0, hs);
+            if (e != hipSuccess) return SSM_E_HIP;
+            st->count_lo = st->count_hi = 0;
+            return SSM_OK;
+        }
         e = ssm::m2_launch_replay(a, st->cfg.dim_p, st->cfg.dim_n, st->cfg.in_dtype,
                                   st->cfg.readcopy, false, st->count_hi + 1, hs);
     } else {

@@ -173,6 +173,13 @@ __device__ __forceinline__ float readlane(float v, int lane) {
 }
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
+// fp32 MFMA 16x16x4 (v_mfma_f32_16x16x4f32): D = A (16x4) * B (4x16) + C. Operand lanes:
+// A[m][k] from lane m + 16k, B[k][c] from lane c + 16k, D[m][c] in lane c + 16(m/4), register m%4.
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
 // ---------------------------------------------------------------------------------------------
 // OCP low-precision codecs, written from the format definitions (OCP OFP8 E4M3: bias 7, three
 // mantissa bits, max 448, no infinity; OCP MX E2M1: bias 1, one mantissa bit, max 6).

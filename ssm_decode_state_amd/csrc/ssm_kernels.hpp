@@ -73,6 +73,8 @@ struct GdnConvArgs {
 // maxe: upper bound on count + ntok over all sequences (<= 64).
 hipError_t m2_launch_replay(const M2Args& a, int P, int N, int bf16, int rc, bool spec, int maxe,
                             hipStream_t s);
+// mode_all: 0 = fold L entries where count >= L, 1 = fold every committed entry, 2 = fused
+// decode + fold of the L-th lock-step token (inputs and y in `a`, ntok = 1).
 hipError_t m2_launch_flush(const M2Args& a, int P, int N, int bf16, int rc, int mode_all,
                            int rewrite_only, hipStream_t s);
 hipError_t m2_launch_conv(const M2ConvArgs& a, int P, int N, int bf16, hipStream_t s);
