@@ -207,8 +207,12 @@ ssm_status ssm_tiles_unpack(const ssm_config *cfg, const float *tiles, float *na
                             void *stream);
 
 /* Test hook: run the device's OCP codecs over n elements (op 0: fp32 -> E4M3 code, 1: E4M3 code
- * -> fp32, 2: fp32 -> E2M1 code, 3: E2M1 code -> fp32; codes are one per byte). Lets tests check
- * the read-copy encoder bit for bit against the format definitions. */
+ * -> fp32, 2: fp32 -> E2M1 code, 3: E2M1 code -> fp32; codes are one per byte; ops 4..7: the same
+ * four through the gfx950 conversion instructions; ops 8..11: packed 32-bit words, n = words:
+ * 8 E4M3 word -> 4 fp32, 9 E2M1 word -> 8 fp32, 10 4 fp32 -> E4M3 word, 11 8 fp32 -> E2M1 word,
+ * element i in byte i / nibble i, low nibble first). n counts work items (values, codes or words
+ * as listed); `in` and `out` must hold n items each -- they are not checked. Lets tests check the
+ * read-copy codecs bit for bit against the format definitions. */
 ssm_status ssm_debug_codec(int32_t op, const void *in, void *out, int64_t n, void *stream);
 
 #ifdef __cplusplus

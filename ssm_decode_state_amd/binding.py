@@ -217,9 +217,23 @@ def ssm_tiles_unpack(cfg: ssm_config, tiles: torch.Tensor, natural: torch.Tensor
                                                      _ptr(natural), _stream(stream)))
 
 
+# bytes of input and output per work item of each ssm_debug_codec op
+_CODEC_IO = {0: (4, 1), 1: (1, 4), 2: (4, 1), 3: (1, 4), 4: (4, 1), 5: (1, 4), 6: (4, 1),
+             7: (1, 4), 8: (4, 16), 9: (4, 32), 10: (16, 4), 11: (32, 4)}
+
+
 def ssm_debug_codec(op: int, inp: torch.Tensor, out: torch.Tensor, stream=None) -> None:
-    _check("ssm_debug_codec", _lib.ssm_debug_codec(op, _ptr(inp), _ptr(out), inp.numel(),
-                                                   _stream(stream)))
+    """n = number of work items implied by the input size; both buffers are checked to hold n
+    items (the C entry point takes plain pointers and cannot check)."""
+    if op not in _CODEC_IO:
+        raise ValueError("unknown codec op %d" % op)
+    bi, bo = _CODEC_IO[op]
+    nin = inp.numel() * inp.element_size()
+    n = nin // bi
+    if n * bi != nin or out.numel() * out.element_size() < n * bo:
+        raise ValueError("codec op %d: input of %d bytes / output of %d bytes do not match"
+                         % (op, nin, out.numel() * out.element_size()))
+    _check("ssm_debug_codec", _lib.ssm_debug_codec(op, _ptr(inp), _ptr(out), n, _stream(stream)))
 
 
 class State:

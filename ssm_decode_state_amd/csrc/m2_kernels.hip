@@ -61,7 +61,12 @@ __device__ __forceinline__ void rc_row_dots(const M2Args& a, long head, int row,
             const uint32_t w[4] = {u[k].x, u[k].y, u[k].z, u[k].w};
             float v[16];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) v[i] = e4m3_decode((w[i / 4] >> (8 * (i % 4))) & 0xff);
+            for (int q = 0; q < 4; ++q) {
+                float o[4];
+                e4m3_word_decode(w[q], o);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) v[4 * q + i] = o[i];
+            }
 #pragma unroll
             for (int j = 0; j < MAXQ; ++j) {
                 if (j >= nq) break;
@@ -94,11 +99,13 @@ __device__ __forceinline__ void rc_row_dots(const M2Args& a, long head, int row,
             for (int half = 0; half < 2; ++half) {
                 const int blk = 2 * k + half;
                 const float S = e4m3_decode((sbw[blk / 4] >> (8 * (blk % 4))) & 0xff) * st;
-                float v[16];
+                float v[16];  // elements 16 half .. 16 half + 15 of the 32-element unit
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int e = 16 * half + i;  // element within the 32-element unit
-                    v[i] = e2m1_decode((w[e / 8] >> (4 * (e % 8))) & 0xf);
+                for (int q = 0; q < 2; ++q) {
+                    float o[8];
+                    e2m1_word_decode(w[2 * half + q], o);
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) v[8 * q + i] = o[i];
                 }
 #pragma unroll
                 for (int j = 0; j < MAXQ; ++j) {
@@ -417,9 +424,8 @@ __device__ __forceinline__ void rc_write_blocks(const M2Args& a, int head, int l
             const int p = 16 * pb + li;
 #pragma unroll
             for (int nb = 0; nb < kNB; ++nb) {
-                const uint32_t w = e4m3_encode(hb[pb][nb][0] * inv) | (e4m3_encode(hb[pb][nb][1] * inv) << 8) |
-                                   (e4m3_encode(hb[pb][nb][2] * inv) << 16) |
-                                   (e4m3_encode(hb[pb][nb][3] * inv) << 24);
+                const uint32_t w = e4m3_word_encode(hb[pb][nb][0] * inv, hb[pb][nb][1] * inv,
+                                                    hb[pb][nb][2] * inv, hb[pb][nb][3] * inv);
                 *reinterpret_cast<uint32_t*>(codes + ((long)nb * P + p) * 16 + 4 * lg) = w;
             }
             if (lg == 0) static_cast<float*>(a.rc_scale)[(long)head * P + p] = sc;
@@ -448,10 +454,9 @@ __device__ __forceinline__ void rc_write_blocks(const M2Args& a, int head, int l
                 const uint32_t sb = e4m3_encode(ab / d6);
                 const float S = e4m3_decode(sb) * st;
                 const float inv = S > 0.f ? 1.f / S : 0.f;
-                uint32_t c = 0;
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    c |= (S > 0.f ? e2m1_encode(hb[pb][nb][r] * inv) : 0u) << (4 * r);
+                const uint32_t c = S > 0.f ? e2m1_half_encode(hb[pb][nb][0] * inv, hb[pb][nb][1] * inv,
+                                                              hb[pb][nb][2] * inv, hb[pb][nb][3] * inv)
+                                           : 0u;
                 *reinterpret_cast<uint16_t*>(codes + ((long)(nb / 2) * P + p) * 16 + 8 * (nb % 2) + 2 * lg) =
                     (uint16_t)c;
                 if (lg == 0) sbp[p * (N / 16) + nb] = (uint8_t)sb;

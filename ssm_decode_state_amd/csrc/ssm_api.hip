@@ -430,7 +430,7 @@ ssm_status ssm_tiles_unpack(const ssm_config* cfg, const float* tiles, float* na
 }
 
 ssm_status ssm_debug_codec(int32_t op, const void* in, void* out, int64_t n, void* stream) {
-    if (op < 0 || op > 3 || n < 0) return SSM_E_ARG;
+    if (op < 0 || op > 11 || n < 0) return SSM_E_ARG;
     if (n > 0 && (!in || !out)) return SSM_E_ARG;
     return hip_status(ssm::launch_codec(op, in, out, (long)n, as_stream(stream)));
 }

@@ -227,4 +227,52 @@ __device__ __forceinline__ float e2m1_decode(uint32_t c) {
     return (c & 8) ? -mag : mag;
 }
 
+// Hardware conversions (gfx950): two codes per instruction; the half/byte selector is a
+// compile-time operand. Used only where a device test has shown them equal to the software codecs
+// above for every code and for the tested inputs.
+template <bool HI>
+__device__ __forceinline__ float2 e4m3x2_decode_hw(uint32_t word) {
+    const auto v = __builtin_amdgcn_cvt_pk_f32_fp8(word, HI);
+    return make_float2(v[0], v[1]);
+}
+template <int BYTE>
+__device__ __forceinline__ float2 e2m1x2_decode_hw(uint32_t word) {
+    const auto v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, BYTE);
+    return make_float2(v[0], v[1]);
+}
+// Encode two values (already inside +-448) into the selected 16-bit half of `old`.
+template <bool HI>
+__device__ __forceinline__ uint32_t e4m3x2_encode_hw(float a, float b, uint32_t old) {
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)old, HI);
+}
+// Encode two values (already inside +-6) into byte BYTE of `old`.
+template <int BYTE>
+__device__ __forceinline__ uint32_t e2m1x2_encode_hw(float a, float b, uint32_t old) {
+    return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, 1.0f, BYTE);
+}
+
+// Packed-word codecs built on the instructions above. Byte i of an E4M3 word is element i;
+// nibble i of an E2M1 word (low nibble first) is element i. Encoders take fp32 values already
+// multiplied by the inverse scale and saturate like the software encoders.
+__device__ __forceinline__ void e4m3_word_decode(uint32_t w, float (&o)[4]) {
+    const float2 lo = e4m3x2_decode_hw<false>(w), hi = e4m3x2_decode_hw<true>(w);
+    o[0] = lo.x; o[1] = lo.y; o[2] = hi.x; o[3] = hi.y;
+}
+__device__ __forceinline__ void e2m1_word_decode(uint32_t w, float (&o)[8]) {
+    const float2 b0 = e2m1x2_decode_hw<0>(w), b1 = e2m1x2_decode_hw<1>(w);
+    const float2 b2 = e2m1x2_decode_hw<2>(w), b3 = e2m1x2_decode_hw<3>(w);
+    o[0] = b0.x; o[1] = b0.y; o[2] = b1.x; o[3] = b1.y;
+    o[4] = b2.x; o[5] = b2.y; o[6] = b3.x; o[7] = b3.y;
+}
+__device__ __forceinline__ float sat(float x, float m) { return fminf(fmaxf(x, -m), m); }
+__device__ __forceinline__ uint32_t e4m3_word_encode(float a, float b, float c, float d) {
+    const uint32_t lo = e4m3x2_encode_hw<false>(sat(a, 448.f), sat(b, 448.f), 0u);
+    return e4m3x2_encode_hw<true>(sat(c, 448.f), sat(d, 448.f), lo);
+}
+// Four E2M1 codes (16 bits) from four values.
+__device__ __forceinline__ uint32_t e2m1_half_encode(float a, float b, float c, float d) {
+    const uint32_t lo = e2m1x2_encode_hw<0>(sat(a, 6.f), sat(b, 6.f), 0u);
+    return e2m1x2_encode_hw<1>(sat(c, 6.f), sat(d, 6.f), lo) & 0xffffu;
+}
+
 }  // namespace ssm

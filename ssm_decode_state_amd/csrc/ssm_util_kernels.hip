@@ -38,14 +38,48 @@ __global__ void pack_kernel(const float* __restrict__ src, float* __restrict__ d
         *reinterpret_cast<float4*>(dst + til) = *reinterpret_cast<const float4*>(src + nat);
 }
 
-// op 0: fp32 -> E4M3 code; 1: E4M3 code -> fp32; 2: fp32 -> E2M1 code; 3: E2M1 code -> fp32.
+// op 0: fp32 -> E4M3 code; 1: E4M3 code -> fp32; 2: fp32 -> E2M1 code; 3: E2M1 code -> fp32
+// (software codecs). ops 4..7: the same through the gfx950 conversion instructions, encoding
+// after clamping to the format's largest magnitude.
 __global__ void codec_kernel(int op, const void* __restrict__ in, void* __restrict__ out, long n) {
     const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= n) return;
-    if (op == 0) static_cast<uint8_t*>(out)[i] = (uint8_t)e4m3_encode(static_cast<const float*>(in)[i]);
-    else if (op == 1) static_cast<float*>(out)[i] = e4m3_decode(static_cast<const uint8_t*>(in)[i]);
-    else if (op == 2) static_cast<uint8_t*>(out)[i] = (uint8_t)e2m1_encode(static_cast<const float*>(in)[i]);
-    else static_cast<float*>(out)[i] = e2m1_decode(static_cast<const uint8_t*>(in)[i]);
+    const float* fin = static_cast<const float*>(in);
+    const uint8_t* cin = static_cast<const uint8_t*>(in);
+    uint8_t* cout = static_cast<uint8_t*>(out);
+    float* fout = static_cast<float*>(out);
+    switch (op) {
+        case 0: cout[i] = (uint8_t)e4m3_encode(fin[i]); break;
+        case 1: fout[i] = e4m3_decode(cin[i]); break;
+        case 2: cout[i] = (uint8_t)e2m1_encode(fin[i]); break;
+        case 3: fout[i] = e2m1_decode(cin[i]); break;
+        case 4: cout[i] = (uint8_t)(e4m3x2_encode_hw<false>(fminf(fmaxf(fin[i], -448.f), 448.f), 0.f, 0u) & 0xff); break;
+        case 5: fout[i] = e4m3x2_decode_hw<false>(cin[i]).x; break;
+        case 6: cout[i] = (uint8_t)(e2m1x2_encode_hw<0>(fminf(fmaxf(fin[i], -6.f), 6.f), 0.f, 0u) & 0xf); break;
+        case 7: fout[i] = e2m1x2_decode_hw<0>(cin[i]).x; break;
+        // packed words (n = number of 32-bit words): the helpers the read-copy kernels use
+        case 8: {
+            float o[4];
+            e4m3_word_decode(static_cast<const uint32_t*>(in)[i], o);
+            for (int k = 0; k < 4; ++k) fout[4 * i + k] = o[k];
+            break;
+        }
+        case 9: {
+            float o[8];
+            e2m1_word_decode(static_cast<const uint32_t*>(in)[i], o);
+            for (int k = 0; k < 8; ++k) fout[8 * i + k] = o[k];
+            break;
+        }
+        case 10:
+            static_cast<uint32_t*>(out)[i] =
+                e4m3_word_encode(fin[4 * i], fin[4 * i + 1], fin[4 * i + 2], fin[4 * i + 3]);
+            break;
+        default:
+            static_cast<uint32_t*>(out)[i] =
+                e2m1_half_encode(fin[8 * i], fin[8 * i + 1], fin[8 * i + 2], fin[8 * i + 3]) |
+                (e2m1_half_encode(fin[8 * i + 4], fin[8 * i + 5], fin[8 * i + 6], fin[8 * i + 7]) << 16);
+            break;
+    }
 }
 
 static unsigned blocks_for(long n, int bs) { return (unsigned)((n + bs - 1) / bs); }

@@ -89,6 +89,7 @@ def test_layout_read_copies():
     (dict(readcopy=bd.SSM_RC_FP8_ROW, dim_p=32, dim_n=64), bd.SSM_E_UNSUPPORTED),
     (dict(kind=bd.SSM_GDN, groups=64), bd.SSM_E_SHAPE),
     (dict(kind=bd.SSM_GDN, readcopy=bd.SSM_RC_FP8_ROW), bd.SSM_E_UNSUPPORTED),
+    (dict(kind=bd.SSM_GDN, dim_p=32), bd.SSM_E_SHAPE),
 ])
 def test_bad_configs_rejected(kw, status):
     with pytest.raises(bd.SSMError) as ei:
@@ -199,5 +200,6 @@ def test_conventional_and_pack_validation():
     bad = cfg(dim_p=48)
     assert raw("ssm_tiles_pack", ctypes.byref(bad), v(FAKE), v(FAKE), None) == bd.SSM_E_SHAPE
     assert raw("ssm_tiles_unpack", ctypes.byref(c), None, v(FAKE), None) == bd.SSM_E_ARG
-    assert raw("ssm_debug_codec", 9, v(FAKE), v(FAKE), 4, None) == bd.SSM_E_ARG
+    assert raw("ssm_debug_codec", 12, v(FAKE), v(FAKE), 4, None) == bd.SSM_E_ARG
+    assert raw("ssm_debug_codec", -1, v(FAKE), v(FAKE), 4, None) == bd.SSM_E_ARG
     assert raw("ssm_debug_codec", 0, None, None, 0, None) == bd.SSM_OK  # empty: nothing to do

@@ -208,3 +208,67 @@ def test_codecs_match_format_definitions():
     bd.ssm_debug_codec(2, torch.from_numpy(v2).to(DEV), enc2)
     np.testing.assert_array_equal(enc2.cpu().numpy(), quant.e2m1_encode(v2))
     del codes
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e2m1"])
+def test_hardware_conversions_match_format_definitions(fmt):
+    """The gfx950 conversion instructions against the OCP definitions: decode of every code, and
+    encode (after clamping to the largest magnitude) of random values, exact midpoints (ties to
+    even), subnormals and saturating values."""
+    from oracle import quant
+    rng = np.random.default_rng(3)
+    if fmt == "e4m3":
+        codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+        dec_op, enc_op, table, top = 5, 4, quant.E4M3, 0x7E
+        enc, dec = quant.e4m3_encode, quant.e4m3_decode
+        scale = 40.0
+    else:
+        codes = np.arange(16, dtype=np.uint8)
+        dec_op, enc_op, table, top = 7, 6, quant.E2M1, 0x7
+        enc, dec = quant.e2m1_encode, quant.e2m1_decode
+        scale = 3.0
+    out = torch.empty(codes.size, device=DEV)
+    bd.ssm_debug_codec(dec_op, torch.from_numpy(codes).to(DEV), out)
+    np.testing.assert_array_equal(out.cpu().numpy(), dec(codes))
+    mags = table[:top + 1]
+    mids = (mags[1:] + mags[:-1]) / 2
+    v = np.concatenate([rng.standard_normal(50000) * scale, mids, -mids, mags, -mags,
+                        [1e9, -1e9, 0.0, -0.0]]).astype(np.float32)
+    got = torch.empty(v.size, dtype=torch.uint8, device=DEV)
+    bd.ssm_debug_codec(enc_op, torch.from_numpy(v).to(DEV), got)
+    np.testing.assert_array_equal(got.cpu().numpy(), enc(v))
+
+
+def test_packed_word_codecs_match_format_definitions():
+    """The packed-word helpers the read-copy kernels use: every byte / nibble position decodes
+    and encodes like the OCP definitions (byte i / nibble i = element i, low nibble first)."""
+    from oracle import quant
+    rng = np.random.default_rng(4)
+    fin = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    c8 = rng.choice(fin, size=4 * 4096).astype(np.uint8)
+    out = torch.empty(c8.size, device=DEV)
+    bd.ssm_debug_codec(8, torch.from_numpy(c8.view(np.uint32).copy()).to(DEV), out)
+    np.testing.assert_array_equal(out.cpu().numpy(), quant.e4m3_decode(c8))
+    c4 = rng.integers(0, 16, size=8 * 4096).astype(np.uint8)
+    words = (c4[0::2] | (c4[1::2] << 4)).astype(np.uint8).view(np.uint32).copy()
+    out4 = torch.empty(c4.size, device=DEV)
+    bd.ssm_debug_codec(9, torch.from_numpy(words).to(DEV), out4)
+    np.testing.assert_array_equal(out4.cpu().numpy(), quant.e2m1_decode(c4))
+    mags = quant.E4M3[:0x7F]
+    v = np.concatenate([rng.standard_normal(4 * 8000) * 60, (mags[1:] + mags[:-1]) / 2,
+                        -(mags[1:] + mags[:-1]) / 2, [1e9, -1e9, -0.0, 0.0, 3e-5, -600.0]])
+    v = v[: v.size // 4 * 4].astype(np.float32)
+    enc = torch.empty(v.size // 4, dtype=torch.int32, device=DEV)
+    bd.ssm_debug_codec(10, torch.from_numpy(v).to(DEV), enc)
+    np.testing.assert_array_equal(enc.cpu().numpy().view(np.uint8), quant.e4m3_encode(v))
+    m2 = quant.E2M1[:8]
+    v2 = np.concatenate([rng.standard_normal(8 * 8000) * 3, (m2[1:] + m2[:-1]) / 2,
+                         -(m2[1:] + m2[:-1]) / 2, [1e9, -1e9, -0.0, 7.0, -0.1, 0.2]])
+    v2 = v2[: v2.size // 8 * 8].astype(np.float32)
+    enc2 = torch.empty(v2.size // 8, dtype=torch.int32, device=DEV)
+    bd.ssm_debug_codec(11, torch.from_numpy(v2).to(DEV), enc2)
+    b = enc2.cpu().numpy().view(np.uint8)
+    got = np.empty(v2.size, dtype=np.uint8)
+    got[0::2] = b & 0xF
+    got[1::2] = b >> 4
+    np.testing.assert_array_equal(got, quant.e2m1_encode(v2))
