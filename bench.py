@@ -33,16 +33,26 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, 8 TB/s
 
 
-def pmc_traffic(kernel_source: str):
-    """HBM bytes per launch of the replay kernel from the committed counter profile
-    (profiles/hbm_traffic_pmc_b256.md), or None when the kernel source changed since."""
+# Sources the one-token replay kernel is compiled from; the counter profile records their hash.
+DECODE_SOURCES = ("m2_kernels.hpp", "m2_decode.hip", "ssm_device.hpp", "ssm_kernels.hpp")
+
+
+def sources_sha(files=DECODE_SOURCES) -> str:
     import hashlib
+    h = hashlib.sha256()
+    for f in files:
+        h.update(open(os.path.join(ROOT, "ssm_decode_state_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def pmc_traffic():
+    """HBM bytes per launch of the replay kernel from the committed counter profile
+    (profiles/hbm_traffic_pmc_b256.md), or None when the kernel sources changed since."""
     prof = os.path.join(ROOT, "profiles", "hbm_traffic_pmc_b256.md")
-    src = os.path.join(ROOT, "ssm_decode_state_amd", "csrc", kernel_source)
     try:
         line = [l for l in open(prof) if l.startswith("traffic-json:")][0]
         rec = json.loads(line.split(":", 1)[1])
-        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+        sha = sources_sha()
     except (OSError, IndexError, ValueError):
         return None
     return rec["bytes_per_launch"] if rec.get("sha") == sha else None
@@ -405,7 +415,7 @@ def main():
                    "groups": G, "head_dim": P, "state_dim": N, "window": L,
                    "inputs": "bf16 x/B/C, fp32 dt", "checkpoint": "fp32"},
         "roofline": {"bound": "hbm", "achieved": rep_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": rep_gbs / HBM_PEAK_GBS, "traffic": pmc_traffic("m2_kernels.hip"),
+                     "frac": rep_gbs / HBM_PEAK_GBS, "traffic": pmc_traffic(),
                      "algorithmic_bytes_per_launch": heads * mean_bytes_per_head,
                      "kernel": "m2_replay_kernel<64,128,bf16,1q>",
                      "avg_launch_us": rep_avg_ms * 1e3,

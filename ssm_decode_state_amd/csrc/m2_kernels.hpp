@@ -1,4 +1,5 @@
-// m2_kernels.hip -- Mamba-2 ReplaySSM kernels for gfx950 (wave64).
+// m2_kernels.hpp -- Mamba-2 ReplaySSM kernel templates for gfx950 (wave64). Instantiated by
+// m2_decode.hip, m2_verify.hip, m2_fold.hip and m2_conv.hip (one translation unit each).
 //
 // Pages: "ReplaySSM: Rethinking State Storage for Faster Hybrid-Model Decoding" -- the deskofai.com
 // news article (paragraphs counted from the first body paragraph) and the nexus-ai-blog.com
@@ -11,6 +12,7 @@
 // wave covers 1 KiB of contiguous memory; the row dot products h[p,:] . C need no cross-lane
 // reduction. For P < 64 the wave holds 64/P copies of the rows, each lane group taking every
 // (64/P)-th quad, and the groups are summed with shuffles at the end.
+#pragma once
 #include "ssm_device.hpp"
 #include "ssm_kernels.hpp"
 
@@ -296,14 +298,19 @@ __global__ __launch_bounds__(256) void m2_replay_kernel(M2Args a) {
     wave_sync();
 
     // ---- 4. replay weights w_{e,j} and checkpoint decays e^{s0_j} ---------------------------
-    float s0[MAXQ];
+    // Inclusive prefix sums of dt over the entries, pre(e) = sum_{m <= e} dt_m (zero past kmax):
+    // the decay exponent from entry e to query j is A (pre(kq_j - 1) - pre(e)).
+    float pre = dte;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const float t = __shfl_up(pre, o, 64);
+        pre += lane >= o ? t : 0.f;
+    }
+    float tot[MAXQ], s0[MAXQ];
 #pragma unroll
     for (int j = 0; j < MAXQ; ++j) {
-        s0[j] = 0.f;
-        if (j >= nq) continue;
-        float tot = 0.f;
-        for (int m = 0; m < count + j + 1; ++m) tot += readlane(dte, m);
-        s0[j] = expf(A * tot);
+        tot[j] = readlane(pre, min(count + j, 63));  // uniform index: entries 0 .. kq_j - 1
+        s0[j] = j < nq ? expf(A * tot[j]) : 0.f;
     }
 #pragma unroll
     for (int c = 0; c < kBC; ++c) {
@@ -321,6 +328,7 @@ __global__ __launch_bounds__(256) void m2_replay_kernel(M2Args a) {
             for (int u = 0; u < kSW; ++u) bf[u] = __uint_as_float(braw[c][u]);
         }
         const float dt_e = __shfl(dte, e & 63, 64);
+        const float pre_e = __shfl(pre, e & 63, 64);
 #pragma unroll
         for (int j = 0; j < MAXQ; ++j) {
             if (j >= nq) break;
@@ -329,13 +337,8 @@ __global__ __launch_bounds__(256) void m2_replay_kernel(M2Args a) {
 #pragma unroll
             for (int i = 0; i < G::kSeg; ++i) d += bf[i] * cj[i];
             d = xor_reduce_sum<16, 32>(d);
-            const int kq = count + j + 1;
-            float suf = 0.f;  // sum of dt over entries e+1 .. kq-1
-            for (int m = 0; m < kq; ++m) {
-                const float dm = readlane(dte, m);
-                suf += (m > e) ? dm : 0.f;
-            }
-            const float w = (e < kq) ? expf(A * suf) * dt_e * d : 0.f;
+            // sum of dt over entries e+1 .. kq-1 with kq = count + j + 1
+            const float w = (e <= count + j) ? expf(A * (tot[j] - pre_e)) * dt_e * d : 0.f;
             if (sg == 0) s_w[wave][e][j] = w;
         }
     }
@@ -563,13 +566,14 @@ __attribute__((amdgpu_waves_per_eu(2))) void m2_fold_kernel(M2Args a, int mode_a
     __builtin_amdgcn_sched_barrier(0);
 
     if (nfold > 0) {
-        float suf = 0.f, tot = 0.f;  // suffix sum of dt after lane's entry; total
-        for (int m = 0; m < nfold; ++m) {
-            const float dm = readlane(dte, m);
-            tot += dm;
-            suf += (m > lane) ? dm : 0.f;
+        float pre = dte;  // inclusive prefix sum of dt; the suffix after lane's entry is tot - pre
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const float t = __shfl_up(pre, o, 64);
+            pre += lane >= o ? t : 0.f;
         }
-        const float ue = expf(A * suf) * dte;  // zero past nfold
+        const float tot = readlane(pre, nfold - 1);
+        const float ue = expf(A * (tot - pre)) * dte;  // zero past nfold
         const float e0 = expf(A * tot);
         if constexpr (FUSED) {
 #pragma unroll
@@ -717,42 +721,11 @@ __global__ __launch_bounds__(256) void m2_conv_kernel(M2ConvArgs a) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// Instantiation tables. Grid: (ceil(H / 4), batch); one wavefront per head.
+// Launch helpers shared by the instantiating translation units. Grid: (ceil(H / 4), batch); one
+// wavefront per head.
 // ---------------------------------------------------------------------------------------------
-static dim3 head_grid(int batch, int heads) {
+static inline dim3 head_grid(int batch, int heads) {
     return dim3((unsigned)((heads + kHeadsPerBlock - 1) / kHeadsPerBlock), (unsigned)batch);
-}
-
-template <int P, int N, typename TIN, int RC>
-static hipError_t launch_replay_pn(const M2Args& a, bool spec, int maxe, hipStream_t s) {
-    const dim3 grid = head_grid(a.batch, a.heads), block(256);
-    if (spec) {
-        if (maxe <= 32)
-            hipLaunchKernelGGL((m2_replay_kernel<P, N, TIN, RC, 8, 32, false>), grid, block, 0, s, a);
-        else
-            hipLaunchKernelGGL((m2_replay_kernel<P, N, TIN, RC, 8, 64, false>), grid, block, 0, s, a);
-    } else {
-        if (maxe <= 16)
-            hipLaunchKernelGGL((m2_replay_kernel<P, N, TIN, RC, 1, 16, true>), grid, block, 0, s, a);
-        else
-            hipLaunchKernelGGL((m2_replay_kernel<P, N, TIN, RC, 1, 32, true>), grid, block, 0, s, a);
-    }
-    return hipGetLastError();
-}
-template <int P, int N, typename TIN, int RC>
-static hipError_t launch_flush_pn(const M2Args& a, int mode_all, int rewrite_only, hipStream_t s) {
-    if (mode_all == 2)  // fused decode + fold of the L-th lock-step token
-        hipLaunchKernelGGL((m2_fold_kernel<P, N, TIN, RC, true>), head_grid(a.batch, a.heads),
-                           dim3(256), 0, s, a, 0, 0);
-    else
-        hipLaunchKernelGGL((m2_fold_kernel<P, N, TIN, RC, false>), head_grid(a.batch, a.heads),
-                           dim3(256), 0, s, a, mode_all, rewrite_only);
-    return hipGetLastError();
-}
-template <int P, int N, typename TIN>
-static hipError_t launch_conv_pn(const M2ConvArgs& a, hipStream_t s) {
-    hipLaunchKernelGGL((m2_conv_kernel<P, N, TIN>), head_grid(a.batch, a.heads), dim3(256), 0, s, a);
-    return hipGetLastError();
 }
 
 #ifdef SSM_SINGLE_SHAPE  // faster builds when inspecting the serving-shape kernels
@@ -765,71 +738,7 @@ static hipError_t launch_conv_pn(const M2ConvArgs& a, hipStream_t s) {
     X(64, 64, __VA_ARGS__) X(64, 128, __VA_ARGS__)
 #endif
 
-template <typename TIN, int RC>
-static hipError_t dispatch_replay(const M2Args& a, int P, int N, bool spec, int maxe,
-                                  hipStream_t s) {
-#define X(PP, NN, ...) \
-    if (P == PP && N == NN) return launch_replay_pn<PP, NN, TIN, RC>(a, spec, maxe, s);
-    if constexpr (RC == 0) {
-        SSM_M2_SHAPES(X, 0)
-    } else {
-        if (P == 64 && N == 64) return launch_replay_pn<64, 64, TIN, RC>(a, spec, maxe, s);
-        if (P == 64 && N == 128) return launch_replay_pn<64, 128, TIN, RC>(a, spec, maxe, s);
-    }
-#undef X
-    return hipErrorNotSupported;
-}
-template <typename TIN, int RC>
-static hipError_t dispatch_flush(const M2Args& a, int P, int N, int mode_all, int rewrite_only,
-                                 hipStream_t s) {
-#define X(PP, NN, ...) \
-    if (P == PP && N == NN) return launch_flush_pn<PP, NN, TIN, RC>(a, mode_all, rewrite_only, s);
-    if constexpr (RC == 0) {
-        SSM_M2_SHAPES(X, 0)
-    } else {
-        if (P == 64 && N == 64) return launch_flush_pn<64, 64, TIN, RC>(a, mode_all, rewrite_only, s);
-        if (P == 64 && N == 128)
-            return launch_flush_pn<64, 128, TIN, RC>(a, mode_all, rewrite_only, s);
-    }
-#undef X
-    return hipErrorNotSupported;
-}
-
-hipError_t m2_launch_replay(const M2Args& a, int P, int N, int bf16, int rc, bool spec, int maxe,
-                            hipStream_t s) {
-    if (maxe > 64) return hipErrorNotSupported;
-    if (bf16) {
-        if (rc == 0) return dispatch_replay<bf16_t, 0>(a, P, N, spec, maxe, s);
-        if (rc == 1) return dispatch_replay<bf16_t, 1>(a, P, N, spec, maxe, s);
-        return dispatch_replay<bf16_t, 2>(a, P, N, spec, maxe, s);
-    }
-    if (rc == 0) return dispatch_replay<float, 0>(a, P, N, spec, maxe, s);
-    if (rc == 1) return dispatch_replay<float, 1>(a, P, N, spec, maxe, s);
-    return dispatch_replay<float, 2>(a, P, N, spec, maxe, s);
-}
-
-hipError_t m2_launch_flush(const M2Args& a, int P, int N, int bf16, int rc, int mode_all,
-                           int rewrite_only, hipStream_t s) {
-    if (bf16) {
-        if (rc == 0) return dispatch_flush<bf16_t, 0>(a, P, N, mode_all, rewrite_only, s);
-        if (rc == 1) return dispatch_flush<bf16_t, 1>(a, P, N, mode_all, rewrite_only, s);
-        return dispatch_flush<bf16_t, 2>(a, P, N, mode_all, rewrite_only, s);
-    }
-    if (rc == 0) return dispatch_flush<float, 0>(a, P, N, mode_all, rewrite_only, s);
-    if (rc == 1) return dispatch_flush<float, 1>(a, P, N, mode_all, rewrite_only, s);
-    return dispatch_flush<float, 2>(a, P, N, mode_all, rewrite_only, s);
-}
-
-hipError_t m2_launch_conv(const M2ConvArgs& a, int P, int N, int bf16, hipStream_t s) {
-#define X(PP, NN, T) \
-    if (P == PP && N == NN) return launch_conv_pn<PP, NN, T>(a, s);
-    if (bf16) {
-        SSM_M2_SHAPES(X, bf16_t)
-    } else {
-        SSM_M2_SHAPES(X, float)
-    }
-#undef X
-    return hipErrorNotSupported;
-}
+// Speculative verify launches (m2_verify.hip); m2_launch_replay forwards multi-token calls here.
+hipError_t m2_launch_verify(const M2Args& a, int P, int N, int bf16, int rc, int maxe, hipStream_t s);
 
 }  // namespace ssm
