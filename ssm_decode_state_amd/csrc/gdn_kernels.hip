@@ -212,9 +212,10 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_conv_kernel(GdnConvArgs a) {
     const float beta = a.in_beta[head];
     const float alpha = expf(a.in_g[head]);
     float4 hv[kNQ];
-    float4* tile = reinterpret_cast<float4*>(a.S) + head * (DV * DK / 4);
+    // float4 q * DV + row of the head's tile
+    const TileIO tio{reinterpret_cast<char*>(a.S) + (long)head * (DV * DK * 4), (uint32_t)(row * 16)};
 #pragma unroll
-    for (int q = 0; q < kNQ; ++q) hv[q] = ld_stream(tile + q * DV + row);
+    for (int q = 0; q < kNQ; ++q) hv[q] = tio.load((uint32_t)(q * DV * 16));
     asm volatile("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -242,7 +243,7 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_conv_kernel(GdnConvArgs a) {
         hv[q].z = alpha * hv[q].z + u * k4.z;
         hv[q].w = alpha * hv[q].w + u * k4.w;
         o += hv[q].x * q4.x + hv[q].y * q4.y + hv[q].z * q4.z + hv[q].w * q4.w;
-        st_stream(hv[q], tile + q * DV + row);
+        tio.store((uint32_t)(q * DV * 16), hv[q]);
     }
     if (lane < kRows) a.o[head * DV + row] = a.scale * o;
 }
@@ -258,12 +259,12 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_conv_kernel(GdnConvArgs a) {
 // (v_mfma_f32_16x16x4f32): A[m][k] from lane l = (m = l%16, k = l/16), B[k][c] from lane l =
 // (k = l/16, c = l%16), D[m][c] in lane l at register r = (m = 4(l/16) + r, c = l%16).
 // Entries past the fold count are zero rows (beta = g = 0, k = v = 0), which leave S unchanged.
-// Requires DV % 64 == 0 and DK % 16 == 0 (one wave per 64 rows).
+// Requires DV % 64 == 0 (one wave per 64 rows) and DK % 64 == 0.
 // ---------------------------------------------------------------------------------------------
 template <int DV, int DK, typename TIN>
 __global__ __launch_bounds__(DV)
 __attribute__((amdgpu_waves_per_eu(2))) void gdn_flush_kernel(GdnArgs a, int mode_all) {
-    static_assert(DV % 64 == 0 && DK % 16 == 0, "flush tile shape");
+    static_assert(DV % 64 == 0 && DK % 64 == 0, "flush tile shape");
     constexpr int kW = DV / 64;
     constexpr int kPB = 4;            // 16-row blocks per wave
     constexpr int kNB = DK / 16;      // 16-column blocks
@@ -322,12 +323,14 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_flush_kernel(GdnArgs a, int mod
     // the tile in accumulator order: block (pb, nb) of lane l = row p_base + 16pb + l%16,
     // columns 16nb + 4(l/16) .. +3
     f32x4 S[kPB][kNB];
-    const float4* tile = reinterpret_cast<const float4*>(a.ckpt) + (long)head * (DV * DK / 4);
+    // float4 (4 nb + lg) * DV + p_base + 16 pb + li of the head's tile
+    const TileIO tio{reinterpret_cast<char*>(a.ckpt) + (long)head * (DV * DK * 4),
+                     (uint32_t)((lg * DV + p_base + li) * 16)};
 #pragma unroll
     for (int pb = 0; pb < kPB; ++pb)
 #pragma unroll
         for (int nb = 0; nb < kNB; ++nb) {
-            const float4 t = ld_stream(tile + (4 * nb + lg) * DV + p_base + 16 * pb + li);
+            const float4 t = tio.load((uint32_t)((4 * nb * DV + 16 * pb) * 16));
             S[pb][nb] = f32x4{t.x, t.y, t.z, t.w};
         }
     asm volatile("" ::: "memory");
@@ -368,78 +371,73 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_flush_kernel(GdnArgs a, int mod
             const float kk = s_k[wave][li][n0 + lg];
             gram = mfma4(kk, kk, gram);
         }
-        // Lm[t][i] for t = 4lg + r, i = li (t varies across lanes: beta_t by a per-lane shuffle)
+        // G_t = sum_{m <= t} g_m within the chunk (inclusive scan over each 16-lane row; the four
+        // rows hold the same entries, so every lane l has G at entry l%16)
+        float G = ge;
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) {
+            const float t = __shfl_up(G, o, 16);
+            G += li >= o ? t : 0.f;
+        }
+        // Lm[t][i] for t = 4lg + r, i = li (t varies across lanes: per-lane shuffles);
+        // the decay from entry i to t is exp(G_t - G_i)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int t = 4 * lg + r, i = li;
-            float part = 0.f;  // sum_{m=i+1..t} g_m
-#pragma unroll
-            for (int m = 0; m < 16; ++m) part += (m > i && m <= t) ? readlane(ge, m) : 0.f;
             const float bt = __shfl(be, t, 64);
-            const float lm = (i < t) ? bt * expf(part) * gram[r] : 0.f;
+            const float Gt = __shfl(G, t, 64);
+            const float lm = (i < t) ? bt * expf(Gt - G) * gram[r] : 0.f;
             s_l[wave][t][i] = lm;
         }
         wave_sync();
 
-        // forward substitution for W (lane owns columns n = lane + 64 j) and U (lane owns row
-        // p_base + lane); W is stored negated for the MFMA below, U as [t][p]
-        constexpr int kWE = DK / 64 > 0 ? DK / 64 : 1;
-        float w[16][kWE], u[16];
-        float gcum = 0.f;
+        // forward substitution, in place in LDS: lane owns the columns n = lane + 64 j of W and
+        // the row p_base + lane of U, so every value it reads back it wrote itself. W is kept
+        // negated (s_w[t] = -W_t) for the MFMA below; U overwrites V in s_v ([t][p]).
+        constexpr int kWE = DK / 64;
 #pragma unroll
         for (int t = 0; t < 16; ++t) {
-            gcum += readlane(ge, t);
             const float bt = readlane(be, t);
-            const float bg = bt * expf(gcum);
+            const float bg = bt * expf(readlane(G, t));
+            float lrow[16];
+#pragma unroll
+            for (int i = 0; i < t; ++i) lrow[i] = s_l[wave][t][i];
 #pragma unroll
             for (int j = 0; j < kWE; ++j) {
                 const int n = lane + 64 * j;
-                float s = n < DK ? bg * s_k[wave][t][n] : 0.f;
+                float sw = -bg * s_k[wave][t][n];
 #pragma unroll
-                for (int i = 0; i < t; ++i) s -= s_l[wave][t][i] * w[i][j];
-                w[t][j] = s;
+                for (int i = 0; i < t; ++i) sw -= lrow[i] * s_w[wave][i][n];
+                s_w[wave][t][n] = sw;
             }
             float su = bt * s_v[wave][t][lane];
 #pragma unroll
-            for (int i = 0; i < t; ++i) su -= s_l[wave][t][i] * u[i];
-            u[t] = su;
+            for (int i = 0; i < t; ++i) su -= lrow[i] * s_v[wave][i][lane];
+            s_v[wave][t][lane] = su;
             asm volatile("" ::: "memory");  // one row of Lm live at a time
         }
-        const float gL = gcum;  // log gamma_L (zero-padded entries add nothing)
-        wave_sync();
-#pragma unroll
-        for (int t = 0; t < 16; ++t) {
-#pragma unroll
-            for (int j = 0; j < kWE; ++j) {
-                const int n = lane + 64 * j;
-                if (n < DK) s_w[wave][t][n] = -w[t][j];
-            }
-            s_v[wave][t][lane] = u[t];  // U as [t][p - p_base]
-        }
+        const float gL = readlane(G, 15);  // log gamma_L (zero-padded entries add nothing)
         wave_sync();
 
         asm volatile("" ::: "memory");
         // Delta^T[p][t] = U^T[p][t] - sum_n S[p][n] W[t][n]   (D layout: p = 4lg + r, t = li)
-        f32x4 wop[kNB];  // B operand: -W[t = li][16nb + 4lg + r]
-#pragma unroll
-        for (int nb = 0; nb < kNB; ++nb)
-            wop[nb] = *reinterpret_cast<const f32x4*>(&s_w[wave][li][16 * nb + 4 * lg]);
-        float tail = 0.f;  // log(gamma_L / gamma_t) for t = li
-#pragma unroll
-        for (int m = 0; m < 16; ++m) tail += (m > li) ? readlane(ge, m) : 0.f;
-        const float dscale = expf(tail);
+        const float dscale = expf(gL - G);  // gamma_L / gamma_t for t = li
         f32x4 delta[kPB];
 #pragma unroll
-        for (int pb = 0; pb < kPB; ++pb) {
-            f32x4 acc;
+        for (int pb = 0; pb < kPB; ++pb)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) acc[r] = s_v[wave][li][16 * pb + 4 * lg + r];
+            for (int r = 0; r < 4; ++r) delta[pb][r] = s_v[wave][li][16 * pb + 4 * lg + r];
 #pragma unroll
-            for (int nb = 0; nb < kNB; ++nb)
+        for (int nb = 0; nb < kNB; ++nb) {
+            // B operand: -W[t = li][16nb + 4lg + r]
+            const f32x4 wop = *reinterpret_cast<const f32x4*>(&s_w[wave][li][16 * nb + 4 * lg]);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) acc = mfma4(S[pb][nb][r], wop[nb][r], acc);
-            delta[pb] = acc * dscale;  // Delta'[p][t] = (gamma_L / gamma_t) Delta[p][t]
+            for (int pb = 0; pb < kPB; ++pb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) delta[pb] = mfma4(S[pb][nb][r], wop[r], delta[pb]);
         }
+#pragma unroll
+        for (int pb = 0; pb < kPB; ++pb) delta[pb] *= dscale;  // Delta' = (gamma_L/gamma_t) Delta
         wave_sync();
         // transpose Delta' through LDS ([p][t])
 #pragma unroll
@@ -468,13 +466,12 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_flush_kernel(GdnArgs a, int mod
         wave_sync();
     }
 
-    float4* wtile = reinterpret_cast<float4*>(a.ckpt) + (long)head * (DV * DK / 4);
 #pragma unroll
     for (int pb = 0; pb < kPB; ++pb)
 #pragma unroll
         for (int nb = 0; nb < kNB; ++nb)
-            st_stream(make_float4(S[pb][nb][0], S[pb][nb][1], S[pb][nb][2], S[pb][nb][3]),
-                      wtile + (4 * nb + lg) * DV + p_base + 16 * pb + li);
+            tio.store((uint32_t)((4 * nb * DV + 16 * pb) * 16),
+                      make_float4(S[pb][nb][0], S[pb][nb][1], S[pb][nb][2], S[pb][nb][3]));
     if constexpr (kW > 1) __builtin_amdgcn_s_barrier();  // every wave has read the pointers
     if (wave == 0 && lane == 0) {
         a.ptr[2 * head] = ring_slot(start, nfold, cap);

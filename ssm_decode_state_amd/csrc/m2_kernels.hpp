@@ -554,12 +554,14 @@ __attribute__((amdgpu_waves_per_eu(2))) void m2_fold_kernel(M2Args a, int mode_a
     if (nfold > 0) fetch(0);
 
     f32x4 hb[kPB][kNB];
-    float4* tile = reinterpret_cast<float4*>(a.ckpt) + (long)head * (P * N / 4);
+    // float4 (4 nb + lg) * P + 16 pb + li of the head's tile
+    const TileIO tio{reinterpret_cast<char*>(a.ckpt) + (long)head * (P * N * 4),
+                     (uint32_t)((lg * P + li) * 16)};
 #pragma unroll
     for (int pb = 0; pb < kPB; ++pb)
 #pragma unroll
         for (int nb = 0; nb < kNB; ++nb) {
-            const float4 t = ld_stream(tile + (4 * nb + lg) * P + 16 * pb + li);
+            const float4 t = tio.load((uint32_t)((4 * nb * P + 16 * pb) * 16));
             hb[pb][nb] = f32x4{t.x, t.y, t.z, t.w};
         }
     asm volatile("" ::: "memory");
@@ -627,8 +629,8 @@ __attribute__((amdgpu_waves_per_eu(2))) void m2_fold_kernel(M2Args a, int mode_a
         for (int pb = 0; pb < kPB; ++pb)
 #pragma unroll
             for (int nb = 0; nb < kNB; ++nb)
-                st_stream(make_float4(hb[pb][nb][0], hb[pb][nb][1], hb[pb][nb][2], hb[pb][nb][3]),
-                          tile + (4 * nb + lg) * P + 16 * pb + li);
+                tio.store((uint32_t)((4 * nb * P + 16 * pb) * 16),
+                          make_float4(hb[pb][nb][0], hb[pb][nb][1], hb[pb][nb][2], hb[pb][nb][3]));
     }
     if constexpr (FUSED) {  // output from the new state: y = h C + D x
         const TIN* xin = static_cast<const TIN*>(a.in_x) + tok * P;
@@ -687,9 +689,11 @@ __global__ __launch_bounds__(256) void m2_conv_kernel(M2ConvArgs a) {
     const float A = a.A[h], D = a.D[h];
 
     float4 hv[G::kQPL];
-    float4* tile = reinterpret_cast<float4*>(a.h) + (long)head * (P * N / 4);
+    // float4 (gq + kGrp j) * P + row of the head's tile
+    const TileIO tio{reinterpret_cast<char*>(a.h) + (long)head * (P * N * 4),
+                     (uint32_t)((gq * P + row) * 16)};
 #pragma unroll
-    for (int j = 0; j < G::kQPL; ++j) hv[j] = ld_stream(tile + (gq + G::kGrp * j) * P + row);
+    for (int j = 0; j < G::kQPL; ++j) hv[j] = tio.load((uint32_t)(G::kGrp * j * P * 16));
     asm volatile("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
 
@@ -714,7 +718,7 @@ __global__ __launch_bounds__(256) void m2_conv_kernel(M2ConvArgs a) {
         hv[j].z = decay * hv[j].z + dx * b4.z;
         hv[j].w = decay * hv[j].w + dx * b4.w;
         acc += hv[j].x * c4.x + hv[j].y * c4.y + hv[j].z * c4.z + hv[j].w * c4.w;
-        st_stream(hv[j], tile + q * P + row);
+        tio.store((uint32_t)(G::kGrp * j * P * 16), hv[j]);
     }
     if constexpr (G::kGrp > 1) acc = xor_reduce_sum<P, 32>(acc);
     if (gq == 0) a.y[(long)head * P + row] = acc + D * x;

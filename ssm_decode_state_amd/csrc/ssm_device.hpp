@@ -27,6 +27,20 @@ __device__ __forceinline__ void st_stream(float4 v, float4* p) {
     __builtin_nontemporal_store(t, reinterpret_cast<f32x4_t*>(p));
 }
 
+// Streaming access to a state tile through a wave-uniform base and a 32-bit per-lane byte
+// offset: each access is an SGPR base plus one shared VGPR offset, so a tile that is loaded at
+// the start of a kernel and stored at its end keeps no per-access 64-bit addresses alive.
+struct TileIO {
+    char* base;     // wave-uniform
+    uint32_t lane;  // this lane's byte offset
+    __device__ __forceinline__ float4 load(uint32_t off) const {
+        return ld_stream(reinterpret_cast<const float4*>((base + off) + lane));
+    }
+    __device__ __forceinline__ void store(uint32_t off, float4 v) const {
+        st_stream(v, reinterpret_cast<float4*>((base + off) + lane));
+    }
+};
+
 // Unpack one 16-byte unit of T (fp32 or bf16 bits) into floats.
 template <typename T> struct Unit;
 template <> struct Unit<float> {
