@@ -21,6 +21,7 @@ HBM before the timed region starts.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import json
 import math
 import os
@@ -83,6 +84,12 @@ def m2_verify_bytes_per_head(P, N, kc, S, esz=2):
     entry_rd = P * esz + N * esz + 4
     token = P * esz + 2 * N * esz + 4
     return P * N * 4 + kc * entry_rd + 2 * S * token + S * P * 4 + 8
+
+
+def m2_snapshot_bytes_per_head(P, N, S, esz=2):
+    """Snapshot-based speculation for one head: state read once, S snapshot states written, the
+    S drafts' inputs read, S outputs written."""
+    return P * N * 4 + S * P * N * 4 + S * (P * esz + 2 * N * esz + 4) + S * P * 4
 
 
 def m2_rc_replay_bytes_per_head(P, N, k, rc, esz=2):
@@ -173,11 +180,84 @@ def bench_spec(dev, rounds=64, warm=16, pool=16):
     rb = sum(e[1].elapsed_time(e[2]) for e in ev)
     accepted = sum(int(accs[r].sum()) for r in range(warm, warm + rounds))
     gbs = ver_bytes / (ver * 1e-3) / 1e9
+    del st
+    # the comparison point: conventional speculation writes the state after every draft and
+    # restores the accepted one
+    Ad, Dd = A.to(dev), D.to(dev)
+    h = torch.empty(Bn * H * P * N, device=dev)
+    h0 = synth.initial_state_device(shape, w["seed"], w["h0_std"])
+    bd.ssm_tiles_pack(cfg, h0, h)
+    del h0
+    snap = torch.empty(S, Bn * H * P * N, device=dev)
+    for r in range(warm):
+        bd.ssm_conventional_spec_snapshot(cfg, h, snap, S, drafts[r % pool], Ad, Dd, y)
+        bd.ssm_conventional_spec_select(cfg, h, snap, S, accs_d[r])
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(rounds):
+        r = warm + i
+        ev[i][0].record()
+        bd.ssm_conventional_spec_snapshot(cfg, h, snap, S, drafts[r % pool], Ad, Dd, y)
+        ev[i][1].record()
+        bd.ssm_conventional_spec_select(cfg, h, snap, S, accs_d[r])
+        ev[i][2].record()
+    torch.cuda.synchronize()
+    swall = time.perf_counter() - t0
+    sn = sum(e[0].elapsed_time(e[1]) for e in ev)
+    sel = sum(e[1].elapsed_time(e[2]) for e in ev)
+    sgbs = Bn * H * m2_snapshot_bytes_per_head(P, N, S) * rounds / (sn * 1e-3) / 1e9
+    del snap, h
     return {"workload": "mamba2_spec_b256_4drafts", "accepted_tokens_per_s": accepted / wall,
             "unit": "accepted tokens/s/layer", "rounds": rounds, "mean_accept": accepted / (Bn * rounds),
             "verify_avg_us": ver / rounds * 1e3, "verify_achieved_gbs": gbs,
             "verify_frac": gbs / HBM_PEAK_GBS,
-            "rollback_and_fold_avg_us": rb / rounds * 1e3, "ms_per_round": wall / rounds * 1e3}
+            "rollback_and_fold_avg_us": rb / rounds * 1e3, "ms_per_round": wall / rounds * 1e3,
+            "conventional_snapshot": {
+                "accepted_tokens_per_s": accepted / swall, "ms_per_round": swall / rounds * 1e3,
+                "snapshot_avg_us": sn / rounds * 1e3, "snapshot_achieved_gbs": sgbs,
+                "snapshot_frac": sgbs / HBM_PEAK_GBS, "select_avg_us": sel / rounds * 1e3},
+            "speedup_vs_snapshot": swall / wall}
+
+
+def bench_m2_decode(dev, shape, seed, h0_std, steps, warm, pool=16):
+    """Lock-step replay decode of one Mamba-2 layer: tokens/s, mean step and the window-closing
+    (fused fold) step."""
+    import torch
+    from ssm_decode_state_amd import binding as bd
+    from ssm_decode_state_amd import synth
+    Bn, H, P, N, L = shape.batch, shape.heads, shape.dim_p, shape.dim_n, shape.window
+    A, D = synth.head_constants(shape, seed)
+    h0 = synth.initial_state_device(shape, seed, h0_std)
+    cfg = bd.make_config(bd.SSM_MAMBA2, Bn, H, shape.groups, P, N, L, 1, bd.SSM_IN_BF16)
+    st = bd.State(cfg, h0, A.to(dev), D.to(dev))
+    del h0
+    inputs = [synth.token_inputs_device(shape, seed, "bench-sweep", i) for i in range(pool)]
+    y = torch.empty(Bn, H, P, device=dev)
+    for i in range(warm):
+        bd.ssm_replay_decode(st, inputs[i % pool], y)
+    wall, ms = timed_calls(steps, lambda i: bd.ssm_replay_decode(st, inputs[(warm + i) % pool], y))
+    fold = [m for i, m in enumerate(ms) if (warm + i) % L == L - 1]
+    rep = [m for i, m in enumerate(ms) if (warm + i) % L != L - 1]
+    rep_b = sum(Bn * H * m2_replay_bytes_per_head(P, N, (warm + i) % L + 1, 2)
+                for i in range(steps) if (warm + i) % L != L - 1)
+    return {"window": L, "groups": shape.groups, "tokens_per_s": Bn * steps / wall,
+            "mean_step_us": sum(ms) / steps * 1e3,
+            "replay_avg_us": sum(rep) / max(len(rep), 1) * 1e3,
+            "replay_frac": (rep_b / (sum(rep) * 1e-3) / 1e9 / HBM_PEAK_GBS) if rep else None,
+            "fold_step_avg_us": sum(fold) / max(len(fold), 1) * 1e3}
+
+
+def bench_lsweep(dev, steps=96, warm=32):
+    """Window sweep on the serving shapes (L = 4, 8, 16, 32; the window-closing step fuses the
+    fold): the checkpoint read and rewrite per window trade against the buffered entries."""
+    import dataclasses
+    from ssm_decode_state_amd import synth
+    w = synth.WORKLOADS["m2_b256"]
+    out = []
+    for L in (4, 8, 16, 32):
+        shape = dataclasses.replace(w["shape"], window=L)
+        out.append(bench_m2_decode(dev, shape, w["seed"], w["h0_std"], steps, warm))
+    return out
 
 
 def bench_readcopy(dev, rc, steps=128, warm=16, layers=4, pool=16):
@@ -314,11 +394,31 @@ def cpu_baseline(seconds_target: float = 10.0):
     for _ in range(reps):
         oracle.m2_sequential(*args)
     el = time.perf_counter() - t0
-    return {"value": reps * nseq * T / el, "unit": "tokens/s/layer", "cores": oracle.num_threads(),
+    cores = oracle.num_threads()
+    # the same oracle on one core, on a sample sized for about a third of the time
+    oracle.set_threads(1)
+    t0 = time.perf_counter()
+    oracle.m2_sequential(*sample(1))
+    t1 = time.perf_counter() - t0
+    n1 = int(max(1, min(full.batch, round(seconds_target / 3 / max(t1, 1e-3)))))
+    args1 = sample(n1)
+    t0 = time.perf_counter()
+    oracle.m2_sequential(*args1)
+    el1 = time.perf_counter() - t0
+    oracle.set_threads(None)
+    model = ""
+    try:
+        model = [l.split(":", 1)[1].strip() for l in open("/proc/cpuinfo")
+                 if l.startswith("model name")][0]
+    except (OSError, IndexError):
+        pass
+    return {"value": reps * nseq * T / el, "unit": "tokens/s/layer", "cores": cores,
             "kind": "oracle",
             "sample": "%d of 256 sequences x 128 heads x %d tokens of the serving workload, run %d "
                       "time(s); fp64 sequential recurrence (C, OpenMP over heads), %.1f s"
-                      % (nseq, T, reps, el)}
+                      % (nseq, T, reps, el),
+            "single_core": {"value": n1 * T / el1, "sample": "%d sequences, %.1f s" % (n1, el1)},
+            "cpu_model": model}
 
 
 def torch_cat(ts):
@@ -336,7 +436,8 @@ def main():
     ap.add_argument("--copy-ref", type=int, default=0,
                     help="also run a plain copy of this many MiB (reference for HBM counters)")
     ap.add_argument("--workloads", default="all",
-                    help="comma list of extra workloads: spec, fp8, fp4, gdn; 'all' or 'none'")
+                    help="comma list of extra workloads: spec, fp8, fp4, gdn, g8 (8 B/C "
+                         "groups), lsweep (window 4..32); 'all' or 'none'")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -404,6 +505,9 @@ def main():
     fold_gbs = fold_bytes / (fold_ms * 1e-3) / 1e9 if fold_ms else None
     tok_s = Bn * K / t_replay
     mean_bytes_per_head = sum(m2_replay_bytes_per_head(P, N, k) for k in range(1, L + 1)) / L
+    per_k = {}
+    for k, ms in zip(ks, step_ms):
+        per_k.setdefault(k, []).append(ms)
 
     out = {
         "metric": "SSM decode tokens/sec per layer at B=256 + % of HBM peak (replay vs "
@@ -424,6 +528,7 @@ def main():
         "fold_step": {"avg_us": None if fold_ms is None else fold_ms * 1e3,
                       "achieved_gbs": fold_gbs, "per_window": 1,
                       "kernel": "m2_fold_kernel<64,128,bf16,fused>"},
+        "step_us_by_count": {str(k): sum(v) / len(v) * 1e3 for k, v in sorted(per_k.items())},
     }
 
     # ---- conventional comparison on the same shapes and inputs ---------------------------------
@@ -463,7 +568,7 @@ def main():
         out["copy_ref"] = {"bytes_read": 4 * n, "bytes_written": 4 * n, "launches": 5,
                            "avg_us": e0.elapsed_time(e1) / 5 * 1e3}
 
-    extra = ({"spec", "fp8", "fp4", "gdn"} if args.workloads == "all" else
+    extra = ({"spec", "fp8", "fp4", "gdn", "g8", "lsweep"} if args.workloads == "all" else
              set() if args.workloads == "none" else set(args.workloads.split(",")))
     if extra:
         del inputs, st, h0
@@ -473,6 +578,15 @@ def main():
         out["workloads"] = {}
         if "spec" in extra:
             out["workloads"]["spec"] = bench_spec(dev)
+            torch.cuda.empty_cache()
+        if "g8" in extra:
+            wg = synth.WORKLOADS["m2_b256"]
+            r = bench_m2_decode(dev, dataclasses.replace(wg["shape"], groups=8), wg["seed"],
+                                wg["h0_std"], 128, 32)
+            out["workloads"]["groups8"] = dict(workload="mamba2_replay_decode_b256_g8", **r)
+            torch.cuda.empty_cache()
+        if "lsweep" in extra:
+            out["workloads"]["window_sweep"] = bench_lsweep(dev)
             torch.cuda.empty_cache()
         if "fp8" in extra:
             out["workloads"]["readcopy_fp8"] = bench_readcopy(dev, 1)

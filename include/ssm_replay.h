@@ -43,8 +43,9 @@
  *     GDN:     q, k [batch][ntok][H][dk], v [batch][ntok][H][dv] in the input dtype,
  *              beta [batch][ntok][H], g [batch][ntok][H] fp32 (g is the log of the decay)
  *   Outputs y are fp32 [batch][ntok][H][P] (GDN: [batch][ntok][H][dv]).
- * - Supported tile shapes: P (dv) and N (dk) each in {16, 32, 64, 128}; window L in [1, 32];
- *   max_draft in [1, min(L, 8)]; fp8 read copy needs N % 16 == 0, fp4 N % 32 == 0.
+ * - Supported shapes: Mamba-2 P in {16, 32, 64} and N in {16, 32, 64, 128} with N >= 4 * 64 / P
+ *   (P = 64 takes every N); GDN dv and dk in {64, 128}; window L in [1, 32]; max_draft in
+ *   [1, min(L, 8)]. The read copies need P = 64 and N in {64, 128} (Mamba-2 only).
  */
 #ifndef SSM_REPLAY_H
 #define SSM_REPLAY_H
@@ -56,7 +57,7 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 1
+#define SSM_ABI_VERSION 2
 
 typedef int32_t ssm_status;
 enum {
@@ -74,6 +75,8 @@ enum { SSM_MAMBA2 = 0, SSM_GDN = 1 };
 enum { SSM_IN_F32 = 0, SSM_IN_BF16 = 1 };
 enum { SSM_RC_NONE = 0, SSM_RC_FP8_ROW = 1, SSM_RC_FP4_B16 = 2 };
 enum { SSM_FLUSH_IF_FULL = 0, SSM_FLUSH_ALL = 1 };
+/* Bits of a state's device flag word (see ssm_debug_flags). */
+enum { SSM_FLAG_ACCEPT_CLAMPED = 1 /* an n_accept value outside [0, pending] was clamped */ };
 
 /* Layer shape and options. */
 typedef struct ssm_config {
@@ -100,7 +103,8 @@ typedef struct ssm_config {
  * codes [b][h][P][N/16], tile scale fp32 [b][h].
  * Rings (slot s of cap): Mamba-2 x [b][h][s][P], B and C [b][g][s][N] (input dtype),
  * dt [b][h][s] fp32; GDN q, k [b][h][s][dk], v [b][h][s][dv] (input dtype), beta, g [b][h][s].
- * Pointers: int32 [b][h][2] = {start slot, committed count}. */
+ * Pointers: int32 [b][h][2] = {start slot, committed count}. Flags: one int32 word of SSM_FLAG_*
+ * bits set by device-side checks. */
 typedef struct ssm_layout {
     uint64_t total_bytes;
     int32_t ring_cap;       /* slots per ring = L + max_draft - 1 */
@@ -111,6 +115,7 @@ typedef struct ssm_layout {
     uint64_t off_rc_tscale; /* fp4: tile scales fp32 */
     uint64_t off_ring[5];   /* Mamba-2: x, B, C, dt, (unused); GDN: q, k, v, beta, g */
     uint64_t off_ptr;       /* int32 [batch][heads][2] */
+    uint64_t off_flags;     /* int32 flag word */
 } ssm_layout;
 
 /* Host handle of one layer's state. Plain data: copyable only while no work is in flight. */
@@ -201,6 +206,23 @@ ssm_status ssm_ckpt_export(const ssm_state *st, float *h_out, void *stream);
 ssm_status ssm_conventional_step(const ssm_config *cfg, float *h, const void *in, const float *A,
                                  const float *D, float *y, void *stream);
 
+/* Conventional speculative decoding, the comparison point for ssm_spec_append (news, para 3:
+ * per-token snapshots; explainer, "Usage examples", example 3: snapshot and restore). Runs the
+ * recurrence of ssm_conventional_step over `ndraft` draft tokens (`in` with ntok = ndraft,
+ * 1 <= ndraft <= 8) starting from h, which is only read, and writes the state after each draft
+ * j = 0..ndraft-1 to h_snap [ndraft][batch][H] tiles (tile layout of ssm_layout) and the outputs
+ * y [batch][ndraft][H][P]. Mamba-2 only (SSM_E_UNSUPPORTED for GDN). h and h_snap must not
+ * overlap. */
+ssm_status ssm_conventional_spec_snapshot(const ssm_config *cfg, const float *h, float *h_snap,
+                                          int32_t ndraft, const void *in, const float *A,
+                                          const float *D, float *y, void *stream);
+
+/* The restore half of the snapshot scheme: sequence b takes the state after its n_accept[b]-th
+ * draft, h[b] <- h_snap[n_accept[b] - 1][b] (device int32 [batch], clamped to [0, ndraft]; 0
+ * keeps h[b]). Moves one state per sequence that accepted a draft. Mamba-2 only. */
+ssm_status ssm_conventional_spec_select(const ssm_config *cfg, float *h, const float *h_snap,
+                                        int32_t ndraft, const int32_t *n_accept, void *stream);
+
 /* Natural [batch][H][P][N] <-> tile layout conversion of fp32 states (out-of-place). */
 ssm_status ssm_tiles_pack(const ssm_config *cfg, const float *natural, float *tiles, void *stream);
 ssm_status ssm_tiles_unpack(const ssm_config *cfg, const float *tiles, float *natural,
@@ -214,6 +236,10 @@ ssm_status ssm_tiles_unpack(const ssm_config *cfg, const float *tiles, float *na
  * as listed); `in` and `out` must hold n items each -- they are not checked. Lets tests check the
  * read-copy codecs bit for bit against the format definitions. */
 ssm_status ssm_debug_codec(int32_t op, const void *in, void *out, int64_t n, void *stream);
+
+/* Test hook: read the state's flag word (SSM_FLAG_* bits) into *host_flags, clearing it on the
+ * device when `clear` is non-zero. Synchronizes `stream`. */
+ssm_status ssm_debug_flags(const ssm_state *st, int32_t *host_flags, int32_t clear, void *stream);
 
 #ifdef __cplusplus
 }

@@ -69,12 +69,25 @@ def _f64(a) -> np.ndarray:
     return np.ascontiguousarray(np.asarray(a, dtype=np.float64))
 
 
+_threads: Optional[int] = None
+
+
 def num_threads() -> int:
-    """OpenMP threads the batch wrappers use (OMP_NUM_THREADS, else all cores in our affinity)."""
+    """OpenMP threads the batch wrappers use (set_threads, else OMP_NUM_THREADS, else all cores
+    in our affinity)."""
+    if _threads is not None:
+        return _threads
     env = os.environ.get("OMP_NUM_THREADS")
     if env:
         return int(env)
     return len(os.sched_getaffinity(0))
+
+
+def set_threads(n: Optional[int]) -> None:
+    """Threads for the batch wrappers (None = back to the default). Timing only."""
+    global _threads
+    _threads = n
+    _load().orc_set_threads(n if n is not None else num_threads())
 
 
 # ----------------------------------------------------------------------------------------------
@@ -198,6 +211,7 @@ def gdn_flush(Sc, k, v, beta, g):
 
 def _declare(lib):
     i, d = ctypes.c_int, ctypes.c_double
+    lib.orc_set_threads.argtypes = [i]
     lib.orc_m2_sequential.argtypes = [i, i, i, d, d] + [_dp] * 7 + [i, _ip, _dp]
     lib.orc_m2_sequential_batch.argtypes = [i, i, i, i] + [_dp] * 9 + [i, _ip, _dp]
     lib.orc_m2_replay_output.argtypes = [i, i, i, d, d] + [_dp] * 6

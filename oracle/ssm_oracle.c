@@ -26,6 +26,7 @@
  * snap_after: ascending token counts t (1-based) after which the state is copied into snaps.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdlib.h>
 #include <string.h>
 
@@ -313,3 +314,6 @@ void orc_gdn_flush(int dv, int dk, int L, const double *Sc, const double *k, con
     free(U);
     free(Lm);
 }
+
+/* Threads of the OpenMP loops over heads (timing only; results do not depend on it). */
+void orc_set_threads(int n) { omp_set_num_threads(n > 0 ? n : 1); }

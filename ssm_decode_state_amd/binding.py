@@ -21,6 +21,7 @@ SSM_MAMBA2, SSM_GDN = 0, 1
 SSM_IN_F32, SSM_IN_BF16 = 0, 1
 SSM_RC_NONE, SSM_RC_FP8_ROW, SSM_RC_FP4_B16 = 0, 1, 2
 SSM_FLUSH_IF_FULL, SSM_FLUSH_ALL = 0, 1
+SSM_FLAG_ACCEPT_CLAMPED = 1
 
 
 class SSMError(RuntimeError):
@@ -43,7 +44,7 @@ class ssm_layout(ctypes.Structure):
                 ("reserved", ctypes.c_int32), ("off_ckpt", ctypes.c_uint64),
                 ("off_rc_codes", ctypes.c_uint64), ("off_rc_scale", ctypes.c_uint64),
                 ("off_rc_tscale", ctypes.c_uint64), ("off_ring", ctypes.c_uint64 * 5),
-                ("off_ptr", ctypes.c_uint64)]
+                ("off_ptr", ctypes.c_uint64), ("off_flags", ctypes.c_uint64)]
 
 
 class ssm_state(ctypes.Structure):
@@ -84,6 +85,9 @@ def _load() -> ctypes.CDLL:
         "ssm_tiles_pack": ([P(ssm_config), vp, vp, vp], st),
         "ssm_tiles_unpack": ([P(ssm_config), vp, vp, vp], st),
         "ssm_debug_codec": ([i32, vp, vp, ctypes.c_int64, vp], st),
+        "ssm_conventional_spec_snapshot": ([P(ssm_config), vp, vp, i32, vp, vp, vp, vp, vp], st),
+        "ssm_conventional_spec_select": ([P(ssm_config), vp, vp, i32, vp, vp], st),
+        "ssm_debug_flags": ([P(ssm_state), P(ctypes.c_int32), i32, vp], st),
     }
     for name, (args, res) in sig.items():
         f = getattr(lib, name)
@@ -96,7 +100,8 @@ _lib = _load()
 EXPORTS = ("ssm_abi_version", "ssm_status_string", "ssm_layout_query", "ssm_ckpt_init",
            "ssm_replay_decode", "ssm_flush", "ssm_spec_append", "ssm_spec_rollback",
            "ssm_ckpt_export", "ssm_conventional_step", "ssm_tiles_pack", "ssm_tiles_unpack",
-           "ssm_debug_codec")
+           "ssm_debug_codec", "ssm_conventional_spec_snapshot", "ssm_conventional_spec_select",
+           "ssm_debug_flags")
 
 
 def _st(st):
@@ -203,6 +208,32 @@ def ssm_conventional_step(cfg: ssm_config, h: torch.Tensor, inputs: Mapping[str,
     _check("ssm_conventional_step", _lib.ssm_conventional_step(
         ctypes.byref(cfg), _ptr(h), ctypes.byref(inp), _ptr(A), _ptr(D), _ptr(y),
         _stream(stream)))
+
+
+def ssm_conventional_spec_snapshot(cfg: ssm_config, h: torch.Tensor, h_snap: torch.Tensor,
+                                   ndraft: int, inputs: Mapping[str, torch.Tensor],
+                                   A: torch.Tensor, D: torch.Tensor, y: torch.Tensor,
+                                   stream=None) -> None:
+    inp = _inputs(cfg, inputs)
+    _check("ssm_conventional_spec_snapshot", _lib.ssm_conventional_spec_snapshot(
+        ctypes.byref(cfg), _ptr(h), _ptr(h_snap), ndraft, ctypes.byref(inp), _ptr(A), _ptr(D),
+        _ptr(y), _stream(stream)))
+
+
+def ssm_conventional_spec_select(cfg: ssm_config, h: torch.Tensor, h_snap: torch.Tensor,
+                                 ndraft: int, n_accept: torch.Tensor, stream=None) -> None:
+    if n_accept.dtype != torch.int32:
+        raise ValueError("n_accept must be int32")
+    _check("ssm_conventional_spec_select", _lib.ssm_conventional_spec_select(
+        ctypes.byref(cfg), _ptr(h), _ptr(h_snap), ndraft, _ptr(n_accept), _stream(stream)))
+
+
+def ssm_debug_flags(st, clear: bool = False, stream=None) -> int:
+    st = _st(st)
+    out = ctypes.c_int32(0)
+    _check("ssm_debug_flags", _lib.ssm_debug_flags(ctypes.byref(st), ctypes.byref(out),
+                                                   int(clear), _stream(stream)))
+    return out.value
 
 
 def ssm_tiles_pack(cfg: ssm_config, natural: torch.Tensor, tiles: torch.Tensor,

@@ -725,6 +725,90 @@ __global__ __launch_bounds__(256) void m2_conv_kernel(M2ConvArgs a) {
 }
 
 // ---------------------------------------------------------------------------------------------
+// Snapshot-based speculative step (the comparison point for the speculative verify; news, para 3
+// -- per-token snapshots): the recurrence of m2_conv_kernel over ntok <= MAXQ draft tokens from
+// the read-only state a.h, writing the state after each draft to its own snapshot tile
+// (a.snap + (j * batch * H + head) * P * N) and y [batch][ntok][H][P].
+// ---------------------------------------------------------------------------------------------
+template <int P, int N, typename TIN, int MAXQ>
+__global__ __launch_bounds__(256) void m2_snap_kernel(M2ConvArgs a) {
+    using G = M2Geo<P, N>;
+    constexpr int kCE = N >= 64 ? N / 64 : 1;
+    __shared__ __attribute__((aligned(16))) float s_bc[kHeadsPerBlock][MAXQ][2][N];
+    const int wave = uniform(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int h = blockIdx.x * kHeadsPerBlock + wave;
+    if (h >= a.heads) return;
+    const int b = blockIdx.y;
+    const int H = a.heads, Gn = a.groups, nq = a.ntok;
+    const int head = b * H + h;
+    const int grp = h / (H / Gn);
+    const int row = lane % P, gq = lane / P;
+
+    const TIN* inB = static_cast<const TIN*>(a.in_B);
+    const TIN* inC = static_cast<const TIN*>(a.in_C);
+    const TIN* inx = static_cast<const TIN*>(a.in_x);
+    TIN braw[MAXQ][kCE], craw[MAXQ][kCE], xraw[MAXQ];
+    float dtj[MAXQ];
+#pragma unroll
+    for (int j = 0; j < MAXQ; ++j) {
+        const long tok = (long)b * nq + (j < nq ? j : 0);  // clamped: padded drafts are unused
+#pragma unroll
+        for (int i = 0; i < kCE; ++i) {
+            const int n = (lane + 64 * i) % N;
+            braw[j][i] = inB[(tok * Gn + grp) * N + n];
+            craw[j][i] = inC[(tok * Gn + grp) * N + n];
+        }
+        xraw[j] = inx[(tok * H + h) * P + row];
+        dtj[j] = a.in_dt[tok * H + h];
+    }
+    const float A = a.A[h], D = a.D[h];
+
+    float4 hv[G::kQPL];
+    const uint32_t lane_off = (uint32_t)((gq * P + row) * 16);
+    const TileIO tin{reinterpret_cast<char*>(a.h) + (long)head * (P * N * 4), lane_off};
+#pragma unroll
+    for (int j = 0; j < G::kQPL; ++j) hv[j] = tin.load((uint32_t)(G::kGrp * j * P * 16));
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+
+#pragma unroll
+    for (int j = 0; j < MAXQ; ++j)
+#pragma unroll
+        for (int i = 0; i < kCE; ++i) {
+            const int n = (lane + 64 * i) % N;
+            s_bc[wave][j][0][n] = to_f32<TIN>(braw[j][i]);
+            s_bc[wave][j][1][n] = to_f32<TIN>(craw[j][i]);
+        }
+    wave_sync();
+    const long nheads = (long)a.batch * H;
+#pragma unroll
+    for (int t = 0; t < MAXQ; ++t) {
+        if (t >= nq) break;
+        const float decay = expf(dtj[t] * A);
+        const float x = to_f32<TIN>(xraw[t]);
+        const float dx = dtj[t] * x;
+        const TileIO tout{reinterpret_cast<char*>(a.snap) + ((long)t * nheads + head) * (P * N * 4),
+                          lane_off};
+        float acc = 0.f;
+#pragma unroll
+        for (int j = 0; j < G::kQPL; ++j) {
+            const int q = gq + G::kGrp * j;
+            const float4 b4 = *reinterpret_cast<const float4*>(&s_bc[wave][t][0][4 * q]);
+            const float4 c4 = *reinterpret_cast<const float4*>(&s_bc[wave][t][1][4 * q]);
+            hv[j].x = decay * hv[j].x + dx * b4.x;
+            hv[j].y = decay * hv[j].y + dx * b4.y;
+            hv[j].z = decay * hv[j].z + dx * b4.z;
+            hv[j].w = decay * hv[j].w + dx * b4.w;
+            acc += hv[j].x * c4.x + hv[j].y * c4.y + hv[j].z * c4.z + hv[j].w * c4.w;
+            tout.store((uint32_t)(G::kGrp * j * P * 16), hv[j]);
+        }
+        if constexpr (G::kGrp > 1) acc = xor_reduce_sum<P, 32>(acc);
+        if (gq == 0) a.y[(((long)b * nq + t) * H + h) * P + row] = acc + D * x;
+    }
+}
+
+// ---------------------------------------------------------------------------------------------
 // Launch helpers shared by the instantiating translation units. Grid: (ceil(H / 4), batch); one
 // wavefront per head.
 // ---------------------------------------------------------------------------------------------
@@ -738,8 +822,8 @@ static inline dim3 head_grid(int batch, int heads) {
 #define SSM_M2_SHAPES(X, ...)                                                                   \
     X(16, 16, __VA_ARGS__) X(16, 32, __VA_ARGS__) X(16, 64, __VA_ARGS__)                       \
     X(16, 128, __VA_ARGS__) X(32, 32, __VA_ARGS__) X(32, 64, __VA_ARGS__)                      \
-    X(32, 128, __VA_ARGS__) X(64, 16, __VA_ARGS__) X(64, 32, __VA_ARGS__)                      \
-    X(64, 64, __VA_ARGS__) X(64, 128, __VA_ARGS__)
+    X(32, 128, __VA_ARGS__) X(32, 16, __VA_ARGS__) X(64, 16, __VA_ARGS__)                      \
+    X(64, 32, __VA_ARGS__) X(64, 64, __VA_ARGS__) X(64, 128, __VA_ARGS__)
 #endif
 
 // Speculative verify launches (m2_verify.hip); m2_launch_replay forwards multi-token calls here.

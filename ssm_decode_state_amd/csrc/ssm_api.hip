@@ -31,9 +31,8 @@ ssm_status check_config(const ssm_config* c) {
     if (c->kind == SSM_MAMBA2) {
         if (c->dim_p > 64) return SSM_E_SHAPE;           // one wavefront per head tile
         if (c->dim_n < 64 / c->dim_p * 4) return SSM_E_SHAPE;  // every lane group owns a quad
-        if (c->readcopy != SSM_RC_NONE && c->dim_p != 64) return SSM_E_UNSUPPORTED;
-        if (c->readcopy == SSM_RC_FP8_ROW && c->dim_n % 16) return SSM_E_SHAPE;
-        if (c->readcopy == SSM_RC_FP4_B16 && c->dim_n % 32) return SSM_E_SHAPE;
+        // read copies: lane p owns row p, N in {64, 128}
+        if (c->readcopy != SSM_RC_NONE && (c->dim_p != 64 || c->dim_n < 64)) return SSM_E_UNSUPPORTED;
     } else {
         if (c->groups != c->heads) return SSM_E_SHAPE;
         if (c->dim_p < 64 || c->dim_n < 64) return SSM_E_SHAPE;  // dv, dk in {64, 128}
@@ -78,6 +77,7 @@ void compute_layout(const ssm_config* c, ssm_layout* L) {
         L->off_ring[4] = take(B * H * cap * 4);        // g
     }
     L->off_ptr = take(B * H * 2 * 4);
+    L->off_flags = take(4);
     L->total_bytes = off;
 }
 
@@ -242,6 +242,8 @@ ssm_status ssm_ckpt_init(ssm_state* st, const ssm_config* cfg, void* mem, uint64
     if (e != hipSuccess) return SSM_E_HIP;
     e = ssm::launch_fill_i32(at<int>(st, lay.off_ptr), 0, nheads * 2, hs);
     if (e != hipSuccess) return SSM_E_HIP;
+    e = ssm::launch_fill_i32(at<int>(st, lay.off_flags), 0, 1, hs);
+    if (e != hipSuccess) return SSM_E_HIP;
     if (cfg->kind == SSM_MAMBA2 && cfg->readcopy != SSM_RC_NONE) {
         ssm::M2Args a = m2_args(st);
         e = ssm::m2_launch_flush(a, cfg->dim_p, cfg->dim_n, cfg->in_dtype, cfg->readcopy, 0, 1, hs);
@@ -354,7 +356,8 @@ ssm_status ssm_spec_rollback(ssm_state* st, const int32_t* n_accept, void* strea
     if (((uintptr_t)n_accept & 3u) != 0) return SSM_E_ALIGN;
     const hipStream_t hs = as_stream(stream);
     const hipError_t e = ssm::launch_commit(at<int>(st, st->lay.off_ptr), n_accept, st->cfg.batch,
-                                            st->cfg.heads, st->pending, hs);
+                                            st->cfg.heads, st->pending, at<int>(st, st->lay.off_flags),
+                                            hs);
     if (e != hipSuccess) return SSM_E_HIP;
     st->count_hi += st->pending;
     st->pending = 0;
@@ -403,6 +406,62 @@ ssm_status ssm_conventional_step(const ssm_config* cfg, float* h, const void* in
         e = ssm::gdn_launch_conv(a, c.dim_p, c.dim_n, c.in_dtype, as_stream(stream));
     }
     if (e == hipErrorNotSupported) return SSM_E_UNSUPPORTED;
+    return hip_status(e);
+}
+
+static ssm_status check_m2_spec_baseline(const ssm_config* cfg, ssm_config* c, int32_t ndraft) {
+    if (!cfg) return SSM_E_ARG;
+    *c = *cfg;
+    c->readcopy = SSM_RC_NONE;
+    const ssm_status s = check_config(c);
+    if (s != SSM_OK) return s;
+    if (c->kind != SSM_MAMBA2) return SSM_E_UNSUPPORTED;
+    if (ndraft < 1 || ndraft > 8) return SSM_E_CAPACITY;
+    return SSM_OK;
+}
+
+ssm_status ssm_conventional_spec_snapshot(const ssm_config* cfg, const float* h, float* h_snap,
+                                          int32_t ndraft, const void* in, const float* A,
+                                          const float* D, float* y, void* stream) {
+    ssm_config c;
+    ssm_status s = check_m2_spec_baseline(cfg, &c, ndraft);
+    if (s != SSM_OK) return s;
+    if (!h || !h_snap || !y || !A || !D) return SSM_E_ARG;
+    if (!aligned16(h) || !aligned16(h_snap) || !aligned16(y) || !aligned16(A) || !aligned16(D))
+        return SSM_E_ALIGN;
+    s = check_inputs(c, in);
+    if (s != SSM_OK) return s;
+    if (c.batch == 0) return SSM_OK;
+    const ssm_m2_in* m = static_cast<const ssm_m2_in*>(in);
+    ssm::M2ConvArgs a{const_cast<float*>(h), m->x, m->B, m->C, m->dt, A, D, y,
+                      c.batch, c.heads, c.groups, h_snap, ndraft};
+    const hipError_t e = ssm::m2_launch_snapshot(a, c.dim_p, c.dim_n, c.in_dtype, as_stream(stream));
+    if (e == hipErrorNotSupported) return SSM_E_UNSUPPORTED;
+    return hip_status(e);
+}
+
+ssm_status ssm_conventional_spec_select(const ssm_config* cfg, float* h, const float* h_snap,
+                                        int32_t ndraft, const int32_t* n_accept, void* stream) {
+    ssm_config c;
+    const ssm_status s = check_m2_spec_baseline(cfg, &c, ndraft);
+    if (s != SSM_OK) return s;
+    if (!h || !h_snap || !n_accept) return SSM_E_ARG;
+    if (!aligned16(h) || !aligned16(h_snap) || ((uintptr_t)n_accept & 3u) != 0) return SSM_E_ALIGN;
+    if (c.batch == 0) return SSM_OK;
+    return hip_status(ssm::launch_snap_select(h, h_snap, n_accept, c.batch,
+                                              (long)c.heads * c.dim_p * c.dim_n, ndraft,
+                                              as_stream(stream)));
+}
+
+ssm_status ssm_debug_flags(const ssm_state* st, int32_t* host_flags, int32_t clear, void* stream) {
+    const ssm_status s = check_state(st);
+    if (s != SSM_OK) return s;
+    if (!host_flags) return SSM_E_ARG;
+    const hipStream_t hs = as_stream(stream);
+    int* dflags = reinterpret_cast<int*>(static_cast<char*>(st->mem) + st->lay.off_flags);
+    hipError_t e = hipMemcpyAsync(host_flags, dflags, sizeof(int32_t), hipMemcpyDeviceToHost, hs);
+    if (e == hipSuccess) e = hipStreamSynchronize(hs);
+    if (e == hipSuccess && clear) e = ssm::launch_fill_i32(dflags, 0, 1, hs);
     return hip_status(e);
 }
 

@@ -37,6 +37,8 @@ struct M2ConvArgs {
     const float* D;
     float* y;
     int batch, heads, groups;
+    float* snap = nullptr;  // speculative snapshots [ntok][batch * heads] tiles (h read only)
+    int ntok = 1;
 };
 
 // Gated DeltaNet launches.
@@ -78,6 +80,7 @@ hipError_t m2_launch_replay(const M2Args& a, int P, int N, int bf16, int rc, boo
 hipError_t m2_launch_flush(const M2Args& a, int P, int N, int bf16, int rc, int mode_all,
                            int rewrite_only, hipStream_t s);
 hipError_t m2_launch_conv(const M2ConvArgs& a, int P, int N, int bf16, hipStream_t s);
+hipError_t m2_launch_snapshot(const M2ConvArgs& a, int P, int N, int bf16, hipStream_t s);
 
 hipError_t gdn_launch_replay(const GdnArgs& a, int dv, int dk, int bf16, hipStream_t s);
 hipError_t gdn_launch_flush(const GdnArgs& a, int dv, int dk, int bf16, int mode_all,
@@ -85,8 +88,10 @@ hipError_t gdn_launch_flush(const GdnArgs& a, int dv, int dk, int bf16, int mode
 hipError_t gdn_launch_conv(const GdnConvArgs& a, int dv, int dk, int bf16, hipStream_t s);
 
 // Pointer commit after a speculative round: count += min(n_accept[b], pending) for every head.
+hipError_t launch_snap_select(float* h, const float* snap, const int32_t* n_accept, int batch,
+                              long seq_floats, int ndraft, hipStream_t s);
 hipError_t launch_commit(int* ptr, const int32_t* n_accept, int batch, int heads, int pending,
-                         hipStream_t s);
+                         int* flags, hipStream_t s);
 hipError_t launch_fill_i32(int* p, int value, long n, hipStream_t s);
 // Natural [heads][P][N] -> quad-interleaved tiles (unpack = 0) or back (unpack = 1).
 hipError_t launch_pack(const float* src, float* dst, long nheads, int P, int N, int unpack,

@@ -1,19 +1,40 @@
 // ssm_util_kernels.hip -- small kernels: pointer commit after a speculative round, int fill,
 // natural <-> tile layout conversion, and the device fp8/fp4 codecs exposed for testing.
+#include <algorithm>
+
 #include "ssm_device.hpp"
 #include "ssm_kernels.hpp"
+#include "ssm_replay.h"
 
 namespace ssm {
 
 // Resolve pending drafts by moving pointers only (news article, para 3): every head of sequence b
-// commits min(n_accept[b], pending) drafts (negative values count as 0).
+// commits min(n_accept[b], pending) drafts (negative values count as 0); a clamped value sets the
+// accept-clamped bit of the state's flag word.
 __global__ void commit_kernel(int* ptr, const int32_t* __restrict__ n_accept, int batch, int heads,
-                              int pending) {
+                              int pending, int* flags) {
     const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= (long)batch * heads) return;
-    int acc = n_accept[i / heads];
-    acc = acc < 0 ? 0 : (acc > pending ? pending : acc);
+    const int raw = n_accept[i / heads];
+    const int acc = raw < 0 ? 0 : (raw > pending ? pending : raw);
     ptr[2 * i + 1] += acc;
+    if (acc != raw && i % heads == 0) atomicOr(flags, SSM_FLAG_ACCEPT_CLAMPED);
+}
+
+// Restore step of snapshot-based speculation: sequence b copies snapshot n_accept[b] - 1 (clamped
+// to [0, ndraft]; 0 copies nothing) over its state. Grid (blocks, batch), float4 per thread.
+__global__ void snap_select_kernel(float* __restrict__ h, const float* __restrict__ snap,
+                                   const int32_t* __restrict__ n_accept, int batch, long seq_floats,
+                                   int ndraft) {
+    const int b = blockIdx.y;
+    int n = n_accept[b];
+    n = n < 0 ? 0 : (n > ndraft ? ndraft : n);
+    if (n == 0) return;
+    const float4* src = reinterpret_cast<const float4*>(snap + ((long)(n - 1) * batch + b) * seq_floats);
+    float4* dst = reinterpret_cast<float4*>(h + (long)b * seq_floats);
+    const long nq = seq_floats / 4;
+    for (long i = (long)blockIdx.x * blockDim.x + threadIdx.x; i < nq; i += (long)gridDim.x * blockDim.x)
+        st_stream(ld_stream(src + i), dst + i);
 }
 
 __global__ void fill_i32_kernel(int* p, int value, long n) {
@@ -85,11 +106,22 @@ __global__ void codec_kernel(int op, const void* __restrict__ in, void* __restri
 static unsigned blocks_for(long n, int bs) { return (unsigned)((n + bs - 1) / bs); }
 
 hipError_t launch_commit(int* ptr, const int32_t* n_accept, int batch, int heads, int pending,
-                         hipStream_t s) {
+                         int* flags, hipStream_t s) {
     const long n = (long)batch * heads;
     if (n == 0) return hipSuccess;
     hipLaunchKernelGGL(commit_kernel, dim3(blocks_for(n, 256)), dim3(256), 0, s, ptr, n_accept,
-                       batch, heads, pending);
+                       batch, heads, pending, flags);
+    return hipGetLastError();
+}
+
+hipError_t launch_snap_select(float* h, const float* snap, const int32_t* n_accept, int batch,
+                              long seq_floats, int ndraft, hipStream_t s) {
+    if (batch == 0 || seq_floats == 0) return hipSuccess;
+    // seq_floats = H * P * N, a multiple of 64; about 8 float4 per thread per block row
+    const long nq = seq_floats / 4;
+    const unsigned bx = (unsigned)std::min<long>(blocks_for(nq, 256 * 8), 1024);
+    hipLaunchKernelGGL(snap_select_kernel, dim3(bx, (unsigned)batch), dim3(256), 0, s, h, snap,
+                       n_accept, batch, seq_floats, ndraft);
     return hipGetLastError();
 }
 

@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert bd.ssm_abi_version() == 1
+    assert bd.ssm_abi_version() == 2
     for s in range(-7, 1):
         assert bd.ssm_status_string(s) not in ("", "unknown status")
     assert bd.ssm_status_string(-99) == "unknown status"
@@ -59,7 +59,8 @@ def test_layout_serving_shape():
             lay.off_ring[3], lay.off_ptr]
     assert all(o % 256 == 0 for o in offs)
     assert offs == sorted(offs)
-    assert lay.total_bytes >= lay.off_ptr + 256 * 128 * 8
+    assert lay.off_flags >= lay.off_ptr + 256 * 128 * 8 and lay.off_flags % 256 == 0
+    assert lay.total_bytes >= lay.off_flags + 4
     spec = bd.ssm_layout_query(cfg(max_draft=4))
     assert spec.ring_cap == 19
 
@@ -70,6 +71,12 @@ def test_layout_read_copies():
     f4 = bd.ssm_layout_query(cfg(readcopy=bd.SSM_RC_FP4_B16))
     assert f4.off_rc_scale - f4.off_rc_codes == 256 * 128 * 64 * 64
     assert f4.off_rc_tscale - f4.off_rc_scale == 256 * 128 * 64 * 8
+
+
+@pytest.mark.parametrize("P,N", [(16, 16), (16, 128), (32, 16), (32, 128), (64, 16), (64, 128)])
+def test_every_accepted_mamba2_shape(P, N):
+    lay = bd.ssm_layout_query(cfg(dim_p=P, dim_n=N))
+    assert lay.off_ring[0] >= 256 * 128 * P * N * 4
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -87,6 +94,9 @@ def test_layout_read_copies():
     (dict(max_draft=5, window=4), bd.SSM_E_SHAPE),
     (dict(batch=-1), bd.SSM_E_SHAPE),
     (dict(readcopy=bd.SSM_RC_FP8_ROW, dim_p=32, dim_n=64), bd.SSM_E_UNSUPPORTED),
+    (dict(readcopy=bd.SSM_RC_FP8_ROW, dim_n=32), bd.SSM_E_UNSUPPORTED),
+    (dict(readcopy=bd.SSM_RC_FP4_B16, dim_n=32), bd.SSM_E_UNSUPPORTED),
+    (dict(dim_p=32, dim_n=4), bd.SSM_E_SHAPE),
     (dict(kind=bd.SSM_GDN, groups=64), bd.SSM_E_SHAPE),
     (dict(kind=bd.SSM_GDN, readcopy=bd.SSM_RC_FP8_ROW), bd.SSM_E_UNSUPPORTED),
     (dict(kind=bd.SSM_GDN, dim_p=32), bd.SSM_E_SHAPE),
@@ -203,3 +213,35 @@ def test_conventional_and_pack_validation():
     assert raw("ssm_debug_codec", 12, v(FAKE), v(FAKE), 4, None) == bd.SSM_E_ARG
     assert raw("ssm_debug_codec", -1, v(FAKE), v(FAKE), 4, None) == bd.SSM_E_ARG
     assert raw("ssm_debug_codec", 0, None, None, 0, None) == bd.SSM_OK  # empty: nothing to do
+
+
+def test_snapshot_baseline_validation():
+    c = cfg(max_draft=4)
+    v = ctypes.c_void_p
+    snap = lambda cc, nd, h=FAKE, s=FAKE, inp=m2_in(), y=FAKE: raw(
+        "ssm_conventional_spec_snapshot", ctypes.byref(cc), v(h), v(s), nd, ctypes.byref(inp),
+        v(FAKE), v(FAKE), v(y), None)
+    assert snap(c, 0) == bd.SSM_E_CAPACITY
+    assert snap(c, 9) == bd.SSM_E_CAPACITY
+    assert snap(c, 2, h=FAKE + 4) == bd.SSM_E_ALIGN
+    assert snap(c, 2, y=FAKE + 8) == bd.SSM_E_ALIGN
+    assert snap(c, 2, inp=m2_in(FAKE + 2)) == bd.SSM_E_ALIGN
+    assert snap(cfg(kind=bd.SSM_GDN, groups=128), 2) == bd.SSM_E_UNSUPPORTED
+    assert snap(cfg(batch=0), 4) == bd.SSM_OK  # nothing to do
+    assert raw("ssm_conventional_spec_snapshot", ctypes.byref(c), None, v(FAKE), 2,
+               ctypes.byref(m2_in()), v(FAKE), v(FAKE), v(FAKE), None) == bd.SSM_E_ARG
+    sel = lambda cc, nd, acc=FAKE: raw("ssm_conventional_spec_select", ctypes.byref(cc), v(FAKE),
+                                       v(FAKE), nd, v(acc), None)
+    assert sel(c, 0) == bd.SSM_E_CAPACITY
+    assert sel(c, 2, acc=FAKE + 2) == bd.SSM_E_ALIGN
+    assert raw("ssm_conventional_spec_select", ctypes.byref(c), v(FAKE), v(FAKE), 2, None,
+               None) == bd.SSM_E_ARG
+    assert sel(cfg(batch=0), 4) == bd.SSM_OK
+
+
+def test_debug_flags_validation():
+    out = ctypes.c_int32(0)
+    assert raw("ssm_debug_flags", ctypes.byref(bd.ssm_state()), ctypes.byref(out), 0,
+               None) == bd.SSM_E_STATE
+    st = empty_state()
+    assert raw("ssm_debug_flags", ctypes.byref(st), None, 0, None) == bd.SSM_E_ARG

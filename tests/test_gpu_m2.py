@@ -91,6 +91,7 @@ def test_small_workload_every_output_and_checkpoint():
     (2, 8, 8, 64, 16, 1, False, 5),      # L = 1: every token is folded at once
     (2, 4, 1, 64, 64, 32, True, 70),     # L = 32, one B/C group for all heads
     (1, 3, 3, 64, 32, 7, True, 22),
+    (2, 6, 3, 32, 16, 4, True, 11),      # two row copies per wave, one quad per lane
 ])
 def test_decode_shapes(B, H, G, P, N, L, bf16, T):
     shape = _shape(B, H, G, P, N, L, bf16)
@@ -139,6 +140,7 @@ def test_flush_all_and_export():
 
 
 @pytest.mark.parametrize("B,H,G,P,N,bf16", [(2, 4, 4, 16, 16, False), (3, 6, 2, 64, 128, True),
+                                            (2, 5, 5, 32, 16, True),
                                             (256, 128, 128, 64, 128, True)])
 def test_conventional_step(B, H, G, P, N, bf16):
     shape = _shape(B, H, G, P, N, 16, bf16)

@@ -149,6 +149,7 @@ def test_rollback_zero_is_bitwise_noop():
     bd.ssm_spec_append(st, 4, to_dev(synth.token_inputs(shape, 31, "draft", 0, ntok=4), DEV), y)
     bd.ssm_spec_rollback(st, torch.zeros(4, dtype=torch.int32, device=DEV))
     torch.cuda.synchronize()
+    assert bd.ssm_debug_flags(st) == 0
     after = regions(st)
     assert torch.equal(before["ckpt"], after["ckpt"])
     assert torch.equal(before["ptr"], after["ptr"])
@@ -160,6 +161,67 @@ def test_rollback_zero_is_bitwise_noop():
     torch.cuda.synchronize()
     cnt = regions(st)["ptr"].cpu()[..., 1]
     assert cnt[0].eq(7).all() and cnt[1].eq(7).all() and cnt[2].eq(9).all() and cnt[3].eq(8).all()
+    # the clamp is recorded in the flag word, which reading with clear=True resets
+    assert bd.ssm_debug_flags(st, clear=True) == bd.SSM_FLAG_ACCEPT_CLAMPED
+    assert bd.ssm_debug_flags(st) == 0
+
+
+@pytest.mark.parametrize("case", ["small", "odd", "serving"])
+def test_snapshot_baseline_matches_oracle(case):
+    """Conventional speculation (per-draft snapshots, then the accepted one restored) computes
+    the same draft outputs and final state as the oracle's speculative rounds."""
+    if case == "small":
+        w = synth.WORKLOADS["m2_small"]
+        shape, seed, R, h0s = w["shape"], 0, 12, 0.0
+    elif case == "odd":
+        shape = synth.Shape(synth.MAMBA2, 3, 6, 3, 32, 16, 8, 3, in_bf16=True)
+        seed, R, h0s = 22, 10, 0.3
+    else:
+        w = synth.WORKLOADS["m2_b256_spec"]
+        shape, seed, R, h0s = w["shape"], w["seed"], 6, w["h0_std"]
+    S = shape.max_draft
+    Bn, H, P, N = shape.batch, shape.heads, shape.dim_p, shape.dim_n
+    pairs = (sample_pairs(Bn, H, 16) if Bn * H > 64 else [(b, h) for b in range(Bn) for h in range(H)])
+    A, D = synth.head_constants(shape, seed)
+    h0 = synth.initial_state(shape, seed, h0s) if h0s else None
+    cfg = bd.make_config(bd.SSM_MAMBA2, Bn, H, shape.groups, P, N, shape.window, S,
+                         bd.SSM_IN_BF16 if shape.in_bf16 else bd.SSM_IN_F32)
+    h = torch.empty(Bn * H * P * N, device=DEV)
+    if h0 is None:
+        h.zero_()
+    else:
+        bd.ssm_tiles_pack(cfg, h0.to(DEV), h)
+    snap = torch.empty(S, Bn * H * P * N, device=DEV)
+    y = torch.empty(Bn, S, H, P, device=DEV)
+    Ad, Dd = A.to(DEV), D.to(DEV)
+    bi = torch.tensor([b for (b, _) in pairs], device=DEV)
+    hi = torch.tensor([hh for (_, hh) in pairs], device=DEV)
+    ys, accs, drafts = [], [], []
+    for r in range(R):
+        d = synth.token_inputs(shape, seed, "draft", r, ntok=S)
+        drafts.append(d)
+        bd.ssm_conventional_spec_snapshot(cfg, h, snap, S, to_dev(d, DEV), Ad, Dd, y)
+        ys.append(y[bi, :, hi].clone())
+        acc = synth.accept_counts(Bn, S, 1002, r)
+        accs.append(acc)
+        if r == 0:  # the restore moves exactly the accepted snapshot (bitwise)
+            before = h.clone()
+        bd.ssm_conventional_spec_select(cfg, h, snap, S, acc.to(DEV))
+        if r == 0:
+            torch.cuda.synchronize()
+            hv, bv, sv = h.view(Bn, -1), before.view(Bn, -1), snap.view(S, Bn, -1)
+            for b in range(Bn):
+                a = int(acc[b])
+                assert torch.equal(hv[b], sv[a - 1, b] if a > 0 else bv[b]), b
+    torch.cuda.synchronize()
+    gy = torch.stack(ys, 1).cpu().double().numpy()
+    oy, hT, _, _ = oracle_spec(A, D, h0, drafts, torch.stack(accs, 1), pairs, shape, S)
+    assert_close(gy, oy, (-1,), "snapshot-baseline draft outputs")
+    nat = torch.empty(Bn, H, P, N, device=DEV)
+    bd.ssm_tiles_unpack(cfg, h, nat)
+    torch.cuda.synchronize()
+    got = np.stack([nat[b, hh].cpu().double().numpy() for (b, hh) in pairs])
+    assert_close(got, hT, (-2, -1), "state after the snapshot rounds")
 
 
 def test_spec_state_equals_sequential_decode_bitwise():
