@@ -259,9 +259,12 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_conv_kernel(GdnConvArgs a) {
 // (v_mfma_f32_16x16x4f32): A[m][k] from lane l = (m = l%16, k = l/16), B[k][c] from lane l =
 // (k = l/16, c = l%16), D[m][c] in lane l at register r = (m = 4(l/16) + r, c = l%16).
 // Entries past the fold count are zero rows (beta = g = 0, k = v = 0), which leave S unchanged.
+// FUSED: the L-th token of a lock-step decode (count == L-1 for every sequence) is folded with
+// the L-1 buffered entries straight from the caller's inputs, and its output is taken from the
+// new state, o = scale S_L q_L (the recurrence's own form); the ring is left empty.
 // Requires DV % 64 == 0 (one wave per 64 rows) and DK % 64 == 0.
 // ---------------------------------------------------------------------------------------------
-template <int DV, int DK, typename TIN>
+template <int DV, int DK, typename TIN, bool FUSED>
 __global__ __launch_bounds__(DV)
 __attribute__((amdgpu_waves_per_eu(2))) void gdn_flush_kernel(GdnArgs a, int mode_all) {
     static_assert(DV % 64 == 0 && DK % 64 == 0, "flush tile shape");
@@ -278,6 +281,7 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_flush_kernel(GdnArgs a, int mod
     __shared__ __attribute__((aligned(16))) float s_v[kW][16][kVP];     // this wave's v slice, then U ([t][p]), then Delta'^T
     __shared__ __attribute__((aligned(16))) float s_l[kW][16][17];      // Lm
     __shared__ __attribute__((aligned(16))) float s_d[kW][64][17];      // Delta' as [p][t] (transpose buffer)
+    __shared__ __attribute__((aligned(16))) float s_q[kW][FUSED ? DK : 4];  // FUSED: the token's q
 
     const int wave = uniform(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
@@ -286,13 +290,24 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_flush_kernel(GdnArgs a, int mod
     const int cap = a.cap;
     const int2 pt = *reinterpret_cast<const int2*>(a.ptr + 2 * head);
     const int start = uniform(pt.x), count = uniform(pt.y);
-    const int nfold = mode_all ? count : (count >= a.window ? a.window : 0);
+    // FUSED: the buffered entries and this token; otherwise the oldest L (or all) entries
+    const int nfold = FUSED ? count + 1 : (mode_all ? count : (count >= a.window ? a.window : 0));
+    const int nring = FUSED ? count : nfold;  // entries that come from the ring
     if (nfold == 0) return;  // uniform over the workgroup
     const TIN* rk = static_cast<const TIN*>(a.ring_k);
     const TIN* rv = static_cast<const TIN*>(a.ring_v);
     const int li = lane & 15, lg = lane >> 4;
     const int p_base = wave * 64;
 
+    // entry e (already clamped to a folded entry): ring slot, or the caller's token (FUSED)
+    auto krow = [&](int e) -> const TIN* {
+        if (FUSED && e >= nring) return static_cast<const TIN*>(a.in_k) + (long)head * DK;
+        return rk + ((long)head * cap + ring_slot(start, e, cap)) * DK;
+    };
+    auto vrow = [&](int e) -> const TIN* {
+        if (FUSED && e >= nring) return static_cast<const TIN*>(a.in_v) + (long)head * DV;
+        return rv + ((long)head * cap + ring_slot(start, e, cap)) * DV;
+    };
     // chunk loader (branch-free: entries past nfold read the last folded entry, zeroed later)
     u32x4_t kraw[kKL], vraw[kVL];
     float be = 0.f, ge = 0.f;
@@ -301,24 +316,30 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_flush_kernel(GdnArgs a, int mod
         for (int i = 0; i < kKL; ++i) {
             const int idx = (lane + 64 * i) % (16 * kKC);
             const int e = min(c0 + idx / kKC, nfold - 1), part = idx % kKC;
-            kraw[i] = *reinterpret_cast<const u32x4_t*>(
-                rk + ((long)head * cap + ring_slot(start, e, cap)) * DK + part * kEPC);
+            kraw[i] = *reinterpret_cast<const u32x4_t*>(krow(e) + part * kEPC);
         }
 #pragma unroll
         for (int i = 0; i < kVL; ++i) {
             const int idx = (lane + 64 * i) % (16 * kVC);
             const int e = min(c0 + idx / kVC, nfold - 1), part = idx % kVC;
-            vraw[i] = *reinterpret_cast<const u32x4_t*>(
-                rv + ((long)head * cap + ring_slot(start, e, cap)) * DV + p_base + part * kEPC);
+            vraw[i] = *reinterpret_cast<const u32x4_t*>(vrow(e) + p_base + part * kEPC);
         }
         const int e = min(c0 + li, nfold - 1);
-        const long s = (long)head * cap + ring_slot(start, e, cap);
-        be = a.ring_beta[s];
-        ge = a.ring_g[s];
+        const long s = (long)head * cap + ring_slot(start, min(e, cap - 1), cap);
+        const bool tok = FUSED && e >= nring;
+        be = tok ? a.in_beta[head] : a.ring_beta[s];
+        ge = tok ? a.in_g[head] : a.ring_g[s];
         be = (c0 + li < nfold) ? be : 0.f;  // lanes 16..63 mirror lanes 0..15
         ge = (c0 + li < nfold) ? ge : 0.f;
     };
     fetch(0);
+    constexpr int kQE = DK / 64;  // FUSED: q elements per lane
+    TIN qraw[FUSED ? kQE : 1];
+    if constexpr (FUSED) {
+        const TIN* inq = static_cast<const TIN*>(a.in_q) + (long)head * DK;
+#pragma unroll
+        for (int i = 0; i < kQE; ++i) qraw[i] = inq[lane + 64 * i];
+    }
 
     // the tile in accumulator order: block (pb, nb) of lane l = row p_base + 16pb + l%16,
     // columns 16nb + 4(l/16) .. +3
@@ -336,6 +357,11 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_flush_kernel(GdnArgs a, int mod
     asm volatile("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
 
+    float opart[kPB] = {};  // FUSED: partial dot products of the new state's rows with q
+    if constexpr (FUSED) {
+#pragma unroll
+        for (int i = 0; i < kQE; ++i) s_q[wave][lane + 64 * i] = to_f32<TIN>(qraw[i]);
+    }
     for (int c0 = 0; c0 < nfold; c0 += 16) {
         if (c0 > 0) fetch(c0);
         const int nc = min(16, nfold - c0);
@@ -451,6 +477,7 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_flush_kernel(GdnArgs a, int mod
         const float gammaL = expf(gL);
 #pragma unroll
         for (int pb = 0; pb < kPB; ++pb) {
+            opart[pb] = 0.f;
             float dop[4];  // B operand: Delta'[p = 16pb + li][t = 4tg + lg]
 #pragma unroll
             for (int tg = 0; tg < 4; ++tg) dop[tg] = s_d[wave][16 * pb + li][4 * tg + lg];
@@ -461,6 +488,11 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_flush_kernel(GdnArgs a, int mod
                 for (int tg = 0; tg < 4; ++tg)
                     acc = mfma4(s_k[wave][4 * tg + lg][16 * nb + li], dop[tg], acc);
                 S[pb][nb] = acc;
+                if constexpr (FUSED) {  // the token's output row partials, o = scale S q
+                    // (every chunk recomputes them; the last chunk's are the new state's)
+                    const float4 q4 = *reinterpret_cast<const float4*>(&s_q[wave][16 * nb + 4 * lg]);
+                    opart[pb] += acc[0] * q4.x + acc[1] * q4.y + acc[2] * q4.z + acc[3] * q4.w;
+                }
             }
         }
         wave_sync();
@@ -472,10 +504,19 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_flush_kernel(GdnArgs a, int mod
         for (int nb = 0; nb < kNB; ++nb)
             tio.store((uint32_t)((4 * nb * DV + 16 * pb) * 16),
                       make_float4(S[pb][nb][0], S[pb][nb][1], S[pb][nb][2], S[pb][nb][3]));
+    if constexpr (FUSED) {
+        // row p_base + 16 pb + li is spread over lanes li + 16 lg: sum the four partials through
+        // the (now free) transpose buffer, then lane p writes row p_base + p
+#pragma unroll
+        for (int pb = 0; pb < kPB; ++pb) s_d[wave][16 * pb + li][lg] = opart[pb];
+        wave_sync();
+        const float* r = s_d[wave][lane];
+        a.o[(long)head * DV + p_base + lane] = a.scale * ((r[0] + r[1]) + (r[2] + r[3]));
+    }
     if constexpr (kW > 1) __builtin_amdgcn_s_barrier();  // every wave has read the pointers
     if (wave == 0 && lane == 0) {
         a.ptr[2 * head] = ring_slot(start, nfold, cap);
-        a.ptr[2 * head + 1] = count - nfold;
+        a.ptr[2 * head + 1] = (FUSED ? count + 1 : count) - nfold;
     }
 }
 
@@ -494,8 +535,12 @@ static hipError_t launch_replay_dd(const GdnArgs& a, hipStream_t s) {
 }
 template <int DV, int DK, typename TIN>
 static hipError_t launch_flush_dd(const GdnArgs& a, int mode_all, hipStream_t s) {
-    hipLaunchKernelGGL((gdn_flush_kernel<DV, DK, TIN>), dim3(a.heads, a.batch), dim3(DV), 0, s, a,
-                       mode_all);
+    if (mode_all == 2)  // fused decode + fold of the L-th lock-step token
+        hipLaunchKernelGGL((gdn_flush_kernel<DV, DK, TIN, true>), dim3(a.heads, a.batch), dim3(DV),
+                           0, s, a, 0);
+    else
+        hipLaunchKernelGGL((gdn_flush_kernel<DV, DK, TIN, false>), dim3(a.heads, a.batch), dim3(DV),
+                           0, s, a, mode_all);
     return hipGetLastError();
 }
 template <int DV, int DK, typename TIN>

@@ -289,6 +289,13 @@ ssm_status ssm_replay_decode(ssm_state* st, const void* in, float* y, void* stre
         a.in_q = g->q; a.in_k = g->k; a.in_v = g->v; a.in_beta = g->beta; a.in_g = g->g;
         a.o = y;
         a.ntok = 1;
+        const int L = st->cfg.window;
+        if (st->count_lo == L - 1 && st->count_hi == L - 1) {  // as for Mamba-2 above
+            e = ssm::gdn_launch_flush(a, st->cfg.dim_p, st->cfg.dim_n, st->cfg.in_dtype, 2, hs);
+            if (e != hipSuccess) return SSM_E_HIP;
+            st->count_lo = st->count_hi = 0;
+            return SSM_OK;
+        }
         e = ssm::gdn_launch_replay(a, st->cfg.dim_p, st->cfg.dim_n, st->cfg.in_dtype, hs);
     }
     if (e == hipErrorNotSupported) return SSM_E_UNSUPPORTED;
