@@ -185,6 +185,31 @@ def gdn_sequential(S0, q, k, v, beta, g, scale: float = 1.0, snap_after: Sequenc
     return o, ST, snaps
 
 
+def gdn_spec_rounds(S0, q, k, v, beta, g, accept, scale: float = 1.0, snap_after=None):
+    """GDN speculative rounds over independent heads.
+
+    q, k [nh][R][S][dk], v [nh][R][S][dv], beta/g [nh][R][S]; accept [nh][R]. snap_after
+    [nh][nsnap]: committed-token counts after which the state is recorded.
+    Returns (o [nh][R][S][dv], S_final [nh][dv][dk], snaps [nh][nsnap][dv][dk])."""
+    lib = _load()
+    q, k, v, beta, g = _f64(q), _f64(k), _f64(v), _f64(beta), _f64(g)
+    nh, R, S, dk = q.shape
+    dv = v.shape[3]
+    acc = np.ascontiguousarray(np.asarray(accept, dtype=np.int32).reshape(nh, R))
+    if snap_after is None:
+        snap_after = np.zeros((nh, 0), dtype=np.int32)
+    snap = np.ascontiguousarray(np.asarray(snap_after, dtype=np.int32).reshape(nh, -1))
+    ns = snap.shape[1]
+    S0 = None if S0 is None else _f64(S0)
+    o = np.zeros((nh, R, S, dv))
+    ST = np.zeros((nh, dv, dk))
+    snaps = np.zeros((nh, ns, dv, dk))
+    lib.orc_gdn_spec_rounds_batch(nh, dv, dk, R, S, ctypes.c_double(scale), _d(S0), _d(q), _d(k),
+                                  _d(v), _d(beta), _d(g), _i(acc), _d(o), _d(ST), ns, _i(snap),
+                                  _d(snaps))
+    return o, ST, snaps
+
+
 def gdn_replay_output(Sc, qk, k, v, beta, g, scale: float = 1.0):
     """GDN replay (backward sweep) for one head: Sc [dv][dk], qk [dk], entries k [kk][dk],
     v [kk][dv], beta/g [kk] (entry kk is the current token)."""
@@ -220,7 +245,9 @@ def _declare(lib):
     lib.orc_gdn_sequential_batch.argtypes = [i, i, i, i, d] + [_dp] * 8 + [i, _ip, _dp]
     lib.orc_gdn_replay_output.argtypes = [i, i, i, d] + [_dp] * 7
     lib.orc_gdn_flush.argtypes = [i, i, i] + [_dp] * 6
+    lib.orc_gdn_spec_rounds_batch.argtypes = ([i, i, i, i, i, d] + [_dp] * 6 +
+                                              [_ip, _dp, _dp, i, _ip, _dp])
     for f in ("orc_m2_sequential", "orc_m2_sequential_batch", "orc_m2_replay_output",
               "orc_m2_flush", "orc_m2_spec_rounds_batch", "orc_gdn_sequential_batch",
-              "orc_gdn_replay_output", "orc_gdn_flush"):
+              "orc_gdn_replay_output", "orc_gdn_flush", "orc_gdn_spec_rounds_batch"):
         getattr(lib, f).restype = None

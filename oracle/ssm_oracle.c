@@ -228,6 +228,55 @@ void orc_gdn_sequential_batch(int nh, int dv, int dk, int T, double scale, const
     }
 }
 
+/* GDN speculative rounds (news, para 3: drafts appended to the buffer, the rejected ones dropped by
+ * moving a pointer). Per round: the S drafts' outputs from the committed state, each draft seeing
+ * the drafts before it; then the state advances by the first accept[r] drafts only. */
+void orc_gdn_spec_rounds(int dv, int dk, int R, int S, double scale, const double *S0,
+                         const double *q, const double *k, const double *v, const double *beta,
+                         const double *g, const int *accept, double *o, double *S_out, int nsnap,
+                         const int *snap_after, double *snaps) {
+    const size_t sz = (size_t)dv * dk;
+    double *St = (double *)malloc(sz * sizeof(double));
+    if (S0) memcpy(St, S0, sz * sizeof(double));
+    else memset(St, 0, sz * sizeof(double));
+    int pos = 0, si = 0;
+    for (int r = 0; r < R; ++r) {
+        const size_t t0 = (size_t)r * S;
+        /* drafts from the committed state (the state itself is not advanced here) */
+        orc_gdn_sequential(dv, dk, S, scale, St, q + t0 * dk, k + t0 * dk, v + t0 * dv,
+                           beta + t0, g + t0, o + t0 * dv, NULL, 0, NULL, NULL);
+        /* commit the accepted prefix one token at a time */
+        for (int j = 0; j < accept[r]; ++j) {
+            const size_t t = t0 + j;
+            orc_gdn_sequential(dv, dk, 1, scale, St, q + t * dk, k + t * dk, v + t * dv,
+                               beta + t, g + t, NULL, St, 0, NULL, NULL);
+            ++pos;
+            while (snaps && si < nsnap && snap_after[si] == pos) {
+                memcpy(snaps + (size_t)si * sz, St, sz * sizeof(double));
+                ++si;
+            }
+        }
+    }
+    if (S_out) memcpy(S_out, St, sz * sizeof(double));
+    free(St);
+}
+
+void orc_gdn_spec_rounds_batch(int nh, int dv, int dk, int R, int S, double scale,
+                               const double *S0, const double *q, const double *k,
+                               const double *v, const double *beta, const double *g,
+                               const int *accept /*[nh][R]*/, double *o, double *S_out, int nsnap,
+                               const int *snap_after /*[nh][nsnap]*/, double *snaps) {
+    const size_t sz = (size_t)dv * dk, tok = (size_t)R * S;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int i = 0; i < nh; ++i) {
+        orc_gdn_spec_rounds(dv, dk, R, S, scale, S0 ? S0 + i * sz : NULL, q + i * tok * dk,
+                            k + i * tok * dk, v + i * tok * dv, beta + i * tok, g + i * tok,
+                            accept + (size_t)i * R, o + i * tok * dv, S_out ? S_out + i * sz : NULL,
+                            nsnap, snap_after + (size_t)i * nsnap,
+                            snaps ? snaps + (size_t)i * nsnap * sz : NULL);
+    }
+}
+
 /* GDN replay form of one output: walking the buffered entries from the newest back to the
  * checkpoint, each delta-rule step maps the query through (I - beta k k^T) alpha and emits a
  * value term.  r <- q_k, acc <- 0; for i = k..1: c_i = beta_i (k_i . r), acc += c_i v_i,

@@ -102,3 +102,28 @@ def test_replay_and_flush_identities(L):
                                   g[0, c:t + 1])
             np.testing.assert_allclose(Sc, snaps[0, (t + 1) // L - 1], rtol=1e-11, atol=1e-12)
             c = t + 1
+
+
+def test_spec_rounds_match_sequential_on_accepted_stream():
+    # Committed state after speculative rounds equals sequential stepping over the accepted
+    # drafts; every draft output equals a sequential run from the state committed before it.
+    rng = np.random.default_rng(16)
+    R, S, dv, dk = 6, 4, 5, 7
+    S0, q, k, v, beta, g = _rand_gdn(rng, 1, R * S, dv, dk)
+    acc = rng.integers(0, S + 1, size=(1, R))
+    acc[0, 1] = 0  # a round that rejects every draft
+    o, ST, _ = oracle.gdn_spec_rounds(S0, q.reshape(1, R, S, dk), k.reshape(1, R, S, dk),
+                                      v.reshape(1, R, S, dv), beta.reshape(1, R, S),
+                                      g.reshape(1, R, S), acc, scale=0.7)
+    keep = np.concatenate([np.arange(r * S, r * S + acc[0, r]) for r in range(R)]).astype(int)
+    _, Sseq, _ = oracle.gdn_sequential(S0, q[:, keep], k[:, keep], v[:, keep], beta[:, keep],
+                                       g[:, keep], scale=0.7)
+    np.testing.assert_allclose(ST, Sseq, rtol=1e-13, atol=1e-14)
+    for r in (1, R - 1):
+        prev = keep[keep < r * S]
+        _, Sprev, _ = oracle.gdn_sequential(S0, q[:, prev], k[:, prev], v[:, prev],
+                                            beta[:, prev], g[:, prev])
+        sl = slice(r * S, (r + 1) * S)
+        od, _, _ = oracle.gdn_sequential(Sprev, q[:, sl], k[:, sl], v[:, sl], beta[:, sl],
+                                         g[:, sl], scale=0.7)
+        np.testing.assert_allclose(o[0, r], od[0], rtol=1e-13, atol=1e-14)
