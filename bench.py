@@ -106,6 +106,14 @@ def gdn_replay_bytes_per_head(dv, dk, k, esz=2):
     return dv * dk * 4 + (k - 1) * entry_rd + 2 * token + dv * 4 + 12
 
 
+def gdn_verify_bytes_per_head(dv, dk, kc, S, esz=2):
+    """GDN speculative verify for one head: state read once, kc committed entries (k, v, beta,
+    g), S drafts read and appended (q, k, v, beta, g), S outputs, pointers."""
+    entry_rd = dk * esz + dv * esz + 8
+    token = 2 * dk * esz + dv * esz + 8
+    return dv * dk * 4 + kc * entry_rd + 2 * S * token + S * dv * 4 + 8
+
+
 def gdn_conv_bytes_per_head(dv, dk, esz=2):
     return 2 * dv * dk * 4 + 2 * dk * esz + dv * esz + 8 + dv * 4
 
@@ -353,6 +361,69 @@ def bench_gdn(dev, steps=128, warm=16, layers=2, pool=16):
             "speedup_vs_conventional": (Bn * n / wall) / (Bn * n / cwall)}
 
 
+def bench_gdn_spec(dev, rounds=64, warm=16, pool=16, layers=2):
+    """Gated DeltaNet speculative decoding at B=256, H=32, dv=dk=128: 4 drafts per round
+    verified in one replay call, U{0..4} accepted, pointer rollback (a fold fires whenever a
+    sequence reaches L); `layers` rotated layer instances."""
+    import torch
+    from ssm_decode_state_amd import binding as bd
+    from ssm_decode_state_amd import synth
+    w = synth.WORKLOADS["gdn_b256_spec"]
+    shape = w["shape"]
+    Bn, H, dv, dk, L, S = shape.batch, shape.heads, shape.dim_p, shape.dim_n, shape.window, w["ndraft"]
+    cfg = bd.make_config(bd.SSM_GDN, Bn, H, H, dv, dk, L, S, bd.SSM_IN_BF16)
+    sts = []
+    for layer in range(layers):
+        s0 = synth.initial_state_device(shape, w["seed"], w["h0_std"], layer)
+        sts.append(bd.State(cfg, s0, None, None))
+        del s0
+    drafts = [synth.token_inputs_device(shape, w["seed"], "bench-draft", i, ntok=S)
+              for i in range(pool)]
+    accs = [synth.accept_counts(Bn, S, w["accept_seed"], r) for r in range(warm + rounds)]
+    accs_d = [a.to(dev) for a in accs]
+    o = torch.empty(Bn, S, H, dv, device=dev)
+    counts = [[0] * Bn for _ in range(layers)]
+
+    def advance(r, layer):
+        for b in range(Bn):
+            counts[layer][b] += int(accs[r][b])
+            if counts[layer][b] >= L:
+                counts[layer][b] -= L
+
+    n_warm, n = warm * layers, rounds * layers
+    for i in range(n_warm):
+        r, layer = i // layers, i % layers
+        bd.ssm_spec_append(sts[layer], S, drafts[i % pool], o)
+        bd.ssm_spec_rollback(sts[layer], accs_d[r])
+        advance(r, layer)
+    ver_bytes = 0.0
+    for i in range(n_warm, n_warm + n):
+        r, layer = i // layers, i % layers
+        ver_bytes += H * sum(gdn_verify_bytes_per_head(dv, dk, c, S) for c in counts[layer])
+        advance(r, layer)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(n):
+        r, layer = (n_warm + i) // layers, (n_warm + i) % layers
+        ev[i][0].record()
+        bd.ssm_spec_append(sts[layer], S, drafts[(n_warm + i) % pool], o)
+        ev[i][1].record()
+        bd.ssm_spec_rollback(sts[layer], accs_d[r])
+        ev[i][2].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ver = sum(e[0].elapsed_time(e[1]) for e in ev)
+    rb = sum(e[1].elapsed_time(e[2]) for e in ev)
+    accepted = sum(int(accs[(n_warm + i) // layers].sum()) for i in range(n))
+    gbs = ver_bytes / (ver * 1e-3) / 1e9
+    return {"workload": "gdn_spec_b256_4drafts", "accepted_tokens_per_s": accepted / wall,
+            "unit": "accepted tokens/s/layer", "rounds": n, "layers_rotated": layers,
+            "mean_accept": accepted / (Bn * n), "verify_avg_us": ver / n * 1e3,
+            "verify_achieved_gbs": gbs, "verify_frac": gbs / HBM_PEAK_GBS,
+            "rollback_and_fold_avg_us": rb / n * 1e3, "ms_per_round": wall / n * 1e3}
+
+
 def cpu_baseline(seconds_target: float = 10.0):
     """The fp64 oracle (sequential recurrence, OpenMP over heads) on a bounded sample of the
     serving workload: S sequences x all 128 heads x 16 tokens, S sized for ~seconds_target of
@@ -436,8 +507,8 @@ def main():
     ap.add_argument("--copy-ref", type=int, default=0,
                     help="also run a plain copy of this many MiB (reference for HBM counters)")
     ap.add_argument("--workloads", default="all",
-                    help="comma list of extra workloads: spec, fp8, fp4, gdn, g8 (8 B/C "
-                         "groups), lsweep (window 4..32); 'all' or 'none'")
+                    help="comma list of extra workloads: spec, fp8, fp4, gdn, gdn_spec, g8 "
+                         "(8 B/C groups), lsweep (window 4..32); 'all' or 'none'")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -568,7 +639,7 @@ def main():
         out["copy_ref"] = {"bytes_read": 4 * n, "bytes_written": 4 * n, "launches": 5,
                            "avg_us": e0.elapsed_time(e1) / 5 * 1e3}
 
-    extra = ({"spec", "fp8", "fp4", "gdn", "g8", "lsweep"} if args.workloads == "all" else
+    extra = ({"spec", "fp8", "fp4", "gdn", "gdn_spec", "g8", "lsweep"} if args.workloads == "all" else
              set() if args.workloads == "none" else set(args.workloads.split(",")))
     if extra:
         del inputs, st, h0
@@ -596,6 +667,9 @@ def main():
             torch.cuda.empty_cache()
         if "gdn" in extra:
             out["workloads"]["gdn"] = bench_gdn(dev)
+            torch.cuda.empty_cache()
+        if "gdn_spec" in extra:
+            out["workloads"]["gdn_spec"] = bench_gdn_spec(dev)
             torch.cuda.empty_cache()
 
     if not args.no_cpu:

@@ -45,7 +45,8 @@
  *   Outputs y are fp32 [batch][ntok][H][P] (GDN: [batch][ntok][H][dv]).
  * - Supported shapes: Mamba-2 P in {16, 32, 64} and N in {16, 32, 64, 128} with N >= 4 * 64 / P
  *   (P = 64 takes every N); GDN dv and dk in {64, 128}; window L in [1, 32]; max_draft in
- *   [1, min(L, 8)]. The read copies need P = 64 and N in {64, 128} (Mamba-2 only).
+ *   [1, min(L, 8)], and for GDN L + max_draft - 1 <= 32 (SSM_E_UNSUPPORTED otherwise). The
+ *   read copies need P = 64 and N in {64, 128} (Mamba-2 only).
  */
 #ifndef SSM_REPLAY_H
 #define SSM_REPLAY_H
@@ -183,8 +184,9 @@ ssm_status ssm_flush(ssm_state *st, int32_t mode, void *stream);
  * draft tokens (`in` with ntok = ndraft) after each sequence's committed entries, marked pending,
  * and compute all their outputs y [batch][ndraft][H][P] in one pass over the checkpoint. Draft j's
  * output is the output the layer would give after the committed tokens and drafts 1..j.
+ * Both layer types (GDN: o [batch][ndraft][H][dv]).
  * Errors: SSM_E_STATE if drafts are already pending; SSM_E_CAPACITY if ndraft > max_draft or the
- * ring could overflow. Mamba-2 only. */
+ * ring could overflow. */
 ssm_status ssm_spec_append(ssm_state *st, int32_t ndraft, const void *in, float *y, void *stream);
 
 /* Resolve the pending drafts by moving pointers only (news, para 3): sequence b commits its

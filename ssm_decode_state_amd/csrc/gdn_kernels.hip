@@ -24,24 +24,41 @@ __device__ __forceinline__ int ring_slot(int start, int e, int cap) {
     return s >= cap ? s - cap : s;
 }
 
-// Sum over all 64 lanes, result in every lane.
-__device__ __forceinline__ float wave_sum(float v) { return xor_reduce_sum<1, 32>(v); }
+// Sum over all 64 lanes, the same value in every lane. Four DPP steps sum each row of 16 lanes
+// (lane i^1, lane i^2, the mirror within 8, the mirror within 16), then the four row sums are
+// read as scalars. No LDS round trips: the sweep below is a serial chain of these sums.
+template <int CTRL> __device__ __forceinline__ float dpp_add(float v) {
+    return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float wave_sum(float v) {
+    v = dpp_add<0xB1>(v);   // quad_perm [1,0,3,2]
+    v = dpp_add<0x4E>(v);   // quad_perm [2,3,0,1]
+    v = dpp_add<0x141>(v);  // row_half_mirror
+    v = dpp_add<0x140>(v);  // row_mirror
+    return (readlane(v, 0) + readlane(v, 16)) + (readlane(v, 32) + readlane(v, 48));
+}
 
 constexpr int kMaxWin = 32;  // largest window (entries a decode call can see)
 
 }  // namespace
 
 // ---------------------------------------------------------------------------------------------
-// Replay decode (one query). With entries 1..k after the checkpoint (entry k = this token):
+// Replay decode / speculative verify. With entries 1..k after the checkpoint (entry k = the query's
+// own token), each query's output is
 //   r <- q_k, acc <- 0; for i = k..1: c_i = beta_i (k_i . r), acc += c_i v_i, r <- alpha_i (r - c_i k_i)
 //   o = scale (S_c r + acc)
 // which is the delta-rule recurrence unrolled k times (each step maps the query through
-// alpha_i (I - beta_i k_i k_i^T) and emits beta_i (k_i . r) v_i).
+// alpha_i (I - beta_i k_i k_i^T) and emits beta_i (k_i . r) v_i). This call's ntok tokens are
+// entries count+1 .. count+ntok (news, para 3: drafts are appended to the buffer); query j sees
+// the committed entries and tokens 0..j. All queries share one read of the checkpoint rows.
+// COMMIT (decode): count += ntok at the end; otherwise the tokens stay pending drafts.
+// MAXW bounds the entries a call sees (count + ntok <= MAXW), MAXQ the tokens per call.
 // ---------------------------------------------------------------------------------------------
-template <int DV, int DK, typename TIN, int MAXW>
+template <int DV, int DK, typename TIN, int MAXW, int MAXQ, bool COMMIT>
 __global__ __launch_bounds__(64 * (DV >= 64 ? DV / 64 : 1))
 __attribute__((amdgpu_waves_per_eu(2))) void gdn_replay_kernel(GdnArgs a) {
     static_assert(DV >= 64 && DK >= 64, "replay tile: dv, dk >= 64");
+    static_assert(MAXW <= 64, "entries per call");
     constexpr int kW = DV / 64;                   // wavefronts per head
     constexpr int kRows = 64;                     // rows per wave
     constexpr int kNQ = DK / 4;
@@ -49,20 +66,22 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_replay_kernel(GdnArgs a) {
     constexpr int kEPC = 16 / (int)sizeof(TIN);
     constexpr int kVC = kRows / kEPC;             // 16-byte chunks of a wave's v slice
     constexpr int kVL = (MAXW * kVC + 63) / 64;
-    __shared__ __attribute__((aligned(16))) float s_r[kW][DK];
+    __shared__ __attribute__((aligned(16))) float s_r[kW][MAXQ][DK];
     __shared__ __attribute__((aligned(16))) u32x4_t s_v[kW][MAXW * kVC];
+    __shared__ __attribute__((aligned(16))) float s_c[kW][MAXW][MAXQ];
+    __shared__ __attribute__((aligned(16))) TIN s_k[kW][MAXW][DK];  // keys, as loaded
 
     const int wave = uniform(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int h = blockIdx.x, b = blockIdx.y;
     const int H = a.heads;
     const int head = b * H + h;
-    const int cap = a.cap;
+    const int cap = a.cap, nq = a.ntok;
     const int2 pt = *reinterpret_cast<const int2*>(a.ptr + 2 * head);
     const int start = uniform(pt.x), count = uniform(pt.y);
-    const int kmax = count + 1;
-    const long tok = (long)b * H + h;  // this token's row in the [batch][1][H] inputs
-    const TIN* rq = static_cast<const TIN*>(a.ring_q);
+    const int kmax = count + nq;
+    // row of token j (clamped to the call's tokens) in the [batch][ntok][H] inputs
+    auto tok = [&](int j) -> long { return ((long)b * nq + min(max(j, 0), nq - 1)) * H + h; };
     const TIN* rk = static_cast<const TIN*>(a.ring_k);
     const TIN* rv = static_cast<const TIN*>(a.ring_v);
     const TIN* inq = static_cast<const TIN*>(a.in_q);
@@ -70,36 +89,36 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_replay_kernel(GdnArgs a) {
     const TIN* inv = static_cast<const TIN*>(a.in_v);
     const int row = wave * kRows + lane;
 
-    // ---- small loads first (in-order memory counter) ------------------------------------------
+    // ---- small loads first (in-order memory counter; branch-free, masked later) ---------------
     const int el = lane;  // lane's key elements: [el*kE, el*kE + kE)
     float be = 0.f, ge = 0.f;  // beta, g of entry e = lane
     {
         const bool ring = lane < count;
         const int s = ring_slot(start, min(lane, cap - 1), cap);
-        const float* pb = ring ? a.ring_beta + (long)head * cap + s : a.in_beta + tok;
-        const float* pg = ring ? a.ring_g + (long)head * cap + s : a.in_g + tok;
+        const float* pb = ring ? a.ring_beta + (long)head * cap + s : a.in_beta + tok(lane - count);
+        const float* pg = ring ? a.ring_g + (long)head * cap + s : a.in_g + tok(lane - count);
         be = *pb;
         ge = *pg;
         be = lane < kmax ? be : 0.f;
         ge = lane < kmax ? ge : 0.f;
     }
-    TIN kraw[MAXW][kE];  // keys of the buffered entries (entry `count` = this token)
+    TIN kraw[MAXW][kE];  // keys of the entries (entries >= count are this call's tokens)
 #pragma unroll
     for (int e = 0; e < MAXW; ++e) {
         const TIN* src = e < count ? rk + ((long)head * cap + ring_slot(start, min(e, cap - 1), cap)) * DK
-                                   : ink + tok * DK;
+                                   : ink + tok(e - count) * DK;
         load_raw<TIN, kE>(src + el * kE, kraw[e]);
     }
-    TIN qraw[kE], kcur[kE];
-    load_raw<TIN, kE>(inq + tok * DK + el * kE, qraw);
-    load_raw<TIN, kE>(ink + tok * DK + el * kE, kcur);
+    TIN qraw[MAXQ][kE];
+#pragma unroll
+    for (int j = 0; j < MAXQ; ++j) load_raw<TIN, kE>(inq + tok(j) * DK + el * kE, qraw[j]);
     u32x4_t vraw[kVL];
 #pragma unroll
     for (int i = 0; i < kVL; ++i) {
         const int idx = (lane + 64 * i) % (MAXW * kVC);
         const int e = idx / kVC, part = idx % kVC;
         const TIN* src = e < count ? rv + ((long)head * cap + ring_slot(start, min(e, cap - 1), cap)) * DV
-                                   : inv + tok * DV;
+                                   : inv + tok(e - count) * DV;
         vraw[i] = *reinterpret_cast<const u32x4_t*>(src + wave * kRows + part * kEPC);
     }
 
@@ -111,75 +130,109 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_replay_kernel(GdnArgs a) {
     asm volatile("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
 
-    // ---- stage v rows, append this token to the rings -------------------------------------------
+    // ---- stage keys and v rows, append this call's tokens to the rings ------------------------
+#pragma unroll
+    for (int e = 0; e < MAXW; ++e)
+#pragma unroll
+        for (int i = 0; i < kE; ++i) s_k[wave][e][el * kE + i] = kraw[e][i];
 #pragma unroll
     for (int i = 0; i < kVL; ++i) {
         const int idx = lane + 64 * i;
         if (idx < MAXW * kVC) s_v[wave][idx] = vraw[i];
     }
     {
-        const int slot = ring_slot(start, count, cap);
-        const long rbase = (long)head * cap + slot;
+        const long rb = (long)head * cap;
 #pragma unroll
         for (int i = 0; i < kVL; ++i) {
             const int idx = lane + 64 * i;
             const int e = idx / kVC, part = idx % kVC;
-            if (e == count && idx < MAXW * kVC)
-                *reinterpret_cast<u32x4_t*>(static_cast<TIN*>(a.ring_v) + rbase * DV + wave * kRows +
+            if (e >= count && e < kmax && idx < MAXW * kVC)
+                *reinterpret_cast<u32x4_t*>(static_cast<TIN*>(a.ring_v) +
+                                            (rb + ring_slot(start, e, cap)) * DV + wave * kRows +
                                             part * kEPC) = vraw[i];
         }
         if (wave == 0) {
-            store_raw<TIN, kE>(static_cast<TIN*>(a.ring_q) + rbase * DK + el * kE, qraw);
-            store_raw<TIN, kE>(static_cast<TIN*>(a.ring_k) + rbase * DK + el * kE, kcur);
-            if (lane == count) {
-                a.ring_beta[rbase] = be;
-                a.ring_g[rbase] = ge;
+#pragma unroll
+            for (int j = 0; j < MAXQ; ++j) {
+                if (j >= nq) break;
+                const long rs = rb + ring_slot(start, count + j, cap);
+                store_raw<TIN, kE>(static_cast<TIN*>(a.ring_q) + rs * DK + el * kE, qraw[j]);
+            }
+#pragma unroll
+            for (int e = 0; e < MAXW; ++e) {
+                if (e >= count && e < kmax)
+                    store_raw<TIN, kE>(static_cast<TIN*>(a.ring_k) +
+                                           (rb + ring_slot(start, e, cap)) * DK + el * kE,
+                                       kraw[e]);
+            }
+            if (lane >= count && lane < kmax) {
+                const long rs = rb + ring_slot(start, lane, cap);
+                a.ring_beta[rs] = be;
+                a.ring_g[rs] = ge;
             }
         }
     }
 
-    // ---- backward sweep over the buffered entries ----------------------------------------------
-    float r[kE];
+    // ---- backward sweeps of every query over the entries it sees --------------------------------
+    float r[MAXQ][kE];
 #pragma unroll
-    for (int j = 0; j < kE; ++j) r[j] = to_f32<TIN>(qraw[j]);
-    float cvals[MAXW];
+    for (int j = 0; j < MAXQ; ++j)
 #pragma unroll
-    for (int e = MAXW - 1; e >= 0; --e) {
-        cvals[e] = 0.f;
-        if (e < kmax) {
-            float kv[kE];
+        for (int i = 0; i < kE; ++i) r[j][i] = to_f32<TIN>(qraw[j][i]);
+    wave_sync();
+    for (int e = kmax - 1; e >= 0; --e) {  // uniform trip count
+        float kv[kE];
 #pragma unroll
-            for (int j = 0; j < kE; ++j) kv[j] = to_f32<TIN>(e == count ? kcur[j] : kraw[e][j]);
+        for (int i = 0; i < kE; ++i) kv[i] = to_f32<TIN>(s_k[wave][e][el * kE + i]);
+        const float bt = readlane(be, e);
+        const float al = expf(readlane(ge, e));
+#pragma unroll
+        for (int j = 0; j < MAXQ; ++j) {
+            if (j >= nq) break;
+            if (e > count + j) continue;  // entry after query j's own token (uniform)
             float d = 0.f;
 #pragma unroll
-            for (int j = 0; j < kE; ++j) d += kv[j] * r[j];
-            d = wave_sum(d);
-            const float c = readlane(be, e) * d;
-            const float al = expf(readlane(ge, e));
+            for (int i = 0; i < kE; ++i) d += kv[i] * r[j][i];
+            const float c = bt * wave_sum(d);
 #pragma unroll
-            for (int j = 0; j < kE; ++j) r[j] = al * (r[j] - c * kv[j]);
-            cvals[e] = c;
+            for (int i = 0; i < kE; ++i) r[j][i] = al * (r[j][i] - c * kv[i]);
+            if (lane == 0) s_c[wave][e][j] = c;
         }
     }
 #pragma unroll
-    for (int j = 0; j < kE; ++j) s_r[wave][el * kE + j] = r[j];
+    for (int j = 0; j < MAXQ; ++j)
+#pragma unroll
+        for (int i = 0; i < kE; ++i) s_r[wave][j][el * kE + i] = r[j][i];
     wave_sync();
 
-    // ---- value terms and the checkpoint row product --------------------------------------------
+    // ---- value terms and the checkpoint row products --------------------------------------------
     const TIN* sv = reinterpret_cast<const TIN*>(&s_v[wave][0]);
-    float acc = 0.f;
+    float acc[MAXQ];
 #pragma unroll
-    for (int e = 0; e < MAXW; ++e)
-        if (e < kmax) acc += cvals[e] * to_f32<TIN>(sv[e * kRows + lane]);
-    float dot = 0.f;
+    for (int j = 0; j < MAXQ; ++j) acc[j] = 0.f;
+    for (int e = 0; e < kmax; ++e) {
+        const float ve = to_f32<TIN>(sv[e * kRows + lane]);
 #pragma unroll
-    for (int q = 0; q < kNQ; ++q) {
-        const float4 r4 = *reinterpret_cast<const float4*>(&s_r[wave][4 * q]);
-        dot += hv[q].x * r4.x + hv[q].y * r4.y + hv[q].z * r4.z + hv[q].w * r4.w;
+        for (int j = 0; j < MAXQ; ++j) {
+            if (j >= nq) break;
+            if (e <= count + j) acc[j] += s_c[wave][e][j] * ve;
+        }
     }
-    a.o[tok * DV + row] = a.scale * (dot + acc);
-    if constexpr (kW > 1) __builtin_amdgcn_s_barrier();  // every wave has read the pointers
-    if (wave == 0 && lane == 0) a.ptr[2 * head + 1] = count + 1;
+#pragma unroll
+    for (int j = 0; j < MAXQ; ++j) {
+        if (j >= nq) break;
+        float dot = 0.f;
+#pragma unroll
+        for (int q = 0; q < kNQ; ++q) {
+            const float4 r4 = *reinterpret_cast<const float4*>(&s_r[wave][j][4 * q]);
+            dot += hv[q].x * r4.x + hv[q].y * r4.y + hv[q].z * r4.z + hv[q].w * r4.w;
+        }
+        a.o[tok(j) * DV + row] = a.scale * (dot + acc[j]);
+    }
+    if constexpr (COMMIT) {
+        if constexpr (kW > 1) __builtin_amdgcn_s_barrier();  // every wave has read the pointers
+        if (wave == 0 && lane == 0) a.ptr[2 * head + 1] = count + nq;
+    }
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -524,13 +577,18 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_flush_kernel(GdnArgs a, int mod
 #define SSM_GDN_SHAPES(X, T) X(64, 64, T) X(64, 128, T) X(128, 64, T) X(128, 128, T)
 
 template <int DV, int DK, typename TIN>
-static hipError_t launch_replay_dd(const GdnArgs& a, hipStream_t s) {
-    if (a.window <= 16)
-        hipLaunchKernelGGL((gdn_replay_kernel<DV, DK, TIN, 16>), dim3(a.heads, a.batch), dim3(DV), 0,
-                           s, a);
-    else
-        hipLaunchKernelGGL((gdn_replay_kernel<DV, DK, TIN, 32>), dim3(a.heads, a.batch), dim3(DV), 0,
-                           s, a);
+static hipError_t launch_replay_dd(const GdnArgs& a, int maxe, bool spec, hipStream_t s) {
+    const dim3 grid(a.heads, a.batch), block(DV);
+    if (!spec) {
+        if (maxe <= 16)
+            hipLaunchKernelGGL((gdn_replay_kernel<DV, DK, TIN, 16, 1, true>), grid, block, 0, s, a);
+        else
+            hipLaunchKernelGGL((gdn_replay_kernel<DV, DK, TIN, 32, 1, true>), grid, block, 0, s, a);
+    } else if (a.ntok <= 4) {
+        hipLaunchKernelGGL((gdn_replay_kernel<DV, DK, TIN, 32, 4, false>), grid, block, 0, s, a);
+    } else {
+        hipLaunchKernelGGL((gdn_replay_kernel<DV, DK, TIN, 32, 8, false>), grid, block, 0, s, a);
+    }
     return hipGetLastError();
 }
 template <int DV, int DK, typename TIN>
@@ -549,10 +607,12 @@ static hipError_t launch_conv_dd(const GdnConvArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
-hipError_t gdn_launch_replay(const GdnArgs& a, int dv, int dk, int bf16, hipStream_t s) {
-    if (a.window > kMaxWin) return hipErrorNotSupported;
+hipError_t gdn_launch_replay(const GdnArgs& a, int dv, int dk, int bf16, bool spec, int maxe,
+                             hipStream_t s) {
+    if (maxe > kMaxWin || a.ntok < 1 || a.ntok > 8 || (!spec && a.ntok != 1))
+        return hipErrorNotSupported;
 #define X(V, K, T) \
-    if (dv == V && dk == K) return launch_replay_dd<V, K, T>(a, s);
+    if (dv == V && dk == K) return launch_replay_dd<V, K, T>(a, maxe, spec, s);
     if (bf16) { SSM_GDN_SHAPES(X, bf16_t) } else { SSM_GDN_SHAPES(X, float) }
 #undef X
     return hipErrorNotSupported;

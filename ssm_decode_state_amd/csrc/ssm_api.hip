@@ -38,6 +38,8 @@ ssm_status check_config(const ssm_config* c) {
         if (c->dim_p < 64 || c->dim_n < 64) return SSM_E_SHAPE;  // dv, dk in {64, 128}
         if (c->readcopy != SSM_RC_NONE) return SSM_E_UNSUPPORTED;
         if (!isfinite(c->gdn_scale)) return SSM_E_ARG;
+        // a call sees at most 32 entries (the replay kernel's sweep bound)
+        if (c->window + c->max_draft - 1 > 32) return SSM_E_UNSUPPORTED;
     }
     return SSM_OK;
 }
@@ -296,7 +298,8 @@ ssm_status ssm_replay_decode(ssm_state* st, const void* in, float* y, void* stre
             st->count_lo = st->count_hi = 0;
             return SSM_OK;
         }
-        e = ssm::gdn_launch_replay(a, st->cfg.dim_p, st->cfg.dim_n, st->cfg.in_dtype, hs);
+        e = ssm::gdn_launch_replay(a, st->cfg.dim_p, st->cfg.dim_n, st->cfg.in_dtype, false,
+                                   st->count_hi + 1, hs);
     }
     if (e == hipErrorNotSupported) return SSM_E_UNSUPPORTED;
     if (e != hipSuccess) return SSM_E_HIP;
@@ -332,7 +335,6 @@ ssm_status ssm_spec_append(ssm_state* st, int32_t ndraft, const void* in, float*
     ssm_status s = check_state(st);
     if (s != SSM_OK) return s;
     if (st->pending) return SSM_E_STATE;
-    if (st->cfg.kind != SSM_MAMBA2) return SSM_E_UNSUPPORTED;
     if (ndraft < 1) return SSM_E_ARG;
     if (ndraft > st->cfg.max_draft) return SSM_E_CAPACITY;
     if (!y) return SSM_E_ARG;
@@ -341,14 +343,25 @@ ssm_status ssm_spec_append(ssm_state* st, int32_t ndraft, const void* in, float*
     if (s != SSM_OK) return s;
     if (st->count_hi + ndraft > st->lay.ring_cap) return SSM_E_CAPACITY;
     if (st->cfg.batch > 0) {
-        ssm::M2Args a = m2_args(st);
-        const ssm_m2_in* m = static_cast<const ssm_m2_in*>(in);
-        a.in_x = m->x; a.in_B = m->B; a.in_C = m->C; a.in_dt = m->dt;
-        a.y = y;
-        a.ntok = ndraft;
-        const hipError_t e = ssm::m2_launch_replay(a, st->cfg.dim_p, st->cfg.dim_n,
-                                                   st->cfg.in_dtype, st->cfg.readcopy, true,
-                                                   st->count_hi + ndraft, as_stream(stream));
+        hipError_t e;
+        if (st->cfg.kind == SSM_MAMBA2) {
+            ssm::M2Args a = m2_args(st);
+            const ssm_m2_in* m = static_cast<const ssm_m2_in*>(in);
+            a.in_x = m->x; a.in_B = m->B; a.in_C = m->C; a.in_dt = m->dt;
+            a.y = y;
+            a.ntok = ndraft;
+            e = ssm::m2_launch_replay(a, st->cfg.dim_p, st->cfg.dim_n, st->cfg.in_dtype,
+                                      st->cfg.readcopy, true, st->count_hi + ndraft,
+                                      as_stream(stream));
+        } else {
+            ssm::GdnArgs a = gdn_args(st);
+            const ssm_gdn_in* g = static_cast<const ssm_gdn_in*>(in);
+            a.in_q = g->q; a.in_k = g->k; a.in_v = g->v; a.in_beta = g->beta; a.in_g = g->g;
+            a.o = y;
+            a.ntok = ndraft;
+            e = ssm::gdn_launch_replay(a, st->cfg.dim_p, st->cfg.dim_n, st->cfg.in_dtype, true,
+                                       st->count_hi + ndraft, as_stream(stream));
+        }
         if (e != hipSuccess) return SSM_E_HIP;
     }
     st->pending = ndraft;

@@ -82,7 +82,8 @@ hipError_t m2_launch_flush(const M2Args& a, int P, int N, int bf16, int rc, int 
 hipError_t m2_launch_conv(const M2ConvArgs& a, int P, int N, int bf16, hipStream_t s);
 hipError_t m2_launch_snapshot(const M2ConvArgs& a, int P, int N, int bf16, hipStream_t s);
 
-hipError_t gdn_launch_replay(const GdnArgs& a, int dv, int dk, int bf16, hipStream_t s);
+hipError_t gdn_launch_replay(const GdnArgs& a, int dv, int dk, int bf16, bool spec, int maxe,
+                             hipStream_t s);
 hipError_t gdn_launch_flush(const GdnArgs& a, int dv, int dk, int bf16, int mode_all,
                             hipStream_t s);
 hipError_t gdn_launch_conv(const GdnConvArgs& a, int dv, int dk, int bf16, hipStream_t s);

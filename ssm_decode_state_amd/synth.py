@@ -47,7 +47,7 @@ class Shape:
         return torch.bfloat16 if self.in_bf16 else torch.float32
 
 
-# The five workloads: a small parity case and four serving-batch cases.
+# A small parity case and the serving-batch cases.
 WORKLOADS: Dict[str, dict] = {
     "m2_small": dict(shape=Shape(MAMBA2, 2, 4, 4, 16, 16, 4, 4, in_bf16=False), steps=64, seed=0,
                      h0_std=0.0),
@@ -59,6 +59,8 @@ WORKLOADS: Dict[str, dict] = {
                              h0_std=math.sqrt(0.1)),
     "gdn_b256": dict(shape=Shape(GDN, 256, 32, 32, 128, 128, 16, 1), steps=256, seed=4,
                      h0_std=math.sqrt(0.1)),
+    "gdn_b256_spec": dict(shape=Shape(GDN, 256, 32, 32, 128, 128, 16, 4), rounds=128, ndraft=4,
+                          seed=5, accept_seed=1002, h0_std=math.sqrt(0.1)),
 }
 
 

@@ -100,6 +100,7 @@ def test_every_accepted_mamba2_shape(P, N):
     (dict(kind=bd.SSM_GDN, groups=64), bd.SSM_E_SHAPE),
     (dict(kind=bd.SSM_GDN, readcopy=bd.SSM_RC_FP8_ROW), bd.SSM_E_UNSUPPORTED),
     (dict(kind=bd.SSM_GDN, dim_p=32), bd.SSM_E_SHAPE),
+    (dict(kind=bd.SSM_GDN, window=32, max_draft=2), bd.SSM_E_UNSUPPORTED),
 ])
 def test_bad_configs_rejected(kw, status):
     with pytest.raises(bd.SSMError) as ei:

@@ -1,9 +1,11 @@
 """GPU parity of the Gated DeltaNet replay path (backward-sweep replay, UT/WY flush on MFMA,
-conventional step) against the fp64 oracle's sequential gated delta rule."""
+speculative verify and rollback, conventional step) against the fp64 oracle's sequential gated
+delta rule."""
 import numpy as np
 import pytest
 import torch
 
+import oracle
 from harness import GdnTokens, assert_close, gdn_oracle, sample_pairs, to_dev
 from ssm_decode_state_amd import synth
 
@@ -113,3 +115,49 @@ def test_gdn_conventional_step(B, H, dv, dk, bf16):
     oo, ST, _ = gdn_oracle(S0, tok, pairs)
     assert_close(torch.stack(os_, 1).cpu().double().numpy(), oo, (-1,), "GDN conventional outputs")
     assert_close(nat[bi, hi].cpu().double().numpy(), ST, (-2, -1), "GDN conventional state")
+
+
+@pytest.mark.parametrize("case", ["small", "odd", "serving"])
+def test_gdn_spec_rounds_match_oracle(case):
+    """Speculative rounds (drafts appended and verified in one pass, U{0..S} accepted, pointer
+    rollback, fold when a sequence reaches L) against the oracle's speculative rounds."""
+    if case == "small":
+        shape, seed, R, s0 = synth.Shape(synth.GDN, 2, 3, 3, 64, 64, 4, 4, in_bf16=False), 51, 20, 0.3
+    elif case == "odd":
+        shape, seed, R, s0 = synth.Shape(synth.GDN, 3, 2, 2, 128, 64, 8, 3, in_bf16=True), 52, 16, 0.3
+    else:
+        w = synth.WORKLOADS["gdn_b256_spec"]
+        shape, seed, R, s0 = w["shape"], w["seed"], 24, w["h0_std"]
+    S = shape.max_draft
+    Bn, H, dv, dk, L = shape.batch, shape.heads, shape.dim_p, shape.dim_n, shape.window
+    pairs = sample_pairs(Bn, H, 16) if Bn * H > 64 else [(b, h) for b in range(Bn) for h in range(H)]
+    S0 = synth.initial_state(shape, seed, s0)
+    cfg = bd.make_config(bd.SSM_GDN, Bn, H, H, dv, dk, L, S,
+                         bd.SSM_IN_BF16 if shape.in_bf16 else bd.SSM_IN_F32, 0, 0.75)
+    st = bd.State(cfg, S0.to(DEV), None, None)
+    bi = torch.tensor([b for (b, _) in pairs], device=DEV)
+    hi = torch.tensor([h for (_, h) in pairs], device=DEV)
+    o = torch.empty(Bn, S, H, dv, device=DEV)
+    outs, drafts, accs = [], [], []
+    for r in range(R):
+        d = synth.token_inputs(shape, seed, "draft", r, ntok=S)
+        drafts.append(d)
+        bd.ssm_spec_append(st, S, to_dev(d, DEV), o)
+        outs.append(o[bi, :, hi].clone())
+        acc = synth.accept_counts(Bn, S, 1002, r)
+        accs.append(acc)
+        bd.ssm_spec_rollback(st, acc.to(DEV))
+    nat = torch.empty(Bn, H, dv, dk, device=DEV)
+    bd.ssm_flush(st, bd.SSM_FLUSH_ALL)
+    bd.ssm_ckpt_export(st, nat)
+    torch.cuda.synchronize()
+    go = torch.stack(outs, 1).cpu().double().numpy()
+    ins = {key: np.stack([np.stack([synth.to_f64(d[key][b, :, h]) for d in drafts])
+                          for (b, h) in pairs]) for key in ("q", "k", "v", "beta", "g")}
+    acc = np.stack([torch.stack(accs, 1)[b].numpy() for (b, _) in pairs]).astype(np.int32)
+    S0p = np.stack([S0[b, h].double().numpy() for (b, h) in pairs])
+    oo, ST, _ = oracle.gdn_spec_rounds(S0p, ins["q"], ins["k"], ins["v"], ins["beta"], ins["g"],
+                                       acc, scale=0.75)
+    assert_close(go, oo, (-1,), "GDN draft outputs")
+    got = np.stack([nat[b, h].cpu().double().numpy() for (b, h) in pairs])
+    assert_close(got, ST, (-2, -1), "GDN state after the speculative rounds")
