@@ -66,7 +66,8 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_replay_kernel(GdnArgs a) {
     constexpr int kEPC = 16 / (int)sizeof(TIN);
     constexpr int kVC = kRows / kEPC;             // 16-byte chunks of a wave's v slice
     constexpr int kVL = (MAXW * kVC + 63) / 64;
-    __shared__ __attribute__((aligned(16))) float s_r[kW][MAXQ][DK];
+    constexpr int kRS = DK + 4;  // r row stride: the 4 rows an MFMA operand read takes hit distinct banks
+    __shared__ __attribute__((aligned(16))) float s_r[kW][MAXQ][kRS];
     __shared__ __attribute__((aligned(16))) u32x4_t s_v[kW][MAXW * kVC];
     __shared__ __attribute__((aligned(16))) float s_c[kW][MAXW][MAXQ];
     __shared__ __attribute__((aligned(16))) TIN s_k[kW][MAXW][DK];  // keys, as loaded
@@ -218,16 +219,43 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_replay_kernel(GdnArgs a) {
             if (e <= count + j) acc[j] += s_c[wave][e][j] * ve;
         }
     }
+    float dot[MAXQ];
+    if constexpr (MAXQ >= 4) {
+        // four queries per 4x4x1 MFMA (lane = row; query 4g + lane%4 supplies its r column),
+        // two accumulator chains per group of four
+        constexpr int kG = MAXQ / 4;
+        f32x4 dq[kG][2];
+#pragma unroll
+        for (int g = 0; g < kG; ++g) dq[g][0] = dq[g][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int q = 0; q < kNQ; ++q) {
+#pragma unroll
+            for (int g = 0; g < kG; ++g) {
+                const float4 r4 = *reinterpret_cast<const float4*>(&s_r[wave][4 * g + (lane & 3)][4 * q]);
+                f32x4& d = dq[g][q & 1];
+                d = mfma4x4(r4.x, hv[q].x, d);
+                d = mfma4x4(r4.y, hv[q].y, d);
+                d = mfma4x4(r4.z, hv[q].z, d);
+                d = mfma4x4(r4.w, hv[q].w, d);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < MAXQ; ++j) dot[j] = dq[j / 4][0][j % 4] + dq[j / 4][1][j % 4];
+    } else {
+#pragma unroll
+        for (int j = 0; j < MAXQ; ++j) {
+            dot[j] = 0.f;
+#pragma unroll
+            for (int q = 0; q < kNQ; ++q) {
+                const float4 r4 = *reinterpret_cast<const float4*>(&s_r[wave][j][4 * q]);
+                dot[j] += hv[q].x * r4.x + hv[q].y * r4.y + hv[q].z * r4.z + hv[q].w * r4.w;
+            }
+        }
+    }
 #pragma unroll
     for (int j = 0; j < MAXQ; ++j) {
         if (j >= nq) break;
-        float dot = 0.f;
-#pragma unroll
-        for (int q = 0; q < kNQ; ++q) {
-            const float4 r4 = *reinterpret_cast<const float4*>(&s_r[wave][j][4 * q]);
-            dot += hv[q].x * r4.x + hv[q].y * r4.y + hv[q].z * r4.z + hv[q].w * r4.w;
-        }
-        a.o[tok(j) * DV + row] = a.scale * (dot + acc[j]);
+        a.o[tok(j) * DV + row] = a.scale * (dot[j] + acc[j]);
     }
     if constexpr (COMMIT) {
         if constexpr (kW > 1) __builtin_amdgcn_s_barrier();  // every wave has read the pointers

@@ -48,9 +48,9 @@ __device__ __forceinline__ int ring_slot(int start, int e, int cap) {
 // Codes: fp8 byte at ((n/16)*P + p)*16 + n%16 of the head's code block; fp4 nibble of byte
 // ((n/32)*P + p)*16 + (n%32)/2, low nibble = even n. Block scales [p][N/16]; row/tile scales fp32.
 // ---------------------------------------------------------------------------------------------
-template <int P, int N, int MAXQ, int RC>
+template <int P, int N, int CS, int MAXQ, int RC>
 __device__ __forceinline__ void rc_row_dots(const M2Args& a, long head, int row, int nq,
-                                            const float* s_c /* [MAXQ][N] */, float (&acc)[MAXQ]) {
+                                            const float* s_c /* [MAXQ][CS] */, float (&acc)[MAXQ]) {
     static_assert(P == 64, "read copy needs P == 64");
     if constexpr (RC == 1) {
         const u32x4_t* codes = reinterpret_cast<const u32x4_t*>(a.rc_codes + head * (long)(P * N));
@@ -74,7 +74,7 @@ __device__ __forceinline__ void rc_row_dots(const M2Args& a, long head, int row,
                 if (j >= nq) break;
                 float d = 0.f;
 #pragma unroll
-                for (int i = 0; i < 16; ++i) d += v[i] * s_c[j * N + 16 * k + i];
+                for (int i = 0; i < 16; ++i) d += v[i] * s_c[j * CS + 16 * k + i];
                 acc[j] += d;
             }
         }
@@ -114,7 +114,7 @@ __device__ __forceinline__ void rc_row_dots(const M2Args& a, long head, int row,
                     if (j >= nq) break;
                     float d = 0.f;
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) d += v[i] * s_c[j * N + 16 * blk + i];
+                    for (int i = 0; i < 16; ++i) d += v[i] * s_c[j * CS + 16 * blk + i];
                     acc[j] += S * d;
                 }
             }
@@ -147,7 +147,8 @@ __global__ __launch_bounds__(256) void m2_replay_kernel(M2Args a) {
     constexpr int kBC = MAXE / 16;                       // 16-entry chunks of B segments
     constexpr int kCE = N >= 64 ? N / 64 : 1;            // C elements per lane
     static_assert(MAXE % 16 == 0 && MAXE <= 64, "MAXE");
-    __shared__ __attribute__((aligned(16))) float s_c[kHeadsPerBlock][MAXQ][N];
+    constexpr int kCS = N + 4;  // C row stride: the 4 rows an MFMA operand read takes hit distinct banks
+    __shared__ __attribute__((aligned(16))) float s_c[kHeadsPerBlock][MAXQ][kCS];
     __shared__ __attribute__((aligned(16))) u32x4_t s_x[kHeadsPerBlock][MAXE * kCPR];
     __shared__ __attribute__((aligned(16))) float s_w[kHeadsPerBlock][MAXE][MAXQ];
 
@@ -363,7 +364,28 @@ __global__ __launch_bounds__(256) void m2_replay_kernel(M2Args a) {
     float acc[MAXQ];
 #pragma unroll
     for (int j = 0; j < MAXQ; ++j) acc[j] = 0.f;
-    if constexpr (RC == 0) {
+    if constexpr (RC == 0 && P == 64 && MAXQ >= 4) {
+        // several queries: four queries per 4x4x1 MFMA (lane p = row p; query j = 4g + lane%4
+        // supplies its C column), two accumulator chains per group of four
+        constexpr int kG = MAXQ / 4;
+        f32x4 dq[kG][2];
+#pragma unroll
+        for (int g = 0; g < kG; ++g) dq[g][0] = dq[g][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int q = 0; q < G::kQPL; ++q) {
+#pragma unroll
+            for (int g = 0; g < kG; ++g) {
+                const float4 c4 = *reinterpret_cast<const float4*>(&s_c[wave][4 * g + (lane & 3)][4 * q]);
+                f32x4& d = dq[g][q & 1];
+                d = mfma4x4(c4.x, hv[q].x, d);
+                d = mfma4x4(c4.y, hv[q].y, d);
+                d = mfma4x4(c4.z, hv[q].z, d);
+                d = mfma4x4(c4.w, hv[q].w, d);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < MAXQ; ++j) acc[j] = dq[j / 4][0][j % 4] + dq[j / 4][1][j % 4];
+    } else if constexpr (RC == 0) {
 #pragma unroll
         for (int jq = 0; jq < G::kQPL; ++jq) {
             const int q = gq + G::kGrp * jq;
@@ -375,7 +397,7 @@ __global__ __launch_bounds__(256) void m2_replay_kernel(M2Args a) {
             }
         }
     } else {
-        rc_row_dots<P, N, MAXQ, RC>(a, head, row, nq, &s_c[wave][0][0], acc);
+        rc_row_dots<P, N, kCS, MAXQ, RC>(a, head, row, nq, &s_c[wave][0][0], acc);
     }
     if constexpr (G::kGrp > 1) {
 #pragma unroll

@@ -193,6 +193,13 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
+// fp32 MFMA 4x4x1 over 16 blocks (v_mfma_f32_4x4x1f32): block b = lane / 4 computes
+// D[i][j] += A[i] B[j] with A[i] from lane 4b + i, B[j] from lane 4b + j, D[i][j] in lane 4b + j,
+// register i. With a = u_{lane%4}[n] and b = h[lane][n], lane p accumulates sum_n u_i[n] h[p][n]
+// in register i: four row dot products of the wave's 64 rows per instruction.
+__device__ __forceinline__ f32x4 mfma4x4(float a, float b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_4x4x1f32(a, b, c, 0, 0, 0);
+}
 
 // ---------------------------------------------------------------------------------------------
 // OCP low-precision codecs, written from the format definitions (OCP OFP8 E4M3: bias 7, three
