@@ -310,23 +310,31 @@ def bench_readcopy(dev, rc, steps=128, warm=16, layers=4, pool=16):
             "fold_step_avg_us": sum(flush_ms) / max(len(flush_ms), 1) * 1e3}
 
 
-def bench_gdn(dev, steps=128, warm=16, layers=2, pool=16):
+def gdn_rc_replay_bytes_per_head(dv, dk, k, rc, esz=2):
+    """GDN replay launch reading the low-precision copy instead of the fp32 state."""
+    copy = dv * dk + dv * 4 if rc == 1 else dv * dk // 2 + dv * dk // 16 + 4
+    return gdn_replay_bytes_per_head(dv, dk, k, esz) - dv * dk * 4 + copy
+
+
+def bench_gdn(dev, steps=128, warm=16, layers=2, pool=16, rc=0):
     """Gated DeltaNet layer at B=256, H=32, dv=dk=128, L=16 on `layers` rotated layer instances:
-    replay path vs the conventional read-modify-write step."""
+    replay path (reading the fp32 state, or its fp8 / fp4 copy) vs the conventional
+    read-modify-write step (fp32 state only)."""
     import torch
     from ssm_decode_state_amd import binding as bd
     from ssm_decode_state_amd import synth
     w = synth.WORKLOADS["gdn_b256"]
     shape = w["shape"]
     Bn, H, dv, dk, L = shape.batch, shape.heads, shape.dim_p, shape.dim_n, shape.window
-    cfg = bd.make_config(bd.SSM_GDN, Bn, H, H, dv, dk, L, 1, bd.SSM_IN_BF16)
+    cfg = bd.make_config(bd.SSM_GDN, Bn, H, H, dv, dk, L, 1, bd.SSM_IN_BF16, rc)
     sts, convs = [], []
     for layer in range(layers):
         s0 = synth.initial_state_device(shape, w["seed"], w["h0_std"], layer)
         sts.append(bd.State(cfg, s0, None, None))
-        t = torch.empty(Bn * H * dv * dk, device=dev)
-        bd.ssm_tiles_pack(cfg, s0, t)
-        convs.append(t)
+        if rc == 0:
+            t = torch.empty(Bn * H * dv * dk, device=dev)
+            bd.ssm_tiles_pack(cfg, s0, t)
+            convs.append(t)
         del s0
     inputs = [synth.token_inputs_device(shape, w["seed"], "bench-gdn", i) for i in range(pool)]
     o = torch.empty(Bn, H, dv, device=dev)
@@ -343,9 +351,16 @@ def bench_gdn(dev, steps=128, warm=16, layers=2, pool=16):
         if k == L:
             fold.append(m)
             continue
-        rep_b += heads * gdn_replay_bytes_per_head(dv, dk, k)
+        rep_b += heads * (gdn_replay_bytes_per_head(dv, dk, k) if rc == 0 else
+                          gdn_rc_replay_bytes_per_head(dv, dk, k, rc))
         rep_ms += m
     gbs = rep_b / (rep_ms * 1e-3) / 1e9
+    if rc != 0:
+        return {"workload": "gdn_readcopy_%s_b256" % ("fp8row" if rc == 1 else "fp4b16"),
+                "tokens_per_s": Bn * n / wall, "unit": "tokens/s/layer", "layers_rotated": layers,
+                "ms_per_step": wall / n * 1e3, "replay_avg_us": rep_ms / (n - len(fold)) * 1e3,
+                "replay_achieved_gbs": gbs, "replay_frac": gbs / HBM_PEAK_GBS,
+                "fold_step_avg_us": sum(fold) / max(len(fold), 1) * 1e3}
     for i in range(n_warm):
         bd.ssm_conventional_step(cfg, convs[i % layers], inputs[i % pool], None, None, o)
     cwall, cms = timed_calls(n, lambda i: bd.ssm_conventional_step(
@@ -507,8 +522,9 @@ def main():
     ap.add_argument("--copy-ref", type=int, default=0,
                     help="also run a plain copy of this many MiB (reference for HBM counters)")
     ap.add_argument("--workloads", default="all",
-                    help="comma list of extra workloads: spec, fp8, fp4, gdn, gdn_spec, g8 "
-                         "(8 B/C groups), lsweep (window 4..32); 'all' or 'none'")
+                    help="comma list of extra workloads: spec, fp8, fp4, gdn, gdn_spec, "
+                         "gdn_fp8, gdn_fp4, g8 (8 B/C groups), lsweep (window 4..32); 'all' or "
+                         "'none'")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -639,7 +655,8 @@ def main():
         out["copy_ref"] = {"bytes_read": 4 * n, "bytes_written": 4 * n, "launches": 5,
                            "avg_us": e0.elapsed_time(e1) / 5 * 1e3}
 
-    extra = ({"spec", "fp8", "fp4", "gdn", "gdn_spec", "g8", "lsweep"} if args.workloads == "all" else
+    extra = ({"spec", "fp8", "fp4", "gdn", "gdn_spec", "gdn_fp8", "gdn_fp4", "g8", "lsweep"}
+             if args.workloads == "all" else
              set() if args.workloads == "none" else set(args.workloads.split(",")))
     if extra:
         del inputs, st, h0
@@ -667,6 +684,12 @@ def main():
             torch.cuda.empty_cache()
         if "gdn" in extra:
             out["workloads"]["gdn"] = bench_gdn(dev)
+            torch.cuda.empty_cache()
+        if "gdn_fp8" in extra:
+            out["workloads"]["gdn_readcopy_fp8"] = bench_gdn(dev, layers=4, rc=1)
+            torch.cuda.empty_cache()
+        if "gdn_fp4" in extra:
+            out["workloads"]["gdn_readcopy_fp4"] = bench_gdn(dev, layers=4, rc=2)
             torch.cuda.empty_cache()
         if "gdn_spec" in extra:
             out["workloads"]["gdn_spec"] = bench_gdn_spec(dev)

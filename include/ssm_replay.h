@@ -46,7 +46,7 @@
  * - Supported shapes: Mamba-2 P in {16, 32, 64} and N in {16, 32, 64, 128} with N >= 4 * 64 / P
  *   (P = 64 takes every N); GDN dv and dk in {64, 128}; window L in [1, 32]; max_draft in
  *   [1, min(L, 8)], and for GDN L + max_draft - 1 <= 32 (SSM_E_UNSUPPORTED otherwise). The
- *   read copies need P = 64 and N in {64, 128} (Mamba-2 only).
+ *   read copies need N (dk) in {64, 128}, and P = 64 for Mamba-2.
  */
 #ifndef SSM_REPLAY_H
 #define SSM_REPLAY_H
@@ -90,7 +90,7 @@ typedef struct ssm_config {
     int32_t window;    /* L: the buffer is folded into the checkpoint when L entries are committed */
     int32_t max_draft; /* most drafts per ssm_spec_append (1 = no speculation) */
     int32_t in_dtype;  /* SSM_IN_F32 or SSM_IN_BF16 for x/B/C (q/k/v); dt/beta/g are always fp32 */
-    int32_t readcopy;  /* SSM_RC_*: low-precision copy read by the output path (Mamba-2 only) */
+    int32_t readcopy;  /* SSM_RC_*: low-precision copy read by the output path */
     float gdn_scale;   /* GDN output scale (1.0 = none); ignored for Mamba-2 */
 } ssm_config;
 

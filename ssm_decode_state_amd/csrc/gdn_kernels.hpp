@@ -1,4 +1,5 @@
-// gdn_kernels.hip -- Gated DeltaNet ReplaySSM kernels for gfx950 (wave64).
+// gdn_kernels.hpp -- Gated DeltaNet ReplaySSM kernel templates for gfx950 (wave64). Instantiated
+// by gdn_decode.hip, gdn_verify.hip, gdn_flush.hip and gdn_conv.hip (one translation unit each).
 //
 // Pages: "ReplaySSM: Rethinking State Storage for Faster Hybrid-Model Decoding" (news article, paras
 // 2-3: checkpoint plus buffered inputs, outputs without a state write, fold when the buffer fills;
@@ -12,17 +13,14 @@
 // p = 64w + lane and every row product with a dk-vector runs inside one lane. The flush holds the
 // tile in fp32 MFMA accumulator order instead (16x16 blocks: lane l owns row 16*pb + l%16 and the
 // quad 4*nb + l/16), which is the same memory layout read with a different lane map.
+#pragma once
+#include "rc_codec.hpp"
 #include "ssm_device.hpp"
 #include "ssm_kernels.hpp"
 
 namespace ssm {
 
 namespace {
-
-__device__ __forceinline__ int ring_slot(int start, int e, int cap) {
-    const int s = start + e;
-    return s >= cap ? s - cap : s;
-}
 
 // Sum over all 64 lanes, the same value in every lane. Four DPP steps sum each row of 16 lanes
 // (lane i^1, lane i^2, the mirror within 8, the mirror within 16), then the four row sums are
@@ -38,9 +36,9 @@ __device__ __forceinline__ float wave_sum(float v) {
     return (readlane(v, 0) + readlane(v, 16)) + (readlane(v, 32) + readlane(v, 48));
 }
 
-constexpr int kMaxWin = 32;  // largest window (entries a decode call can see)
-
 }  // namespace
+
+constexpr int kGdnMaxWin = 32;  // most entries a replay call can see
 
 // ---------------------------------------------------------------------------------------------
 // Replay decode / speculative verify. With entries 1..k after the checkpoint (entry k = the query's
@@ -54,7 +52,7 @@ constexpr int kMaxWin = 32;  // largest window (entries a decode call can see)
 // COMMIT (decode): count += ntok at the end; otherwise the tokens stay pending drafts.
 // MAXW bounds the entries a call sees (count + ntok <= MAXW), MAXQ the tokens per call.
 // ---------------------------------------------------------------------------------------------
-template <int DV, int DK, typename TIN, int MAXW, int MAXQ, bool COMMIT>
+template <int DV, int DK, typename TIN, int RC, int MAXW, int MAXQ, bool COMMIT>
 __global__ __launch_bounds__(64 * (DV >= 64 ? DV / 64 : 1))
 __attribute__((amdgpu_waves_per_eu(2))) void gdn_replay_kernel(GdnArgs a) {
     static_assert(DV >= 64 && DK >= 64, "replay tile: dv, dk >= 64");
@@ -124,10 +122,12 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_replay_kernel(GdnArgs a) {
     }
 
     // ---- the checkpoint rows of this wave ------------------------------------------------------
-    float4 hv[kNQ];
-    const float4* tile = reinterpret_cast<const float4*>(a.ckpt) + (long)head * (DV * DK / 4);
+    float4 hv[kNQ];  // the fp32 rows (no read copy); with a read copy its codes are read later
+    if constexpr (RC == 0) {
+        const float4* tile = reinterpret_cast<const float4*>(a.ckpt) + (long)head * (DV * DK / 4);
 #pragma unroll
-    for (int q = 0; q < kNQ; ++q) hv[q] = ld_stream(tile + q * DV + row);
+        for (int q = 0; q < kNQ; ++q) hv[q] = ld_stream(tile + q * DV + row);
+    }
     asm volatile("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
 
@@ -220,7 +220,12 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_replay_kernel(GdnArgs a) {
         }
     }
     float dot[MAXQ];
-    if constexpr (MAXQ >= 4) {
+    if constexpr (RC != 0) {  // the decoded copy's rows against every r_j (news, para 4)
+#pragma unroll
+        for (int j = 0; j < MAXQ; ++j) dot[j] = 0.f;
+        rc_row_dots<DV, DK, kRS, MAXQ, RC>(RcView{a.rc_codes, a.rc_scale, a.rc_tscale}, head, row, nq,
+                                           &s_r[wave][0][0], dot);
+    } else if constexpr (MAXQ >= 4) {
         // four queries per 4x4x1 MFMA (lane = row; query 4g + lane%4 supplies its r column),
         // two accumulator chains per group of four
         constexpr int kG = MAXQ / 4;
@@ -345,9 +350,10 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_conv_kernel(GdnConvArgs a) {
 // new state, o = scale S_L q_L (the recurrence's own form); the ring is left empty.
 // Requires DV % 64 == 0 (one wave per 64 rows) and DK % 64 == 0.
 // ---------------------------------------------------------------------------------------------
-template <int DV, int DK, typename TIN, bool FUSED>
+template <int DV, int DK, typename TIN, int RC, bool FUSED>
 __global__ __launch_bounds__(DV)
-__attribute__((amdgpu_waves_per_eu(2))) void gdn_flush_kernel(GdnArgs a, int mode_all) {
+__attribute__((amdgpu_waves_per_eu(2))) void gdn_flush_kernel(GdnArgs a, int mode_all,
+                                                              int rewrite_only) {
     static_assert(DV % 64 == 0 && DK % 64 == 0, "flush tile shape");
     constexpr int kW = DV / 64;
     constexpr int kPB = 4;            // 16-row blocks per wave
@@ -363,6 +369,7 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_flush_kernel(GdnArgs a, int mod
     __shared__ __attribute__((aligned(16))) float s_l[kW][16][17];      // Lm
     __shared__ __attribute__((aligned(16))) float s_d[kW][64][17];      // Delta' as [p][t] (transpose buffer)
     __shared__ __attribute__((aligned(16))) float s_q[kW][FUSED ? DK : 4];  // FUSED: the token's q
+    __shared__ float s_amax[kW];  // fp4 read copy: the waves' largest magnitudes
 
     const int wave = uniform(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
@@ -372,9 +379,10 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_flush_kernel(GdnArgs a, int mod
     const int2 pt = *reinterpret_cast<const int2*>(a.ptr + 2 * head);
     const int start = uniform(pt.x), count = uniform(pt.y);
     // FUSED: the buffered entries and this token; otherwise the oldest L (or all) entries
-    const int nfold = FUSED ? count + 1 : (mode_all ? count : (count >= a.window ? a.window : 0));
+    const int nfold = FUSED ? count + 1
+                            : (rewrite_only ? 0 : (mode_all ? count : (count >= a.window ? a.window : 0)));
     const int nring = FUSED ? count : nfold;  // entries that come from the ring
-    if (nfold == 0) return;  // uniform over the workgroup
+    if (nfold == 0 && !rewrite_only) return;  // uniform over the workgroup
     const TIN* rk = static_cast<const TIN*>(a.ring_k);
     const TIN* rv = static_cast<const TIN*>(a.ring_v);
     const int li = lane & 15, lg = lane >> 4;
@@ -396,16 +404,16 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_flush_kernel(GdnArgs a, int mod
 #pragma unroll
         for (int i = 0; i < kKL; ++i) {
             const int idx = (lane + 64 * i) % (16 * kKC);
-            const int e = min(c0 + idx / kKC, nfold - 1), part = idx % kKC;
+            const int e = min(c0 + idx / kKC, max(nfold - 1, 0)), part = idx % kKC;
             kraw[i] = *reinterpret_cast<const u32x4_t*>(krow(e) + part * kEPC);
         }
 #pragma unroll
         for (int i = 0; i < kVL; ++i) {
             const int idx = (lane + 64 * i) % (16 * kVC);
-            const int e = min(c0 + idx / kVC, nfold - 1), part = idx % kVC;
+            const int e = min(c0 + idx / kVC, max(nfold - 1, 0)), part = idx % kVC;
             vraw[i] = *reinterpret_cast<const u32x4_t*>(vrow(e) + p_base + part * kEPC);
         }
-        const int e = min(c0 + li, nfold - 1);
+        const int e = min(c0 + li, max(nfold - 1, 0));
         const long s = (long)head * cap + ring_slot(start, min(e, cap - 1), cap);
         const bool tok = FUSED && e >= nring;
         be = tok ? a.in_beta[head] : a.ring_beta[s];
@@ -413,7 +421,7 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_flush_kernel(GdnArgs a, int mod
         be = (c0 + li < nfold) ? be : 0.f;  // lanes 16..63 mirror lanes 0..15
         ge = (c0 + li < nfold) ? ge : 0.f;
     };
-    fetch(0);
+    fetch(0);  // entries clamped to >= 0: in bounds also when nothing is folded (rewrite only)
     constexpr int kQE = DK / 64;  // FUSED: q elements per lane
     TIN qraw[FUSED ? kQE : 1];
     if constexpr (FUSED) {
@@ -580,7 +588,7 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_flush_kernel(GdnArgs a, int mod
     }
 
 #pragma unroll
-    for (int pb = 0; pb < kPB; ++pb)
+    for (int pb = 0; pb < kPB; ++pb)  // (a rewrite-only pass stores the tile unchanged)
 #pragma unroll
         for (int nb = 0; nb < kNB; ++nb)
             tio.store((uint32_t)((4 * nb * DV + 16 * pb) * 16),
@@ -594,71 +602,37 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_flush_kernel(GdnArgs a, int mod
         const float* r = s_d[wave][lane];
         a.o[(long)head * DV + p_base + lane] = a.scale * ((r[0] + r[1]) + (r[2] + r[3]));
     }
+    if constexpr (RC != 0) {  // rewrite the read copy from the new fp32 tile (news, para 4)
+        float amax_t = 0.f;
+        if constexpr (RC == 2) {
+            const float wmax = xor_reduce_max<1, 32>(rc_local_amax<DK>(S));
+            if constexpr (kW > 1) {
+                if (lane == 0) s_amax[wave] = wmax;
+                __syncthreads();
+#pragma unroll
+                for (int w = 0; w < kW; ++w) amax_t = fmaxf(amax_t, s_amax[w]);
+            } else {
+                amax_t = wmax;
+            }
+        }
+        rc_write_blocks<DV, DK, RC>(RcView{a.rc_codes, a.rc_scale, a.rc_tscale}, head, p_base, li, lg,
+                                    S, amax_t, wave == 0 && lane == 0);
+    }
     if constexpr (kW > 1) __builtin_amdgcn_s_barrier();  // every wave has read the pointers
-    if (wave == 0 && lane == 0) {
+    if (nfold > 0 && wave == 0 && lane == 0) {
         a.ptr[2 * head] = ring_slot(start, nfold, cap);
         a.ptr[2 * head + 1] = (FUSED ? count + 1 : count) - nfold;
     }
 }
 
 // ---------------------------------------------------------------------------------------------
+// Launch helpers shared by the instantiating translation units: grid (H, batch), one workgroup of
+// dv/64 wavefronts per head.
+// ---------------------------------------------------------------------------------------------
 #define SSM_GDN_SHAPES(X, T) X(64, 64, T) X(64, 128, T) X(128, 64, T) X(128, 128, T)
 
-template <int DV, int DK, typename TIN>
-static hipError_t launch_replay_dd(const GdnArgs& a, int maxe, bool spec, hipStream_t s) {
-    const dim3 grid(a.heads, a.batch), block(DV);
-    if (!spec) {
-        if (maxe <= 16)
-            hipLaunchKernelGGL((gdn_replay_kernel<DV, DK, TIN, 16, 1, true>), grid, block, 0, s, a);
-        else
-            hipLaunchKernelGGL((gdn_replay_kernel<DV, DK, TIN, 32, 1, true>), grid, block, 0, s, a);
-    } else if (a.ntok <= 4) {
-        hipLaunchKernelGGL((gdn_replay_kernel<DV, DK, TIN, 32, 4, false>), grid, block, 0, s, a);
-    } else {
-        hipLaunchKernelGGL((gdn_replay_kernel<DV, DK, TIN, 32, 8, false>), grid, block, 0, s, a);
-    }
-    return hipGetLastError();
-}
-template <int DV, int DK, typename TIN>
-static hipError_t launch_flush_dd(const GdnArgs& a, int mode_all, hipStream_t s) {
-    if (mode_all == 2)  // fused decode + fold of the L-th lock-step token
-        hipLaunchKernelGGL((gdn_flush_kernel<DV, DK, TIN, true>), dim3(a.heads, a.batch), dim3(DV),
-                           0, s, a, 0);
-    else
-        hipLaunchKernelGGL((gdn_flush_kernel<DV, DK, TIN, false>), dim3(a.heads, a.batch), dim3(DV),
-                           0, s, a, mode_all);
-    return hipGetLastError();
-}
-template <int DV, int DK, typename TIN>
-static hipError_t launch_conv_dd(const GdnConvArgs& a, hipStream_t s) {
-    hipLaunchKernelGGL((gdn_conv_kernel<DV, DK, TIN>), dim3(a.heads, a.batch), dim3(DV), 0, s, a);
-    return hipGetLastError();
-}
-
-hipError_t gdn_launch_replay(const GdnArgs& a, int dv, int dk, int bf16, bool spec, int maxe,
-                             hipStream_t s) {
-    if (maxe > kMaxWin || a.ntok < 1 || a.ntok > 8 || (!spec && a.ntok != 1))
-        return hipErrorNotSupported;
-#define X(V, K, T) \
-    if (dv == V && dk == K) return launch_replay_dd<V, K, T>(a, maxe, spec, s);
-    if (bf16) { SSM_GDN_SHAPES(X, bf16_t) } else { SSM_GDN_SHAPES(X, float) }
-#undef X
-    return hipErrorNotSupported;
-}
-hipError_t gdn_launch_flush(const GdnArgs& a, int dv, int dk, int bf16, int mode_all,
-                            hipStream_t s) {
-#define X(V, K, T) \
-    if (dv == V && dk == K) return launch_flush_dd<V, K, T>(a, mode_all, s);
-    if (bf16) { SSM_GDN_SHAPES(X, bf16_t) } else { SSM_GDN_SHAPES(X, float) }
-#undef X
-    return hipErrorNotSupported;
-}
-hipError_t gdn_launch_conv(const GdnConvArgs& a, int dv, int dk, int bf16, hipStream_t s) {
-#define X(V, K, T) \
-    if (dv == V && dk == K) return launch_conv_dd<V, K, T>(a, s);
-    if (bf16) { SSM_GDN_SHAPES(X, bf16_t) } else { SSM_GDN_SHAPES(X, float) }
-#undef X
-    return hipErrorNotSupported;
-}
+// Speculative verify launches (gdn_verify.hip); gdn_launch_replay forwards multi-token calls here.
+hipError_t gdn_launch_verify(const GdnArgs& a, int dv, int dk, int bf16, int rc, int maxe,
+                             hipStream_t s);
 
 }  // namespace ssm

@@ -13,6 +13,7 @@
 // reduction. For P < 64 the wave holds 64/P copies of the rows, each lane group taking every
 // (64/P)-th quad, and the groups are summed with shuffles at the end.
 #pragma once
+#include "rc_codec.hpp"
 #include "ssm_device.hpp"
 #include "ssm_kernels.hpp"
 
@@ -31,96 +32,6 @@ template <int P, int N> struct M2Geo {
 constexpr int kHeadsPerBlock = 4;
 constexpr int kMaxEntries = 64;  // ring entries a wave can address (cap <= 63)
 
-// Ring slot of entry e (0-based after the checkpoint): (start + e) mod cap for start < cap and
-// e < cap, without an integer division (keeps the address arithmetic branch-free).
-__device__ __forceinline__ int ring_slot(int start, int e, int cap) {
-    const int s = start + e;
-    return s >= cap ? s - cap : s;
-}
-
-// ---------------------------------------------------------------------------------------------
-// Read copy (news, para 4: a low-precision copy of the checkpoint serves the reads while the
-// recurrence keeps the fp32 checkpoint). Only P = 64 tiles, where lane p owns row p:
-//   fp8 row copy: s = amax_row / 448 (1 if zero), code = RNE_sat_e4m3(h * (1/s)), value*s.
-//   fp4 copy (NVFP4 reading): s_t = amax_tile / 2688 (1 if zero); per 16-element block
-//     s_b = value(RNE_sat_e4m3(amax_blk / (6 s_t))), S = s_b s_t,
-//     code = RNE_sat_e2m1(h * (1/S)) (all zero when S == 0), value*S.
-// Codes: fp8 byte at ((n/16)*P + p)*16 + n%16 of the head's code block; fp4 nibble of byte
-// ((n/32)*P + p)*16 + (n%32)/2, low nibble = even n. Block scales [p][N/16]; row/tile scales fp32.
-// ---------------------------------------------------------------------------------------------
-template <int P, int N, int CS, int MAXQ, int RC>
-__device__ __forceinline__ void rc_row_dots(const M2Args& a, long head, int row, int nq,
-                                            const float* s_c /* [MAXQ][CS] */, float (&acc)[MAXQ]) {
-    static_assert(P == 64, "read copy needs P == 64");
-    if constexpr (RC == 1) {
-        const u32x4_t* codes = reinterpret_cast<const u32x4_t*>(a.rc_codes + head * (long)(P * N));
-        u32x4_t u[N / 16];
-#pragma unroll
-        for (int k = 0; k < N / 16; ++k) u[k] = __builtin_nontemporal_load(codes + k * P + row);
-        const float s = static_cast<const float*>(a.rc_scale)[head * P + row];
-#pragma unroll
-        for (int k = 0; k < N / 16; ++k) {
-            const uint32_t w[4] = {u[k].x, u[k].y, u[k].z, u[k].w};
-            float v[16];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                float o[4];
-                e4m3_word_decode(w[q], o);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) v[4 * q + i] = o[i];
-            }
-#pragma unroll
-            for (int j = 0; j < MAXQ; ++j) {
-                if (j >= nq) break;
-                float d = 0.f;
-#pragma unroll
-                for (int i = 0; i < 16; ++i) d += v[i] * s_c[j * CS + 16 * k + i];
-                acc[j] += d;
-            }
-        }
-#pragma unroll
-        for (int j = 0; j < MAXQ; ++j) acc[j] *= s;
-    } else {
-        const u32x4_t* codes = reinterpret_cast<const u32x4_t*>(a.rc_codes + head * (long)(P * N / 2));
-        u32x4_t u[N / 32];
-#pragma unroll
-        for (int k = 0; k < N / 32; ++k) u[k] = __builtin_nontemporal_load(codes + k * P + row);
-        const uint8_t* sbp = static_cast<const uint8_t*>(a.rc_scale) + (head * P + row) * (N / 16);
-        uint32_t sbw[(N / 16 + 3) / 4];
-        if constexpr (N / 16 >= 8) {
-            const uint2 t = *reinterpret_cast<const uint2*>(sbp);
-            sbw[0] = t.x; sbw[1] = t.y;
-        } else {
-            sbw[0] = *reinterpret_cast<const uint32_t*>(sbp);
-        }
-        const float st = a.rc_tscale[head];
-#pragma unroll
-        for (int k = 0; k < N / 32; ++k) {
-            const uint32_t w[4] = {u[k].x, u[k].y, u[k].z, u[k].w};
-#pragma unroll
-            for (int half = 0; half < 2; ++half) {
-                const int blk = 2 * k + half;
-                const float S = e4m3_decode((sbw[blk / 4] >> (8 * (blk % 4))) & 0xff) * st;
-                float v[16];  // elements 16 half .. 16 half + 15 of the 32-element unit
-#pragma unroll
-                for (int q = 0; q < 2; ++q) {
-                    float o[8];
-                    e2m1_word_decode(w[2 * half + q], o);
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) v[8 * q + i] = o[i];
-                }
-#pragma unroll
-                for (int j = 0; j < MAXQ; ++j) {
-                    if (j >= nq) break;
-                    float d = 0.f;
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) d += v[i] * s_c[j * CS + 16 * blk + i];
-                    acc[j] += S * d;
-                }
-            }
-        }
-    }
-}
 
 // ---------------------------------------------------------------------------------------------
 // Replay decode / speculative verify.
@@ -397,7 +308,8 @@ __global__ __launch_bounds__(256) void m2_replay_kernel(M2Args a) {
             }
         }
     } else {
-        rc_row_dots<P, N, kCS, MAXQ, RC>(a, head, row, nq, &s_c[wave][0][0], acc);
+        rc_row_dots<P, N, kCS, MAXQ, RC>(RcView{a.rc_codes, a.rc_scale, a.rc_tscale}, head, row, nq,
+                                         &s_c[wave][0][0], acc);
     }
     if constexpr (G::kGrp > 1) {
 #pragma unroll
@@ -429,68 +341,6 @@ __global__ __launch_bounds__(256) void m2_replay_kernel(M2Args a) {
 //   separate replay pass over the checkpoint on that step.
 // The read copy (news, para 4) is rewritten from the new fp32 checkpoint in the same pass.
 // ---------------------------------------------------------------------------------------------
-template <int P, int N, int RC>
-__device__ __forceinline__ void rc_write_blocks(const M2Args& a, int head, int li, int lg,
-                                                const f32x4 (&hb)[P / 16][N / 16]) {
-    static_assert(P == 64, "read copy needs P == 64");
-    constexpr int kPB = P / 16, kNB = N / 16;
-    if constexpr (RC == 1) {
-        uint8_t* codes = a.rc_codes + (long)head * (P * N);
-#pragma unroll
-        for (int pb = 0; pb < kPB; ++pb) {
-            float amax = 0.f;
-#pragma unroll
-            for (int nb = 0; nb < kNB; ++nb)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) amax = fmaxf(amax, fabsf(hb[pb][nb][r]));
-            amax = xor_reduce_max<16, 32>(amax);  // the row is spread over lanes li + 16 lg
-            const float sc = amax > 0.f ? amax / 448.f : 1.f;
-            const float inv = 1.f / sc;
-            const int p = 16 * pb + li;
-#pragma unroll
-            for (int nb = 0; nb < kNB; ++nb) {
-                const uint32_t w = e4m3_word_encode(hb[pb][nb][0] * inv, hb[pb][nb][1] * inv,
-                                                    hb[pb][nb][2] * inv, hb[pb][nb][3] * inv);
-                *reinterpret_cast<uint32_t*>(codes + ((long)nb * P + p) * 16 + 4 * lg) = w;
-            }
-            if (lg == 0) static_cast<float*>(a.rc_scale)[(long)head * P + p] = sc;
-        }
-    } else {
-        float amax = 0.f;
-#pragma unroll
-        for (int pb = 0; pb < kPB; ++pb)
-#pragma unroll
-            for (int nb = 0; nb < kNB; ++nb)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) amax = fmaxf(amax, fabsf(hb[pb][nb][r]));
-        const float amax_t = xor_reduce_max<1, 32>(amax);
-        const float st = amax_t > 0.f ? amax_t / 2688.f : 1.f;
-        const float d6 = 6.f * st;
-        uint8_t* codes = a.rc_codes + (long)head * (P * N / 2);
-        uint8_t* sbp = static_cast<uint8_t*>(a.rc_scale) + (long)head * P * (N / 16);
-#pragma unroll
-        for (int pb = 0; pb < kPB; ++pb) {
-            const int p = 16 * pb + li;
-#pragma unroll
-            for (int nb = 0; nb < kNB; ++nb) {
-                float ab = fmaxf(fmaxf(fabsf(hb[pb][nb][0]), fabsf(hb[pb][nb][1])),
-                                 fmaxf(fabsf(hb[pb][nb][2]), fabsf(hb[pb][nb][3])));
-                ab = xor_reduce_max<16, 32>(ab);  // the 16-element block spans lanes li + 16 lg
-                const uint32_t sb = e4m3_encode(ab / d6);
-                const float S = e4m3_decode(sb) * st;
-                const float inv = S > 0.f ? 1.f / S : 0.f;
-                const uint32_t c = S > 0.f ? e2m1_half_encode(hb[pb][nb][0] * inv, hb[pb][nb][1] * inv,
-                                                              hb[pb][nb][2] * inv, hb[pb][nb][3] * inv)
-                                           : 0u;
-                *reinterpret_cast<uint16_t*>(codes + ((long)(nb / 2) * P + p) * 16 + 8 * (nb % 2) + 2 * lg) =
-                    (uint16_t)c;
-                if (lg == 0) sbp[p * (N / 16) + nb] = (uint8_t)sb;
-            }
-        }
-        if (threadIdx.x % 64 == 0) a.rc_tscale[head] = st;
-    }
-}
-
 template <int P, int N, typename TIN, int RC, bool FUSED>
 __global__ __launch_bounds__(256)
 __attribute__((amdgpu_waves_per_eu(2))) void m2_fold_kernel(M2Args a, int mode_all, int rewrite_only) {
@@ -672,7 +522,12 @@ __attribute__((amdgpu_waves_per_eu(2))) void m2_fold_kernel(M2Args a, int mode_a
             }
         }
     }
-    if constexpr (RC != 0) rc_write_blocks<P, N, RC>(a, head, li, lg, hb);
+    if constexpr (RC != 0) {
+        static_assert(P == 64, "read copy needs P == 64");
+        const float amax_t = RC == 2 ? xor_reduce_max<1, 32>(rc_local_amax<N>(hb)) : 0.f;
+        rc_write_blocks<P, N, RC>(RcView{a.rc_codes, a.rc_scale, a.rc_tscale}, head, 0, li, lg, hb,
+                                  amax_t, lane == 0);
+    }
     if (nfold > 0 && lane == 0) {
         a.ptr[2 * head] = ring_slot(start, nfold, cap);
         a.ptr[2 * head + 1] = (FUSED ? count + 1 : count) - nfold;

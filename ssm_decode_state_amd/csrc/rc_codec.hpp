@@ -1,0 +1,172 @@
+// rc_codec.hpp -- the low-precision read copy of a state tile (news article, para 4: a
+// low-precision copy of the checkpoint serves the reads while the recurrence keeps the fp32
+// checkpoint), shared by the Mamba-2 and Gated DeltaNet kernels.
+//
+// A head's tile has ROWS rows (Mamba-2 P = 64, GDN dv) of N elements (Mamba-2 N, GDN dk):
+//   fp8 row copy: s = amax_row / 448 (1 if zero), code = RNE_sat_e4m3(h * (1/s)), value*s.
+//   fp4 copy (NVFP4 reading): s_t = amax_tile / 2688 (1 if zero); per 16-element block
+//     s_b = value(RNE_sat_e4m3(amax_blk / (6 s_t))), S = s_b s_t,
+//     code = RNE_sat_e2m1(h * (1/S)) (all zero when S == 0), value*S.
+// Codes: fp8 byte at ((n/16)*ROWS + p)*16 + n%16 of the head's code block; fp4 nibble of byte
+// ((n/32)*ROWS + p)*16 + (n%32)/2, low nibble = even n. Block scales [p][N/16]; row and tile
+// scales fp32.
+#pragma once
+#include "ssm_device.hpp"
+
+namespace ssm {
+
+// Device pointers of one layer's read copy.
+struct RcView {
+    uint8_t* codes;
+    void* scale;    // fp8: fp32 row scales; fp4: E4M3 block-scale codes
+    float* tscale;  // fp4: fp32 tile scales
+};
+
+// Row dot products of the decoded copy's row `row` with MAXQ query vectors (s_q, row stride CS),
+// accumulated into acc[j] for j < nq. The lane owning row `row` reads its whole row.
+template <int ROWS, int N, int CS, int MAXQ, int RC>
+__device__ __forceinline__ void rc_row_dots(const RcView& v, long head, int row, int nq,
+                                            const float* s_q, float (&acc)[MAXQ]) {
+    static_assert(N == 64 || N == 128, "read copy: N in {64, 128}");
+    if constexpr (RC == 1) {
+        const u32x4_t* codes = reinterpret_cast<const u32x4_t*>(v.codes + head * (long)(ROWS * N));
+        u32x4_t u[N / 16];
+#pragma unroll
+        for (int k = 0; k < N / 16; ++k) u[k] = __builtin_nontemporal_load(codes + k * ROWS + row);
+        const float s = static_cast<const float*>(v.scale)[head * ROWS + row];
+#pragma unroll
+        for (int k = 0; k < N / 16; ++k) {
+            const uint32_t w[4] = {u[k].x, u[k].y, u[k].z, u[k].w};
+            float val[16];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                float o[4];
+                e4m3_word_decode(w[q], o);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) val[4 * q + i] = o[i];
+            }
+#pragma unroll
+            for (int j = 0; j < MAXQ; ++j) {
+                if (j >= nq) break;
+                float d = 0.f;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) d += val[i] * s_q[j * CS + 16 * k + i];
+                acc[j] += s * d;
+            }
+        }
+    } else {
+        const u32x4_t* codes = reinterpret_cast<const u32x4_t*>(v.codes + head * (long)(ROWS * N / 2));
+        u32x4_t u[N / 32];
+#pragma unroll
+        for (int k = 0; k < N / 32; ++k) u[k] = __builtin_nontemporal_load(codes + k * ROWS + row);
+        const uint8_t* sbp = static_cast<const uint8_t*>(v.scale) + (head * ROWS + row) * (N / 16);
+        uint32_t sbw[(N / 16 + 3) / 4];
+        if constexpr (N / 16 >= 8) {
+            const uint2 t = *reinterpret_cast<const uint2*>(sbp);
+            sbw[0] = t.x; sbw[1] = t.y;
+        } else {
+            sbw[0] = *reinterpret_cast<const uint32_t*>(sbp);
+        }
+        const float st = v.tscale[head];
+#pragma unroll
+        for (int k = 0; k < N / 32; ++k) {
+            const uint32_t w[4] = {u[k].x, u[k].y, u[k].z, u[k].w};
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                const int blk = 2 * k + half;
+                const float S = e4m3_decode((sbw[blk / 4] >> (8 * (blk % 4))) & 0xff) * st;
+                float val[16];  // elements 16 half .. 16 half + 15 of the 32-element unit
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+                    float o[8];
+                    e2m1_word_decode(w[2 * half + q], o);
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) val[8 * q + i] = o[i];
+                }
+#pragma unroll
+                for (int j = 0; j < MAXQ; ++j) {
+                    if (j >= nq) break;
+                    float d = 0.f;
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) d += val[i] * s_q[j * CS + 16 * blk + i];
+                    acc[j] += S * d;
+                }
+            }
+        }
+    }
+}
+
+// Largest magnitude among this lane's values of a tile held in MFMA accumulator order (hb[pb][nb]
+// holds row row0 + 16 pb + l%16, columns 16 nb + 4 (l/16) .. + 3). The caller reduces it over the
+// lanes (and waves) that hold the head's tile: the fp4 tile scale.
+template <int N>
+__device__ __forceinline__ float rc_local_amax(const f32x4 (&hb)[4][N / 16]) {
+    float amax = 0.f;
+#pragma unroll
+    for (int pb = 0; pb < 4; ++pb)
+#pragma unroll
+        for (int nb = 0; nb < N / 16; ++nb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) amax = fmaxf(amax, fabsf(hb[pb][nb][r]));
+    return amax;
+}
+
+// Write the copy of rows row0 .. row0 + 63 of a head's tile from its fp32 values in MFMA
+// accumulator order (see rc_local_amax). fp4 needs amax_tile, the largest magnitude over the whole
+// head tile; `tile_writer` is true in exactly one lane of the head, which stores the tile scale.
+template <int ROWS, int N, int RC>
+__device__ __forceinline__ void rc_write_blocks(const RcView& v, long head, int row0, int li, int lg,
+                                                const f32x4 (&hb)[4][N / 16], float amax_tile,
+                                                bool tile_writer) {
+    static_assert(N == 64 || N == 128, "read copy: N in {64, 128}");
+    constexpr int kNB = N / 16;
+    if constexpr (RC == 1) {
+        uint8_t* codes = v.codes + head * (long)(ROWS * N);
+#pragma unroll
+        for (int pb = 0; pb < 4; ++pb) {
+            float amax = 0.f;
+#pragma unroll
+            for (int nb = 0; nb < kNB; ++nb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) amax = fmaxf(amax, fabsf(hb[pb][nb][r]));
+            amax = xor_reduce_max<16, 32>(amax);  // the row is spread over lanes li + 16 lg
+            const float sc = amax > 0.f ? amax / 448.f : 1.f;
+            const float inv = 1.f / sc;
+            const int p = row0 + 16 * pb + li;
+#pragma unroll
+            for (int nb = 0; nb < kNB; ++nb) {
+                const uint32_t w = e4m3_word_encode(hb[pb][nb][0] * inv, hb[pb][nb][1] * inv,
+                                                    hb[pb][nb][2] * inv, hb[pb][nb][3] * inv);
+                *reinterpret_cast<uint32_t*>(codes + ((long)nb * ROWS + p) * 16 + 4 * lg) = w;
+            }
+            if (lg == 0) static_cast<float*>(v.scale)[head * ROWS + p] = sc;
+        }
+    } else {
+        const float st = amax_tile > 0.f ? amax_tile / 2688.f : 1.f;
+        const float d6 = 6.f * st;
+        uint8_t* codes = v.codes + head * (long)(ROWS * N / 2);
+        uint8_t* sbp = static_cast<uint8_t*>(v.scale) + head * (long)ROWS * (N / 16);
+#pragma unroll
+        for (int pb = 0; pb < 4; ++pb) {
+            const int p = row0 + 16 * pb + li;
+#pragma unroll
+            for (int nb = 0; nb < kNB; ++nb) {
+                float ab = fmaxf(fmaxf(fabsf(hb[pb][nb][0]), fabsf(hb[pb][nb][1])),
+                                 fmaxf(fabsf(hb[pb][nb][2]), fabsf(hb[pb][nb][3])));
+                ab = xor_reduce_max<16, 32>(ab);  // the 16-element block spans lanes li + 16 lg
+                const uint32_t sb = e4m3_encode(ab / d6);
+                const float S = e4m3_decode(sb) * st;
+                const float inv = S > 0.f ? 1.f / S : 0.f;
+                const uint32_t c = S > 0.f ? e2m1_half_encode(hb[pb][nb][0] * inv, hb[pb][nb][1] * inv,
+                                                              hb[pb][nb][2] * inv, hb[pb][nb][3] * inv)
+                                           : 0u;
+                *reinterpret_cast<uint16_t*>(codes + ((long)(nb / 2) * ROWS + p) * 16 + 8 * (nb % 2) +
+                                             2 * lg) = (uint16_t)c;
+                if (lg == 0) sbp[(long)p * (N / 16) + nb] = (uint8_t)sb;
+            }
+        }
+        if (tile_writer) v.tscale[head] = st;
+    }
+}
+
+}  // namespace ssm

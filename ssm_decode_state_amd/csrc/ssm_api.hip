@@ -36,7 +36,6 @@ ssm_status check_config(const ssm_config* c) {
     } else {
         if (c->groups != c->heads) return SSM_E_SHAPE;
         if (c->dim_p < 64 || c->dim_n < 64) return SSM_E_SHAPE;  // dv, dk in {64, 128}
-        if (c->readcopy != SSM_RC_NONE) return SSM_E_UNSUPPORTED;
         if (!isfinite(c->gdn_scale)) return SSM_E_ARG;
         // a call sees at most 32 entries (the replay kernel's sweep bound)
         if (c->window + c->max_draft - 1 > 32) return SSM_E_UNSUPPORTED;
@@ -122,6 +121,9 @@ ssm::GdnArgs gdn_args(const ssm_state* st) {
     memset(&a, 0, sizeof(a));
     const ssm_layout& L = st->lay;
     a.ckpt = at<float>(st, L.off_ckpt);
+    a.rc_codes = at<uint8_t>(st, L.off_rc_codes);
+    a.rc_scale = at<void>(st, L.off_rc_scale);
+    a.rc_tscale = at<float>(st, L.off_rc_tscale);
     a.ring_q = at<void>(st, L.off_ring[0]);
     a.ring_k = at<void>(st, L.off_ring[1]);
     a.ring_v = at<void>(st, L.off_ring[2]);
@@ -176,7 +178,8 @@ ssm_status launch_flush(ssm_state* st, int mode_all, hipStream_t s) {
                                  mode_all, 0, s);
     } else {
         ssm::GdnArgs a = gdn_args(st);
-        e = ssm::gdn_launch_flush(a, st->cfg.dim_p, st->cfg.dim_n, st->cfg.in_dtype, mode_all, s);
+        e = ssm::gdn_launch_flush(a, st->cfg.dim_p, st->cfg.dim_n, st->cfg.in_dtype,
+                                  st->cfg.readcopy, mode_all, 0, s);
     }
     if (e == hipErrorNotSupported) return SSM_E_UNSUPPORTED;
     return hip_status(e);
@@ -246,9 +249,14 @@ ssm_status ssm_ckpt_init(ssm_state* st, const ssm_config* cfg, void* mem, uint64
     if (e != hipSuccess) return SSM_E_HIP;
     e = ssm::launch_fill_i32(at<int>(st, lay.off_flags), 0, 1, hs);
     if (e != hipSuccess) return SSM_E_HIP;
-    if (cfg->kind == SSM_MAMBA2 && cfg->readcopy != SSM_RC_NONE) {
-        ssm::M2Args a = m2_args(st);
-        e = ssm::m2_launch_flush(a, cfg->dim_p, cfg->dim_n, cfg->in_dtype, cfg->readcopy, 0, 1, hs);
+    if (cfg->readcopy != SSM_RC_NONE) {  // the copy of the initial checkpoint
+        if (cfg->kind == SSM_MAMBA2) {
+            ssm::M2Args a = m2_args(st);
+            e = ssm::m2_launch_flush(a, cfg->dim_p, cfg->dim_n, cfg->in_dtype, cfg->readcopy, 0, 1, hs);
+        } else {
+            ssm::GdnArgs a = gdn_args(st);
+            e = ssm::gdn_launch_flush(a, cfg->dim_p, cfg->dim_n, cfg->in_dtype, cfg->readcopy, 0, 1, hs);
+        }
         if (e != hipSuccess) return SSM_E_HIP;
     }
     return SSM_OK;
@@ -292,13 +300,16 @@ ssm_status ssm_replay_decode(ssm_state* st, const void* in, float* y, void* stre
         a.o = y;
         a.ntok = 1;
         const int L = st->cfg.window;
-        if (st->count_lo == L - 1 && st->count_hi == L - 1) {  // as for Mamba-2 above
-            e = ssm::gdn_launch_flush(a, st->cfg.dim_p, st->cfg.dim_n, st->cfg.in_dtype, 2, hs);
+        if (st->cfg.readcopy == SSM_RC_NONE && st->count_lo == L - 1 && st->count_hi == L - 1) {
+            // as for Mamba-2 above (with a read copy: replay, then the fold below)
+            e = ssm::gdn_launch_flush(a, st->cfg.dim_p, st->cfg.dim_n, st->cfg.in_dtype,
+                                      st->cfg.readcopy, 2, 0, hs);
             if (e != hipSuccess) return SSM_E_HIP;
             st->count_lo = st->count_hi = 0;
             return SSM_OK;
         }
-        e = ssm::gdn_launch_replay(a, st->cfg.dim_p, st->cfg.dim_n, st->cfg.in_dtype, false,
+        e = ssm::gdn_launch_replay(a, st->cfg.dim_p, st->cfg.dim_n, st->cfg.in_dtype,
+                                   st->cfg.readcopy, false,
                                    st->count_hi + 1, hs);
     }
     if (e == hipErrorNotSupported) return SSM_E_UNSUPPORTED;
@@ -359,7 +370,8 @@ ssm_status ssm_spec_append(ssm_state* st, int32_t ndraft, const void* in, float*
             a.in_q = g->q; a.in_k = g->k; a.in_v = g->v; a.in_beta = g->beta; a.in_g = g->g;
             a.o = y;
             a.ntok = ndraft;
-            e = ssm::gdn_launch_replay(a, st->cfg.dim_p, st->cfg.dim_n, st->cfg.in_dtype, true,
+            e = ssm::gdn_launch_replay(a, st->cfg.dim_p, st->cfg.dim_n, st->cfg.in_dtype,
+                                       st->cfg.readcopy, true,
                                        st->count_hi + ndraft, as_stream(stream));
         }
         if (e != hipSuccess) return SSM_E_HIP;

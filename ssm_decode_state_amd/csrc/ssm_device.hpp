@@ -27,6 +27,13 @@ __device__ __forceinline__ void st_stream(float4 v, float4* p) {
     __builtin_nontemporal_store(t, reinterpret_cast<f32x4_t*>(p));
 }
 
+// Ring slot of entry e (0-based after the checkpoint): (start + e) mod cap for start < cap and
+// e < cap, without an integer division (keeps the address arithmetic branch-free).
+__device__ __forceinline__ int ring_slot(int start, int e, int cap) {
+    const int s = start + e;
+    return s >= cap ? s - cap : s;
+}
+
 // Streaming access to a state tile through a wave-uniform base and a 32-bit per-lane byte
 // offset: each access is an SGPR base plus one shared VGPR offset, so a tile that is loaded at
 // the start of a kernel and stored at its end keeps no per-access 64-bit addresses alive.
@@ -165,18 +172,49 @@ __device__ __forceinline__ void wave_sync() {
 
 __device__ __forceinline__ float shfl_xor(float v, int m) { return __shfl_xor(v, m, 64); }
 
+// Pair of values {v[l], v[l ^ M]} (in an unspecified order) for a lane exchange mask M, taken
+// without LDS where gfx950 allows: M = 16 and 32 by v_permlane16_swap / v_permlane32_swap (with
+// both operands v, the odd rows of one swap with the even rows of the other), M = 1 and 2 by
+// DPP quad permutes; other masks by ds_bpermute. A commutative op on the pair gives the xor
+// exchange, identical in both lanes of every pair.
+template <int M> struct XorPair {
+    __device__ __forceinline__ static void get(float v, float& a, float& b) {
+        if constexpr (M == 16 || M == 32) {
+            const auto p = M == 16 ? __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false)
+                                   : __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+            a = __uint_as_float(p[0]);
+            b = __uint_as_float(p[1]);
+        } else if constexpr (M == 1 || M == 2) {
+            constexpr int ctrl = M == 1 ? 0xB1 : 0x4E;  // quad_perm [1,0,3,2] / [2,3,0,1]
+            a = v;
+            b = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), ctrl, 0xF, 0xF, false));
+        } else {
+            a = v;
+            b = shfl_xor(v, M);
+        }
+    }
+};
+
 // Sum over lanes that differ only in the bits of `lo..hi` (masks lo, 2lo, ..., hi).
 template <int LO, int HI>
 __device__ __forceinline__ float xor_reduce_sum(float v) {
-#pragma unroll
-    for (int m = LO; m <= HI; m <<= 1) v += shfl_xor(v, m);
-    return v;
+    if constexpr (LO <= HI) {
+        float a, b;
+        XorPair<LO>::get(v, a, b);
+        return xor_reduce_sum<2 * LO, HI>(a + b);
+    } else {
+        return v;
+    }
 }
 template <int LO, int HI>
 __device__ __forceinline__ float xor_reduce_max(float v) {
-#pragma unroll
-    for (int m = LO; m <= HI; m <<= 1) v = fmaxf(v, shfl_xor(v, m));
-    return v;
+    if constexpr (LO <= HI) {
+        float a, b;
+        XorPair<LO>::get(v, a, b);
+        return xor_reduce_max<2 * LO, HI>(fmaxf(a, b));
+    } else {
+        return v;
+    }
 }
 
 // Value of v in lane `lane`. The index MUST be wave-uniform: a per-lane index is silently

@@ -44,6 +44,9 @@ struct M2ConvArgs {
 // Gated DeltaNet launches.
 struct GdnArgs {
     float* ckpt;
+    uint8_t* rc_codes;  // read-copy codes (null without a read copy)
+    void* rc_scale;     // fp8: fp32 row scales; fp4: E4M3 block-scale codes
+    float* rc_tscale;   // fp4: fp32 tile scales
     void* ring_q;
     void* ring_k;
     void* ring_v;
@@ -82,10 +85,10 @@ hipError_t m2_launch_flush(const M2Args& a, int P, int N, int bf16, int rc, int 
 hipError_t m2_launch_conv(const M2ConvArgs& a, int P, int N, int bf16, hipStream_t s);
 hipError_t m2_launch_snapshot(const M2ConvArgs& a, int P, int N, int bf16, hipStream_t s);
 
-hipError_t gdn_launch_replay(const GdnArgs& a, int dv, int dk, int bf16, bool spec, int maxe,
-                             hipStream_t s);
-hipError_t gdn_launch_flush(const GdnArgs& a, int dv, int dk, int bf16, int mode_all,
-                            hipStream_t s);
+hipError_t gdn_launch_replay(const GdnArgs& a, int dv, int dk, int bf16, int rc, bool spec,
+                             int maxe, hipStream_t s);
+hipError_t gdn_launch_flush(const GdnArgs& a, int dv, int dk, int bf16, int rc, int mode_all,
+                            int rewrite_only, hipStream_t s);
 hipError_t gdn_launch_conv(const GdnConvArgs& a, int dv, int dk, int bf16, hipStream_t s);
 
 // Pointer commit after a speculative round: count += min(n_accept[b], pending) for every head.

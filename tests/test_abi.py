@@ -65,6 +65,16 @@ def test_layout_serving_shape():
     assert spec.ring_cap == 19
 
 
+def test_layout_gdn_read_copies():
+    c = cfg(kind=bd.SSM_GDN, heads=32, groups=32, dim_p=128, dim_n=128)
+    f8 = bd.ssm_layout_query(bd.make_config(**{**{f: getattr(c, f) for f, _ in c._fields_},
+                                              "readcopy": bd.SSM_RC_FP8_ROW}))
+    assert f8.off_rc_scale - f8.off_rc_codes == 256 * 32 * 128 * 128
+    f4 = bd.ssm_layout_query(bd.make_config(**{**{f: getattr(c, f) for f, _ in c._fields_},
+                                              "readcopy": bd.SSM_RC_FP4_B16}))
+    assert f4.off_rc_tscale - f4.off_rc_scale == 256 * 32 * 128 * 8
+
+
 def test_layout_read_copies():
     f8 = bd.ssm_layout_query(cfg(readcopy=bd.SSM_RC_FP8_ROW))
     assert f8.off_rc_scale - f8.off_rc_codes == 256 * 128 * 64 * 128
@@ -98,7 +108,6 @@ def test_every_accepted_mamba2_shape(P, N):
     (dict(readcopy=bd.SSM_RC_FP4_B16, dim_n=32), bd.SSM_E_UNSUPPORTED),
     (dict(dim_p=32, dim_n=4), bd.SSM_E_SHAPE),
     (dict(kind=bd.SSM_GDN, groups=64), bd.SSM_E_SHAPE),
-    (dict(kind=bd.SSM_GDN, readcopy=bd.SSM_RC_FP8_ROW), bd.SSM_E_UNSUPPORTED),
     (dict(kind=bd.SSM_GDN, dim_p=32), bd.SSM_E_SHAPE),
     (dict(kind=bd.SSM_GDN, window=32, max_draft=2), bd.SSM_E_UNSUPPORTED),
 ])
