@@ -5,8 +5,9 @@ shares no code with the HIP library (ssm_decode_state_amd/csrc) and never import
 module both sides use is ssm_decode_state_amd.synth, which draws the seeded inputs.
 
 Contents:
-  ssm_oracle.c  plain fp64 loops: Mamba-2 and Gated DeltaNet sequential recurrences (the
-                definitions), their replay and flush forms, and speculative rounds.
+  ssm_oracle.c  plain fp64 loops: Mamba-2, Gated DeltaNet and Kimi Delta Attention sequential
+                recurrences (the definitions), their replay and flush forms, and speculative
+                rounds.
   quant.py      fp8 e4m3 / fp4 e2m1 read-copy quantizers emulated in fp32 numpy, with error bounds.
   ring.py       the ring-buffer pointer state machine (start / count / pending per sequence).
 
@@ -210,6 +211,65 @@ def gdn_spec_rounds(S0, q, k, v, beta, g, accept, scale: float = 1.0, snap_after
     return o, ST, snaps
 
 
+# ----------------------------------------------------------------------------------------------
+# Kimi Delta Attention (g is [..][dk]: one log-decay per key channel)
+# ----------------------------------------------------------------------------------------------
+def kda_sequential(S0, q, k, v, beta, g, scale: float = 1.0, snap_after: Sequence[int] = ()):
+    """Sequential KDA recurrence over independent heads.
+
+    S0 [nh][dv][dk] or None; q, k, g [nh][T][dk]; v [nh][T][dv]; beta [nh][T].
+    Returns (o [nh][T][dv], S_T [nh][dv][dk], snaps [nh][nsnap][dv][dk])."""
+    lib = _load()
+    q, k, v, beta, g = _f64(q), _f64(k), _f64(v), _f64(beta), _f64(g)
+    nh, T, dk = q.shape
+    dv = v.shape[2]
+    assert g.shape == (nh, T, dk)
+    S0 = None if S0 is None else _f64(S0)
+    o = np.zeros((nh, T, dv))
+    ST = np.zeros((nh, dv, dk))
+    snap = np.ascontiguousarray(np.asarray(snap_after, dtype=np.int32))
+    ns = snap.size
+    snaps = np.zeros((nh, ns, dv, dk))
+    lib.orc_kda_sequential_batch(nh, dv, dk, T, ctypes.c_double(scale), _d(S0), _d(q), _d(k),
+                                 _d(v), _d(beta), _d(g), _d(o), _d(ST), ns, _i(snap), _d(snaps))
+    return o, ST, snaps
+
+
+def kda_replay_output(Sc, qk, k, v, beta, g, scale: float = 1.0):
+    """KDA replay form for one head: checkpoint Sc [dv][dk], query qk [dk], entries k [kk][dk],
+    v [kk][dv], beta [kk], g [kk][dk]. Returns o [dv]."""
+    lib = _load()
+    Sc, qk, k, v, beta, g = _f64(Sc), _f64(qk), _f64(k), _f64(v), _f64(beta), _f64(g)
+    kk, dk = k.shape
+    dv = v.shape[1]
+    out = np.zeros(dv)
+    lib.orc_kda_replay_output(dv, dk, kk, ctypes.c_double(scale), _d(Sc), _d(qk), _d(k), _d(v),
+                              _d(beta), _d(g), _d(out))
+    return out
+
+
+def kda_spec_rounds(S0, q, k, v, beta, g, accept, scale: float = 1.0, snap_after=None):
+    """KDA speculative rounds over independent heads: q, k, g [nh][R][S][dk], v [nh][R][S][dv],
+    beta [nh][R][S], accept [nh][R]. Returns (o [nh][R][S][dv], S_final, snaps)."""
+    lib = _load()
+    q, k, v, beta, g = _f64(q), _f64(k), _f64(v), _f64(beta), _f64(g)
+    nh, R, S, dk = q.shape
+    dv = v.shape[3]
+    acc = np.ascontiguousarray(np.asarray(accept, dtype=np.int32).reshape(nh, R))
+    if snap_after is None:
+        snap_after = np.zeros((nh, 0), dtype=np.int32)
+    snap = np.ascontiguousarray(np.asarray(snap_after, dtype=np.int32).reshape(nh, -1))
+    ns = snap.shape[1]
+    S0 = None if S0 is None else _f64(S0)
+    o = np.zeros((nh, R, S, dv))
+    ST = np.zeros((nh, dv, dk))
+    snaps = np.zeros((nh, ns, dv, dk))
+    lib.orc_kda_spec_rounds_batch(nh, dv, dk, R, S, ctypes.c_double(scale), _d(S0), _d(q), _d(k),
+                                  _d(v), _d(beta), _d(g), _i(acc), _d(o), _d(ST), ns, _i(snap),
+                                  _d(snaps))
+    return o, ST, snaps
+
+
 def gdn_replay_output(Sc, qk, k, v, beta, g, scale: float = 1.0):
     """GDN replay (backward sweep) for one head: Sc [dv][dk], qk [dk], entries k [kk][dk],
     v [kk][dv], beta/g [kk] (entry kk is the current token)."""
@@ -247,7 +307,12 @@ def _declare(lib):
     lib.orc_gdn_flush.argtypes = [i, i, i] + [_dp] * 6
     lib.orc_gdn_spec_rounds_batch.argtypes = ([i, i, i, i, i, d] + [_dp] * 6 +
                                               [_ip, _dp, _dp, i, _ip, _dp])
+    lib.orc_kda_sequential_batch.argtypes = [i, i, i, i, d] + [_dp] * 8 + [i, _ip, _dp]
+    lib.orc_kda_replay_output.argtypes = [i, i, i, d] + [_dp] * 7
+    lib.orc_kda_spec_rounds_batch.argtypes = ([i, i, i, i, i, d] + [_dp] * 6 +
+                                              [_ip, _dp, _dp, i, _ip, _dp])
     for f in ("orc_m2_sequential", "orc_m2_sequential_batch", "orc_m2_replay_output",
               "orc_m2_flush", "orc_m2_spec_rounds_batch", "orc_gdn_sequential_batch",
-              "orc_gdn_replay_output", "orc_gdn_flush", "orc_gdn_spec_rounds_batch"):
+              "orc_gdn_replay_output", "orc_gdn_flush", "orc_gdn_spec_rounds_batch",
+              "orc_kda_sequential_batch", "orc_kda_replay_output", "orc_kda_spec_rounds_batch"):
         getattr(lib, f).restype = None

@@ -10,12 +10,15 @@
  *   [feed]      babnews.org feed excerpt (names Mamba-2, Gated DeltaNet and KDA as the SSM layers)
  *   [news]      deskofai.com news article; "para n" = n-th body paragraph
  *   [explainer] nexus-ai-blog.com article; cited by section heading
- * The pages only name the two layer types; their recurrences are the published definitions:
+ * The pages only name the layer types; their recurrences are the published definitions:
  *   Mamba-2: Dao & Gu, "Transformers are SSMs" (ICML 2024), the SSD recurrence with a scalar
  *            (times identity) state matrix per head: h_t = exp(dt_t A) h_{t-1} + dt_t x_t B_t^T,
  *            y_t = h_t C_t + D x_t.
  *   GDN:     Yang, Kautz & Hatamizadeh, "Gated Delta Networks" (ICLR 2025), the gated delta rule:
  *            S_t = S_{t-1} alpha_t (I - beta_t k_t k_t^T) + beta_t v_t k_t^T, o_t = S_t q_t.
+ *   KDA:     Kimi Delta Attention (Kimi Linear, Moonshot AI 2025), the gated delta rule with a
+ *            per-key-channel decay: S_t = S_{t-1} D_t (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,
+ *            D_t = diag(exp(g_t)), o_t = S_t q_t.
  *
  * Everything is fp64, one (sequence, head) at a time, in the order the definitions state. The
  * *_batch wrappers only loop over independent heads (OpenMP across heads, nothing inside a head).
@@ -23,6 +26,7 @@
  * Layouts (row-major, last index fastest):
  *   Mamba-2 state h [P][N]; inputs x [T][P], B [T][N], C [T][N], dt [T]; output y [T][P].
  *   GDN state S [dv][dk]; inputs q,k [T][dk], v [T][dv], beta [T], g [T] (log-decay); out o [T][dv].
+ *   KDA as GDN with g [T][dk] (one log-decay per key channel).
  * snap_after: ascending token counts t (1-based) after which the state is copied into snaps.
  */
 #include <math.h>
@@ -271,6 +275,124 @@ void orc_gdn_spec_rounds_batch(int nh, int dv, int dk, int R, int S, double scal
     for (int i = 0; i < nh; ++i) {
         orc_gdn_spec_rounds(dv, dk, R, S, scale, S0 ? S0 + i * sz : NULL, q + i * tok * dk,
                             k + i * tok * dk, v + i * tok * dv, beta + i * tok, g + i * tok,
+                            accept + (size_t)i * R, o + i * tok * dv, S_out ? S_out + i * sz : NULL,
+                            nsnap, snap_after + (size_t)i * nsnap,
+                            snaps ? snaps + (size_t)i * nsnap * sz : NULL);
+    }
+}
+
+/* ---------------------------------------------------------------------------------------------
+ * Kimi Delta Attention sequential recurrence (named as an SSM layer in [feed] and [news] para 7;
+ * the published KDA form, the gated delta rule with a per-key-channel decay). Per token, with
+ * alpha_t = exp(g_t) a dk-vector (D_t = diag(alpha_t)):
+ *   S_t = S_{t-1} D_t + beta_t (v_t - S_{t-1} D_t k_t) k_t^T,   o_t = scale S_t q_t.
+ * Row by row: the decayed row is row[n] * alpha[n]; its product with k gives the prediction.
+ * g is [T][dk] here (one decay per key channel).
+ * ------------------------------------------------------------------------------------------- */
+void orc_kda_sequential(int dv, int dk, int T, double scale, const double *S0, const double *q,
+                        const double *k, const double *v, const double *beta, const double *g,
+                        double *o, double *S_out, int nsnap, const int *snap_after,
+                        double *snaps) {
+    const size_t sz = (size_t)dv * dk;
+    double *S = (double *)malloc(sz * sizeof(double));
+    double *alpha = (double *)malloc((size_t)dk * sizeof(double));
+    if (S0) memcpy(S, S0, sz * sizeof(double));
+    else memset(S, 0, sz * sizeof(double));
+    int si = 0;
+    for (int t = 0; t < T; ++t) {
+        const double *qt = q + (size_t)t * dk, *kt = k + (size_t)t * dk, *vt = v + (size_t)t * dv;
+        for (int n = 0; n < dk; ++n) alpha[n] = exp(g[(size_t)t * dk + n]);
+        for (int p = 0; p < dv; ++p) {
+            double *row = S + (size_t)p * dk;
+            for (int n = 0; n < dk; ++n) row[n] *= alpha[n]; /* S_{t-1} D_t */
+            const double u = beta[t] * (vt[p] - dotd(row, kt, dk));
+            for (int n = 0; n < dk; ++n) row[n] += u * kt[n];
+            if (o) o[(size_t)t * dv + p] = scale * dotd(row, qt, dk);
+        }
+        while (snaps && si < nsnap && snap_after[si] == t + 1) {
+            memcpy(snaps + (size_t)si * sz, S, sz * sizeof(double));
+            ++si;
+        }
+    }
+    if (S_out) memcpy(S_out, S, sz * sizeof(double));
+    free(alpha);
+    free(S);
+}
+
+void orc_kda_sequential_batch(int nh, int dv, int dk, int T, double scale, const double *S0,
+                              const double *q, const double *k, const double *v,
+                              const double *beta, const double *g, double *o, double *S_out,
+                              int nsnap, const int *snap_after, double *snaps) {
+    const size_t sz = (size_t)dv * dk;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int i = 0; i < nh; ++i) {
+        orc_kda_sequential(dv, dk, T, scale, S0 ? S0 + i * sz : NULL, q + (size_t)i * T * dk,
+                           k + (size_t)i * T * dk, v + (size_t)i * T * dv, beta + (size_t)i * T,
+                           g + (size_t)i * T * dk, o ? o + (size_t)i * T * dv : NULL,
+                           S_out ? S_out + i * sz : NULL, nsnap, snap_after,
+                           snaps ? snaps + (size_t)i * nsnap * sz : NULL);
+    }
+}
+
+/* KDA replay form of one output (the GDN walk with a per-channel decay): r <- q_k, acc <- 0;
+ * for i = k..1: c_i = beta_i (k_i . r), acc += c_i v_i, r <- alpha_i * (r - c_i k_i)
+ * (elementwise); o = scale (Sc r + acc). */
+void orc_kda_replay_output(int dv, int dk, int kk, double scale, const double *Sc,
+                           const double *qk, const double *k, const double *v,
+                           const double *beta, const double *g, double *o) {
+    double *r = (double *)malloc((size_t)dk * sizeof(double));
+    double *acc = (double *)calloc((size_t)dv, sizeof(double));
+    memcpy(r, qk, (size_t)dk * sizeof(double));
+    for (int i = kk - 1; i >= 0; --i) {
+        const double *ki = k + (size_t)i * dk;
+        const double c = beta[i] * dotd(ki, r, dk);
+        for (int p = 0; p < dv; ++p) acc[p] += c * v[(size_t)i * dv + p];
+        for (int n = 0; n < dk; ++n) r[n] = exp(g[(size_t)i * dk + n]) * (r[n] - c * ki[n]);
+    }
+    for (int p = 0; p < dv; ++p) o[p] = scale * (dotd(Sc + (size_t)p * dk, r, dk) + acc[p]);
+    free(acc);
+    free(r);
+}
+
+/* KDA speculative rounds: as orc_gdn_spec_rounds, with the per-channel recurrence. */
+void orc_kda_spec_rounds(int dv, int dk, int R, int S, double scale, const double *S0,
+                         const double *q, const double *k, const double *v, const double *beta,
+                         const double *g, const int *accept, double *o, double *S_out, int nsnap,
+                         const int *snap_after, double *snaps) {
+    const size_t sz = (size_t)dv * dk;
+    double *St = (double *)malloc(sz * sizeof(double));
+    if (S0) memcpy(St, S0, sz * sizeof(double));
+    else memset(St, 0, sz * sizeof(double));
+    int pos = 0, si = 0;
+    for (int r = 0; r < R; ++r) {
+        const size_t t0 = (size_t)r * S;
+        orc_kda_sequential(dv, dk, S, scale, St, q + t0 * dk, k + t0 * dk, v + t0 * dv,
+                           beta + t0, g + t0 * dk, o + t0 * dv, NULL, 0, NULL, NULL);
+        for (int j = 0; j < accept[r]; ++j) {
+            const size_t t = t0 + j;
+            orc_kda_sequential(dv, dk, 1, scale, St, q + t * dk, k + t * dk, v + t * dv,
+                               beta + t, g + t * dk, NULL, St, 0, NULL, NULL);
+            ++pos;
+            while (snaps && si < nsnap && snap_after[si] == pos) {
+                memcpy(snaps + (size_t)si * sz, St, sz * sizeof(double));
+                ++si;
+            }
+        }
+    }
+    if (S_out) memcpy(S_out, St, sz * sizeof(double));
+    free(St);
+}
+
+void orc_kda_spec_rounds_batch(int nh, int dv, int dk, int R, int S, double scale,
+                               const double *S0, const double *q, const double *k,
+                               const double *v, const double *beta, const double *g,
+                               const int *accept, double *o, double *S_out, int nsnap,
+                               const int *snap_after, double *snaps) {
+    const size_t sz = (size_t)dv * dk, tok = (size_t)R * S;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int i = 0; i < nh; ++i) {
+        orc_kda_spec_rounds(dv, dk, R, S, scale, S0 ? S0 + i * sz : NULL, q + i * tok * dk,
+                            k + i * tok * dk, v + i * tok * dv, beta + i * tok, g + i * tok * dk,
                             accept + (size_t)i * R, o + i * tok * dv, S_out ? S_out + i * sz : NULL,
                             nsnap, snap_after + (size_t)i * nsnap,
                             snaps ? snaps + (size_t)i * nsnap * sz : NULL);
