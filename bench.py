@@ -98,11 +98,12 @@ def m2_rc_replay_bytes_per_head(P, N, k, rc, esz=2):
     return m2_replay_bytes_per_head(P, N, k, esz) - P * N * 4 + copy
 
 
-def gdn_replay_bytes_per_head(dv, dk, k, esz=2):
+def gdn_replay_bytes_per_head(dv, dk, k, esz=2, gsz=4):
     """GDN replay for one head at count k: state read + k-1 older entries (k, v, beta, g) + this
-    token read and appended (q, k, v, beta, g) + o written + pointers."""
-    entry_rd = dk * esz + dv * esz + 8
-    token = 2 * dk * esz + dv * esz + 8
+    token read and appended (q, k, v, beta, g) + o written + pointers. gsz: bytes of g per entry
+    (4; Kimi Delta Attention: 4 dk)."""
+    entry_rd = dk * esz + dv * esz + 4 + gsz
+    token = 2 * dk * esz + dv * esz + 4 + gsz
     return dv * dk * 4 + (k - 1) * entry_rd + 2 * token + dv * 4 + 12
 
 
@@ -114,8 +115,8 @@ def gdn_verify_bytes_per_head(dv, dk, kc, S, esz=2):
     return dv * dk * 4 + kc * entry_rd + 2 * S * token + S * dv * 4 + 8
 
 
-def gdn_conv_bytes_per_head(dv, dk, esz=2):
-    return 2 * dv * dk * 4 + 2 * dk * esz + dv * esz + 8 + dv * 4
+def gdn_conv_bytes_per_head(dv, dk, esz=2, gsz=4):
+    return 2 * dv * dk * 4 + 2 * dk * esz + dv * esz + 4 + gsz + dv * 4
 
 
 def timed_calls(n, fn):
@@ -316,17 +317,19 @@ def gdn_rc_replay_bytes_per_head(dv, dk, k, rc, esz=2):
     return gdn_replay_bytes_per_head(dv, dk, k, esz) - dv * dk * 4 + copy
 
 
-def bench_gdn(dev, steps=128, warm=16, layers=2, pool=16, rc=0):
-    """Gated DeltaNet layer at B=256, H=32, dv=dk=128, L=16 on `layers` rotated layer instances:
-    replay path (reading the fp32 state, or its fp8 / fp4 copy) vs the conventional
-    read-modify-write step (fp32 state only)."""
+def bench_gdn(dev, steps=128, warm=16, layers=2, pool=16, rc=0, kda=False):
+    """Gated DeltaNet (or, kda=True, Kimi Delta Attention) layer at B=256, H=32, dv=dk=128,
+    L=16 on `layers` rotated layer instances: replay path (reading the fp32 state, or its fp8 /
+    fp4 copy) vs the conventional read-modify-write step (fp32 state only)."""
     import torch
     from ssm_decode_state_amd import binding as bd
     from ssm_decode_state_amd import synth
-    w = synth.WORKLOADS["gdn_b256"]
+    w = synth.WORKLOADS["kda_b256" if kda else "gdn_b256"]
     shape = w["shape"]
     Bn, H, dv, dk, L = shape.batch, shape.heads, shape.dim_p, shape.dim_n, shape.window
-    cfg = bd.make_config(bd.SSM_GDN, Bn, H, H, dv, dk, L, 1, bd.SSM_IN_BF16, rc)
+    gsz = 4 * dk if kda else 4
+    cfg = bd.make_config(bd.SSM_KDA if kda else bd.SSM_GDN, Bn, H, H, dv, dk, L, 1,
+                         bd.SSM_IN_BF16, rc)
     sts, convs = [], []
     for layer in range(layers):
         s0 = synth.initial_state_device(shape, w["seed"], w["h0_std"], layer)
@@ -351,7 +354,7 @@ def bench_gdn(dev, steps=128, warm=16, layers=2, pool=16, rc=0):
         if k == L:
             fold.append(m)
             continue
-        rep_b += heads * (gdn_replay_bytes_per_head(dv, dk, k) if rc == 0 else
+        rep_b += heads * (gdn_replay_bytes_per_head(dv, dk, k, gsz=gsz) if rc == 0 else
                           gdn_rc_replay_bytes_per_head(dv, dk, k, rc))
         rep_ms += m
     gbs = rep_b / (rep_ms * 1e-3) / 1e9
@@ -365,8 +368,9 @@ def bench_gdn(dev, steps=128, warm=16, layers=2, pool=16, rc=0):
         bd.ssm_conventional_step(cfg, convs[i % layers], inputs[i % pool], None, None, o)
     cwall, cms = timed_calls(n, lambda i: bd.ssm_conventional_step(
         cfg, convs[i % layers], inputs[(n_warm + i) % pool], None, None, o))
-    cgbs = heads * gdn_conv_bytes_per_head(dv, dk) / (sum(cms) / n * 1e-3) / 1e9
-    return {"workload": "gdn_replay_decode_b256", "tokens_per_s": Bn * n / wall,
+    cgbs = heads * gdn_conv_bytes_per_head(dv, dk, gsz=gsz) / (sum(cms) / n * 1e-3) / 1e9
+    return {"workload": "kda_replay_decode_b256" if kda else "gdn_replay_decode_b256",
+            "tokens_per_s": Bn * n / wall,
             "unit": "tokens/s/layer", "layers_rotated": layers, "ms_per_step": wall / n * 1e3,
             "replay_avg_us": rep_ms / (n - len(fold)) * 1e3, "replay_achieved_gbs": gbs,
             "replay_frac": gbs / HBM_PEAK_GBS,
@@ -523,8 +527,8 @@ def main():
                     help="also run a plain copy of this many MiB (reference for HBM counters)")
     ap.add_argument("--workloads", default="all",
                     help="comma list of extra workloads: spec, fp8, fp4, gdn, gdn_spec, "
-                         "gdn_fp8, gdn_fp4, g8 (8 B/C groups), lsweep (window 4..32); 'all' or "
-                         "'none'")
+                         "gdn_fp8, gdn_fp4, kda, g8 (8 B/C groups), lsweep (window 4..32); 'all' "
+                         "or 'none'")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -655,7 +659,7 @@ def main():
         out["copy_ref"] = {"bytes_read": 4 * n, "bytes_written": 4 * n, "launches": 5,
                            "avg_us": e0.elapsed_time(e1) / 5 * 1e3}
 
-    extra = ({"spec", "fp8", "fp4", "gdn", "gdn_spec", "gdn_fp8", "gdn_fp4", "g8", "lsweep"}
+    extra = ({"spec", "fp8", "fp4", "gdn", "gdn_spec", "gdn_fp8", "gdn_fp4", "kda", "g8", "lsweep"}
              if args.workloads == "all" else
              set() if args.workloads == "none" else set(args.workloads.split(",")))
     if extra:
@@ -684,6 +688,9 @@ def main():
             torch.cuda.empty_cache()
         if "gdn" in extra:
             out["workloads"]["gdn"] = bench_gdn(dev)
+            torch.cuda.empty_cache()
+        if "kda" in extra:
+            out["workloads"]["kda"] = bench_gdn(dev, kda=True)
             torch.cuda.empty_cache()
         if "gdn_fp8" in extra:
             out["workloads"]["gdn_readcopy_fp8"] = bench_gdn(dev, layers=4, rc=1)

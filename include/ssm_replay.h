@@ -18,12 +18,15 @@
  *     h_t = exp(dt_t A) h_{t-1} + dt_t x_t B_t^T,      y_t = h_t C_t + D x_t
  *   Gated DeltaNet (per head, state S in R^{dv x dk}, alpha_t = exp(g_t)):
  *     S_t = alpha_t S_{t-1} + beta_t (v_t - alpha_t S_{t-1} k_t) k_t^T,   o_t = scale S_t q_t
+ *   Kimi Delta Attention (named beside them in the feed excerpt and news para 7): the same with
+ *   one decay per key channel, D_t = diag(exp(g_t)), g_t in R^{dk}:
+ *     S_t = S_{t-1} D_t + beta_t (v_t - S_{t-1} D_t k_t) k_t^T,           o_t = scale S_t q_t
  * Replay computes exactly these outputs (up to fp32 rounding) from the checkpoint h_c at token
  * position c and the buffered entries c+1..c+k:
  *   Mamba-2: y_k = e^{s_0} h_c C_k + sum_{i<=k} e^{s_i} dt_i (B_i . C_k) x_i + D x_k,
  *            s_i = A * sum_{m=i+1..k} dt_m
  *   GDN:     backward sweep r <- q_k; for i = k..1: c_i = beta_i (k_i . r), acc += c_i v_i,
- *            r <- alpha_i (r - c_i k_i); o = scale (S_c r + acc)
+ *            r <- alpha_i (r - c_i k_i); o = scale (S_c r + acc)   (KDA: alpha_i elementwise)
  *
  * Conventions shared by every entry point
  * - All device pointers are plain device addresses (hipMalloc / torch CUDA tensors) and must be
@@ -42,11 +45,13 @@
  *              dt [batch][ntok][H] fp32 (already positive: the caller applies softplus/bias)
  *     GDN:     q, k [batch][ntok][H][dk], v [batch][ntok][H][dv] in the input dtype,
  *              beta [batch][ntok][H], g [batch][ntok][H] fp32 (g is the log of the decay)
+ *     KDA:     as GDN (ssm_gdn_in) with g [batch][ntok][H][dk] fp32, one log-decay per channel
  *   Outputs y are fp32 [batch][ntok][H][P] (GDN: [batch][ntok][H][dv]).
  * - Supported shapes: Mamba-2 P in {16, 32, 64} and N in {16, 32, 64, 128} with N >= 4 * 64 / P
  *   (P = 64 takes every N); GDN dv and dk in {64, 128}; window L in [1, 32]; max_draft in
- *   [1, min(L, 8)], and for GDN L + max_draft - 1 <= 32 (SSM_E_UNSUPPORTED otherwise). The
- *   read copies need N (dk) in {64, 128}, and P = 64 for Mamba-2.
+ *   [1, min(L, 8)], and for GDN / KDA L + max_draft - 1 <= 32 (SSM_E_UNSUPPORTED otherwise).
+ *   KDA takes the GDN shapes. The read copies need N (dk) in {64, 128}, and P = 64 for Mamba-2;
+ *   KDA has none (SSM_E_UNSUPPORTED).
  */
 #ifndef SSM_REPLAY_H
 #define SSM_REPLAY_H
@@ -72,7 +77,7 @@ enum {
     SSM_E_HIP = -7          /* a HIP launch failed */
 };
 
-enum { SSM_MAMBA2 = 0, SSM_GDN = 1 };
+enum { SSM_MAMBA2 = 0, SSM_GDN = 1, SSM_KDA = 2 };
 enum { SSM_IN_F32 = 0, SSM_IN_BF16 = 1 };
 enum { SSM_RC_NONE = 0, SSM_RC_FP8_ROW = 1, SSM_RC_FP4_B16 = 2 };
 enum { SSM_FLUSH_IF_FULL = 0, SSM_FLUSH_ALL = 1 };
@@ -81,17 +86,17 @@ enum { SSM_FLAG_ACCEPT_CLAMPED = 1 /* an n_accept value outside [0, pending] was
 
 /* Layer shape and options. */
 typedef struct ssm_config {
-    int32_t kind;      /* SSM_MAMBA2 or SSM_GDN */
+    int32_t kind;      /* SSM_MAMBA2, SSM_GDN or SSM_KDA */
     int32_t batch;     /* sequences B (0 allowed: every call is then a no-op) */
     int32_t heads;     /* H */
-    int32_t groups;    /* Mamba-2: B/C groups G, H % G == 0 (head h uses group h / (H/G)); GDN: H */
+    int32_t groups;    /* Mamba-2: B/C groups G, H % G == 0 (head h uses group h / (H/G)); GDN/KDA: H */
     int32_t dim_p;     /* Mamba-2 head dim P; GDN value dim dv (rows of a state tile) */
     int32_t dim_n;     /* Mamba-2 state dim N; GDN key dim dk (columns of a state tile) */
     int32_t window;    /* L: the buffer is folded into the checkpoint when L entries are committed */
     int32_t max_draft; /* most drafts per ssm_spec_append (1 = no speculation) */
     int32_t in_dtype;  /* SSM_IN_F32 or SSM_IN_BF16 for x/B/C (q/k/v); dt/beta/g are always fp32 */
     int32_t readcopy;  /* SSM_RC_*: low-precision copy read by the output path */
-    float gdn_scale;   /* GDN output scale (1.0 = none); ignored for Mamba-2 */
+    float gdn_scale;   /* GDN / KDA output scale (1.0 = none); ignored for Mamba-2 */
 } ssm_config;
 
 /* Byte offsets of the regions inside one state's device memory (each 256-byte aligned).
@@ -103,7 +108,8 @@ typedef struct ssm_config {
  * low nibble = even n) at byte (b*H + h)*P*N/2 + ((n/32)*P + p)*16 + (n%32)/2, block-scale E4M3
  * codes [b][h][P][N/16], tile scale fp32 [b][h].
  * Rings (slot s of cap): Mamba-2 x [b][h][s][P], B and C [b][g][s][N] (input dtype),
- * dt [b][h][s] fp32; GDN q, k [b][h][s][dk], v [b][h][s][dv] (input dtype), beta, g [b][h][s].
+ * dt [b][h][s] fp32; GDN q, k [b][h][s][dk], v [b][h][s][dv] (input dtype), beta, g [b][h][s];
+ * KDA as GDN with g [b][h][s][dk].
  * Pointers: int32 [b][h][2] = {start slot, committed count}. Flags: one int32 word of SSM_FLAG_*
  * bits set by device-side checks. */
 typedef struct ssm_layout {
@@ -140,7 +146,7 @@ typedef struct ssm_m2_in {
     const float *dt;
 } ssm_m2_in;
 
-/* Gated DeltaNet token inputs (device pointers, layouts above). */
+/* Gated DeltaNet and Kimi Delta Attention token inputs (device pointers, layouts above). */
 typedef struct ssm_gdn_in {
     const void *q;
     const void *k;

@@ -17,7 +17,7 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libssm_rep
 
 SSM_OK, SSM_E_ARG, SSM_E_SHAPE, SSM_E_ALIGN, SSM_E_STATE, SSM_E_CAPACITY, SSM_E_UNSUPPORTED, \
     SSM_E_HIP = 0, -1, -2, -3, -4, -5, -6, -7
-SSM_MAMBA2, SSM_GDN = 0, 1
+SSM_MAMBA2, SSM_GDN, SSM_KDA = 0, 1, 2
 SSM_IN_F32, SSM_IN_BF16 = 0, 1
 SSM_RC_NONE, SSM_RC_FP8_ROW, SSM_RC_FP4_B16 = 0, 1, 2
 SSM_FLUSH_IF_FULL, SSM_FLUSH_ALL = 0, 1

@@ -1,11 +1,14 @@
-// gdn_conv.hip -- instantiations of the conventional (state-writing) GDN decode step.
+// gdn_conv.hip -- instantiations of the conventional (state-writing) GDN / KDA decode step.
 #include "gdn_kernels.hpp"
 
 namespace ssm {
 
 template <int DV, int DK, typename TIN>
 static hipError_t launch_conv_dd(const GdnConvArgs& a, hipStream_t s) {
-    hipLaunchKernelGGL((gdn_conv_kernel<DV, DK, TIN>), dim3(a.heads, a.batch), dim3(DV), 0, s, a);
+    if (a.kda)
+        hipLaunchKernelGGL((gdn_conv_kernel<DV, DK, TIN, true>), dim3(a.heads, a.batch), dim3(DV), 0, s, a);
+    else
+        hipLaunchKernelGGL((gdn_conv_kernel<DV, DK, TIN, false>), dim3(a.heads, a.batch), dim3(DV), 0, s, a);
     return hipGetLastError();
 }
 

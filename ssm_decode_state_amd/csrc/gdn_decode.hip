@@ -1,17 +1,25 @@
-// gdn_decode.hip -- instantiations of the one-token GDN replay decode (the entries a call sees
-// bounded by 16 or 32) and the entry of every GDN replay launch.
+// gdn_decode.hip -- instantiations of the one-token GDN / KDA replay decode (the entries a call
+// sees bounded by 16 or 32) and the entry of every GDN / KDA replay launch.
 #include "gdn_kernels.hpp"
 
 namespace ssm {
 
-template <int DV, int DK, typename TIN, int RC>
-static hipError_t launch_decode_dd(const GdnArgs& a, int maxe, hipStream_t s) {
+template <int DV, int DK, typename TIN, int RC, bool VG>
+static hipError_t launch_decode_vg(const GdnArgs& a, int maxe, hipStream_t s) {
     const dim3 grid(a.heads, a.batch), block(DV);
     if (maxe <= 16)
-        hipLaunchKernelGGL((gdn_replay_kernel<DV, DK, TIN, RC, 16, 1, true>), grid, block, 0, s, a);
+        hipLaunchKernelGGL((gdn_replay_kernel<DV, DK, TIN, RC, 16, 1, true, VG>), grid, block, 0, s, a);
     else
-        hipLaunchKernelGGL((gdn_replay_kernel<DV, DK, TIN, RC, 32, 1, true>), grid, block, 0, s, a);
+        hipLaunchKernelGGL((gdn_replay_kernel<DV, DK, TIN, RC, 32, 1, true, VG>), grid, block, 0, s, a);
     return hipGetLastError();
+}
+template <int DV, int DK, typename TIN, int RC>
+static hipError_t launch_decode_dd(const GdnArgs& a, int maxe, hipStream_t s) {
+    if (a.kda) {  // per-channel gate: no read copy
+        if constexpr (RC == 0) return launch_decode_vg<DV, DK, TIN, 0, true>(a, maxe, s);
+        else return hipErrorNotSupported;
+    }
+    return launch_decode_vg<DV, DK, TIN, RC, false>(a, maxe, s);
 }
 
 template <typename TIN, int RC>

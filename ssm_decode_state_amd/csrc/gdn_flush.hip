@@ -1,22 +1,30 @@
-// gdn_flush.hip -- instantiations of the GDN UT/WY flush: plain, fused with the window's closing
+// gdn_flush.hip -- instantiations of the GDN / KDA UT/WY flush: plain, fused with the window's closing
 // decode step, and the read-copy rewrite (init).
 #include "gdn_kernels.hpp"
 
 namespace ssm {
 
-template <int DV, int DK, typename TIN, int RC>
-static hipError_t launch_flush_dd(const GdnArgs& a, int mode_all, int rewrite_only, hipStream_t s) {
+template <int DV, int DK, typename TIN, int RC, bool VG>
+static hipError_t launch_flush_vg(const GdnArgs& a, int mode_all, int rewrite_only, hipStream_t s) {
     const dim3 grid(a.heads, a.batch), block(DV);
     if (mode_all == 2) {  // fused decode + fold of the L-th lock-step token
         // not with a read copy: there the closing step's replay reads only the copy, and the
         // fused kernel with the copy rewrite does not fit the register budget
         if constexpr (RC != 0) return hipErrorNotSupported;
-        else hipLaunchKernelGGL((gdn_flush_kernel<DV, DK, TIN, RC, true>), grid, block, 0, s, a, 0, 0);
+        else hipLaunchKernelGGL((gdn_flush_kernel<DV, DK, TIN, RC, true, VG>), grid, block, 0, s, a, 0, 0);
     } else {
-        hipLaunchKernelGGL((gdn_flush_kernel<DV, DK, TIN, RC, false>), grid, block, 0, s, a,
+        hipLaunchKernelGGL((gdn_flush_kernel<DV, DK, TIN, RC, false, VG>), grid, block, 0, s, a,
                            mode_all, rewrite_only);
     }
     return hipGetLastError();
+}
+template <int DV, int DK, typename TIN, int RC>
+static hipError_t launch_flush_dd(const GdnArgs& a, int mode_all, int rewrite_only, hipStream_t s) {
+    if (a.kda) {  // per-channel gate: no read copy
+        if constexpr (RC == 0) return launch_flush_vg<DV, DK, TIN, 0, true>(a, mode_all, rewrite_only, s);
+        else return hipErrorNotSupported;
+    }
+    return launch_flush_vg<DV, DK, TIN, RC, false>(a, mode_all, rewrite_only, s);
 }
 
 template <typename TIN, int RC>

@@ -51,8 +51,10 @@ constexpr int kGdnMaxWin = 32;  // most entries a replay call can see
 // the committed entries and tokens 0..j. All queries share one read of the checkpoint rows.
 // COMMIT (decode): count += ntok at the end; otherwise the tokens stay pending drafts.
 // MAXW bounds the entries a call sees (count + ntok <= MAXW), MAXQ the tokens per call.
+// VG (Kimi Delta Attention): alpha_i is a dk-vector (one decay per key channel), so the sweep's
+// decay is elementwise: r <- alpha_i * (r - c_i k_i); g rings and inputs hold dk values per entry.
 // ---------------------------------------------------------------------------------------------
-template <int DV, int DK, typename TIN, int RC, int MAXW, int MAXQ, bool COMMIT>
+template <int DV, int DK, typename TIN, int RC, int MAXW, int MAXQ, bool COMMIT, bool VG = false>
 __global__ __launch_bounds__(64 * (DV >= 64 ? DV / 64 : 1))
 __attribute__((amdgpu_waves_per_eu(2))) void gdn_replay_kernel(GdnArgs a) {
     static_assert(DV >= 64 && DK >= 64, "replay tile: dv, dk >= 64");
@@ -69,6 +71,7 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_replay_kernel(GdnArgs a) {
     __shared__ __attribute__((aligned(16))) u32x4_t s_v[kW][MAXW * kVC];
     __shared__ __attribute__((aligned(16))) float s_c[kW][MAXW][MAXQ];
     __shared__ __attribute__((aligned(16))) TIN s_k[kW][MAXW][DK];  // keys, as loaded
+    __shared__ __attribute__((aligned(16))) float s_al[kW][VG ? MAXW : 1][VG ? DK : 4];  // VG: alpha
 
     const int wave = uniform(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
@@ -95,11 +98,13 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_replay_kernel(GdnArgs a) {
         const bool ring = lane < count;
         const int s = ring_slot(start, min(lane, cap - 1), cap);
         const float* pb = ring ? a.ring_beta + (long)head * cap + s : a.in_beta + tok(lane - count);
-        const float* pg = ring ? a.ring_g + (long)head * cap + s : a.in_g + tok(lane - count);
         be = *pb;
-        ge = *pg;
         be = lane < kmax ? be : 0.f;
-        ge = lane < kmax ? ge : 0.f;
+        if constexpr (!VG) {
+            const float* pg = ring ? a.ring_g + (long)head * cap + s : a.in_g + tok(lane - count);
+            ge = *pg;
+            ge = lane < kmax ? ge : 0.f;
+        }
     }
     TIN kraw[MAXW][kE];  // keys of the entries (entries >= count are this call's tokens)
 #pragma unroll
@@ -108,6 +113,19 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_replay_kernel(GdnArgs a) {
                                    : ink + tok(e - count) * DK;
         load_raw<TIN, kE>(src + el * kE, kraw[e]);
     }
+    float graw[VG ? MAXW : 1][kE];  // VG: the lane's log-decays of every entry
+    // (issued before the state stream for up to 16 entries; after it for more, where holding
+    // them across the stream would exceed the register budget)
+    constexpr bool kLateG = VG && MAXW > 16;
+    auto load_g = [&]() {
+#pragma unroll
+        for (int e = 0; e < MAXW; ++e) {
+            const float* src = e < count ? a.ring_g + ((long)head * cap + ring_slot(start, min(e, cap - 1), cap)) * DK
+                                         : a.in_g + tok(e - count) * DK;
+            load_raw<float, kE>(src + el * kE, graw[e]);
+        }
+    };
+    if constexpr (VG && !kLateG) load_g();
     TIN qraw[MAXQ][kE];
 #pragma unroll
     for (int j = 0; j < MAXQ; ++j) load_raw<TIN, kE>(inq + tok(j) * DK + el * kE, qraw[j]);
@@ -136,6 +154,33 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_replay_kernel(GdnArgs a) {
     for (int e = 0; e < MAXW; ++e)
 #pragma unroll
         for (int i = 0; i < kE; ++i) s_k[wave][e][el * kE + i] = kraw[e][i];
+    if constexpr (VG && !kLateG) {
+#pragma unroll
+        for (int e = 0; e < MAXW; ++e)
+#pragma unroll
+            for (int i = 0; i < kE; ++i) s_al[wave][e][el * kE + i] = expf(graw[e][i]);
+    } else if constexpr (VG) {  // eight entries at a time: few registers live beside the rows
+#pragma unroll
+        for (int e0 = 0; e0 < MAXW; e0 += 8) {
+            float gb[8][kE];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int ee = e0 + e;
+                const float* src = ee < count ? a.ring_g + ((long)head * cap + ring_slot(start, min(ee, cap - 1), cap)) * DK
+                                              : a.in_g + tok(ee - count) * DK;
+                load_raw<float, kE>(src + el * kE, gb[e]);
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int ee = e0 + e;
+#pragma unroll
+                for (int i = 0; i < kE; ++i) s_al[wave][ee][el * kE + i] = expf(gb[e][i]);
+                if (wave == 0 && ee >= count && ee < kmax)  // this call's tokens: append g
+                    store_raw<float, kE>(a.ring_g + ((long)head * cap + ring_slot(start, ee, cap)) * DK +
+                                             el * kE, gb[e]);
+            }
+        }
+    }
 #pragma unroll
     for (int i = 0; i < kVL; ++i) {
         const int idx = lane + 64 * i;
@@ -169,7 +214,15 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_replay_kernel(GdnArgs a) {
             if (lane >= count && lane < kmax) {
                 const long rs = rb + ring_slot(start, lane, cap);
                 a.ring_beta[rs] = be;
-                a.ring_g[rs] = ge;
+                if constexpr (!VG) a.ring_g[rs] = ge;
+            }
+            if constexpr (VG && !kLateG) {
+#pragma unroll
+                for (int e = 0; e < MAXW; ++e) {
+                    if (e >= count && e < kmax)
+                        store_raw<float, kE>(a.ring_g + (rb + ring_slot(start, e, cap)) * DK + el * kE,
+                                             graw[e]);
+                }
             }
         }
     }
@@ -186,7 +239,15 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_replay_kernel(GdnArgs a) {
 #pragma unroll
         for (int i = 0; i < kE; ++i) kv[i] = to_f32<TIN>(s_k[wave][e][el * kE + i]);
         const float bt = readlane(be, e);
-        const float al = expf(readlane(ge, e));
+        float al[kE];  // the decay of the lane's key elements
+        if constexpr (VG) {
+#pragma unroll
+            for (int i = 0; i < kE; ++i) al[i] = s_al[wave][e][el * kE + i];
+        } else {
+            const float as = expf(readlane(ge, e));
+#pragma unroll
+            for (int i = 0; i < kE; ++i) al[i] = as;
+        }
 #pragma unroll
         for (int j = 0; j < MAXQ; ++j) {
             if (j >= nq) break;
@@ -196,7 +257,7 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_replay_kernel(GdnArgs a) {
             for (int i = 0; i < kE; ++i) d += kv[i] * r[j][i];
             const float c = bt * wave_sum(d);
 #pragma unroll
-            for (int i = 0; i < kE; ++i) r[j][i] = al * (r[j][i] - c * kv[i]);
+            for (int i = 0; i < kE; ++i) r[j][i] = al[i] * (r[j][i] - c * kv[i]);
             if (lane == 0) s_c[wave][e][j] = c;
         }
     }
@@ -271,15 +332,16 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_replay_kernel(GdnArgs a) {
 // ---------------------------------------------------------------------------------------------
 // Conventional step (comparison point; the full state rewritten every token):
 //   S <- alpha S + beta (v - alpha S k) k^T (in place),  o = scale S q.
+// VG (Kimi Delta Attention): alpha is a dk-vector and scales the state's columns.
 // ---------------------------------------------------------------------------------------------
-template <int DV, int DK, typename TIN>
+template <int DV, int DK, typename TIN, bool VG = false>
 __global__ __launch_bounds__(64 * (DV >= 64 ? DV / 64 : 1))
 __attribute__((amdgpu_waves_per_eu(2))) void gdn_conv_kernel(GdnConvArgs a) {
     constexpr int kW = DV >= 64 ? DV / 64 : 1;
     constexpr int kRows = DV >= 64 ? 64 : DV;
     constexpr int kNQ = DK / 4;
     constexpr int kCE = DK >= 64 ? DK / 64 : 1;
-    __shared__ __attribute__((aligned(16))) float s_kq[kW][2][DK];
+    __shared__ __attribute__((aligned(16))) float s_kq[kW][VG ? 3 : 2][DK];  // k, q (, alpha)
     const int wave = uniform(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int h = blockIdx.x, b = blockIdx.y;
@@ -288,15 +350,17 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_conv_kernel(GdnConvArgs a) {
     const TIN* ink = static_cast<const TIN*>(a.in_k) + head * DK;
     const TIN* inq = static_cast<const TIN*>(a.in_q) + head * DK;
     TIN kraw[kCE], qraw[kCE];
+    float graw[kCE];
 #pragma unroll
     for (int i = 0; i < kCE; ++i) {
         const int n = (lane + 64 * i) % DK;
         kraw[i] = ink[n];
         qraw[i] = inq[n];
+        if constexpr (VG) graw[i] = a.in_g[head * DK + n];
     }
     const float v = to_f32<TIN>(static_cast<const TIN*>(a.in_v)[head * DV + row]);
     const float beta = a.in_beta[head];
-    const float alpha = expf(a.in_g[head]);
+    const float alpha = VG ? 1.f : expf(a.in_g[head]);
     float4 hv[kNQ];
     // float4 q * DV + row of the head's tile
     const TileIO tio{reinterpret_cast<char*>(a.S) + (long)head * (DV * DK * 4), (uint32_t)(row * 16)};
@@ -309,12 +373,17 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_conv_kernel(GdnConvArgs a) {
         const int n = (lane + 64 * i) % DK;
         s_kq[wave][0][n] = to_f32<TIN>(kraw[i]);
         s_kq[wave][1][n] = to_f32<TIN>(qraw[i]);
+        if constexpr (VG) s_kq[wave][2][n] = expf(graw[i]);
     }
     wave_sync();
-    float sk = 0.f;
+    float sk = 0.f;  // (S k) for a scalar decay; (S diag(alpha) k) with VG
 #pragma unroll
     for (int q = 0; q < kNQ; ++q) {
-        const float4 k4 = *reinterpret_cast<const float4*>(&s_kq[wave][0][4 * q]);
+        float4 k4 = *reinterpret_cast<const float4*>(&s_kq[wave][0][4 * q]);
+        if constexpr (VG) {
+            const float4 a4 = *reinterpret_cast<const float4*>(&s_kq[wave][2][4 * q]);
+            k4 = make_float4(k4.x * a4.x, k4.y * a4.y, k4.z * a4.z, k4.w * a4.w);
+        }
         sk += hv[q].x * k4.x + hv[q].y * k4.y + hv[q].z * k4.z + hv[q].w * k4.w;
     }
     const float u = beta * (v - alpha * sk);
@@ -324,10 +393,12 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_conv_kernel(GdnConvArgs a) {
     for (int q = 0; q < kNQ; ++q) {
         const float4 k4 = *reinterpret_cast<const float4*>(&s_kq[wave][0][4 * q]);
         const float4 q4 = *reinterpret_cast<const float4*>(&s_kq[wave][1][4 * q]);
-        hv[q].x = alpha * hv[q].x + u * k4.x;
-        hv[q].y = alpha * hv[q].y + u * k4.y;
-        hv[q].z = alpha * hv[q].z + u * k4.z;
-        hv[q].w = alpha * hv[q].w + u * k4.w;
+        float4 a4 = make_float4(alpha, alpha, alpha, alpha);
+        if constexpr (VG) a4 = *reinterpret_cast<const float4*>(&s_kq[wave][2][4 * q]);
+        hv[q].x = a4.x * hv[q].x + u * k4.x;
+        hv[q].y = a4.y * hv[q].y + u * k4.y;
+        hv[q].z = a4.z * hv[q].z + u * k4.z;
+        hv[q].w = a4.w * hv[q].w + u * k4.w;
         o += hv[q].x * q4.x + hv[q].y * q4.y + hv[q].z * q4.z + hv[q].w * q4.w;
         tio.store((uint32_t)(q * DV * 16), hv[q]);
     }
@@ -349,8 +420,14 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_conv_kernel(GdnConvArgs a) {
 // the L-1 buffered entries straight from the caller's inputs, and its output is taken from the
 // new state, o = scale S_L q_L (the recurrence's own form); the ring is left empty.
 // Requires DV % 64 == 0 (one wave per 64 rows) and DK % 64 == 0.
+// VG (Kimi Delta Attention): the decay is a dk-vector per entry. With G_t[n] the within-chunk
+// cumulative log-decay of key channel n, the same UT/WY steps hold with
+//   Lm[t][i] = beta_t sum_n k_t[n] k_i[n] exp(G_t[n] - G_i[n])   (a gated Gram matrix, on MFMA
+//     as (K * exp(G - G_ref)) (K * exp(G_ref - G))^T around the mid-chunk reference G_ref),
+//   W_t = beta_t (exp(G_t) * k_t) - sum_{i<t} Lm[t][i] W_i,
+//   S <- S diag(exp(G_L)) + sum_t Delta_t (k_t * exp(G_L - G_t))^T.
 // ---------------------------------------------------------------------------------------------
-template <int DV, int DK, typename TIN, int RC, bool FUSED>
+template <int DV, int DK, typename TIN, int RC, bool FUSED, bool VG = false>
 __global__ __launch_bounds__(DV)
 __attribute__((amdgpu_waves_per_eu(2))) void gdn_flush_kernel(GdnArgs a, int mode_all,
                                                               int rewrite_only) {
@@ -363,13 +440,15 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_flush_kernel(GdnArgs a, int mod
     constexpr int kEPC = 16 / (int)sizeof(TIN);
     constexpr int kKC = DK / kEPC, kVC = 64 / kEPC;   // 16-byte chunks per k row / per v slice
     constexpr int kKL = (16 * kKC + 63) / 64, kVL = (16 * kVC + 63) / 64;
-    __shared__ __attribute__((aligned(16))) float s_k[kW][16][kKP];     // K chunk (fp32)
-    __shared__ __attribute__((aligned(16))) float s_w[kW][16][kKP];     // -W
+    constexpr int kGC = DK / 4, kGL = (16 * kGC + 63) / 64;  // VG: 16-byte chunks of g rows
+    __shared__ __attribute__((aligned(16))) float s_k[kW][16][kKP];     // K chunk (fp32); VG: then K~
+    __shared__ __attribute__((aligned(16))) float s_w[kW][16][kKP];     // VG: G first; then -W
     __shared__ __attribute__((aligned(16))) float s_v[kW][16][kVP];     // this wave's v slice, then U ([t][p]), then Delta'^T
     __shared__ __attribute__((aligned(16))) float s_l[kW][16][17];      // Lm
     __shared__ __attribute__((aligned(16))) float s_d[kW][64][17];      // Delta' as [p][t] (transpose buffer)
     __shared__ __attribute__((aligned(16))) float s_q[kW][FUSED ? DK : 4];  // FUSED: the token's q
     __shared__ float s_amax[kW];  // fp4 read copy: the waves' largest magnitudes
+    __shared__ __attribute__((aligned(16))) float s_gl[kW][VG ? DK : 4];  // VG: exp(G_L) per column
 
     const int wave = uniform(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
@@ -397,8 +476,12 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_flush_kernel(GdnArgs a, int mod
         if (FUSED && e >= nring) return static_cast<const TIN*>(a.in_v) + (long)head * DV;
         return rv + ((long)head * cap + ring_slot(start, e, cap)) * DV;
     };
+    auto grow = [&](int e) -> const float* {  // VG: the entry's dk log-decays
+        if (FUSED && e >= nring) return a.in_g + (long)head * DK;
+        return a.ring_g + ((long)head * cap + ring_slot(start, e, cap)) * DK;
+    };
     // chunk loader (branch-free: entries past nfold read the last folded entry, zeroed later)
-    u32x4_t kraw[kKL], vraw[kVL];
+    u32x4_t kraw[kKL], vraw[kVL], graw[VG ? 4 : 1];
     float be = 0.f, ge = 0.f;
     auto fetch = [&](int c0) {
 #pragma unroll
@@ -417,9 +500,11 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_flush_kernel(GdnArgs a, int mod
         const long s = (long)head * cap + ring_slot(start, min(e, cap - 1), cap);
         const bool tok = FUSED && e >= nring;
         be = tok ? a.in_beta[head] : a.ring_beta[s];
-        ge = tok ? a.in_g[head] : a.ring_g[s];
         be = (c0 + li < nfold) ? be : 0.f;  // lanes 16..63 mirror lanes 0..15
-        ge = (c0 + li < nfold) ? ge : 0.f;
+        if constexpr (!VG) {
+            ge = tok ? a.in_g[head] : a.ring_g[s];
+            ge = (c0 + li < nfold) ? ge : 0.f;
+        }
     };
     fetch(0);  // entries clamped to >= 0: in bounds also when nothing is folded (rewrite only)
     constexpr int kQE = DK / 64;  // FUSED: q elements per lane
@@ -477,14 +562,60 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_flush_kernel(GdnArgs a, int mod
                 for (int j = 0; j < kEPC; ++j) s_v[wave][e][part * kEPC + j] = e < nc ? f[j] : 0.f;
             }
         }
+        constexpr int kWE = DK / 64;  // columns n = lane + 64 j owned in the substitution
+        float glog[VG ? kWE : 1];    // VG: G_L of the lane's own columns
+        if constexpr (VG) {  // g rows -> s_w, then the within-chunk cumulative G in place
+            // (loaded here, after the state stream, four 16-byte pieces at a time: held across
+            // the stream they would spill)
+#pragma unroll
+            for (int i0 = 0; i0 < kGL; i0 += 4) {
+#pragma unroll
+                for (int i = i0; i < i0 + 4 && i < kGL; ++i) {
+                    const int idx = (lane + 64 * i) % (16 * kGC);
+                    const int e = min(c0 + idx / kGC, max(nfold - 1, 0)), part = idx % kGC;
+                    graw[i - i0] = *reinterpret_cast<const u32x4_t*>(grow(e) + part * 4);
+                }
+#pragma unroll
+                for (int i = i0; i < i0 + 4 && i < kGL; ++i) {
+                    const int idx = lane + 64 * i;
+                    if (idx < 16 * kGC) {
+                        const int e = idx / kGC, part = idx % kGC;
+                        const u32x4_t u = graw[i - i0];
+                        const float f[4] = {__uint_as_float(u.x), __uint_as_float(u.y),
+                                            __uint_as_float(u.z), __uint_as_float(u.w)};
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) s_w[wave][e][part * 4 + j] = e < nc ? f[j] : 0.f;
+                    }
+                }
+            }
+            wave_sync();
+#pragma unroll
+            for (int j = 0; j < kWE; ++j) {
+                const int n = lane + 64 * j;
+                float Gc = 0.f;
+#pragma unroll
+                for (int t = 0; t < 16; ++t) {
+                    Gc += s_w[wave][t][n];
+                    s_w[wave][t][n] = Gc;
+                }
+                glog[j] = Gc;
+                s_gl[wave][n] = expf(Gc);
+            }
+        }
         wave_sync();
 
-        // Gram matrix K K^T on MFMA: lane l supplies K[l%16][n0 + l/16] as both operands
+        // Gram matrix K K^T on MFMA: lane l supplies K[l%16][n0 + l/16] as both operands (VG:
+        // scaled by exp(G - G_ref) as the left and exp(G_ref - G) as the right operand)
         f32x4 gram = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int n0 = 0; n0 < DK; n0 += 4) {
             const float kk = s_k[wave][li][n0 + lg];
-            gram = mfma4(kk, kk, gram);
+            if constexpr (VG) {
+                const float d = s_w[wave][li][n0 + lg] - s_w[wave][7][n0 + lg];
+                gram = mfma4(kk * expf(d), kk * expf(-d), gram);
+            } else {
+                gram = mfma4(kk, kk, gram);
+            }
         }
         // G_t = sum_{m <= t} g_m within the chunk (inclusive scan over each 16-lane row; the four
         // rows hold the same entries, so every lane l has G at entry l%16)
@@ -501,7 +632,8 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_flush_kernel(GdnArgs a, int mod
             const int t = 4 * lg + r, i = li;
             const float bt = __shfl(be, t, 64);
             const float Gt = __shfl(G, t, 64);
-            const float lm = (i < t) ? bt * expf(Gt - G) * gram[r] : 0.f;
+            const float dec = VG ? 1.f : expf(Gt - G);  // VG: the decay is inside the Gram matrix
+            const float lm = (i < t) ? bt * dec * gram[r] : 0.f;
             s_l[wave][t][i] = lm;
         }
         wave_sync();
@@ -509,18 +641,25 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_flush_kernel(GdnArgs a, int mod
         // forward substitution, in place in LDS: lane owns the columns n = lane + 64 j of W and
         // the row p_base + lane of U, so every value it reads back it wrote itself. W is kept
         // negated (s_w[t] = -W_t) for the MFMA below; U overwrites V in s_v ([t][p]).
-        constexpr int kWE = DK / 64;
 #pragma unroll
         for (int t = 0; t < 16; ++t) {
             const float bt = readlane(be, t);
-            const float bg = bt * expf(readlane(G, t));
+            const float bg = bt * (VG ? 1.f : expf(readlane(G, t)));
             float lrow[16];
 #pragma unroll
             for (int i = 0; i < t; ++i) lrow[i] = s_l[wave][t][i];
 #pragma unroll
             for (int j = 0; j < kWE; ++j) {
                 const int n = lane + 64 * j;
-                float sw = -bg * s_k[wave][t][n];
+                const float kt = s_k[wave][t][n];
+                float sw;
+                if constexpr (VG) {  // row t of s_w still holds G_t here
+                    const float Gt = s_w[wave][t][n];
+                    sw = -bg * expf(Gt) * kt;
+                    s_k[wave][t][n] = kt * expf(glog[j] - Gt);  // K~ for the update below
+                } else {
+                    sw = -bg * kt;
+                }
 #pragma unroll
                 for (int i = 0; i < t; ++i) sw -= lrow[i] * s_w[wave][i][n];
                 s_w[wave][t][n] = sw;
@@ -536,7 +675,7 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_flush_kernel(GdnArgs a, int mod
 
         asm volatile("" ::: "memory");
         // Delta^T[p][t] = U^T[p][t] - sum_n S[p][n] W[t][n]   (D layout: p = 4lg + r, t = li)
-        const float dscale = expf(gL - G);  // gamma_L / gamma_t for t = li
+        const float dscale = VG ? 1.f : expf(gL - G);  // gamma_L / gamma_t for t = li (VG: in K~)
         f32x4 delta[kPB];
 #pragma unroll
         for (int pb = 0; pb < kPB; ++pb)
@@ -572,7 +711,13 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_flush_kernel(GdnArgs a, int mod
             for (int tg = 0; tg < 4; ++tg) dop[tg] = s_d[wave][16 * pb + li][4 * tg + lg];
 #pragma unroll
             for (int nb = 0; nb < kNB; ++nb) {
-                f32x4 acc = S[pb][nb] * gammaL;
+                f32x4 acc;
+                if constexpr (VG) {  // column n = 16 nb + 4 lg + r scaled by exp(G_L[n])
+                    const f32x4 gc = *reinterpret_cast<const f32x4*>(&s_gl[wave][16 * nb + 4 * lg]);
+                    acc = S[pb][nb] * gc;
+                } else {
+                    acc = S[pb][nb] * gammaL;
+                }
 #pragma unroll
                 for (int tg = 0; tg < 4; ++tg)
                     acc = mfma4(s_k[wave][4 * tg + lg][16 * nb + li], dop[tg], acc);

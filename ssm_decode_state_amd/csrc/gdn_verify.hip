@@ -1,17 +1,25 @@
-// gdn_verify.hip -- instantiations of the GDN speculative verify: up to 8 draft tokens per call
+// gdn_verify.hip -- instantiations of the GDN / KDA speculative verify: up to 8 draft tokens per call
 // (rounded up to 4 or 8 queries), at most 32 entries seen.
 #include "gdn_kernels.hpp"
 
 namespace ssm {
 
-template <int DV, int DK, typename TIN, int RC>
-static hipError_t launch_verify_dd(const GdnArgs& a, hipStream_t s) {
+template <int DV, int DK, typename TIN, int RC, bool VG>
+static hipError_t launch_verify_vg(const GdnArgs& a, hipStream_t s) {
     const dim3 grid(a.heads, a.batch), block(DV);
     if (a.ntok <= 4)
-        hipLaunchKernelGGL((gdn_replay_kernel<DV, DK, TIN, RC, 32, 4, false>), grid, block, 0, s, a);
+        hipLaunchKernelGGL((gdn_replay_kernel<DV, DK, TIN, RC, 32, 4, false, VG>), grid, block, 0, s, a);
     else
-        hipLaunchKernelGGL((gdn_replay_kernel<DV, DK, TIN, RC, 32, 8, false>), grid, block, 0, s, a);
+        hipLaunchKernelGGL((gdn_replay_kernel<DV, DK, TIN, RC, 32, 8, false, VG>), grid, block, 0, s, a);
     return hipGetLastError();
+}
+template <int DV, int DK, typename TIN, int RC>
+static hipError_t launch_verify_dd(const GdnArgs& a, hipStream_t s) {
+    if (a.kda) {  // per-channel gate: no read copy
+        if constexpr (RC == 0) return launch_verify_vg<DV, DK, TIN, 0, true>(a, s);
+        else return hipErrorNotSupported;
+    }
+    return launch_verify_vg<DV, DK, TIN, RC, false>(a, s);
 }
 
 template <typename TIN, int RC>

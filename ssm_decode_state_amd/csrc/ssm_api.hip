@@ -19,7 +19,7 @@ hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 
 ssm_status check_config(const ssm_config* c) {
     if (!c) return SSM_E_ARG;
-    if (c->kind != SSM_MAMBA2 && c->kind != SSM_GDN) return SSM_E_ARG;
+    if (c->kind != SSM_MAMBA2 && c->kind != SSM_GDN && c->kind != SSM_KDA) return SSM_E_ARG;
     if (c->in_dtype != SSM_IN_F32 && c->in_dtype != SSM_IN_BF16) return SSM_E_ARG;
     if (c->readcopy < SSM_RC_NONE || c->readcopy > SSM_RC_FP4_B16) return SSM_E_ARG;
     if (c->batch < 0 || c->heads < 1 || c->groups < 1) return SSM_E_SHAPE;
@@ -39,6 +39,7 @@ ssm_status check_config(const ssm_config* c) {
         if (!isfinite(c->gdn_scale)) return SSM_E_ARG;
         // a call sees at most 32 entries (the replay kernel's sweep bound)
         if (c->window + c->max_draft - 1 > 32) return SSM_E_UNSUPPORTED;
+        if (c->kind == SSM_KDA && c->readcopy != SSM_RC_NONE) return SSM_E_UNSUPPORTED;
     }
     return SSM_OK;
 }
@@ -75,7 +76,7 @@ void compute_layout(const ssm_config* c, ssm_layout* L) {
         L->off_ring[1] = take(B * H * cap * N * esz);  // k  (dk)
         L->off_ring[2] = take(B * H * cap * P * esz);  // v  (dv)
         L->off_ring[3] = take(B * H * cap * 4);        // beta
-        L->off_ring[4] = take(B * H * cap * 4);        // g
+        L->off_ring[4] = take(B * H * cap * (c->kind == SSM_KDA ? N : 1) * 4);  // g (KDA: dk)
     }
     L->off_ptr = take(B * H * 2 * 4);
     L->off_flags = take(4);
@@ -135,6 +136,7 @@ ssm::GdnArgs gdn_args(const ssm_state* st) {
     a.heads = st->cfg.heads;
     a.cap = L.ring_cap;
     a.window = st->cfg.window;
+    a.kda = st->cfg.kind == SSM_KDA;
     return a;
 }
 
@@ -434,7 +436,8 @@ ssm_status ssm_conventional_step(const ssm_config* cfg, float* h, const void* in
         e = ssm::m2_launch_conv(a, c.dim_p, c.dim_n, c.in_dtype, as_stream(stream));
     } else {
         const ssm_gdn_in* g = static_cast<const ssm_gdn_in*>(in);
-        ssm::GdnConvArgs a{h, g->q, g->k, g->v, g->beta, g->g, y, c.gdn_scale, c.batch, c.heads};
+        ssm::GdnConvArgs a{h, g->q, g->k, g->v, g->beta, g->g, y, c.gdn_scale, c.batch, c.heads,
+                           c.kind == SSM_KDA};
         e = ssm::gdn_launch_conv(a, c.dim_p, c.dim_n, c.in_dtype, as_stream(stream));
     }
     if (e == hipErrorNotSupported) return SSM_E_UNSUPPORTED;

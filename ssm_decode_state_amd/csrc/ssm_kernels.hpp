@@ -61,6 +61,7 @@ struct GdnArgs {
     float* o;
     float scale;
     int batch, heads, cap, ntok, window;
+    int kda;  // Kimi Delta Attention: g holds dk decays per entry (per-channel gate)
 };
 
 struct GdnConvArgs {
@@ -73,6 +74,7 @@ struct GdnConvArgs {
     float* o;
     float scale;
     int batch, heads;
+    int kda;  // per-channel gate (g [batch][H][dk])
 };
 
 // maxe: upper bound on count + ntok over all sequences (<= 64).

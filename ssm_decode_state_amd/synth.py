@@ -27,12 +27,13 @@ import torch
 
 MAMBA2 = 0
 GDN = 1
+KDA = 2
 
 
 @dataclasses.dataclass(frozen=True)
 class Shape:
     """Problem shape of one SSM layer (names follow the pages' two layer types)."""
-    kind: int          # MAMBA2 or GDN
+    kind: int          # MAMBA2, GDN or KDA
     batch: int         # sequences
     heads: int         # H
     groups: int        # Mamba-2: B/C groups G (H % G == 0); GDN: == heads
@@ -61,6 +62,8 @@ WORKLOADS: Dict[str, dict] = {
                      h0_std=math.sqrt(0.1)),
     "gdn_b256_spec": dict(shape=Shape(GDN, 256, 32, 32, 128, 128, 16, 4), rounds=128, ndraft=4,
                           seed=5, accept_seed=1002, h0_std=math.sqrt(0.1)),
+    "kda_b256": dict(shape=Shape(KDA, 256, 32, 32, 128, 128, 16, 1), steps=256, seed=6,
+                     h0_std=math.sqrt(0.1)),
 }
 
 
@@ -114,6 +117,7 @@ def token_inputs(shape: Shape, seed: int, tag: str, index: int, ntok: int = 1,
              dt [batch][ntok][H] fp32.
     GDN:     q, k [batch][ntok][H][dk], v [batch][ntok][H][dv] in the storage dtype;
              beta, g [batch][ntok][H] fp32.
+    KDA:     as GDN with g [batch][ntok][H][dk] (one log-decay per key channel).
     """
     g = _gen(seed, tag, layer, index)
     bsz, H = shape.batch, shape.heads
@@ -134,7 +138,8 @@ def token_inputs(shape: Shape, seed: int, tag: str, index: int, ntok: int = 1,
     k = k / k.norm(dim=-1, keepdim=True)
     v = torch.randn(bsz, ntok, H, dv, generator=g)
     beta = torch.sigmoid(torch.randn(bsz, ntok, H, generator=g, dtype=torch.float64))
-    gl = -_softplus64(torch.randn(bsz, ntok, H, generator=g, dtype=torch.float64))
+    gshape = (bsz, ntok, H, dk) if shape.kind == KDA else (bsz, ntok, H)
+    gl = -_softplus64(torch.randn(*gshape, generator=g, dtype=torch.float64))
     return {"q": q.to(torch.float32).to(dt_), "k": k.to(torch.float32).to(dt_), "v": v.to(dt_),
             "beta": beta.to(torch.float32), "g": gl.to(torch.float32)}
 
@@ -163,7 +168,8 @@ def token_inputs_device(shape: Shape, seed: int, tag: str, index: int, ntok: int
     k = k / k.norm(dim=-1, keepdim=True)
     v = torch.randn(bsz, ntok, H, dv, **kw)
     beta = torch.sigmoid(torch.randn(bsz, ntok, H, dtype=torch.float64, **kw))
-    gl = -_softplus64(torch.randn(bsz, ntok, H, dtype=torch.float64, **kw))
+    gshape = (bsz, ntok, H, dk) if shape.kind == KDA else (bsz, ntok, H)
+    gl = -_softplus64(torch.randn(*gshape, dtype=torch.float64, **kw))
     return {"q": q.to(torch.float32).to(dt_), "k": k.to(torch.float32).to(dt_), "v": v.to(dt_),
             "beta": beta.to(torch.float32), "g": gl.to(torch.float32)}
 

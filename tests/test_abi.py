@@ -75,6 +75,15 @@ def test_layout_gdn_read_copies():
     assert f4.off_rc_tscale - f4.off_rc_scale == 256 * 32 * 128 * 8
 
 
+def test_layout_kda_gate_ring():
+    c = dict(kind=bd.SSM_KDA, heads=32, groups=32, dim_p=128, dim_n=128)
+    kda = bd.ssm_layout_query(cfg(**c))
+    gdn = bd.ssm_layout_query(cfg(**{**c, "kind": bd.SSM_GDN}))
+    # KDA keeps dk log-decays per entry: the g ring is dk times the GDN one
+    assert kda.off_ptr - kda.off_ring[4] == 256 * 32 * 16 * 128 * 4
+    assert gdn.off_ptr - gdn.off_ring[4] == 256 * 32 * 16 * 4
+
+
 def test_layout_read_copies():
     f8 = bd.ssm_layout_query(cfg(readcopy=bd.SSM_RC_FP8_ROW))
     assert f8.off_rc_scale - f8.off_rc_codes == 256 * 128 * 64 * 128
@@ -110,6 +119,10 @@ def test_every_accepted_mamba2_shape(P, N):
     (dict(kind=bd.SSM_GDN, groups=64), bd.SSM_E_SHAPE),
     (dict(kind=bd.SSM_GDN, dim_p=32), bd.SSM_E_SHAPE),
     (dict(kind=bd.SSM_GDN, window=32, max_draft=2), bd.SSM_E_UNSUPPORTED),
+    (dict(kind=bd.SSM_KDA, groups=64), bd.SSM_E_SHAPE),
+    (dict(kind=bd.SSM_KDA, dim_p=32), bd.SSM_E_SHAPE),
+    (dict(kind=bd.SSM_KDA, readcopy=bd.SSM_RC_FP8_ROW), bd.SSM_E_UNSUPPORTED),
+    (dict(kind=3), bd.SSM_E_ARG),
 ])
 def test_bad_configs_rejected(kw, status):
     with pytest.raises(bd.SSMError) as ei:
