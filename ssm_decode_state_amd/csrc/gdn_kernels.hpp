@@ -439,16 +439,21 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_flush_kernel(GdnArgs a, int mod
     constexpr int kVP = 64 + 4;
     constexpr int kEPC = 16 / (int)sizeof(TIN);
     constexpr int kKC = DK / kEPC, kVC = 64 / kEPC;   // 16-byte chunks per k row / per v slice
-    constexpr int kKL = (16 * kKC + 63) / 64, kVL = (16 * kVC + 63) / 64;
-    constexpr int kGC = DK / 4, kGL = (16 * kGC + 63) / 64;  // VG: 16-byte chunks of g rows
-    __shared__ __attribute__((aligned(16))) float s_k[kW][16][kKP];     // K chunk (fp32); VG: then K~
-    __shared__ __attribute__((aligned(16))) float s_w[kW][16][kKP];     // VG: G first; then -W
-    __shared__ __attribute__((aligned(16))) float s_v[kW][16][kVP];     // this wave's v slice, then U ([t][p]), then Delta'^T
-    __shared__ __attribute__((aligned(16))) float s_l[kW][16][17];      // Lm
-    __shared__ __attribute__((aligned(16))) float s_d[kW][64][17];      // Delta' as [p][t] (transpose buffer)
-    __shared__ __attribute__((aligned(16))) float s_q[kW][FUSED ? DK : 4];  // FUSED: the token's q
+    // the waves of a head split the staging of the chunk's keys (and VG log-decays)
+    constexpr int kKL = (16 * kKC / kW + 63) / 64, kVL = (16 * kVC + 63) / 64;
+    constexpr int kGC = DK / 4, kGL = (16 * kGC / kW + 63) / 64;  // VG: 16-byte pieces of g rows
+    constexpr int kWE = DK / 64;      // columns n = lane + 64 j, j < kWE, of the substitution
+    // Shared by the head's waves (the keys, W and Lm do not depend on the state rows):
+    __shared__ __attribute__((aligned(16))) float s_k[16][kKP];   // K chunk (fp32); VG: then K~
+    __shared__ __attribute__((aligned(16))) float s_w[16][kKP];   // VG: G first; then -W
+    __shared__ __attribute__((aligned(16))) float s_l[16][17];    // Lm
+    __shared__ __attribute__((aligned(16))) float s_q[FUSED ? DK : 4];   // FUSED: the token's q
+    __shared__ __attribute__((aligned(16))) float s_gl[VG ? DK : 4];     // VG: exp(G_L) per column
+    // Per wave: its v slice, then U ([t][p]); after step A the same floats hold Delta' as [p][t]
+    // (64 x 17 == 16 x 68), the transpose buffer
+    __shared__ __attribute__((aligned(16))) float s_v[kW][16][kVP];
     __shared__ float s_amax[kW];  // fp4 read copy: the waves' largest magnitudes
-    __shared__ __attribute__((aligned(16))) float s_gl[kW][VG ? DK : 4];  // VG: exp(G_L) per column
+    static_assert(16 * kVP == 64 * 17, "transpose buffer aliases the v slice");
 
     const int wave = uniform(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
@@ -461,11 +466,12 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_flush_kernel(GdnArgs a, int mod
     const int nfold = FUSED ? count + 1
                             : (rewrite_only ? 0 : (mode_all ? count : (count >= a.window ? a.window : 0)));
     const int nring = FUSED ? count : nfold;  // entries that come from the ring
-    if (nfold == 0 && !rewrite_only) return;  // uniform over the workgroup
+    if (nfold == 0 && !rewrite_only) return;  // uniform over the workgroup: no barrier is skipped
     const TIN* rk = static_cast<const TIN*>(a.ring_k);
     const TIN* rv = static_cast<const TIN*>(a.ring_v);
     const int li = lane & 15, lg = lane >> 4;
     const int p_base = wave * 64;
+    float (*s_d)[17] = reinterpret_cast<float (*)[17]>(&s_v[wave][0][0]);
 
     // entry e (already clamped to a folded entry): ring slot, or the caller's token (FUSED)
     auto krow = [&](int e) -> const TIN* {
@@ -480,13 +486,14 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_flush_kernel(GdnArgs a, int mod
         if (FUSED && e >= nring) return a.in_g + (long)head * DK;
         return a.ring_g + ((long)head * cap + ring_slot(start, e, cap)) * DK;
     };
-    // chunk loader (branch-free: entries past nfold read the last folded entry, zeroed later)
-    u32x4_t kraw[kKL], vraw[kVL], graw[VG ? 4 : 1];
+    // chunk loader (branch-free: entries past nfold read the last folded entry, zeroed later);
+    // wave w loads key pieces w * 16 kKC / kW .. of the chunk
+    u32x4_t kraw[kKL], vraw[kVL];
     float be = 0.f, ge = 0.f;
     auto fetch = [&](int c0) {
 #pragma unroll
         for (int i = 0; i < kKL; ++i) {
-            const int idx = (lane + 64 * i) % (16 * kKC);
+            const int idx = (wave * (16 * kKC / kW) + lane + 64 * i) % (16 * kKC);
             const int e = min(c0 + idx / kKC, max(nfold - 1, 0)), part = idx % kKC;
             kraw[i] = *reinterpret_cast<const u32x4_t*>(krow(e) + part * kEPC);
         }
@@ -533,22 +540,24 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_flush_kernel(GdnArgs a, int mod
 
     float opart[kPB] = {};  // FUSED: partial dot products of the new state's rows with q
     if constexpr (FUSED) {
+        if (wave == 0) {
 #pragma unroll
-        for (int i = 0; i < kQE; ++i) s_q[wave][lane + 64 * i] = to_f32<TIN>(qraw[i]);
+            for (int i = 0; i < kQE; ++i) s_q[lane + 64 * i] = to_f32<TIN>(qraw[i]);
+        }
     }
     for (int c0 = 0; c0 < nfold; c0 += 16) {
         if (c0 > 0) fetch(c0);
         const int nc = min(16, nfold - c0);
-        // stage K and V (entries >= nc as zeros)
+        // ---- stage this wave's share of K, its own V slice (entries >= nc as zeros) ----------
 #pragma unroll
         for (int i = 0; i < kKL; ++i) {
-            const int idx = lane + 64 * i;
-            if (idx < 16 * kKC) {
+            const int idx = wave * (16 * kKC / kW) + lane + 64 * i;
+            if (lane + 64 * i < 16 * kKC / kW) {
                 const int e = idx / kKC, part = idx % kKC;
                 float f[kEPC];
                 Unit<TIN>::unpack(make_uint4(kraw[i].x, kraw[i].y, kraw[i].z, kraw[i].w), f);
 #pragma unroll
-                for (int j = 0; j < kEPC; ++j) s_k[wave][e][part * kEPC + j] = e < nc ? f[j] : 0.f;
+                for (int j = 0; j < kEPC; ++j) s_k[e][part * kEPC + j] = e < nc ? f[j] : 0.f;
             }
         }
 #pragma unroll
@@ -562,61 +571,51 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_flush_kernel(GdnArgs a, int mod
                 for (int j = 0; j < kEPC; ++j) s_v[wave][e][part * kEPC + j] = e < nc ? f[j] : 0.f;
             }
         }
-        constexpr int kWE = DK / 64;  // columns n = lane + 64 j owned in the substitution
-        float glog[VG ? kWE : 1];    // VG: G_L of the lane's own columns
-        if constexpr (VG) {  // g rows -> s_w, then the within-chunk cumulative G in place
-            // (loaded here, after the state stream, four 16-byte pieces at a time: held across
-            // the stream they would spill)
+        float glog[VG ? kWE : 1];  // VG: G_L of the lane's own columns
+        if constexpr (VG) {
+            // g rows -> s_w (this wave's share, loaded here after the state stream, four 16-byte
+            // pieces at a time: held across the stream they would spill)
 #pragma unroll
             for (int i0 = 0; i0 < kGL; i0 += 4) {
+                u32x4_t graw[4];
 #pragma unroll
                 for (int i = i0; i < i0 + 4 && i < kGL; ++i) {
-                    const int idx = (lane + 64 * i) % (16 * kGC);
+                    const int idx = (wave * (16 * kGC / kW) + lane + 64 * i) % (16 * kGC);
                     const int e = min(c0 + idx / kGC, max(nfold - 1, 0)), part = idx % kGC;
                     graw[i - i0] = *reinterpret_cast<const u32x4_t*>(grow(e) + part * 4);
                 }
 #pragma unroll
                 for (int i = i0; i < i0 + 4 && i < kGL; ++i) {
-                    const int idx = lane + 64 * i;
-                    if (idx < 16 * kGC) {
+                    if (lane + 64 * i < 16 * kGC / kW) {
+                        const int idx = wave * (16 * kGC / kW) + lane + 64 * i;
                         const int e = idx / kGC, part = idx % kGC;
                         const u32x4_t u = graw[i - i0];
                         const float f[4] = {__uint_as_float(u.x), __uint_as_float(u.y),
                                             __uint_as_float(u.z), __uint_as_float(u.w)};
 #pragma unroll
-                        for (int j = 0; j < 4; ++j) s_w[wave][e][part * 4 + j] = e < nc ? f[j] : 0.f;
+                        for (int j = 0; j < 4; ++j) s_w[e][part * 4 + j] = e < nc ? f[j] : 0.f;
                     }
                 }
             }
-            wave_sync();
+            __syncthreads();
+            // the within-chunk cumulative G of the columns this lane owns, in place
 #pragma unroll
             for (int j = 0; j < kWE; ++j) {
+                if (j % kW != wave) continue;  // the waves split the columns
                 const int n = lane + 64 * j;
                 float Gc = 0.f;
 #pragma unroll
                 for (int t = 0; t < 16; ++t) {
-                    Gc += s_w[wave][t][n];
-                    s_w[wave][t][n] = Gc;
+                    Gc += s_w[t][n];
+                    s_w[t][n] = Gc;
                 }
                 glog[j] = Gc;
-                s_gl[wave][n] = expf(Gc);
+                s_gl[n] = expf(Gc);
             }
         }
-        wave_sync();
+        __syncthreads();
 
-        // Gram matrix K K^T on MFMA: lane l supplies K[l%16][n0 + l/16] as both operands (VG:
-        // scaled by exp(G - G_ref) as the left and exp(G_ref - G) as the right operand)
-        f32x4 gram = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int n0 = 0; n0 < DK; n0 += 4) {
-            const float kk = s_k[wave][li][n0 + lg];
-            if constexpr (VG) {
-                const float d = s_w[wave][li][n0 + lg] - s_w[wave][7][n0 + lg];
-                gram = mfma4(kk * expf(d), kk * expf(-d), gram);
-            } else {
-                gram = mfma4(kk, kk, gram);
-            }
-        }
+        // ---- Gram matrix and Lm (once per head, by wave 0) ------------------------------------
         // G_t = sum_{m <= t} g_m within the chunk (inclusive scan over each 16-lane row; the four
         // rows hold the same entries, so every lane l has G at entry l%16)
         float G = ge;
@@ -625,44 +624,60 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_flush_kernel(GdnArgs a, int mod
             const float t = __shfl_up(G, o, 16);
             G += li >= o ? t : 0.f;
         }
-        // Lm[t][i] for t = 4lg + r, i = li (t varies across lanes: per-lane shuffles);
-        // the decay from entry i to t is exp(G_t - G_i)
+        if (wave == 0) {
+            // K K^T on MFMA: lane l supplies K[l%16][n0 + l/16] as both operands (VG: scaled by
+            // exp(G - G_ref) as the left and exp(G_ref - G) as the right operand)
+            f32x4 gram = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int t = 4 * lg + r, i = li;
-            const float bt = __shfl(be, t, 64);
-            const float Gt = __shfl(G, t, 64);
-            const float dec = VG ? 1.f : expf(Gt - G);  // VG: the decay is inside the Gram matrix
-            const float lm = (i < t) ? bt * dec * gram[r] : 0.f;
-            s_l[wave][t][i] = lm;
+            for (int n0 = 0; n0 < DK; n0 += 4) {
+                const float kk = s_k[li][n0 + lg];
+                if constexpr (VG) {
+                    const float d = s_w[li][n0 + lg] - s_w[7][n0 + lg];
+                    gram = mfma4(kk * expf(d), kk * expf(-d), gram);
+                } else {
+                    gram = mfma4(kk, kk, gram);
+                }
+            }
+            // Lm[t][i] for t = 4lg + r, i = li (t varies across lanes: per-lane shuffles);
+            // the decay from entry i to t is exp(G_t - G_i) (VG: inside the Gram matrix)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = 4 * lg + r, i = li;
+                const float bt = __shfl(be, t, 64);
+                const float Gt = __shfl(G, t, 64);
+                const float dec = VG ? 1.f : expf(Gt - G);
+                s_l[t][i] = (i < t) ? bt * dec * gram[r] : 0.f;
+            }
         }
-        wave_sync();
+        __syncthreads();
 
-        // forward substitution, in place in LDS: lane owns the columns n = lane + 64 j of W and
-        // the row p_base + lane of U, so every value it reads back it wrote itself. W is kept
-        // negated (s_w[t] = -W_t) for the MFMA below; U overwrites V in s_v ([t][p]).
+        // ---- forward substitution, in place in LDS ---------------------------------------------
+        // W: lane owns the columns n = lane + 64 j (the waves split them); U: lane owns row
+        // p_base + lane. Every value a lane reads back it wrote itself. W is kept negated
+        // (s_w[t] = -W_t) for the MFMA below; U overwrites V in s_v ([t][p]).
 #pragma unroll
         for (int t = 0; t < 16; ++t) {
             const float bt = readlane(be, t);
             const float bg = bt * (VG ? 1.f : expf(readlane(G, t)));
             float lrow[16];
 #pragma unroll
-            for (int i = 0; i < t; ++i) lrow[i] = s_l[wave][t][i];
+            for (int i = 0; i < t; ++i) lrow[i] = s_l[t][i];
 #pragma unroll
             for (int j = 0; j < kWE; ++j) {
+                if (j % kW != wave) continue;
                 const int n = lane + 64 * j;
-                const float kt = s_k[wave][t][n];
+                const float kt = s_k[t][n];
                 float sw;
                 if constexpr (VG) {  // row t of s_w still holds G_t here
-                    const float Gt = s_w[wave][t][n];
+                    const float Gt = s_w[t][n];
                     sw = -bg * expf(Gt) * kt;
-                    s_k[wave][t][n] = kt * expf(glog[j] - Gt);  // K~ for the update below
+                    s_k[t][n] = kt * expf(glog[j] - Gt);  // K~ for the update below
                 } else {
                     sw = -bg * kt;
                 }
 #pragma unroll
-                for (int i = 0; i < t; ++i) sw -= lrow[i] * s_w[wave][i][n];
-                s_w[wave][t][n] = sw;
+                for (int i = 0; i < t; ++i) sw -= lrow[i] * s_w[i][n];
+                s_w[t][n] = sw;
             }
             float su = bt * s_v[wave][t][lane];
 #pragma unroll
@@ -671,10 +686,10 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_flush_kernel(GdnArgs a, int mod
             asm volatile("" ::: "memory");  // one row of Lm live at a time
         }
         const float gL = readlane(G, 15);  // log gamma_L (zero-padded entries add nothing)
-        wave_sync();
+        __syncthreads();  // W and K~ complete for every column
 
         asm volatile("" ::: "memory");
-        // Delta^T[p][t] = U^T[p][t] - sum_n S[p][n] W[t][n]   (D layout: p = 4lg + r, t = li)
+        // ---- Delta^T[p][t] = U^T[p][t] - sum_n S[p][n] W[t][n]   (D layout: p = 4lg + r, t = li)
         const float dscale = VG ? 1.f : expf(gL - G);  // gamma_L / gamma_t for t = li (VG: in K~)
         f32x4 delta[kPB];
 #pragma unroll
@@ -684,7 +699,7 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_flush_kernel(GdnArgs a, int mod
 #pragma unroll
         for (int nb = 0; nb < kNB; ++nb) {
             // B operand: -W[t = li][16nb + 4lg + r]
-            const f32x4 wop = *reinterpret_cast<const f32x4*>(&s_w[wave][li][16 * nb + 4 * lg]);
+            const f32x4 wop = *reinterpret_cast<const f32x4*>(&s_w[li][16 * nb + 4 * lg]);
 #pragma unroll
             for (int pb = 0; pb < kPB; ++pb)
 #pragma unroll
@@ -692,44 +707,46 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_flush_kernel(GdnArgs a, int mod
         }
 #pragma unroll
         for (int pb = 0; pb < kPB; ++pb) delta[pb] *= dscale;  // Delta' = (gamma_L/gamma_t) Delta
-        wave_sync();
+        wave_sync();  // every lane of the wave has read U: its floats become the transpose buffer
         // transpose Delta' through LDS ([p][t])
 #pragma unroll
         for (int pb = 0; pb < kPB; ++pb)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) s_d[wave][16 * pb + 4 * lg + r][li] = delta[pb][r];
+            for (int r = 0; r < 4; ++r) s_d[16 * pb + 4 * lg + r][li] = delta[pb][r];
         wave_sync();
 
         asm volatile("" ::: "memory");
-        // S <- gamma_L S + sum_t K^T[n][t] Delta'^T[t][p]   (D rows = n, columns = p)
+        // ---- S <- gamma_L S + sum_t K^T[n][t] Delta'^T[t][p]   (D rows = n, columns = p) -----
         const float gammaL = expf(gL);
+        if constexpr (VG) {  // column n = 16 nb + 4 lg + r scaled by exp(G_L[n]), one block at a time
+#pragma unroll
+            for (int nb = 0; nb < kNB; ++nb) {
+                const f32x4 gc = *reinterpret_cast<const f32x4*>(&s_gl[16 * nb + 4 * lg]);
+#pragma unroll
+                for (int pb = 0; pb < kPB; ++pb) S[pb][nb] *= gc;
+            }
+        }
 #pragma unroll
         for (int pb = 0; pb < kPB; ++pb) {
             opart[pb] = 0.f;
             float dop[4];  // B operand: Delta'[p = 16pb + li][t = 4tg + lg]
 #pragma unroll
-            for (int tg = 0; tg < 4; ++tg) dop[tg] = s_d[wave][16 * pb + li][4 * tg + lg];
+            for (int tg = 0; tg < 4; ++tg) dop[tg] = s_d[16 * pb + li][4 * tg + lg];
 #pragma unroll
             for (int nb = 0; nb < kNB; ++nb) {
-                f32x4 acc;
-                if constexpr (VG) {  // column n = 16 nb + 4 lg + r scaled by exp(G_L[n])
-                    const f32x4 gc = *reinterpret_cast<const f32x4*>(&s_gl[wave][16 * nb + 4 * lg]);
-                    acc = S[pb][nb] * gc;
-                } else {
-                    acc = S[pb][nb] * gammaL;
-                }
+                f32x4 acc = VG ? S[pb][nb] : S[pb][nb] * gammaL;  // (VG: scaled above)
 #pragma unroll
                 for (int tg = 0; tg < 4; ++tg)
-                    acc = mfma4(s_k[wave][4 * tg + lg][16 * nb + li], dop[tg], acc);
+                    acc = mfma4(s_k[4 * tg + lg][16 * nb + li], dop[tg], acc);
                 S[pb][nb] = acc;
                 if constexpr (FUSED) {  // the token's output row partials, o = scale S q
                     // (every chunk recomputes them; the last chunk's are the new state's)
-                    const float4 q4 = *reinterpret_cast<const float4*>(&s_q[wave][16 * nb + 4 * lg]);
+                    const float4 q4 = *reinterpret_cast<const float4*>(&s_q[16 * nb + 4 * lg]);
                     opart[pb] += acc[0] * q4.x + acc[1] * q4.y + acc[2] * q4.z + acc[3] * q4.w;
                 }
             }
         }
-        wave_sync();
+        __syncthreads();  // the next chunk overwrites the shared K, W and Lm
     }
 
 #pragma unroll
@@ -740,11 +757,11 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_flush_kernel(GdnArgs a, int mod
                       make_float4(S[pb][nb][0], S[pb][nb][1], S[pb][nb][2], S[pb][nb][3]));
     if constexpr (FUSED) {
         // row p_base + 16 pb + li is spread over lanes li + 16 lg: sum the four partials through
-        // the (now free) transpose buffer, then lane p writes row p_base + p
+        // the wave's (now free) transpose buffer, then lane p writes row p_base + p
 #pragma unroll
-        for (int pb = 0; pb < kPB; ++pb) s_d[wave][16 * pb + li][lg] = opart[pb];
+        for (int pb = 0; pb < kPB; ++pb) s_d[16 * pb + li][lg] = opart[pb];
         wave_sync();
-        const float* r = s_d[wave][lane];
+        const float* r = s_d[lane];
         a.o[(long)head * DV + p_base + lane] = a.scale * ((r[0] + r[1]) + (r[2] + r[3]));
     }
     if constexpr (RC != 0) {  // rewrite the read copy from the new fp32 tile (news, para 4)
