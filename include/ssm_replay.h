@@ -202,6 +202,22 @@ ssm_status ssm_spec_append(ssm_state *st, int32_t ndraft, const void *in, float 
  * Errors: SSM_E_STATE if no drafts are pending. */
 ssm_status ssm_spec_rollback(ssm_state *st, const int32_t *n_accept, void *stream);
 
+/* Restore to an earlier position (explainer, "What a Replay-First Design Implies": restore state
+ * to position p): sequence b drops its newest min(n_back[b], committed count) entries (device
+ * int32 [batch]; negative values count as 0). Positions back to the checkpoint are reached by
+ * moving a pointer, since replay rebuilds the output at any of them; earlier positions are not
+ * kept. Errors: SSM_E_STATE if drafts are pending. */
+ssm_status ssm_restore(ssm_state *st, const int32_t *n_back, void *stream);
+
+/* Fork (explainer, "The State-Storage Bottleneck in Branching Workloads": beam search and
+ * best-of-n branch one prefix into several continuations): for k < n, sequence dst[k] becomes a
+ * copy of sequence src[k] -- its checkpoint tiles, read copy, buffered entries and pointers.
+ * src and dst are HOST arrays of n sequence indices in [0, batch); destinations must be distinct
+ * and none may also be a source in the same call (SSM_E_ARG otherwise). The checkpoint is copied,
+ * not shared: every copy folds into its own tiles. Errors: SSM_E_STATE if drafts are pending. */
+ssm_status ssm_fork(ssm_state *st, const int32_t *src, const int32_t *dst, int32_t n,
+                    void *stream);
+
 /* Checkpoint of every head in the natural layout, h_out device fp32 [batch][H][P][N]. Only the
  * folded tokens are in it: call ssm_flush(SSM_FLUSH_ALL) first to include the buffered ones. */
 ssm_status ssm_ckpt_export(const ssm_state *st, float *h_out, void *stream);

@@ -88,6 +88,8 @@ def _load() -> ctypes.CDLL:
         "ssm_conventional_spec_snapshot": ([P(ssm_config), vp, vp, i32, vp, vp, vp, vp, vp], st),
         "ssm_conventional_spec_select": ([P(ssm_config), vp, vp, i32, vp, vp], st),
         "ssm_debug_flags": ([P(ssm_state), P(ctypes.c_int32), i32, vp], st),
+        "ssm_restore": ([P(ssm_state), vp, vp], st),
+        "ssm_fork": ([P(ssm_state), P(ctypes.c_int32), P(ctypes.c_int32), i32, vp], st),
     }
     for name, (args, res) in sig.items():
         f = getattr(lib, name)
@@ -101,7 +103,7 @@ EXPORTS = ("ssm_abi_version", "ssm_status_string", "ssm_layout_query", "ssm_ckpt
            "ssm_replay_decode", "ssm_flush", "ssm_spec_append", "ssm_spec_rollback",
            "ssm_ckpt_export", "ssm_conventional_step", "ssm_tiles_pack", "ssm_tiles_unpack",
            "ssm_debug_codec", "ssm_conventional_spec_snapshot", "ssm_conventional_spec_select",
-           "ssm_debug_flags")
+           "ssm_debug_flags", "ssm_restore", "ssm_fork")
 
 
 def _st(st):
@@ -193,6 +195,25 @@ def ssm_spec_rollback(st: ssm_state, n_accept: torch.Tensor, stream=None) -> Non
     st = _st(st)
     _check("ssm_spec_rollback", _lib.ssm_spec_rollback(ctypes.byref(st), _ptr(n_accept),
                                                        _stream(stream)))
+
+
+def ssm_restore(st, n_back: torch.Tensor, stream=None) -> None:
+    if n_back.dtype != torch.int32:
+        raise ValueError("n_back must be int32")
+    st = _st(st)
+    _check("ssm_restore", _lib.ssm_restore(ctypes.byref(st), _ptr(n_back), _stream(stream)))
+
+
+def ssm_fork(st, src, dst, stream=None) -> None:
+    """src, dst: sequences of host ints (copied into host int32 arrays)."""
+    src, dst = list(src), list(dst)
+    if len(src) != len(dst):
+        raise ValueError("src and dst must have the same length")
+    n = len(src)
+    a = (ctypes.c_int32 * max(n, 1))(*src)
+    b = (ctypes.c_int32 * max(n, 1))(*dst)
+    st = _st(st)
+    _check("ssm_fork", _lib.ssm_fork(ctypes.byref(st), a, b, n, _stream(stream)))
 
 
 def ssm_ckpt_export(st: ssm_state, h_out: torch.Tensor, stream=None) -> None:

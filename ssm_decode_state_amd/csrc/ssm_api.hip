@@ -404,6 +404,80 @@ ssm_status ssm_spec_rollback(ssm_state* st, const int32_t* n_accept, void* strea
     return SSM_OK;
 }
 
+ssm_status ssm_restore(ssm_state* st, const int32_t* n_back, void* stream) {
+    ssm_status s = check_state(st);
+    if (s != SSM_OK) return s;
+    if (st->pending) return SSM_E_STATE;
+    if (!n_back) return SSM_E_ARG;
+    if (((uintptr_t)n_back & 3u) != 0) return SSM_E_ALIGN;
+    const hipError_t e = ssm::launch_restore(at<int>(st, st->lay.off_ptr), n_back, st->cfg.batch,
+                                             st->cfg.heads, as_stream(stream));
+    if (e != hipSuccess) return SSM_E_HIP;
+    st->count_lo = 0;  // the rewound counts are known only on the device
+    return SSM_OK;
+}
+
+ssm_status ssm_fork(ssm_state* st, const int32_t* src, const int32_t* dst, int32_t n, void* stream) {
+    ssm_status s = check_state(st);
+    if (s != SSM_OK) return s;
+    if (st->pending) return SSM_E_STATE;
+    if (n < 0 || (n > 0 && (!src || !dst))) return SSM_E_ARG;
+    const int B = st->cfg.batch;
+    for (int i = 0; i < n; ++i) {
+        if (src[i] < 0 || src[i] >= B || dst[i] < 0 || dst[i] >= B) return SSM_E_ARG;
+        for (int j = 0; j < n; ++j) {
+            if (j != i && dst[j] == dst[i]) return SSM_E_ARG;  // one source per destination
+            if (dst[i] == src[j]) return SSM_E_ARG;            // no chains within one call
+        }
+    }
+    if (n == 0) return SSM_OK;
+    // every region's per-sequence slice (the layout's regions are all [batch][...])
+    const ssm_config& c = st->cfg;
+    const ssm_layout& L = st->lay;
+    const uint64_t H = c.heads, G = c.groups, P = c.dim_p, N = c.dim_n, cap = L.ring_cap;
+    const uint64_t esz = c.in_dtype == SSM_IN_BF16 ? 2 : 4;
+    ssm::ForkRegions r;
+    memset(&r, 0, sizeof(r));
+    auto add = [&](uint64_t off, uint64_t slice) {
+        if (slice) { r.off[r.n] = off; r.slice[r.n] = slice; ++r.n; }
+    };
+    add(L.off_ckpt, H * P * N * 4);
+    if (c.readcopy == SSM_RC_FP8_ROW) {
+        add(L.off_rc_codes, H * P * N);
+        add(L.off_rc_scale, H * P * 4);
+    } else if (c.readcopy == SSM_RC_FP4_B16) {
+        add(L.off_rc_codes, H * P * N / 2);
+        add(L.off_rc_scale, H * P * (N / 16));
+        add(L.off_rc_tscale, H * 4);
+    }
+    if (c.kind == SSM_MAMBA2) {
+        add(L.off_ring[0], H * cap * P * esz);
+        add(L.off_ring[1], G * cap * N * esz);
+        add(L.off_ring[2], G * cap * N * esz);
+        add(L.off_ring[3], H * cap * 4);
+    } else {
+        add(L.off_ring[0], H * cap * N * esz);
+        add(L.off_ring[1], H * cap * N * esz);
+        add(L.off_ring[2], H * cap * P * esz);
+        add(L.off_ring[3], H * cap * 4);
+        add(L.off_ring[4], H * cap * (c.kind == SSM_KDA ? N : 1) * 4);
+    }
+    add(L.off_ptr, H * 2 * 4);
+    const hipStream_t hs = as_stream(stream);
+    for (int i0 = 0; i0 < n; i0 += ssm::kMaxForkPairs) {
+        ssm::ForkPairs p;
+        memset(&p, 0, sizeof(p));
+        p.n = n - i0 < ssm::kMaxForkPairs ? n - i0 : ssm::kMaxForkPairs;
+        for (int i = 0; i < p.n; ++i) {
+            p.src[i] = src[i0 + i];
+            p.dst[i] = dst[i0 + i];
+        }
+        const hipError_t e = ssm::launch_fork_copy(static_cast<char*>(st->mem), r, p, hs);
+        if (e != hipSuccess) return SSM_E_HIP;
+    }
+    return SSM_OK;  // the copies' counts are sources' counts: the host bounds still hold
+}
+
 ssm_status ssm_ckpt_export(const ssm_state* st, float* h_out, void* stream) {
     ssm_status s = check_state(st);
     if (s != SSM_OK) return s;

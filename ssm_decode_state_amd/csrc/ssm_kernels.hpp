@@ -99,6 +99,21 @@ hipError_t launch_snap_select(float* h, const float* snap, const int32_t* n_acce
 hipError_t launch_commit(int* ptr, const int32_t* n_accept, int batch, int heads, int pending,
                          int* flags, hipStream_t s);
 hipError_t launch_fill_i32(int* p, int value, long n, hipStream_t s);
+
+// Per-sequence slices of a state's regions, for copying whole sequences (fork).
+constexpr int kMaxForkRegions = 12, kMaxForkPairs = 64;
+struct ForkRegions {
+    uint64_t off[kMaxForkRegions];    // region byte offset in the state memory
+    uint64_t slice[kMaxForkRegions];  // bytes per sequence (a multiple of 4)
+    int n;
+};
+struct ForkPairs {
+    int src[kMaxForkPairs];
+    int dst[kMaxForkPairs];
+    int n;
+};
+hipError_t launch_fork_copy(char* mem, const ForkRegions& r, const ForkPairs& p, hipStream_t s);
+hipError_t launch_restore(int* ptr, const int32_t* n_back, int batch, int heads, hipStream_t s);
 // Natural [heads][P][N] -> quad-interleaved tiles (unpack = 0) or back (unpack = 1).
 hipError_t launch_pack(const float* src, float* dst, long nheads, int P, int N, int unpack,
                        hipStream_t s);

@@ -37,6 +37,41 @@ __global__ void snap_select_kernel(float* __restrict__ h, const float* __restric
         st_stream(ld_stream(src + i), dst + i);
 }
 
+// Rewind to an earlier position inside the buffered window (explainer, "What a Replay-First Design
+// Implies": restore state to position p): every head of sequence b drops its newest
+// min(n_back[b], count) committed entries (negative values count as 0). Pointers only: replay
+// rebuilds the output at any position between the checkpoint and the newest entry.
+__global__ void restore_kernel(int* ptr, const int32_t* __restrict__ n_back, int batch, int heads) {
+    const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= (long)batch * heads) return;
+    const int c = ptr[2 * i + 1];
+    int n = n_back[i / heads];
+    n = n < 0 ? 0 : (n > c ? c : n);
+    ptr[2 * i + 1] = c - n;
+}
+
+// Fork (explainer, "The State-Storage Bottleneck in Branching Workloads": one prefix, several
+// continuations): sequence dst[k] becomes a copy of sequence src[k] in every region of the state.
+// Grid (x blocks, pair, region); 16-byte copies where the slice allows, 4-byte otherwise.
+__global__ void fork_copy_kernel(char* __restrict__ mem, ForkRegions r, ForkPairs p) {
+    const int k = blockIdx.y, g = blockIdx.z;
+    if (k >= p.n || g >= r.n) return;
+    const uint64_t slice = r.slice[g];
+    const char* src = mem + r.off[g] + (uint64_t)p.src[k] * slice;
+    char* dst = mem + r.off[g] + (uint64_t)p.dst[k] * slice;
+    const uint64_t t0 = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const uint64_t step = (uint64_t)gridDim.x * blockDim.x;
+    if (slice % 16 == 0) {
+        const uint4* s4 = reinterpret_cast<const uint4*>(src);
+        uint4* d4 = reinterpret_cast<uint4*>(dst);
+        for (uint64_t i = t0; i < slice / 16; i += step) d4[i] = s4[i];
+    } else {
+        const uint32_t* s1 = reinterpret_cast<const uint32_t*>(src);
+        uint32_t* d1 = reinterpret_cast<uint32_t*>(dst);
+        for (uint64_t i = t0; i < slice / 4; i += step) d1[i] = s1[i];
+    }
+}
+
 __global__ void fill_i32_kernel(int* p, int value, long n) {
     const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
     if (i < n) p[i] = value;
@@ -122,6 +157,27 @@ hipError_t launch_snap_select(float* h, const float* snap, const int32_t* n_acce
     const unsigned bx = (unsigned)std::min<long>(blocks_for(nq, 256 * 8), 1024);
     hipLaunchKernelGGL(snap_select_kernel, dim3(bx, (unsigned)batch), dim3(256), 0, s, h, snap,
                        n_accept, batch, seq_floats, ndraft);
+    return hipGetLastError();
+}
+
+hipError_t launch_restore(int* ptr, const int32_t* n_back, int batch, int heads, hipStream_t s) {
+    const long n = (long)batch * heads;
+    if (n == 0) return hipSuccess;
+    hipLaunchKernelGGL(restore_kernel, dim3(blocks_for(n, 256)), dim3(256), 0, s, ptr, n_back,
+                       batch, heads);
+    return hipGetLastError();
+}
+
+hipError_t launch_fork_copy(char* mem, const ForkRegions& r, const ForkPairs& p, hipStream_t s) {
+    if (p.n == 0 || r.n == 0) return hipSuccess;
+    uint64_t most = 0;
+    for (int g = 0; g < r.n; ++g) {
+        if (r.slice[g] % 4 != 0 || r.off[g] % 16 != 0) return hipErrorInvalidValue;
+        most = r.slice[g] > most ? r.slice[g] : most;
+    }
+    const unsigned bx = (unsigned)std::max<uint64_t>(1, std::min<uint64_t>((most / 16 + 255) / 256, 64));
+    hipLaunchKernelGGL(fork_copy_kernel, dim3(bx, (unsigned)p.n, (unsigned)r.n), dim3(256), 0, s,
+                       mem, r, p);
     return hipGetLastError();
 }
 

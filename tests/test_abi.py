@@ -268,3 +268,34 @@ def test_debug_flags_validation():
                None) == bd.SSM_E_STATE
     st = empty_state()
     assert raw("ssm_debug_flags", ctypes.byref(st), None, 0, None) == bd.SSM_E_ARG
+
+
+def test_restore_and_fork_validation():
+    v = ctypes.c_void_p
+    I = lambda *xs: (ctypes.c_int32 * max(len(xs), 1))(*xs)
+    assert raw("ssm_restore", ctypes.byref(bd.ssm_state()), v(FAKE), None) == bd.SSM_E_STATE
+    assert raw("ssm_fork", ctypes.byref(bd.ssm_state()), I(0), I(1), 1, None) == bd.SSM_E_STATE
+    st = empty_state(max_draft=4)
+    assert raw("ssm_restore", ctypes.byref(st), None, None) == bd.SSM_E_ARG
+    assert raw("ssm_restore", ctypes.byref(st), v(FAKE + 2), None) == bd.SSM_E_ALIGN
+    for _ in range(3):
+        assert raw("ssm_replay_decode", ctypes.byref(st), ctypes.byref(m2_in()), v(FAKE),
+                   None) == bd.SSM_OK
+    assert (st.count_lo, st.count_hi) == (3, 3)
+    assert raw("ssm_restore", ctypes.byref(st), v(FAKE), None) == bd.SSM_OK  # empty batch
+    assert (st.count_lo, st.count_hi) == (0, 3)  # device counts now unknown below the old bound
+    assert raw("ssm_fork", ctypes.byref(st), I(), I(), 0, None) == bd.SSM_OK
+    assert raw("ssm_fork", ctypes.byref(st), I(), I(), -1, None) == bd.SSM_E_ARG
+    assert raw("ssm_fork", ctypes.byref(st), None, None, 1, None) == bd.SSM_E_ARG
+    assert raw("ssm_fork", ctypes.byref(st), I(0), I(0), 1, None) == bd.SSM_E_ARG  # batch is 0
+    # index checks on a batch of 4 (each case fails before any launch)
+    st.cfg.batch = 4
+    assert raw("ssm_fork", ctypes.byref(st), I(0, 1), I(2, 2), 2, None) == bd.SSM_E_ARG
+    assert raw("ssm_fork", ctypes.byref(st), I(0, 2), I(2, 3), 2, None) == bd.SSM_E_ARG  # chain
+    assert raw("ssm_fork", ctypes.byref(st), I(0), I(4), 1, None) == bd.SSM_E_ARG
+    assert raw("ssm_fork", ctypes.byref(st), I(-1), I(1), 1, None) == bd.SSM_E_ARG
+    st.cfg.batch = 0
+    assert raw("ssm_spec_append", ctypes.byref(st), 2, ctypes.byref(m2_in()), v(FAKE),
+               None) == bd.SSM_OK
+    assert raw("ssm_restore", ctypes.byref(st), v(FAKE), None) == bd.SSM_E_STATE
+    assert raw("ssm_fork", ctypes.byref(st), I(), I(), 0, None) == bd.SSM_E_STATE

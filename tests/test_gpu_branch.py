@@ -1,0 +1,255 @@
+"""GPU parity of branching: restore to an earlier position and fork one sequence into others.
+
+Each case keeps, per sequence, the token stream the state should now hold (a host simulation of
+the window counts decides which entries a restore can drop), runs the fp64 oracle on exactly that
+stream and compares every later replay output and the final state. A fork is also checked bit for
+bit: right after it the destination's bytes equal the source's in every region, untouched
+sequences keep theirs, and a copy fed the source's inputs reproduces the source's outputs.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from harness import assert_close, sample_pairs, to_dev
+from ssm_decode_state_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():
+    pytest.skip("needs a GPU", allow_module_level=True)
+bd = pytest.importorskip("ssm_decode_state_amd.binding")
+DEV = torch.device("cuda:0")
+
+GDN_KEYS = ("q", "k", "v", "beta", "g")
+
+
+class Branches:
+    """One state on the GPU plus the host record of what each sequence holds."""
+
+    def __init__(self, shape, seed, h0_std, rc=0, scale=1.0):
+        self.shape, self.seed, self.scale = shape, seed, scale
+        self.m2 = shape.kind == synth.MAMBA2
+        self.A, self.D = synth.head_constants(shape, seed)
+        self.h0 = synth.initial_state(shape, seed, h0_std) if h0_std else None
+        cfg = bd.make_config(shape.kind, shape.batch, shape.heads, shape.groups, shape.dim_p,
+                             shape.dim_n, shape.window, shape.max_draft,
+                             bd.SSM_IN_BF16 if shape.in_bf16 else bd.SSM_IN_F32, rc, scale)
+        self.st = bd.State(cfg, None if self.h0 is None else self.h0.to(DEV),
+                           None if self.A is None else self.A.to(DEV),
+                           None if self.D is None else self.D.to(DEV))
+        self.steps = []
+        self.stream = [[] for _ in range(shape.batch)]  # (step, batch row) of every held entry
+        self.count = [0] * shape.batch                   # entries since the last fold
+        self.origin = list(range(shape.batch))            # whose initial state a sequence holds
+        self.got = {}                                     # (b, h) -> [(stream position, y)]
+        self.y = torch.empty(shape.batch, shape.heads, shape.dim_p, device=DEV)
+
+    def decode(self, pairs, inputs=None):
+        t = len(self.steps)
+        d = inputs if inputs is not None else synth.token_inputs(self.shape, self.seed, "branch", t)
+        self.steps.append(d)
+        bd.ssm_replay_decode(self.st, to_dev(d, DEV), self.y)
+        for b in range(self.shape.batch):
+            self.stream[b].append((t, b))
+            self.count[b] += 1
+            if self.count[b] == self.shape.window:
+                self.count[b] = 0
+        if pairs:
+            bi = torch.tensor([b for (b, _) in pairs], device=DEV)
+            hi = torch.tensor([h for (_, h) in pairs], device=DEV)
+            ys = self.y[bi, hi].cpu().double().numpy()
+            for i, (b, h) in enumerate(pairs):
+                self.got.setdefault((b, h), []).append((len(self.stream[b]) - 1, ys[i]))
+
+    def restore(self, n_back):
+        bd.ssm_restore(self.st, torch.tensor(n_back, dtype=torch.int32, device=DEV))
+        for b, n in enumerate(n_back):
+            n = max(0, min(n, self.count[b]))
+            if n:
+                del self.stream[b][-n:]
+            self.count[b] -= n
+            keep = len(self.stream[b])  # outputs of dropped positions belong to the old stream
+            for key in [k for k in self.got if k[0] == b]:
+                self.got[key] = [(p, y) for (p, y) in self.got[key] if p < keep]
+
+    def fork(self, src, dst):
+        bd.ssm_fork(self.st, src, dst)
+        for s, d in zip(src, dst):
+            self.stream[d] = list(self.stream[s])
+            self.count[d] = self.count[s]
+            self.origin[d] = self.origin[s]
+            for key in [k for k in self.got if k[0] == d]:
+                del self.got[key]  # outputs from before the fork belong to the old stream
+
+    def oracle_pair(self, b, h):
+        """fp64 outputs over the stream sequence b holds, and its final state, for head h."""
+        sh = self.shape
+        hg = h // (sh.heads // sh.groups)
+        ent, o = self.stream[b], self.origin[b]
+
+        def col(key, hh):
+            return synth.to_f64(torch.stack([self.steps[t][key][r, 0, hh] for (t, r) in ent]))[None]
+
+        if self.m2:
+            h0 = None if self.h0 is None else self.h0[o, h].double().numpy()[None]
+            y, hT, _ = oracle.m2_sequential(self.A.double().numpy()[[h]],
+                                            self.D.double().numpy()[[h]], h0, col("x", h),
+                                            col("B", hg), col("C", hg), col("dt", h))
+        else:
+            S0 = None if self.h0 is None else self.h0[o, h].double().numpy()[None]
+            fn = oracle.kda_sequential if sh.kind == synth.KDA else oracle.gdn_sequential
+            y, hT, _ = fn(S0, *[col(k, h) for k in GDN_KEYS], scale=self.scale)
+        return y[0], hT[0]
+
+    def check(self, pairs, what):
+        bd.ssm_flush(self.st, bd.SSM_FLUSH_ALL)
+        sh = self.shape
+        nat = torch.empty(sh.batch, sh.heads, sh.dim_p, sh.dim_n, device=DEV)
+        bd.ssm_ckpt_export(self.st, nat)
+        torch.cuda.synchronize()
+        for (b, h) in pairs:
+            oy, oT = self.oracle_pair(b, h)
+            rec = self.got.get((b, h), [])
+            if rec:
+                gy = np.stack([y for (_, y) in rec])
+                assert_close(gy, oy[[p for (p, _) in rec]], (-1,), "%s outputs (%d, %d)" % (what, b, h))
+            assert_close(nat[b, h].cpu().double().numpy(), oT, (-2, -1),
+                         "%s final state (%d, %d)" % (what, b, h))
+
+
+def _shape(kind, B, H, L=8, bf16=True):
+    if kind == synth.MAMBA2:
+        return synth.Shape(kind, B, H, 1, 64, 128, L, 1, in_bf16=bf16)
+    return synth.Shape(kind, B, H, H, 128, 64, L, 1, in_bf16=bf16)
+
+
+KINDS = [synth.MAMBA2, synth.GDN, synth.KDA]
+
+
+@pytest.mark.parametrize("kind", KINDS)
+def test_restore_then_decode(kind):
+    B, H = 5, 2
+    br = Branches(_shape(kind, B, H), 300 + kind, 0.3, scale=0.7 if kind else 1.0)
+    pairs = [(b, h) for b in range(B) for h in range(H)]
+    for _ in range(13):  # one fold, then five entries buffered
+        br.decode(pairs)
+    br.restore([2, 0, 9, -3, 5])  # 9 is clamped to the five buffered entries
+    for _ in range(6):
+        br.decode(pairs)
+    br.restore([1, 3, 0, 7, 2])
+    br.restore([1, 0, 0, 0, 0])  # two restores in a row
+    for _ in range(9):  # every sequence folds again
+        br.decode(pairs)
+    br.check(pairs, "restore")
+
+
+def test_restore_after_fold_drops_nothing():
+    br = Branches(_shape(synth.MAMBA2, 2, 2, L=4), 311, 0.3)
+    pairs = [(0, 0), (1, 1)]
+    for _ in range(8):  # both windows just folded
+        br.decode(pairs)
+    br.restore([4, 1])
+    for _ in range(3):
+        br.decode(pairs)
+    br.check(pairs, "restore after a fold")
+
+
+@pytest.mark.parametrize("kind", KINDS)
+def test_fork_then_decode(kind):
+    B, H = 6, 2
+    br = Branches(_shape(kind, B, H), 320 + kind, 0.3)
+    pairs = [(b, h) for b in range(B) for h in range(H)]
+    for _ in range(11):
+        br.decode(pairs)
+    br.fork([0, 0, 1], [3, 4, 5])  # one prefix into two continuations, and a plain copy
+    for _ in range(10):
+        br.decode(pairs)
+    br.restore([0, 2, 0, 1, 3, 0])  # a restore on forked sequences
+    for _ in range(4):
+        br.decode(pairs)
+    br.check(pairs, "fork")
+
+
+def _seq_regions(st):
+    """(offset, bytes per sequence) of every region of the state, batch outermost."""
+    c, L = st.cfg, st.layout
+    H, G, P, N, cap = c.heads, c.groups, c.dim_p, c.dim_n, L.ring_cap
+    e = 2 if c.in_dtype == bd.SSM_IN_BF16 else 4
+    r = [(L.off_ckpt, H * P * N * 4)]
+    if c.readcopy == bd.SSM_RC_FP8_ROW:
+        r += [(L.off_rc_codes, H * P * N), (L.off_rc_scale, H * P * 4)]
+    elif c.readcopy == bd.SSM_RC_FP4_B16:
+        r += [(L.off_rc_codes, H * P * N // 2), (L.off_rc_scale, H * P * (N // 16)),
+              (L.off_rc_tscale, H * 4)]
+    if c.kind == bd.SSM_MAMBA2:
+        r += [(L.off_ring[0], H * cap * P * e), (L.off_ring[1], G * cap * N * e),
+              (L.off_ring[2], G * cap * N * e), (L.off_ring[3], H * cap * 4)]
+    else:
+        r += [(L.off_ring[0], H * cap * N * e), (L.off_ring[1], H * cap * N * e),
+              (L.off_ring[2], H * cap * P * e), (L.off_ring[3], H * cap * 4),
+              (L.off_ring[4], H * cap * (N if c.kind == bd.SSM_KDA else 1) * 4)]
+    r.append((L.off_ptr, H * 8))
+    return r
+
+
+def _rows(st, off, slice_):
+    return st.region(off, st.cfg.batch * slice_).view(st.cfg.batch, slice_)
+
+
+def _same_inputs(d, src, dst):
+    d = {k: v.clone() for k, v in d.items()}
+    for s, t in zip(src, dst):
+        for v in d.values():
+            v[t] = v[s]
+    return d
+
+
+@pytest.mark.parametrize("name,rc", [("m2_b256", bd.SSM_RC_NONE), ("m2_b256_readcopy", bd.SSM_RC_FP8_ROW),
+                                     ("m2_b256_readcopy", bd.SSM_RC_FP4_B16),
+                                     ("gdn_b256", bd.SSM_RC_FP8_ROW), ("kda_b256", bd.SSM_RC_NONE)])
+def test_fork_serving_batch_bit_exact(name, rc):
+    w = synth.WORKLOADS[name]
+    sh = w["shape"]
+    br = Branches(sh, w["seed"], w["h0_std"], rc=rc)
+    for _ in range(21):  # a fold, then five buffered entries
+        br.decode(None)
+    src = list(range(0, 160, 2))           # 80 pairs: more than one launch of the copy
+    dst = [s + 1 for s in src]
+    before = br.st.mem.clone()
+    br.fork(src, dst)
+    torch.cuda.synchronize()
+    si, di = torch.tensor(src, device=DEV), torch.tensor(dst, device=DEV)
+    keep = torch.ones(sh.batch, dtype=torch.bool, device=DEV)
+    keep[di] = False
+    for (off, sl) in _seq_regions(br.st):
+        now, old = _rows(br.st, off, sl), before[off:off + sh.batch * sl].view(sh.batch, sl)
+        assert torch.equal(now[di], now[si]), "region at %d differs after the fork" % off
+        assert torch.equal(now[keep], old[keep]), "region at %d changed outside the copies" % off
+    del before
+    ys = []
+    for t in range(13):  # across the next fold
+        d = _same_inputs(synth.token_inputs(sh, w["seed"], "branch", 100 + t), src, dst)
+        br.decode(None, d)
+        ys.append(br.y.clone())
+    for t, y in enumerate(ys):
+        assert torch.equal(y[di], y[si]), "step %d: a copy's outputs differ from its source" % t
+    bd.ssm_flush(br.st, bd.SSM_FLUSH_ALL)
+    torch.cuda.synchronize()
+    ck = _rows(br.st, *_seq_regions(br.st)[0])
+    assert torch.equal(ck[di], ck[si])
+
+
+@pytest.mark.parametrize("name", ["m2_b256", "gdn_b256", "kda_b256"])
+def test_restore_serving_batch_sampled(name):
+    w = synth.WORKLOADS[name]
+    sh = w["shape"]
+    br = Branches(sh, w["seed"], w["h0_std"])
+    pairs = sample_pairs(sh.batch, sh.heads, 12)
+    for _ in range(20):
+        br.decode(pairs)
+    rng = np.random.default_rng(7)
+    br.restore([int(v) for v in rng.integers(-2, 7, size=sh.batch)])
+    for _ in range(14):
+        br.decode(pairs)
+    br.check(pairs, name + " restore")
