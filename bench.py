@@ -269,6 +269,55 @@ def bench_lsweep(dev, steps=96, warm=32):
     return out
 
 
+def seq_state_bytes(cfg, lay):
+    """Bytes one sequence owns in every region of the state (what a fork copies)."""
+    H, G, P, N, cap = cfg.heads, cfg.groups, cfg.dim_p, cfg.dim_n, lay.ring_cap
+    e = 2 if cfg.in_dtype == 1 else 4
+    n = H * P * N * 4 + H * 8
+    if cfg.readcopy == 1:
+        n += H * P * N + H * P * 4
+    elif cfg.readcopy == 2:
+        n += H * P * N // 2 + H * P * (N // 16) + H * 4
+    if cfg.kind == 0:
+        n += H * cap * P * e + 2 * G * cap * N * e + H * cap * 4
+    else:
+        n += 2 * H * cap * N * e + H * cap * P * e + H * cap * 4
+        n += H * cap * (N if cfg.kind == 2 else 1) * 4
+    return n
+
+
+def bench_branch(dev, reps=20, pairs=64):
+    """Branching on the serving state: a fork of `pairs` sequences (every region copied, one
+    launch) and a restore of every sequence (pointer move)."""
+    import torch
+    from ssm_decode_state_amd import binding as bd
+    from ssm_decode_state_amd import synth
+    w = synth.WORKLOADS["m2_b256"]
+    shape = w["shape"]
+    Bn, H, P, N = shape.batch, shape.heads, shape.dim_p, shape.dim_n
+    A, D = synth.head_constants(shape, w["seed"])
+    h0 = synth.initial_state_device(shape, w["seed"], w["h0_std"])
+    cfg = bd.make_config(bd.SSM_MAMBA2, Bn, H, shape.groups, P, N, shape.window, 1, bd.SSM_IN_BF16)
+    st = bd.State(cfg, h0, A.to(dev), D.to(dev))
+    del h0
+    y = torch.empty(Bn, H, P, device=dev)
+    for i in range(21):  # a fold, then five buffered entries
+        bd.ssm_replay_decode(st, synth.token_inputs_device(shape, w["seed"], "bench-branch", i), y)
+    src = list(range(0, 2 * pairs, 2))
+    dst = [s + 1 for s in src]
+    bd.ssm_fork(st, src, dst)
+    _, ms = timed_calls(reps, lambda i: bd.ssm_fork(st, src, dst))
+    fork_us = sum(ms) / reps * 1e3
+    per_seq = seq_state_bytes(cfg, st.layout)
+    gbs = pairs * per_seq * 2 / (fork_us * 1e-6) / 1e9
+    zero = torch.zeros(Bn, dtype=torch.int32, device=dev)
+    bd.ssm_restore(st, zero)
+    _, ms = timed_calls(reps, lambda i: bd.ssm_restore(st, zero))
+    return {"workload": "mamba2_branch_b256", "fork_pairs": pairs, "bytes_per_sequence": per_seq,
+            "fork_avg_us": fork_us, "fork_achieved_gbs": gbs, "fork_frac": gbs / HBM_PEAK_GBS,
+            "restore_avg_us": sum(ms) / reps * 1e3}
+
+
 def bench_readcopy(dev, rc, steps=128, warm=16, layers=4, pool=16):
     """Decode with the fp8 or fp4 read copy on `layers` rotated layer instances (the fp4 copy of
     one layer fits the 256 MB last-level cache, so each step reads a different layer)."""
@@ -659,7 +708,8 @@ def main():
         out["copy_ref"] = {"bytes_read": 4 * n, "bytes_written": 4 * n, "launches": 5,
                            "avg_us": e0.elapsed_time(e1) / 5 * 1e3}
 
-    extra = ({"spec", "fp8", "fp4", "gdn", "gdn_spec", "gdn_fp8", "gdn_fp4", "kda", "g8", "lsweep"}
+    extra = ({"spec", "fp8", "fp4", "gdn", "gdn_spec", "gdn_fp8", "gdn_fp4", "kda", "g8", "lsweep",
+              "branch"}
              if args.workloads == "all" else
              set() if args.workloads == "none" else set(args.workloads.split(",")))
     if extra:
@@ -676,6 +726,9 @@ def main():
             r = bench_m2_decode(dev, dataclasses.replace(wg["shape"], groups=8), wg["seed"],
                                 wg["h0_std"], 128, 32)
             out["workloads"]["groups8"] = dict(workload="mamba2_replay_decode_b256_g8", **r)
+            torch.cuda.empty_cache()
+        if "branch" in extra:
+            out["workloads"]["branch"] = bench_branch(dev)
             torch.cuda.empty_cache()
         if "lsweep" in extra:
             out["workloads"]["window_sweep"] = bench_lsweep(dev)

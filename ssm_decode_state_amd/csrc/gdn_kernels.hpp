@@ -140,11 +140,14 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_replay_kernel(GdnArgs a) {
     }
 
     // ---- the checkpoint rows of this wave ------------------------------------------------------
-    float4 hv[kNQ];  // the fp32 rows (no read copy); with a read copy its codes are read later
+    float4 hv[kNQ];  // the fp32 rows (no read copy)
+    RcRow<DV, DK, RC> rc;  // or the read copy's row, issued at the same point (news, para 4)
     if constexpr (RC == 0) {
         const float4* tile = reinterpret_cast<const float4*>(a.ckpt) + (long)head * (DV * DK / 4);
 #pragma unroll
         for (int q = 0; q < kNQ; ++q) hv[q] = ld_stream(tile + q * DV + row);
+    } else {
+        rc.load(RcView{a.rc_codes, a.rc_scale, a.rc_tscale}, head, row);
     }
     asm volatile("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
@@ -284,8 +287,7 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_replay_kernel(GdnArgs a) {
     if constexpr (RC != 0) {  // the decoded copy's rows against every r_j (news, para 4)
 #pragma unroll
         for (int j = 0; j < MAXQ; ++j) dot[j] = 0.f;
-        rc_row_dots<DV, DK, kRS, MAXQ, RC>(RcView{a.rc_codes, a.rc_scale, a.rc_tscale}, head, row, nq,
-                                           &s_r[wave][0][0], dot);
+        rc.template dots<kRS, MAXQ>(nq, &s_r[wave][0][0], dot);
     } else if constexpr (MAXQ >= 4) {
         // four queries per 4x4x1 MFMA (lane = row; query 4g + lane%4 supplies its r column),
         // two accumulator chains per group of four

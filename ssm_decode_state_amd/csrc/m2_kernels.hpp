@@ -55,7 +55,9 @@ __global__ __launch_bounds__(256) void m2_replay_kernel(M2Args a) {
     constexpr int kEPC = 16 / (int)sizeof(TIN);          // elements per 16-byte chunk
     constexpr int kCPR = P / kEPC;                       // chunks per x row
     constexpr int kXL = (MAXE * kCPR + 63) / 64;         // x-row chunks per lane
-    constexpr int kBC = MAXE / 16;                       // 16-entry chunks of B segments
+    constexpr int kBCE = N / kEPC;                       // 16-byte chunks per B row
+    constexpr int kBL = (MAXE * kBCE + 63) / 64;         // B chunks per lane
+    static_assert(kBCE >= 2 && kBCE <= 64 && 64 % kBCE == 0, "B row chunks");
     constexpr int kCE = N >= 64 ? N / 64 : 1;            // C elements per lane
     static_assert(MAXE % 16 == 0 && MAXE <= 64, "MAXE");
     constexpr int kCS = N + 4;  // C row stride: the 4 rows an MFMA operand read takes hit distinct banks
@@ -108,30 +110,15 @@ __global__ __launch_bounds__(256) void m2_replay_kernel(M2Args a) {
                                      : a.in_dt + (tok0 + min(max(lane - count, 0), nq - 1)) * H + h;
     float dte = *dsrc;
     dte = lane < kmax ? dte : 0.f;
-    // B segments: lane (ei, sg) holds entry e = 16c + ei, elements [sg*kSeg, sg*kSeg + kSeg)
-    const int ei = lane & 15, sg = lane >> 4;
-    constexpr int kSW = G::kSeg * (int)sizeof(TIN) / 4;  // 32-bit words per segment
-    uint32_t braw[kBC][kSW];
+    // B rows of every entry in 16-byte chunks, chunk idx = lane + 64 i -> (entry idx / kBCE,
+    // part idx % kBCE): each load instruction covers whole rows, 1 KiB per ring run
+    u32x4_t braw[kBL];
 #pragma unroll
-    for (int c = 0; c < kBC; ++c) {
-        const int e = 16 * c + ei;
+    for (int i = 0; i < kBL; ++i) {
+        const int e = (lane + 64 * i) / kBCE, part = lane % kBCE;
         const TIN* src = e < count ? rB + ((long)bg * cap + ring_slot(start, min(e, cap - 1), cap)) * N
                                    : inB + ((tok0 + min(max(e - count, 0), nq - 1)) * Gn + grp) * N;
-        const uint32_t* w = reinterpret_cast<const uint32_t*>(src + sg * G::kSeg);
-        if constexpr (kSW % 4 == 0) {
-#pragma unroll
-            for (int u = 0; u < kSW / 4; ++u) {
-                const u32x4_t t = reinterpret_cast<const u32x4_t*>(w)[u];
-                braw[c][4 * u] = t.x; braw[c][4 * u + 1] = t.y;
-                braw[c][4 * u + 2] = t.z; braw[c][4 * u + 3] = t.w;
-            }
-        } else {
-#pragma unroll
-            for (int u = 0; u < kSW / 2; ++u) {
-                const uint2 t = reinterpret_cast<const uint2*>(w)[u];
-                braw[c][2 * u] = t.x; braw[c][2 * u + 1] = t.y;
-            }
-        }
+        braw[i] = *reinterpret_cast<const u32x4_t*>(src + part * kEPC);
     }
     // x rows of every entry, in 16-byte chunks: chunk idx -> (row e = idx / kCPR, part idx % kCPR)
     u32x4_t xraw[kXL];
@@ -179,22 +166,11 @@ __global__ __launch_bounds__(256) void m2_replay_kernel(M2Args a) {
     if (lane >= count && lane < kmax) a.ring_dt[head * cap + ring_slot(start, lane, cap)] = dte;
     if (h % hpg == 0) {  // the group's first head writes the shared B and C entries
 #pragma unroll
-        for (int c = 0; c < kBC; ++c) {
-            const int e = 16 * c + ei;
-            if (e >= count && e < kmax) {
-                uint32_t* w = reinterpret_cast<uint32_t*>(rB + ((long)bg * cap + ring_slot(start, e, cap)) * N +
-                                                          sg * G::kSeg);
-                if constexpr (kSW % 4 == 0) {
-#pragma unroll
-                    for (int u = 0; u < kSW / 4; ++u)
-                        reinterpret_cast<u32x4_t*>(w)[u] = u32x4_t{braw[c][4 * u], braw[c][4 * u + 1],
-                                                                   braw[c][4 * u + 2], braw[c][4 * u + 3]};
-                } else {
-#pragma unroll
-                    for (int u = 0; u < kSW / 2; ++u)
-                        reinterpret_cast<uint2*>(w)[u] = make_uint2(braw[c][2 * u], braw[c][2 * u + 1]);
-                }
-            }
+        for (int i = 0; i < kBL; ++i) {
+            const int e = (lane + 64 * i) / kBCE, part = lane % kBCE;
+            if (e >= count && e < kmax)
+                *reinterpret_cast<u32x4_t*>(rB + ((long)bg * cap + ring_slot(start, e, cap)) * N + part * kEPC) =
+                    braw[i];
         }
 #pragma unroll
         for (int j = 0; j < MAXQ; ++j) {
@@ -225,33 +201,24 @@ __global__ __launch_bounds__(256) void m2_replay_kernel(M2Args a) {
         s0[j] = j < nq ? expf(A * tot[j]) : 0.f;
     }
 #pragma unroll
-    for (int c = 0; c < kBC; ++c) {
-        const int e = 16 * c + ei;
-        if (16 * c >= kmax) break;
-        float bf[G::kSeg];
-        if constexpr (sizeof(TIN) == 2) {
-#pragma unroll
-            for (int u = 0; u < kSW; ++u) {
-                bf[2 * u] = __uint_as_float(braw[c][u] << 16);
-                bf[2 * u + 1] = __uint_as_float(braw[c][u] & 0xffff0000u);
-            }
-        } else {
-#pragma unroll
-            for (int u = 0; u < kSW; ++u) bf[u] = __uint_as_float(braw[c][u]);
-        }
+    for (int i = 0; i < kBL; ++i) {
+        if (i * (64 / kBCE) >= kmax) continue;  // uniform: no entry of this chunk is in use
+        const int e = (lane + 64 * i) / kBCE, part = lane % kBCE;
+        float bf[kEPC];
+        Unit<TIN>::unpack(make_uint4(braw[i].x, braw[i].y, braw[i].z, braw[i].w), bf);
         const float dt_e = __shfl(dte, e & 63, 64);
         const float pre_e = __shfl(pre, e & 63, 64);
 #pragma unroll
         for (int j = 0; j < MAXQ; ++j) {
             if (j >= nq) break;
-            const float* cj = &s_c[wave][j][sg * G::kSeg];
+            const float* cj = &s_c[wave][j][part * kEPC];
             float d = 0.f;
 #pragma unroll
-            for (int i = 0; i < G::kSeg; ++i) d += bf[i] * cj[i];
-            d = xor_reduce_sum<16, 32>(d);
+            for (int t = 0; t < kEPC; ++t) d += bf[t] * cj[t];
+            d = group_sum<kBCE>(d);
             // sum of dt over entries e+1 .. kq-1 with kq = count + j + 1
             const float w = (e <= count + j) ? expf(A * (tot[j] - pre_e)) * dt_e * d : 0.f;
-            if (sg == 0) s_w[wave][e][j] = w;
+            if (part == 0 && e < MAXE) s_w[wave][e][j] = w;
         }
     }
     wave_sync();
@@ -308,8 +275,9 @@ __global__ __launch_bounds__(256) void m2_replay_kernel(M2Args a) {
             }
         }
     } else {
-        rc_row_dots<P, N, kCS, MAXQ, RC>(RcView{a.rc_codes, a.rc_scale, a.rc_tscale}, head, row, nq,
-                                         &s_c[wave][0][0], acc);
+        RcRow<P, N, RC> rc;  // the read copy's row (news, para 4: reads from the copy)
+        rc.load(RcView{a.rc_codes, a.rc_scale, a.rc_tscale}, head, row);
+        rc.template dots<kCS, MAXQ>(nq, &s_c[wave][0][0], acc);
     }
     if constexpr (G::kGrp > 1) {
 #pragma unroll

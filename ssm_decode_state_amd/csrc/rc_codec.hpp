@@ -22,79 +22,99 @@ struct RcView {
     float* tscale;  // fp4: fp32 tile scales
 };
 
-// Row dot products of the decoded copy's row `row` with MAXQ query vectors (s_q, row stride CS),
-// accumulated into acc[j] for j < nq. The lane owning row `row` reads its whole row.
-template <int ROWS, int N, int CS, int MAXQ, int RC>
-__device__ __forceinline__ void rc_row_dots(const RcView& v, long head, int row, int nq,
-                                            const float* s_q, float (&acc)[MAXQ]) {
+// One row of the decoded copy, held by the lane that owns the row. load() only issues the reads
+// (so a kernel can put them in flight next to its other early loads); dots() waits for them,
+// decodes, and accumulates the row's dot products with MAXQ query vectors (s_q, row stride CS)
+// into acc[j] for j < nq.
+template <int ROWS, int N, int RC>
+struct RcRow {
     static_assert(N == 64 || N == 128, "read copy: N in {64, 128}");
-    if constexpr (RC == 1) {
-        const u32x4_t* codes = reinterpret_cast<const u32x4_t*>(v.codes + head * (long)(ROWS * N));
-        u32x4_t u[N / 16];
+    static_assert(RC == 1 || RC == 2, "read copy kind");
+    static constexpr int kU = RC == 1 ? N / 16 : N / 32;  // 16-byte code units per row
+    static constexpr int kSB = RC == 1 ? 1 : (N / 16 + 3) / 4;  // scale words
+    u32x4_t u[kU];
+    uint32_t sbw[kSB];  // fp8: the fp32 row scale's bits; fp4: the row's E4M3 block-scale codes
+    float st;           // fp4 tile scale
+
+    __device__ __forceinline__ void load(const RcView& v, long head, int row) {
+        const u32x4_t* codes = reinterpret_cast<const u32x4_t*>(
+            v.codes + head * (long)(RC == 1 ? ROWS * N : ROWS * N / 2));
 #pragma unroll
-        for (int k = 0; k < N / 16; ++k) u[k] = __builtin_nontemporal_load(codes + k * ROWS + row);
-        const float s = static_cast<const float*>(v.scale)[head * ROWS + row];
-#pragma unroll
-        for (int k = 0; k < N / 16; ++k) {
-            const uint32_t w[4] = {u[k].x, u[k].y, u[k].z, u[k].w};
-            float val[16];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                float o[4];
-                e4m3_word_decode(w[q], o);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) val[4 * q + i] = o[i];
-            }
-#pragma unroll
-            for (int j = 0; j < MAXQ; ++j) {
-                if (j >= nq) break;
-                float d = 0.f;
-#pragma unroll
-                for (int i = 0; i < 16; ++i) d += val[i] * s_q[j * CS + 16 * k + i];
-                acc[j] += s * d;
-            }
-        }
-    } else {
-        const u32x4_t* codes = reinterpret_cast<const u32x4_t*>(v.codes + head * (long)(ROWS * N / 2));
-        u32x4_t u[N / 32];
-#pragma unroll
-        for (int k = 0; k < N / 32; ++k) u[k] = __builtin_nontemporal_load(codes + k * ROWS + row);
-        const uint8_t* sbp = static_cast<const uint8_t*>(v.scale) + (head * ROWS + row) * (N / 16);
-        uint32_t sbw[(N / 16 + 3) / 4];
-        if constexpr (N / 16 >= 8) {
-            const uint2 t = *reinterpret_cast<const uint2*>(sbp);
-            sbw[0] = t.x; sbw[1] = t.y;
+        for (int k = 0; k < kU; ++k) u[k] = __builtin_nontemporal_load(codes + k * ROWS + row);
+        if constexpr (RC == 1) {
+            sbw[0] = static_cast<const uint32_t*>(v.scale)[head * ROWS + row];
+            st = 1.f;
         } else {
-            sbw[0] = *reinterpret_cast<const uint32_t*>(sbp);
+            const uint8_t* sbp = static_cast<const uint8_t*>(v.scale) + (head * ROWS + row) * (N / 16);
+            if constexpr (N / 16 >= 8) {
+                const uint2 t = *reinterpret_cast<const uint2*>(sbp);
+                sbw[0] = t.x; sbw[1] = t.y;
+            } else {
+                sbw[0] = *reinterpret_cast<const uint32_t*>(sbp);
+            }
+            st = v.tscale[head];
         }
-        const float st = v.tscale[head];
+    }
+
+    template <int CS, int MAXQ>
+    __device__ __forceinline__ void dots(int nq, const float* s_q, float (&acc)[MAXQ]) const {
+        if constexpr (RC == 1) {
+            const float s = __uint_as_float(sbw[0]);
 #pragma unroll
-        for (int k = 0; k < N / 32; ++k) {
-            const uint32_t w[4] = {u[k].x, u[k].y, u[k].z, u[k].w};
+            for (int k = 0; k < kU; ++k) {
+                const uint32_t w[4] = {u[k].x, u[k].y, u[k].z, u[k].w};
+                float val[16];
 #pragma unroll
-            for (int half = 0; half < 2; ++half) {
-                const int blk = 2 * k + half;
-                const float S = e4m3_decode((sbw[blk / 4] >> (8 * (blk % 4))) & 0xff) * st;
-                float val[16];  // elements 16 half .. 16 half + 15 of the 32-element unit
+                for (int q = 0; q < 4; ++q) {
+                    float o[4];
+                    e4m3_word_decode(w[q], o);
 #pragma unroll
-                for (int q = 0; q < 2; ++q) {
-                    float o[8];
-                    e2m1_word_decode(w[2 * half + q], o);
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) val[8 * q + i] = o[i];
+                    for (int i = 0; i < 4; ++i) val[4 * q + i] = o[i];
                 }
 #pragma unroll
                 for (int j = 0; j < MAXQ; ++j) {
                     if (j >= nq) break;
                     float d = 0.f;
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) d += val[i] * s_q[j * CS + 16 * blk + i];
-                    acc[j] += S * d;
+                    for (int i = 0; i < 16; ++i) d += val[i] * s_q[j * CS + 16 * k + i];
+                    acc[j] += s * d;
+                }
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < kU; ++k) {
+                const uint32_t w[4] = {u[k].x, u[k].y, u[k].z, u[k].w};
+#pragma unroll
+                for (int half = 0; half < 2; ++half) {
+                    const int blk = 2 * k + half;
+                    const float S = e4m3_decode((sbw[blk / 4] >> (8 * (blk % 4))) & 0xff) * st;
+                    float val[16];  // elements 16 half .. 16 half + 15 of the 32-element unit
+#pragma unroll
+                    for (int q = 0; q < 2; ++q) {
+                        float o[8];
+                        e2m1_word_decode(w[2 * half + q], o);
+#pragma unroll
+                        for (int i = 0; i < 8; ++i) val[8 * q + i] = o[i];
+                    }
+#pragma unroll
+                    for (int j = 0; j < MAXQ; ++j) {
+                        if (j >= nq) break;
+                        float d = 0.f;
+#pragma unroll
+                        for (int i = 0; i < 16; ++i) d += val[i] * s_q[j * CS + 16 * blk + i];
+                        acc[j] += S * d;
+                    }
                 }
             }
         }
     }
-}
+};
+
+// No read copy: nothing to hold (the kernels read the fp32 tile instead).
+template <int ROWS, int N>
+struct RcRow<ROWS, N, 0> {
+    __device__ __forceinline__ void load(const RcView&, long, int) {}
+};
 
 // Largest magnitude among this lane's values of a tile held in MFMA accumulator order (hb[pb][nb]
 // holds row row0 + 16 pb + l%16, columns 16 nb + 4 (l/16) .. + 3). The caller reduces it over the

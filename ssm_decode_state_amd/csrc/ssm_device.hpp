@@ -217,6 +217,24 @@ __device__ __forceinline__ float xor_reduce_max(float v) {
     }
 }
 
+// Sum over aligned groups of GS lanes (GS a power of two up to 64), left in every lane of the
+// group. Quad steps by DPP quad_perm; then, with every quad (half row) holding its sum, the
+// half-row and row mirrors (lane i <-> 7 - i, 15 - i) pair each half with the other; rows by
+// permlane16/32 swaps.
+template <int GS>
+__device__ __forceinline__ float group_sum(float v) {
+    static_assert(GS >= 1 && GS <= 64 && (GS & (GS - 1)) == 0, "group size");
+    if constexpr (GS >= 2) { float a, b; XorPair<1>::get(v, a, b); v = a + b; }
+    if constexpr (GS >= 4) { float a, b; XorPair<2>::get(v, a, b); v = a + b; }
+    if constexpr (GS >= 8)
+        v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));
+    if constexpr (GS >= 16)
+        v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false));
+    if constexpr (GS >= 32) { float a, b; XorPair<16>::get(v, a, b); v = a + b; }
+    if constexpr (GS >= 64) { float a, b; XorPair<32>::get(v, a, b); v = a + b; }
+    return v;
+}
+
 // Value of v in lane `lane`. The index MUST be wave-uniform: a per-lane index is silently
 // replaced by the first active lane's (v_readlane takes a scalar lane select). Use __shfl for
 // per-lane indices.

@@ -62,9 +62,19 @@ __global__ void fork_copy_kernel(char* __restrict__ mem, ForkRegions r, ForkPair
     const uint64_t t0 = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const uint64_t step = (uint64_t)gridDim.x * blockDim.x;
     if (slice % 16 == 0) {
-        const uint4* s4 = reinterpret_cast<const uint4*>(src);
-        uint4* d4 = reinterpret_cast<uint4*>(dst);
-        for (uint64_t i = t0; i < slice / 16; i += step) d4[i] = s4[i];
+        // four independent 16-byte loads in flight per thread before their stores
+        const u32x4_t* s4 = reinterpret_cast<const u32x4_t*>(src);
+        u32x4_t* d4 = reinterpret_cast<u32x4_t*>(dst);
+        const uint64_t n = slice / 16;
+        for (uint64_t i = t0; i < n; i += 4 * step) {
+            u32x4_t v[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                if (i + u * step < n) v[u] = __builtin_nontemporal_load(s4 + i + u * step);
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                if (i + u * step < n) __builtin_nontemporal_store(v[u], d4 + i + u * step);
+        }
     } else {
         const uint32_t* s1 = reinterpret_cast<const uint32_t*>(src);
         uint32_t* d1 = reinterpret_cast<uint32_t*>(dst);
@@ -175,7 +185,7 @@ hipError_t launch_fork_copy(char* mem, const ForkRegions& r, const ForkPairs& p,
         if (r.slice[g] % 4 != 0 || r.off[g] % 16 != 0) return hipErrorInvalidValue;
         most = r.slice[g] > most ? r.slice[g] : most;
     }
-    const unsigned bx = (unsigned)std::max<uint64_t>(1, std::min<uint64_t>((most / 16 + 255) / 256, 64));
+    const unsigned bx = (unsigned)std::max<uint64_t>(1, std::min<uint64_t>((most / 64 + 255) / 256, 64));
     hipLaunchKernelGGL(fork_copy_kernel, dim3(bx, (unsigned)p.n, (unsigned)r.n), dim3(256), 0, s,
                        mem, r, p);
     return hipGetLastError();
