@@ -576,8 +576,8 @@ def main():
                     help="also run a plain copy of this many MiB (reference for HBM counters)")
     ap.add_argument("--workloads", default="all",
                     help="comma list of extra workloads: spec, fp8, fp4, gdn, gdn_spec, "
-                         "gdn_fp8, gdn_fp4, kda, g8 (8 B/C groups), lsweep (window 4..32); 'all' "
-                         "or 'none'")
+                         "gdn_fp8, gdn_fp4, kda, g8 (8 B/C groups), lsweep (window 4..32), "
+                         "branch (fork and restore); 'all' or 'none'")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
