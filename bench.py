@@ -270,14 +270,17 @@ def bench_lsweep(dev, steps=96, warm=32):
 
 
 def seq_state_bytes(cfg, lay):
-    """Bytes one sequence owns in every region of the state (what a fork copies)."""
+    """Bytes a fork copies per sequence: pointers and buffered entries, plus the checkpoint tiles
+    and read copy unless checkpoints are shared."""
     H, G, P, N, cap = cfg.heads, cfg.groups, cfg.dim_p, cfg.dim_n, lay.ring_cap
     e = 2 if cfg.in_dtype == 1 else 4
-    n = H * P * N * 4 + H * 8
-    if cfg.readcopy == 1:
-        n += H * P * N + H * P * 4
-    elif cfg.readcopy == 2:
-        n += H * P * N // 2 + H * P * (N // 16) + H * 4
+    n = H * 16
+    if not cfg.share_ckpt:
+        n += H * P * N * 4
+        if cfg.readcopy == 1:
+            n += H * P * N + H * P * 4
+        elif cfg.readcopy == 2:
+            n += H * P * N // 2 + H * P * (N // 16) + H * 4
     if cfg.kind == 0:
         n += H * cap * P * e + 2 * G * cap * N * e + H * cap * 4
     else:
@@ -286,9 +289,10 @@ def seq_state_bytes(cfg, lay):
     return n
 
 
-def bench_branch(dev, reps=20, pairs=64):
-    """Branching on the serving state: a fork of `pairs` sequences (every region copied, one
-    launch) and a restore of every sequence (pointer move)."""
+def bench_branch(dev, reps=20, pairs=64, share=0):
+    """Branching on the serving state: a fork of `pairs` sequences (share = 0: every region
+    copied in one launch; share = 1: pointers and buffered entries copied, the checkpoint shared,
+    plus the slot reader recount) and a restore of every sequence (pointer move)."""
     import torch
     from ssm_decode_state_amd import binding as bd
     from ssm_decode_state_amd import synth
@@ -297,7 +301,8 @@ def bench_branch(dev, reps=20, pairs=64):
     Bn, H, P, N = shape.batch, shape.heads, shape.dim_p, shape.dim_n
     A, D = synth.head_constants(shape, w["seed"])
     h0 = synth.initial_state_device(shape, w["seed"], w["h0_std"])
-    cfg = bd.make_config(bd.SSM_MAMBA2, Bn, H, shape.groups, P, N, shape.window, 1, bd.SSM_IN_BF16)
+    cfg = bd.make_config(bd.SSM_MAMBA2, Bn, H, shape.groups, P, N, shape.window, 1, bd.SSM_IN_BF16,
+                         share_ckpt=share)
     st = bd.State(cfg, h0, A.to(dev), D.to(dev))
     del h0
     y = torch.empty(Bn, H, P, device=dev)
@@ -313,7 +318,8 @@ def bench_branch(dev, reps=20, pairs=64):
     zero = torch.zeros(Bn, dtype=torch.int32, device=dev)
     bd.ssm_restore(st, zero)
     _, ms = timed_calls(reps, lambda i: bd.ssm_restore(st, zero))
-    return {"workload": "mamba2_branch_b256", "fork_pairs": pairs, "bytes_per_sequence": per_seq,
+    return {"workload": "mamba2_branch_b256" + ("_shared" if share else "_copy"),
+            "fork_pairs": pairs, "bytes_per_sequence": per_seq,
             "fork_avg_us": fork_us, "fork_achieved_gbs": gbs, "fork_frac": gbs / HBM_PEAK_GBS,
             "restore_avg_us": sum(ms) / reps * 1e3}
 
@@ -729,6 +735,7 @@ def main():
             torch.cuda.empty_cache()
         if "branch" in extra:
             out["workloads"]["branch"] = bench_branch(dev)
+            out["workloads"]["branch_shared"] = bench_branch(dev, share=1)
             torch.cuda.empty_cache()
         if "lsweep" in extra:
             out["workloads"]["window_sweep"] = bench_lsweep(dev)

@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 2
+#define SSM_ABI_VERSION 3
 
 typedef int32_t ssm_status;
 enum {
@@ -97,32 +97,38 @@ typedef struct ssm_config {
     int32_t in_dtype;  /* SSM_IN_F32 or SSM_IN_BF16 for x/B/C (q/k/v); dt/beta/g are always fp32 */
     int32_t readcopy;  /* SSM_RC_*: low-precision copy read by the output path */
     float gdn_scale;   /* GDN / KDA output scale (1.0 = none); ignored for Mamba-2 */
+    int32_t share_ckpt; /* 1: ssm_fork shares checkpoints (2 batch checkpoint slots); 0: it copies */
 } ssm_config;
 
 /* Byte offsets of the regions inside one state's device memory (each 256-byte aligned).
- * Checkpoint tile layout ("quad-interleaved"): the P x N tile of head (b, h) starts at float
- * offset (b*H + h)*P*N and element (p, n) sits at float ((n/4)*P + p)*4 + n%4, i.e. groups of
- * four consecutive n of one row are 16-byte units and consecutive rows' units are adjacent. The
- * read copy uses the same idea with wider units: fp8 codes of head (b, h) at byte
- * (b*H + h)*P*N + ((n/16)*P + p)*16 + n%16, row scales fp32 [b][h][P]; fp4 codes (two per byte,
- * low nibble = even n) at byte (b*H + h)*P*N/2 + ((n/32)*P + p)*16 + (n%32)/2, block-scale E4M3
- * codes [b][h][P][N/16], tile scale fp32 [b][h].
+ * Checkpoint slots: the checkpoint region holds ckpt_slots sets of H tiles (batch, or 2 batch
+ * with share_ckpt). Without share_ckpt sequence b always uses slot b (its pointers' slot field
+ * is not read); with it, sequence b reads the slot s recorded in its pointers: b, batch + b, or
+ * a fork source's slot. t = s*H + h is the tile index of head (b, h). Checkpoint tile layout ("quad-interleaved"): tile t starts at float
+ * offset t*P*N and element (p, n) sits at float ((n/4)*P + p)*4 + n%4, i.e. groups of four
+ * consecutive n of one row are 16-byte units and consecutive rows' units are adjacent. The read
+ * copy follows the tiles' slots and uses the same idea with wider units: fp8 codes of tile t at
+ * byte t*P*N + ((n/16)*P + p)*16 + n%16, row scales fp32 [t][P]; fp4 codes (two per byte, low
+ * nibble = even n) at byte t*P*N/2 + ((n/32)*P + p)*16 + (n%32)/2, block-scale E4M3 codes
+ * [t][P][N/16], tile scale fp32 [t].
  * Rings (slot s of cap): Mamba-2 x [b][h][s][P], B and C [b][g][s][N] (input dtype),
  * dt [b][h][s] fp32; GDN q, k [b][h][s][dk], v [b][h][s][dv] (input dtype), beta, g [b][h][s];
  * KDA as GDN with g [b][h][s][dk].
- * Pointers: int32 [b][h][2] = {start slot, committed count}. Flags: one int32 word of SSM_FLAG_*
- * bits set by device-side checks. */
+ * Pointers: int32 [b][h][4] = {start slot, committed count, checkpoint slot, 0}. Flags: one int32
+ * word of SSM_FLAG_* bits set by device-side checks. Reader counts: int32 [ckpt_slots], the
+ * number of sequences reading each checkpoint slot (kept by the library). */
 typedef struct ssm_layout {
     uint64_t total_bytes;
     int32_t ring_cap;       /* slots per ring = L + max_draft - 1 */
-    int32_t reserved;
+    int32_t ckpt_slots;     /* checkpoint slots: batch, or 2 batch with share_ckpt */
     uint64_t off_ckpt;      /* fp32 checkpoint tiles */
     uint64_t off_rc_codes;  /* read-copy codes (0 bytes when readcopy == SSM_RC_NONE) */
     uint64_t off_rc_scale;  /* fp8: row scales fp32; fp4: block-scale codes u8 */
     uint64_t off_rc_tscale; /* fp4: tile scales fp32 */
     uint64_t off_ring[5];   /* Mamba-2: x, B, C, dt, (unused); GDN: q, k, v, beta, g */
-    uint64_t off_ptr;       /* int32 [batch][heads][2] */
+    uint64_t off_ptr;       /* int32 [batch][heads][4] */
     uint64_t off_flags;     /* int32 flag word */
+    uint64_t off_refcnt;    /* int32 [ckpt_slots] reader counts */
 } ssm_layout;
 
 /* Host handle of one layer's state. Plain data: copyable only while no work is in flight. */
@@ -210,11 +216,14 @@ ssm_status ssm_spec_rollback(ssm_state *st, const int32_t *n_accept, void *strea
 ssm_status ssm_restore(ssm_state *st, const int32_t *n_back, void *stream);
 
 /* Fork (explainer, "The State-Storage Bottleneck in Branching Workloads": beam search and
- * best-of-n branch one prefix into several continuations): for k < n, sequence dst[k] becomes a
- * copy of sequence src[k] -- its checkpoint tiles, read copy, buffered entries and pointers.
- * src and dst are HOST arrays of n sequence indices in [0, batch); destinations must be distinct
- * and none may also be a source in the same call (SSM_E_ARG otherwise). The checkpoint is copied,
- * not shared: every copy folds into its own tiles. Errors: SSM_E_STATE if drafts are pending. */
+ * best-of-n branch one prefix into several continuations): for k < n, sequence dst[k] continues
+ * from sequence src[k]'s position. With share_ckpt the destination gets src's pointers and
+ * buffered entries and reads src's checkpoint slot: no checkpoint bytes move. A sequence whose
+ * slot is shared, or that reads another's, folds everything it holds into one of its own slots
+ * (b or batch + b) at the next fold launch (copy-on-write), whatever its count. Without
+ * share_ckpt the checkpoint tiles and read copy are copied too. src and dst are HOST arrays of n
+ * sequence indices in [0, batch); destinations must be distinct and none may also be a source in
+ * the same call (SSM_E_ARG otherwise). Errors: SSM_E_STATE if drafts are pending. */
 ssm_status ssm_fork(ssm_state *st, const int32_t *src, const int32_t *dst, int32_t n,
                     void *stream);
 

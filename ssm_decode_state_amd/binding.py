@@ -36,15 +36,16 @@ class ssm_config(ctypes.Structure):
                 ("groups", ctypes.c_int32), ("dim_p", ctypes.c_int32), ("dim_n", ctypes.c_int32),
                 ("window", ctypes.c_int32), ("max_draft", ctypes.c_int32),
                 ("in_dtype", ctypes.c_int32), ("readcopy", ctypes.c_int32),
-                ("gdn_scale", ctypes.c_float)]
+                ("gdn_scale", ctypes.c_float), ("share_ckpt", ctypes.c_int32)]
 
 
 class ssm_layout(ctypes.Structure):
     _fields_ = [("total_bytes", ctypes.c_uint64), ("ring_cap", ctypes.c_int32),
-                ("reserved", ctypes.c_int32), ("off_ckpt", ctypes.c_uint64),
+                ("ckpt_slots", ctypes.c_int32), ("off_ckpt", ctypes.c_uint64),
                 ("off_rc_codes", ctypes.c_uint64), ("off_rc_scale", ctypes.c_uint64),
                 ("off_rc_tscale", ctypes.c_uint64), ("off_ring", ctypes.c_uint64 * 5),
-                ("off_ptr", ctypes.c_uint64), ("off_flags", ctypes.c_uint64)]
+                ("off_ptr", ctypes.c_uint64), ("off_flags", ctypes.c_uint64),
+                ("off_refcnt", ctypes.c_uint64)]
 
 
 class ssm_state(ctypes.Structure):
@@ -134,9 +135,10 @@ def _stream(stream) -> ctypes.c_void_p:
 
 def make_config(kind: int, batch: int, heads: int, groups: int, dim_p: int, dim_n: int,
                 window: int, max_draft: int = 1, in_dtype: int = SSM_IN_BF16,
-                readcopy: int = SSM_RC_NONE, gdn_scale: float = 1.0) -> ssm_config:
+                readcopy: int = SSM_RC_NONE, gdn_scale: float = 1.0,
+                share_ckpt: int = 0) -> ssm_config:
     return ssm_config(kind, batch, heads, groups, dim_p, dim_n, window, max_draft, in_dtype,
-                      readcopy, gdn_scale)
+                      readcopy, gdn_scale, share_ckpt)
 
 
 def _inputs(cfg: ssm_config, inp: Mapping[str, torch.Tensor]):

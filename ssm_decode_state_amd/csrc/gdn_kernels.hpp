@@ -79,8 +79,9 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_replay_kernel(GdnArgs a) {
     const int H = a.heads;
     const int head = b * H + h;
     const int cap = a.cap, nq = a.ntok;
-    const int2 pt = *reinterpret_cast<const int2*>(a.ptr + 2 * head);
+    const int4 pt = *reinterpret_cast<const int4*>(a.ptr + kPtrInts * head);
     const int start = uniform(pt.x), count = uniform(pt.y);
+    const long th = a.share ? (long)uniform(pt.z) * H + h : head;  // this head's checkpoint tile
     const int kmax = count + nq;
     // row of token j (clamped to the call's tokens) in the [batch][ntok][H] inputs
     auto tok = [&](int j) -> long { return ((long)b * nq + min(max(j, 0), nq - 1)) * H + h; };
@@ -143,11 +144,11 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_replay_kernel(GdnArgs a) {
     float4 hv[kNQ];  // the fp32 rows (no read copy)
     RcRow<DV, DK, RC> rc;  // or the read copy's row, issued at the same point (news, para 4)
     if constexpr (RC == 0) {
-        const float4* tile = reinterpret_cast<const float4*>(a.ckpt) + (long)head * (DV * DK / 4);
+        const float4* tile = reinterpret_cast<const float4*>(a.ckpt) + th * (DV * DK / 4);
 #pragma unroll
         for (int q = 0; q < kNQ; ++q) hv[q] = ld_stream(tile + q * DV + row);
     } else {
-        rc.load(RcView{a.rc_codes, a.rc_scale, a.rc_tscale}, head, row);
+        rc.load(RcView{a.rc_codes, a.rc_scale, a.rc_tscale}, th, row);
     }
     asm volatile("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
@@ -327,7 +328,7 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_replay_kernel(GdnArgs a) {
     }
     if constexpr (COMMIT) {
         if constexpr (kW > 1) __builtin_amdgcn_s_barrier();  // every wave has read the pointers
-        if (wave == 0 && lane == 0) a.ptr[2 * head + 1] = count + nq;
+        if (wave == 0 && lane == 0) a.ptr[kPtrInts * head + 1] = count + nq;
     }
 }
 
@@ -462,13 +463,18 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_flush_kernel(GdnArgs a, int mod
     const int h = blockIdx.x, b = blockIdx.y;
     const int head = b * a.heads + h;
     const int cap = a.cap;
-    const int2 pt = *reinterpret_cast<const int2*>(a.ptr + 2 * head);
-    const int start = uniform(pt.x), count = uniform(pt.y);
+    const int4 pt = *reinterpret_cast<const int4*>(a.ptr + kPtrInts * head);
+    const int start = uniform(pt.x), count = uniform(pt.y), slot = uniform(pt.z);
+    // copy-on-write of a shared checkpoint: a sequence that must move folds whatever it holds
+    const FoldTarget ft = fold_target(a.refcnt, a.share, a.batch, b, slot);
     // FUSED: the buffered entries and this token; otherwise the oldest L (or all) entries
     const int nfold = FUSED ? count + 1
-                            : (rewrite_only ? 0 : (mode_all ? count : (count >= a.window ? a.window : 0)));
+                            : (rewrite_only ? 0 : (mode_all ? count : (count >= a.window ? a.window : (ft.move ? count : 0))));
     const int nring = FUSED ? count : nfold;  // entries that come from the ring
-    if (nfold == 0 && !rewrite_only) return;  // uniform over the workgroup: no barrier is skipped
+    // uniform over the workgroup: no barrier is skipped
+    if (nfold == 0 && !rewrite_only && !ft.move) return;
+    const long th = a.share ? (long)slot * a.heads + h : head;   // tile read
+    const long tw = a.share ? (long)ft.wr * a.heads + h : head;  // tile written
     const TIN* rk = static_cast<const TIN*>(a.ring_k);
     const TIN* rv = static_cast<const TIN*>(a.ring_v);
     const int li = lane & 15, lg = lane >> 4;
@@ -528,8 +534,9 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_flush_kernel(GdnArgs a, int mod
     // columns 16nb + 4(l/16) .. +3
     f32x4 S[kPB][kNB];
     // float4 (4 nb + lg) * DV + p_base + 16 pb + li of the head's tile
-    const TileIO tio{reinterpret_cast<char*>(a.ckpt) + (long)head * (DV * DK * 4),
+    const TileIO tio{reinterpret_cast<char*>(a.ckpt) + th * (DV * DK * 4),
                      (uint32_t)((lg * DV + p_base + li) * 16)};
+    const TileIO tiow{reinterpret_cast<char*>(a.ckpt) + tw * (DV * DK * 4), tio.lane};
 #pragma unroll
     for (int pb = 0; pb < kPB; ++pb)
 #pragma unroll
@@ -755,8 +762,8 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_flush_kernel(GdnArgs a, int mod
     for (int pb = 0; pb < kPB; ++pb)  // (a rewrite-only pass stores the tile unchanged)
 #pragma unroll
         for (int nb = 0; nb < kNB; ++nb)
-            tio.store((uint32_t)((4 * nb * DV + 16 * pb) * 16),
-                      make_float4(S[pb][nb][0], S[pb][nb][1], S[pb][nb][2], S[pb][nb][3]));
+            tiow.store((uint32_t)((4 * nb * DV + 16 * pb) * 16),
+                       make_float4(S[pb][nb][0], S[pb][nb][1], S[pb][nb][2], S[pb][nb][3]));
     if constexpr (FUSED) {
         // row p_base + 16 pb + li is spread over lanes li + 16 lg: sum the four partials through
         // the wave's (now free) transpose buffer, then lane p writes row p_base + p
@@ -779,14 +786,13 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_flush_kernel(GdnArgs a, int mod
                 amax_t = wmax;
             }
         }
-        rc_write_blocks<DV, DK, RC>(RcView{a.rc_codes, a.rc_scale, a.rc_tscale}, head, p_base, li, lg,
+        rc_write_blocks<DV, DK, RC>(RcView{a.rc_codes, a.rc_scale, a.rc_tscale}, tw, p_base, li, lg,
                                     S, amax_t, wave == 0 && lane == 0);
     }
     if constexpr (kW > 1) __builtin_amdgcn_s_barrier();  // every wave has read the pointers
-    if (nfold > 0 && wave == 0 && lane == 0) {
-        a.ptr[2 * head] = ring_slot(start, nfold, cap);
-        a.ptr[2 * head + 1] = (FUSED ? count + 1 : count) - nfold;
-    }
+    if ((nfold > 0 || ft.move) && wave == 0 && lane == 0)
+        *reinterpret_cast<int4*>(a.ptr + kPtrInts * head) =
+            make_int4(ring_slot(start, nfold, cap), (FUSED ? count + 1 : count) - nfold, ft.wr, 0);
 }
 
 // ---------------------------------------------------------------------------------------------

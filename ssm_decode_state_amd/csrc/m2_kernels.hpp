@@ -77,9 +77,10 @@ __global__ __launch_bounds__(256) void m2_replay_kernel(M2Args a) {
     const int cap = a.cap, nq = a.ntok;
     const int H = a.heads, Gn = a.groups;
 
-    const int2 pt = *reinterpret_cast<const int2*>(a.ptr + 2 * head);
+    const int4 pt = *reinterpret_cast<const int4*>(a.ptr + kPtrInts * head);
     const int start = uniform(pt.x);
     const int count = uniform(pt.y);
+    const long th = a.share ? (long)uniform(pt.z) * H + h : head;  // this head's checkpoint tile
     const int kmax = count + nq;
     const float A = a.A[h];
     const float D = a.D[h];
@@ -134,7 +135,7 @@ __global__ __launch_bounds__(256) void m2_replay_kernel(M2Args a) {
     // ---- 2. the checkpoint stream (explainer, "Why Decoding, Not Prefill, Is the Hard Part":
     //         decode time goes to reading the state) ----------------------------------------
     float4 hv[G::kQPL];
-    const float4* tile = reinterpret_cast<const float4*>(a.ckpt) + (long)head * (P * N / 4);
+    const float4* tile = reinterpret_cast<const float4*>(a.ckpt) + th * (P * N / 4);
     if constexpr (RC == 0) {
 #pragma unroll
         for (int j = 0; j < G::kQPL; ++j) hv[j] = ld_stream(tile + (gq + G::kGrp * j) * P + row);
@@ -276,7 +277,7 @@ __global__ __launch_bounds__(256) void m2_replay_kernel(M2Args a) {
         }
     } else {
         RcRow<P, N, RC> rc;  // the read copy's row (news, para 4: reads from the copy)
-        rc.load(RcView{a.rc_codes, a.rc_scale, a.rc_tscale}, head, row);
+        rc.load(RcView{a.rc_codes, a.rc_scale, a.rc_tscale}, th, row);
         rc.template dots<kCS, MAXQ>(nq, &s_c[wave][0][0], acc);
     }
     if constexpr (G::kGrp > 1) {
@@ -291,7 +292,7 @@ __global__ __launch_bounds__(256) void m2_replay_kernel(M2Args a) {
         }
     }
     if constexpr (COMMIT) {
-        if (lane == 0) a.ptr[2 * head + 1] = count + nq;
+        if (lane == 0) a.ptr[kPtrInts * head + 1] = count + nq;
     }
 }
 
@@ -334,16 +335,19 @@ __attribute__((amdgpu_waves_per_eu(2))) void m2_fold_kernel(M2Args a, int mode_a
     const int grp = h / (H / a.groups);
     const int bg = b * a.groups + grp;
     const int cap = a.cap;
-    const int2 pt = *reinterpret_cast<const int2*>(a.ptr + 2 * head);
+    const int4 pt = *reinterpret_cast<const int4*>(a.ptr + kPtrInts * head);
     const int start = uniform(pt.x);
     const int count = uniform(pt.y);
+    const int slot = uniform(pt.z);
+    // copy-on-write of a shared checkpoint: a sequence that must move folds whatever it holds
+    const FoldTarget ft = fold_target(a.refcnt, a.share, a.batch, b, slot);
     int nfold, nring;
     if constexpr (FUSED) {
         nfold = count + 1;  // the buffered entries and this token
         nring = count;
     } else {
-        nfold = rewrite_only ? 0 : (mode_all ? count : (count >= a.window ? a.window : 0));
-        if (nfold == 0 && !rewrite_only) return;
+        nfold = rewrite_only ? 0 : (mode_all ? count : (count >= a.window ? a.window : (ft.move ? count : 0)));
+        if (nfold == 0 && !rewrite_only && !ft.move) return;
         nring = nfold;
     }
     const int li = lane & 15, lg = lane >> 4;
@@ -394,9 +398,13 @@ __attribute__((amdgpu_waves_per_eu(2))) void m2_fold_kernel(M2Args a, int mode_a
     if (nfold > 0) fetch(0);
 
     f32x4 hb[kPB][kNB];
-    // float4 (4 nb + lg) * P + 16 pb + li of the head's tile
-    const TileIO tio{reinterpret_cast<char*>(a.ckpt) + (long)head * (P * N * 4),
+    // float4 (4 nb + lg) * P + 16 pb + li of the head's tile: read from its slot, written to the
+    // fold target's
+    const long th = a.share ? (long)slot * H + h : head;
+    const long tw = a.share ? (long)ft.wr * H + h : head;
+    const TileIO tio{reinterpret_cast<char*>(a.ckpt) + th * (P * N * 4),
                      (uint32_t)((lg * P + li) * 16)};
+    const TileIO tiow{reinterpret_cast<char*>(a.ckpt) + tw * (P * N * 4), tio.lane};
 #pragma unroll
     for (int pb = 0; pb < kPB; ++pb)
 #pragma unroll
@@ -465,12 +473,14 @@ __attribute__((amdgpu_waves_per_eu(2))) void m2_fold_kernel(M2Args a, int mode_a
             }
             wave_sync();
         }
+    }
+    if (nfold > 0 || ft.move) {
 #pragma unroll
         for (int pb = 0; pb < kPB; ++pb)
 #pragma unroll
             for (int nb = 0; nb < kNB; ++nb)
-                tio.store((uint32_t)((4 * nb * P + 16 * pb) * 16),
-                          make_float4(hb[pb][nb][0], hb[pb][nb][1], hb[pb][nb][2], hb[pb][nb][3]));
+                tiow.store((uint32_t)((4 * nb * P + 16 * pb) * 16),
+                           make_float4(hb[pb][nb][0], hb[pb][nb][1], hb[pb][nb][2], hb[pb][nb][3]));
     }
     if constexpr (FUSED) {  // output from the new state: y = h C + D x
         const TIN* xin = static_cast<const TIN*>(a.in_x) + tok * P;
@@ -493,13 +503,12 @@ __attribute__((amdgpu_waves_per_eu(2))) void m2_fold_kernel(M2Args a, int mode_a
     if constexpr (RC != 0) {
         static_assert(P == 64, "read copy needs P == 64");
         const float amax_t = RC == 2 ? xor_reduce_max<1, 32>(rc_local_amax<N>(hb)) : 0.f;
-        rc_write_blocks<P, N, RC>(RcView{a.rc_codes, a.rc_scale, a.rc_tscale}, head, 0, li, lg, hb,
+        rc_write_blocks<P, N, RC>(RcView{a.rc_codes, a.rc_scale, a.rc_tscale}, tw, 0, li, lg, hb,
                                   amax_t, lane == 0);
     }
-    if (nfold > 0 && lane == 0) {
-        a.ptr[2 * head] = ring_slot(start, nfold, cap);
-        a.ptr[2 * head + 1] = (FUSED ? count + 1 : count) - nfold;
-    }
+    if ((nfold > 0 || ft.move) && lane == 0)
+        *reinterpret_cast<int4*>(a.ptr + kPtrInts * head) =
+            make_int4(ring_slot(start, nfold, cap), (FUSED ? count + 1 : count) - nfold, ft.wr, 0);
 }
 
 // ---------------------------------------------------------------------------------------------

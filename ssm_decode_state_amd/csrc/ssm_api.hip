@@ -22,6 +22,7 @@ ssm_status check_config(const ssm_config* c) {
     if (c->kind != SSM_MAMBA2 && c->kind != SSM_GDN && c->kind != SSM_KDA) return SSM_E_ARG;
     if (c->in_dtype != SSM_IN_F32 && c->in_dtype != SSM_IN_BF16) return SSM_E_ARG;
     if (c->readcopy < SSM_RC_NONE || c->readcopy > SSM_RC_FP4_B16) return SSM_E_ARG;
+    if (c->share_ckpt != 0 && c->share_ckpt != 1) return SSM_E_ARG;
     if (c->batch < 0 || c->heads < 1 || c->groups < 1) return SSM_E_SHAPE;
     if ((int64_t)c->batch * c->heads > (int64_t)1 << 30) return SSM_E_SHAPE;
     if (c->heads % c->groups != 0) return SSM_E_SHAPE;
@@ -50,18 +51,20 @@ void compute_layout(const ssm_config* c, ssm_layout* L) {
     const uint64_t P = (uint64_t)c->dim_p, N = (uint64_t)c->dim_n;
     const uint64_t cap = (uint64_t)(c->window + c->max_draft - 1);
     const uint64_t esz = c->in_dtype == SSM_IN_BF16 ? 2 : 4;
+    const uint64_t S = c->share_ckpt ? 2 * B : B;  // checkpoint slots (tile sets of H heads)
     L->ring_cap = (int32_t)cap;
+    L->ckpt_slots = (int32_t)S;
     uint64_t off = 0;
     auto take = [&](uint64_t bytes) { const uint64_t o = off; off = align_up(off + bytes); return o; };
-    L->off_ckpt = take(B * H * P * N * 4);
+    L->off_ckpt = take(S * H * P * N * 4);
     if (c->readcopy == SSM_RC_FP8_ROW) {
-        L->off_rc_codes = take(B * H * P * N);
-        L->off_rc_scale = take(B * H * P * 4);
+        L->off_rc_codes = take(S * H * P * N);
+        L->off_rc_scale = take(S * H * P * 4);
         L->off_rc_tscale = take(0);
     } else if (c->readcopy == SSM_RC_FP4_B16) {
-        L->off_rc_codes = take(B * H * P * N / 2);
-        L->off_rc_scale = take(B * H * P * (N / 16));
-        L->off_rc_tscale = take(B * H * 4);
+        L->off_rc_codes = take(S * H * P * N / 2);
+        L->off_rc_scale = take(S * H * P * (N / 16));
+        L->off_rc_tscale = take(S * H * 4);
     } else {
         L->off_rc_codes = L->off_rc_scale = L->off_rc_tscale = take(0);
     }
@@ -78,8 +81,9 @@ void compute_layout(const ssm_config* c, ssm_layout* L) {
         L->off_ring[3] = take(B * H * cap * 4);        // beta
         L->off_ring[4] = take(B * H * cap * (c->kind == SSM_KDA ? N : 1) * 4);  // g (KDA: dk)
     }
-    L->off_ptr = take(B * H * 2 * 4);
+    L->off_ptr = take(B * H * ssm::kPtrInts * 4);
     L->off_flags = take(4);
+    L->off_refcnt = take(S * 4);
     L->total_bytes = off;
 }
 
@@ -107,6 +111,8 @@ ssm::M2Args m2_args(const ssm_state* st) {
     a.ring_C = at<void>(st, L.off_ring[2]);
     a.ring_dt = at<float>(st, L.off_ring[3]);
     a.ptr = at<int>(st, L.off_ptr);
+    a.refcnt = at<int>(st, L.off_refcnt);
+    a.share = st->cfg.share_ckpt;
     a.A = st->A;
     a.D = st->D;
     a.batch = st->cfg.batch;
@@ -131,6 +137,8 @@ ssm::GdnArgs gdn_args(const ssm_state* st) {
     a.ring_beta = at<float>(st, L.off_ring[3]);
     a.ring_g = at<float>(st, L.off_ring[4]);
     a.ptr = at<int>(st, L.off_ptr);
+    a.refcnt = at<int>(st, L.off_refcnt);
+    a.share = st->cfg.share_ckpt;
     a.scale = st->cfg.gdn_scale;
     a.batch = st->cfg.batch;
     a.heads = st->cfg.heads;
@@ -171,6 +179,14 @@ void fold_bounds(ssm_state* st) {
     }
 }
 
+// Shared checkpoints: recount every slot's readers after a launch that can move sequences
+// between slots (a fold or a fork), so that the next fold launch sees who still shares.
+hipError_t recount(ssm_state* st, hipStream_t s) {
+    if (!st->cfg.share_ckpt) return hipSuccess;
+    return ssm::launch_recount(at<int>(st, st->lay.off_refcnt), at<int>(st, st->lay.off_ptr),
+                               st->cfg.batch, st->cfg.heads, st->lay.ckpt_slots, s);
+}
+
 ssm_status launch_flush(ssm_state* st, int mode_all, hipStream_t s) {
     if (st->cfg.batch == 0) return SSM_OK;
     hipError_t e;
@@ -184,7 +200,10 @@ ssm_status launch_flush(ssm_state* st, int mode_all, hipStream_t s) {
                                   st->cfg.readcopy, mode_all, 0, s);
     }
     if (e == hipErrorNotSupported) return SSM_E_UNSUPPORTED;
-    return hip_status(e);
+    if (e != hipSuccess) return SSM_E_HIP;
+    // a sequence that shared its checkpoint folded everything it held: its count may now be 0
+    if (st->cfg.share_ckpt) st->count_lo = 0;
+    return hip_status(recount(st, s));
 }
 
 }  // namespace
@@ -241,13 +260,15 @@ ssm_status ssm_ckpt_init(ssm_state* st, const ssm_config* cfg, void* mem, uint64
     if (nheads == 0) return SSM_OK;
     float* ck = at<float>(st, lay.off_ckpt);
     hipError_t e;
-    if (h0) {
-        e = ssm::launch_pack(h0, ck, nheads, cfg->dim_p, cfg->dim_n, 0, hs);
+    if (h0) {  // sequence b starts in its own slot b: tile index = head index
+        e = ssm::launch_pack(h0, ck, nheads, cfg->dim_p, cfg->dim_n, 0, nullptr, 0, hs);
     } else {
         e = ssm::launch_fill_i32(reinterpret_cast<int*>(ck), 0, nheads * cfg->dim_p * cfg->dim_n, hs);
     }
     if (e != hipSuccess) return SSM_E_HIP;
-    e = ssm::launch_fill_i32(at<int>(st, lay.off_ptr), 0, nheads * 2, hs);
+    e = ssm::launch_ptr_init(at<int>(st, lay.off_ptr), cfg->batch, cfg->heads, hs);
+    if (e != hipSuccess) return SSM_E_HIP;
+    e = recount(st, hs);
     if (e != hipSuccess) return SSM_E_HIP;
     e = ssm::launch_fill_i32(at<int>(st, lay.off_flags), 0, 1, hs);
     if (e != hipSuccess) return SSM_E_HIP;
@@ -289,6 +310,7 @@ ssm_status ssm_replay_decode(ssm_state* st, const void* in, float* y, void* stre
             // emits the output from the new checkpoint (no replay pass, no ring append)
             e = ssm::m2_launch_flush(a, st->cfg.dim_p, st->cfg.dim_n, st->cfg.in_dtype,
                                      st->cfg.readcopy, 2, 0, hs);
+            if (e == hipSuccess) e = recount(st, hs);
             if (e != hipSuccess) return SSM_E_HIP;
             st->count_lo = st->count_hi = 0;
             return SSM_OK;
@@ -306,6 +328,7 @@ ssm_status ssm_replay_decode(ssm_state* st, const void* in, float* y, void* stre
             // as for Mamba-2 above (with a read copy: replay, then the fold below)
             e = ssm::gdn_launch_flush(a, st->cfg.dim_p, st->cfg.dim_n, st->cfg.in_dtype,
                                       st->cfg.readcopy, 2, 0, hs);
+            if (e == hipSuccess) e = recount(st, hs);
             if (e != hipSuccess) return SSM_E_HIP;
             st->count_lo = st->count_hi = 0;
             return SSM_OK;
@@ -431,7 +454,8 @@ ssm_status ssm_fork(ssm_state* st, const int32_t* src, const int32_t* dst, int32
         }
     }
     if (n == 0) return SSM_OK;
-    // every region's per-sequence slice (the layout's regions are all [batch][...])
+    // every region's per-sequence slice (the layout's regions are all [batch][...]); with shared
+    // checkpoints the copies point at the source's checkpoint slot instead of copying its tiles
     const ssm_config& c = st->cfg;
     const ssm_layout& L = st->lay;
     const uint64_t H = c.heads, G = c.groups, P = c.dim_p, N = c.dim_n, cap = L.ring_cap;
@@ -441,14 +465,16 @@ ssm_status ssm_fork(ssm_state* st, const int32_t* src, const int32_t* dst, int32
     auto add = [&](uint64_t off, uint64_t slice) {
         if (slice) { r.off[r.n] = off; r.slice[r.n] = slice; ++r.n; }
     };
-    add(L.off_ckpt, H * P * N * 4);
-    if (c.readcopy == SSM_RC_FP8_ROW) {
-        add(L.off_rc_codes, H * P * N);
-        add(L.off_rc_scale, H * P * 4);
-    } else if (c.readcopy == SSM_RC_FP4_B16) {
-        add(L.off_rc_codes, H * P * N / 2);
-        add(L.off_rc_scale, H * P * (N / 16));
-        add(L.off_rc_tscale, H * 4);
+    if (!c.share_ckpt) {
+        add(L.off_ckpt, H * P * N * 4);
+        if (c.readcopy == SSM_RC_FP8_ROW) {
+            add(L.off_rc_codes, H * P * N);
+            add(L.off_rc_scale, H * P * 4);
+        } else if (c.readcopy == SSM_RC_FP4_B16) {
+            add(L.off_rc_codes, H * P * N / 2);
+            add(L.off_rc_scale, H * P * (N / 16));
+            add(L.off_rc_tscale, H * 4);
+        }
     }
     if (c.kind == SSM_MAMBA2) {
         add(L.off_ring[0], H * cap * P * esz);
@@ -462,7 +488,7 @@ ssm_status ssm_fork(ssm_state* st, const int32_t* src, const int32_t* dst, int32
         add(L.off_ring[3], H * cap * 4);
         add(L.off_ring[4], H * cap * (c.kind == SSM_KDA ? N : 1) * 4);
     }
-    add(L.off_ptr, H * 2 * 4);
+    add(L.off_ptr, H * ssm::kPtrInts * 4);  // start, count and checkpoint slot
     const hipStream_t hs = as_stream(stream);
     for (int i0 = 0; i0 < n; i0 += ssm::kMaxForkPairs) {
         ssm::ForkPairs p;
@@ -475,6 +501,7 @@ ssm_status ssm_fork(ssm_state* st, const int32_t* src, const int32_t* dst, int32
         const hipError_t e = ssm::launch_fork_copy(static_cast<char*>(st->mem), r, p, hs);
         if (e != hipSuccess) return SSM_E_HIP;
     }
+    if (recount(st, hs) != hipSuccess) return SSM_E_HIP;
     return SSM_OK;  // the copies' counts are sources' counts: the host bounds still hold
 }
 
@@ -485,7 +512,9 @@ ssm_status ssm_ckpt_export(const ssm_state* st, float* h_out, void* stream) {
     if (!aligned16(h_out)) return SSM_E_ALIGN;
     const long nheads = (long)st->cfg.batch * st->cfg.heads;
     return hip_status(ssm::launch_pack(at<float>(st, st->lay.off_ckpt), h_out, nheads,
-                                       st->cfg.dim_p, st->cfg.dim_n, 1, as_stream(stream)));
+                                       st->cfg.dim_p, st->cfg.dim_n, 1,
+                                       st->cfg.share_ckpt ? at<int>(st, st->lay.off_ptr) : nullptr,
+                                       st->cfg.heads, as_stream(stream)));
 }
 
 ssm_status ssm_conventional_step(const ssm_config* cfg, float* h, const void* in, const float* A,
@@ -585,7 +614,7 @@ static ssm_status pack_common(const ssm_config* cfg, const float* src, float* ds
     if (!src || !dst) return SSM_E_ARG;
     if (!aligned16(src) || !aligned16(dst)) return SSM_E_ALIGN;
     return hip_status(ssm::launch_pack(src, dst, (long)c.batch * c.heads, c.dim_p, c.dim_n, unpack,
-                                       as_stream(stream)));
+                                       nullptr, 0, as_stream(stream)));
 }
 
 ssm_status ssm_tiles_pack(const ssm_config* cfg, const float* natural, float* tiles, void* stream) {

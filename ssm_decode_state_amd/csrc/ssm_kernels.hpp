@@ -5,6 +5,27 @@
 
 namespace ssm {
 
+// Pointer entry of one head: {start slot, committed count, checkpoint slot, 0}.
+constexpr int kPtrInts = 4;
+
+// Where a fold writes a head's new checkpoint. Without shared checkpoints a sequence reads and
+// writes its own slot b. With them (a fork points its copies at the source's slot), sequence b
+// owns slots b and batch + b: it folds in place when it reads one of them and no other sequence
+// reads it; otherwise it must fold at this launch (copy-on-write) into whichever of its two slots
+// nobody reads. At most one of a sequence's slots is read by anyone: every sequence that shares
+// a slot moves at the next fold launch, so a slot it left is free again by the one after.
+struct FoldTarget {
+    int wr;
+    bool move;
+};
+__device__ __forceinline__ FoldTarget fold_target(const int* refcnt, int share, int batch, int b,
+                                                  int slot) {
+    if (!share) return {slot, false};
+    const int own0 = b, own1 = batch + b;
+    if ((slot == own0 || slot == own1) && refcnt[slot] == 1) return {slot, false};
+    return {refcnt[own0] == 0 ? own0 : own1, true};
+}
+
 // Everything a Mamba-2 replay / verify / flush launch touches. Device pointers into one state's
 // memory (see the layout in ssm_replay.h) plus this call's inputs and outputs.
 struct M2Args {
@@ -16,7 +37,8 @@ struct M2Args {
     void* ring_B;
     void* ring_C;
     float* ring_dt;
-    int* ptr;           // int32 [batch][heads][2] = {start, count}
+    int* ptr;           // int32 [batch][heads][4] = {start, count, checkpoint slot, 0}
+    const int* refcnt;  // shared checkpoints: readers of each slot [2 batch]
     const void* in_x;   // this call's tokens, [batch][ntok][...]
     const void* in_B;
     const void* in_C;
@@ -25,6 +47,7 @@ struct M2Args {
     const float* D;
     float* y;           // [batch][ntok][H][P]
     int batch, heads, groups, cap, ntok, window;
+    int share;          // shared checkpoints enabled (slots 0 .. 2 batch - 1)
 };
 
 struct M2ConvArgs {
@@ -52,7 +75,8 @@ struct GdnArgs {
     void* ring_v;
     float* ring_beta;
     float* ring_g;
-    int* ptr;
+    int* ptr;           // as M2Args
+    const int* refcnt;
     const void* in_q;
     const void* in_k;
     const void* in_v;
@@ -62,6 +86,7 @@ struct GdnArgs {
     float scale;
     int batch, heads, cap, ntok, window;
     int kda;  // Kimi Delta Attention: g holds dk decays per entry (per-channel gate)
+    int share;
 };
 
 struct GdnConvArgs {
@@ -114,9 +139,16 @@ struct ForkPairs {
 };
 hipError_t launch_fork_copy(char* mem, const ForkRegions& r, const ForkPairs& p, hipStream_t s);
 hipError_t launch_restore(int* ptr, const int32_t* n_back, int batch, int heads, hipStream_t s);
-// Natural [heads][P][N] -> quad-interleaved tiles (unpack = 0) or back (unpack = 1).
+// Natural [heads][P][N] -> quad-interleaved tiles (unpack = 0) or back (unpack = 1). With ptr
+// (a state's pointer array, `heads` per sequence) the tiles of head (b, h) are those of its
+// checkpoint slot, tile index slot * heads + h; without it tile index = head index.
 hipError_t launch_pack(const float* src, float* dst, long nheads, int P, int N, int unpack,
-                       hipStream_t s);
+                       const int* ptr, int heads, hipStream_t s);
+// Pointer entries {0, 0, b, 0} for every head of sequence b.
+hipError_t launch_ptr_init(int* ptr, int batch, int heads, hipStream_t s);
+// refcnt[s] = number of sequences whose checkpoint slot is s, for s < nslot.
+hipError_t launch_recount(int* refcnt, const int* ptr, int batch, int heads, int nslot,
+                          hipStream_t s);
 hipError_t launch_codec(int op, const void* in, void* out, long n, hipStream_t s);
 
 }  // namespace ssm

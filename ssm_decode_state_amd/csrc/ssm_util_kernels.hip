@@ -17,7 +17,7 @@ __global__ void commit_kernel(int* ptr, const int32_t* __restrict__ n_accept, in
     if (i >= (long)batch * heads) return;
     const int raw = n_accept[i / heads];
     const int acc = raw < 0 ? 0 : (raw > pending ? pending : raw);
-    ptr[2 * i + 1] += acc;
+    ptr[kPtrInts * i + 1] += acc;
     if (acc != raw && i % heads == 0) atomicOr(flags, SSM_FLAG_ACCEPT_CLAMPED);
 }
 
@@ -44,10 +44,10 @@ __global__ void snap_select_kernel(float* __restrict__ h, const float* __restric
 __global__ void restore_kernel(int* ptr, const int32_t* __restrict__ n_back, int batch, int heads) {
     const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= (long)batch * heads) return;
-    const int c = ptr[2 * i + 1];
+    const int c = ptr[kPtrInts * i + 1];
     int n = n_back[i / heads];
     n = n < 0 ? 0 : (n > c ? c : n);
-    ptr[2 * i + 1] = c - n;
+    ptr[kPtrInts * i + 1] = c - n;
 }
 
 // Fork (explainer, "The State-Storage Bottleneck in Branching Workloads": one prefix, several
@@ -82,6 +82,28 @@ __global__ void fork_copy_kernel(char* __restrict__ mem, ForkRegions r, ForkPair
     }
 }
 
+// Fresh pointers: start 0, nothing committed, sequence b reads its own checkpoint slot b.
+__global__ void ptr_init_kernel(int* ptr, long n, int heads) {
+    const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) *reinterpret_cast<int4*>(ptr + kPtrInts * i) = make_int4(0, 0, (int)(i / heads), 0);
+}
+
+// Readers of every checkpoint slot (shared checkpoints): one 256-thread block per slot scans the
+// sequences' slot fields (every head of a sequence holds the same slot; head 0's is read) and
+// sums its lanes' counts. No atomics.
+__global__ __launch_bounds__(256) void recount_kernel(int* refcnt, const int* __restrict__ ptr,
+                                                      int batch, int heads) {
+    __shared__ int s_part[4];
+    const int s = blockIdx.x;
+    int c = 0;
+    for (int b = threadIdx.x; b < batch; b += blockDim.x) c += ptr[(long)kPtrInts * b * heads + 2] == s;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o, 64);
+    if ((threadIdx.x & 63) == 0) s_part[threadIdx.x >> 6] = c;
+    __syncthreads();
+    if (threadIdx.x == 0) refcnt[s] = s_part[0] + s_part[1] + s_part[2] + s_part[3];
+}
+
 __global__ void fill_i32_kernel(int* p, int value, long n) {
     const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
     if (i < n) p[i] = value;
@@ -89,15 +111,16 @@ __global__ void fill_i32_kernel(int* p, int value, long n) {
 
 // One thread per 16-byte quad of a tile: quad (q, p) of head hd <-> natural row p, columns 4q..4q+3.
 __global__ void pack_kernel(const float* __restrict__ src, float* __restrict__ dst, long nheads,
-                            int P, int N, int unpack) {
+                            int P, int N, int unpack, const int* __restrict__ ptr, int heads) {
     const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
     const long per = (long)P * N / 4;
     if (i >= nheads * per) return;
     const long hd = i / per;
     const int r = (int)(i % per);
     const int q = r / P, p = r % P;
+    const long th = ptr ? (long)ptr[kPtrInts * hd + 2] * heads + hd % heads : hd;
     const long nat = hd * (long)P * N + (long)p * N + 4 * q;  // float offset, natural layout
-    const long til = hd * (long)P * N + (long)r * 4;          // float offset, tile layout
+    const long til = th * (long)P * N + (long)r * 4;          // float offset, tile layout
     if (unpack)
         *reinterpret_cast<float4*>(dst + nat) = *reinterpret_cast<const float4*>(src + til);
     else
@@ -198,11 +221,26 @@ hipError_t launch_fill_i32(int* p, int value, long n, hipStream_t s) {
 }
 
 hipError_t launch_pack(const float* src, float* dst, long nheads, int P, int N, int unpack,
-                       hipStream_t s) {
+                       const int* ptr, int heads, hipStream_t s) {
     const long n = nheads * P * N / 4;
     if (n == 0) return hipSuccess;
     hipLaunchKernelGGL(pack_kernel, dim3(blocks_for(n, 256)), dim3(256), 0, s, src, dst, nheads, P,
-                       N, unpack);
+                       N, unpack, ptr, heads);
+    return hipGetLastError();
+}
+
+hipError_t launch_ptr_init(int* ptr, int batch, int heads, hipStream_t s) {
+    const long n = (long)batch * heads;
+    if (n == 0) return hipSuccess;
+    hipLaunchKernelGGL(ptr_init_kernel, dim3(blocks_for(n, 256)), dim3(256), 0, s, ptr, n, heads);
+    return hipGetLastError();
+}
+
+hipError_t launch_recount(int* refcnt, const int* ptr, int batch, int heads, int nslot,
+                          hipStream_t s) {
+    if (nslot == 0) return hipSuccess;
+    hipLaunchKernelGGL(recount_kernel, dim3((unsigned)nslot), dim3(256), 0, s, refcnt, ptr, batch,
+                       heads);
     return hipGetLastError();
 }
 

@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert bd.ssm_abi_version() == 2
+    assert bd.ssm_abi_version() == 3
     for s in range(-7, 1):
         assert bd.ssm_status_string(s) not in ("", "unknown status")
     assert bd.ssm_status_string(-99) == "unknown status"
@@ -59,10 +59,22 @@ def test_layout_serving_shape():
             lay.off_ring[3], lay.off_ptr]
     assert all(o % 256 == 0 for o in offs)
     assert offs == sorted(offs)
-    assert lay.off_flags >= lay.off_ptr + 256 * 128 * 8 and lay.off_flags % 256 == 0
-    assert lay.total_bytes >= lay.off_flags + 4
+    assert lay.off_flags >= lay.off_ptr + 256 * 128 * 16 and lay.off_flags % 256 == 0
+    assert lay.ckpt_slots == 256 and lay.off_refcnt >= lay.off_flags + 4
+    assert lay.total_bytes >= lay.off_refcnt + 256 * 4
     spec = bd.ssm_layout_query(cfg(max_draft=4))
     assert spec.ring_cap == 19
+
+
+def test_layout_shared_checkpoints():
+    # sharing doubles the checkpoint slots (tiles and read copy); rings and pointers are unchanged
+    plain = bd.ssm_layout_query(cfg(readcopy=bd.SSM_RC_FP8_ROW))
+    shared = bd.ssm_layout_query(cfg(readcopy=bd.SSM_RC_FP8_ROW, share_ckpt=1))
+    assert shared.ckpt_slots == 512
+    assert shared.off_rc_codes == 2 * 256 * 128 * 64 * 128 * 4
+    assert shared.off_rc_scale - shared.off_rc_codes == 2 * 256 * 128 * 64 * 128
+    assert shared.off_ptr - shared.off_ring[0] == plain.off_ptr - plain.off_ring[0]
+    assert shared.total_bytes >= shared.off_refcnt + 512 * 4
 
 
 def test_layout_gdn_read_copies():
@@ -123,6 +135,7 @@ def test_every_accepted_mamba2_shape(P, N):
     (dict(kind=bd.SSM_KDA, dim_p=32), bd.SSM_E_SHAPE),
     (dict(kind=bd.SSM_KDA, readcopy=bd.SSM_RC_FP8_ROW), bd.SSM_E_UNSUPPORTED),
     (dict(kind=3), bd.SSM_E_ARG),
+    (dict(share_ckpt=2), bd.SSM_E_ARG),
 ])
 def test_bad_configs_rejected(kw, status):
     with pytest.raises(bd.SSMError) as ei:

@@ -2,9 +2,13 @@
 
 Each case keeps, per sequence, the token stream the state should now hold (a host simulation of
 the window counts decides which entries a restore can drop), runs the fp64 oracle on exactly that
-stream and compares every later replay output and the final state. A fork is also checked bit for
-bit: right after it the destination's bytes equal the source's in every region, untouched
-sequences keep theirs, and a copy fed the source's inputs reproduces the source's outputs.
+stream and compares every later replay output and the final state. Forks run both ways: copying
+the checkpoint, and sharing it (the copies read the source's checkpoint slot and move to a slot
+of their own at the next fold). A fork is also checked bit for bit: right after it the
+destination's buffered entries and pointers equal the source's (and, when copied, its checkpoint
+bytes), untouched sequences keep theirs, and a copy fed the source's inputs reproduces the
+source's outputs. With shared checkpoints every fold launch must leave each sequence on one of
+its own two slots with no slot read twice.
 """
 import numpy as np
 import pytest
@@ -27,20 +31,21 @@ GDN_KEYS = ("q", "k", "v", "beta", "g")
 class Branches:
     """One state on the GPU plus the host record of what each sequence holds."""
 
-    def __init__(self, shape, seed, h0_std, rc=0, scale=1.0):
+    def __init__(self, shape, seed, h0_std, rc=0, scale=1.0, share=0):
         self.shape, self.seed, self.scale = shape, seed, scale
         self.m2 = shape.kind == synth.MAMBA2
         self.A, self.D = synth.head_constants(shape, seed)
         self.h0 = synth.initial_state(shape, seed, h0_std) if h0_std else None
         cfg = bd.make_config(shape.kind, shape.batch, shape.heads, shape.groups, shape.dim_p,
                              shape.dim_n, shape.window, shape.max_draft,
-                             bd.SSM_IN_BF16 if shape.in_bf16 else bd.SSM_IN_F32, rc, scale)
+                             bd.SSM_IN_BF16 if shape.in_bf16 else bd.SSM_IN_F32, rc, scale, share)
         self.st = bd.State(cfg, None if self.h0 is None else self.h0.to(DEV),
                            None if self.A is None else self.A.to(DEV),
                            None if self.D is None else self.D.to(DEV))
         self.steps = []
         self.stream = [[] for _ in range(shape.batch)]  # (step, batch row) of every held entry
         self.count = [0] * shape.batch                   # entries since the last fold
+        self.counts_known = True                          # false once shared folds make them vary
         self.origin = list(range(shape.batch))            # whose initial state a sequence holds
         self.got = {}                                     # (b, h) -> [(stream position, y)]
         self.y = torch.empty(shape.batch, shape.heads, shape.dim_p, device=DEV)
@@ -62,7 +67,26 @@ class Branches:
             for i, (b, h) in enumerate(pairs):
                 self.got.setdefault((b, h), []).append((len(self.stream[b]) - 1, ys[i]))
 
+    def spec(self, S, acc, pairs):
+        """One speculative round of S drafts; sequence b keeps its first acc[b] drafts."""
+        t = len(self.steps)
+        d = synth.token_inputs(self.shape, self.seed, "branch-spec", t, ntok=S)
+        for j in range(S):
+            self.steps.append({k: v[:, j:j + 1] for k, v in d.items()})
+        sh = self.shape
+        y = torch.empty(sh.batch, S, sh.heads, sh.dim_p, device=DEV)
+        bd.ssm_spec_append(self.st, S, to_dev(d, DEV), y)
+        bd.ssm_spec_rollback(self.st, torch.tensor(acc, dtype=torch.int32, device=DEV))
+        ys = y.cpu().double().numpy()
+        for (b, h) in pairs:
+            for j in range(acc[b]):
+                self.got.setdefault((b, h), []).append((len(self.stream[b]) + j, ys[b, j, h]))
+        for b in range(sh.batch):
+            self.stream[b] += [(t + j, b) for j in range(acc[b])]
+        self.counts_known = False  # the folds after a rollback are decided on the device
+
     def restore(self, n_back):
+        assert self.counts_known
         bd.ssm_restore(self.st, torch.tensor(n_back, dtype=torch.int32, device=DEV))
         for b, n in enumerate(n_back):
             n = max(0, min(n, self.count[b]))
@@ -102,8 +126,29 @@ class Branches:
             y, hT, _ = fn(S0, *[col(k, h) for k in GDN_KEYS], scale=self.scale)
         return y[0], hT[0]
 
+    def slots(self):
+        """(checkpoint slot of every head [B][H], reader count of every slot)."""
+        c, L = self.st.cfg, self.st.layout
+        p = self.st.region(L.off_ptr, c.batch * c.heads * 16).view(torch.int32).view(c.batch, c.heads, 4)
+        rc = self.st.region(L.off_refcnt, L.ckpt_slots * 4).view(torch.int32)
+        return p[..., 2].cpu(), rc.cpu()
+
+    def check_slots_after_fold(self):
+        """After a fold launch nobody shares: every sequence is on one of its own slots and the
+        reader counts are exact."""
+        torch.cuda.synchronize()
+        slot, rc = self.slots()
+        B = self.shape.batch
+        assert torch.all(slot == slot[:, :1]), "the heads of a sequence disagree on its slot"
+        s0 = slot[:, 0]
+        own = (s0 == torch.arange(B)) | (s0 == torch.arange(B) + B)
+        assert bool(own.all()), "a sequence still reads a slot it does not own: %s" % s0.tolist()
+        assert torch.equal(rc, torch.bincount(s0.long(), minlength=rc.numel()).int())
+
     def check(self, pairs, what):
         bd.ssm_flush(self.st, bd.SSM_FLUSH_ALL)
+        if self.st.cfg.share_ckpt:
+            self.check_slots_after_fold()
         sh = self.shape
         nat = torch.empty(sh.batch, sh.heads, sh.dim_p, sh.dim_n, device=DEV)
         bd.ssm_ckpt_export(self.st, nat)
@@ -118,19 +163,20 @@ class Branches:
                          "%s final state (%d, %d)" % (what, b, h))
 
 
-def _shape(kind, B, H, L=8, bf16=True):
+def _shape(kind, B, H, L=8, bf16=True, S=1):
     if kind == synth.MAMBA2:
-        return synth.Shape(kind, B, H, 1, 64, 128, L, 1, in_bf16=bf16)
-    return synth.Shape(kind, B, H, H, 128, 64, L, 1, in_bf16=bf16)
+        return synth.Shape(kind, B, H, 1, 64, 128, L, S, in_bf16=bf16)
+    return synth.Shape(kind, B, H, H, 128, 64, L, S, in_bf16=bf16)
 
 
 KINDS = [synth.MAMBA2, synth.GDN, synth.KDA]
 
 
+@pytest.mark.parametrize("share", [0, 1])
 @pytest.mark.parametrize("kind", KINDS)
-def test_restore_then_decode(kind):
+def test_restore_then_decode(kind, share):
     B, H = 5, 2
-    br = Branches(_shape(kind, B, H), 300 + kind, 0.3, scale=0.7 if kind else 1.0)
+    br = Branches(_shape(kind, B, H), 300 + kind, 0.3, scale=0.7 if kind else 1.0, share=share)
     pairs = [(b, h) for b in range(B) for h in range(H)]
     for _ in range(13):  # one fold, then five entries buffered
         br.decode(pairs)
@@ -155,20 +201,47 @@ def test_restore_after_fold_drops_nothing():
     br.check(pairs, "restore after a fold")
 
 
+@pytest.mark.parametrize("share", [0, 1])
 @pytest.mark.parametrize("kind", KINDS)
-def test_fork_then_decode(kind):
+def test_fork_then_decode(kind, share):
     B, H = 6, 2
-    br = Branches(_shape(kind, B, H), 320 + kind, 0.3)
+    br = Branches(_shape(kind, B, H), 320 + kind, 0.3, share=share)
     pairs = [(b, h) for b in range(B) for h in range(H)]
     for _ in range(11):
         br.decode(pairs)
     br.fork([0, 0, 1], [3, 4, 5])  # one prefix into two continuations, and a plain copy
-    for _ in range(10):
+    for _ in range(2):
         br.decode(pairs)
+    br.fork([3, 2], [1, 0])        # sources that read a shared slot, and a sharer overwritten
+    for _ in range(8):
+        br.decode(pairs)
+    if share:
+        br.check_slots_after_fold()  # the window closed: every sharer moved
     br.restore([0, 2, 0, 1, 3, 0])  # a restore on forked sequences
     for _ in range(4):
         br.decode(pairs)
     br.check(pairs, "fork")
+
+
+@pytest.mark.parametrize("share", [0, 1])
+@pytest.mark.parametrize("kind", KINDS)
+def test_fork_then_speculative_rounds(kind, share):
+    # after a rollback the fold is a device predicate: sharers with fewer than L entries must
+    # still move at that launch
+    B, H, S = 6, 2, 3
+    br = Branches(_shape(kind, B, H, L=8, S=S), 340 + kind, 0.3, share=share)
+    pairs = [(b, h) for b in range(B) for h in range(H)]
+    rng = np.random.default_rng(9 + kind)
+    for _ in range(5):
+        br.decode(pairs)
+    br.fork([0, 0, 2], [3, 4, 5])
+    for r in range(6):
+        br.spec(S, [int(v) for v in rng.integers(0, S + 1, size=B)], pairs)
+        if r == 2:
+            br.fork([4], [1])
+    for _ in range(3):
+        br.decode(pairs)
+    br.check(pairs, "fork + speculation")
 
 
 def _seq_regions(st):
@@ -189,7 +262,7 @@ def _seq_regions(st):
         r += [(L.off_ring[0], H * cap * N * e), (L.off_ring[1], H * cap * N * e),
               (L.off_ring[2], H * cap * P * e), (L.off_ring[3], H * cap * 4),
               (L.off_ring[4], H * cap * (N if c.kind == bd.SSM_KDA else 1) * 4)]
-    r.append((L.off_ptr, H * 8))
+    r.append((L.off_ptr, H * 16))
     return r
 
 
@@ -205,13 +278,16 @@ def _same_inputs(d, src, dst):
     return d
 
 
-@pytest.mark.parametrize("name,rc", [("m2_b256", bd.SSM_RC_NONE), ("m2_b256_readcopy", bd.SSM_RC_FP8_ROW),
-                                     ("m2_b256_readcopy", bd.SSM_RC_FP4_B16),
-                                     ("gdn_b256", bd.SSM_RC_FP8_ROW), ("kda_b256", bd.SSM_RC_NONE)])
-def test_fork_serving_batch_bit_exact(name, rc):
+@pytest.mark.parametrize("name,rc,share", [
+    ("m2_b256", bd.SSM_RC_NONE, 0), ("m2_b256_readcopy", bd.SSM_RC_FP8_ROW, 0),
+    ("m2_b256_readcopy", bd.SSM_RC_FP4_B16, 0), ("gdn_b256", bd.SSM_RC_FP8_ROW, 0),
+    ("kda_b256", bd.SSM_RC_NONE, 0), ("m2_b256", bd.SSM_RC_NONE, 1),
+    ("m2_b256_readcopy", bd.SSM_RC_FP4_B16, 1), ("gdn_b256", bd.SSM_RC_FP8_ROW, 1),
+    ("kda_b256", bd.SSM_RC_NONE, 1)])
+def test_fork_serving_batch_bit_exact(name, rc, share):
     w = synth.WORKLOADS[name]
     sh = w["shape"]
-    br = Branches(sh, w["seed"], w["h0_std"], rc=rc)
+    br = Branches(sh, w["seed"], w["h0_std"], rc=rc, share=share)
     for _ in range(21):  # a fold, then five buffered entries
         br.decode(None)
     src = list(range(0, 160, 2))           # 80 pairs: more than one launch of the copy
@@ -222,7 +298,14 @@ def test_fork_serving_batch_bit_exact(name, rc):
     si, di = torch.tensor(src, device=DEV), torch.tensor(dst, device=DEV)
     keep = torch.ones(sh.batch, dtype=torch.bool, device=DEV)
     keep[di] = False
-    for (off, sl) in _seq_regions(br.st):
+    regions = _seq_regions(br.st)
+    ck_off, ck_bytes = br.st.layout.off_ckpt, br.st.layout.off_ring[0] - br.st.layout.off_ckpt
+    if share:  # no checkpoint or read-copy byte moves: the copies read the source's slot
+        regions = [(o, sl) for (o, sl) in regions if o >= br.st.layout.off_ring[0]]
+        assert torch.equal(br.st.mem[ck_off:ck_off + ck_bytes], before[ck_off:ck_off + ck_bytes])
+        slot, rcnt = br.slots()
+        assert torch.equal(slot[di.cpu()], slot[si.cpu()]) and int(rcnt[src[0]]) == 2
+    for (off, sl) in regions:
         now, old = _rows(br.st, off, sl), before[off:off + sh.batch * sl].view(sh.batch, sl)
         assert torch.equal(now[di], now[si]), "region at %d differs after the fork" % off
         assert torch.equal(now[keep], old[keep]), "region at %d changed outside the copies" % off
@@ -234,10 +317,13 @@ def test_fork_serving_batch_bit_exact(name, rc):
         ys.append(br.y.clone())
     for t, y in enumerate(ys):
         assert torch.equal(y[di], y[si]), "step %d: a copy's outputs differ from its source" % t
+    if share:
+        br.check_slots_after_fold()
     bd.ssm_flush(br.st, bd.SSM_FLUSH_ALL)
+    nat = torch.empty(sh.batch, sh.heads, sh.dim_p, sh.dim_n, device=DEV)
+    bd.ssm_ckpt_export(br.st, nat)
     torch.cuda.synchronize()
-    ck = _rows(br.st, *_seq_regions(br.st)[0])
-    assert torch.equal(ck[di], ck[si])
+    assert torch.equal(nat[di], nat[si])
 
 
 @pytest.mark.parametrize("name", ["m2_b256", "gdn_b256", "kda_b256"])

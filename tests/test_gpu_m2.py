@@ -34,8 +34,8 @@ def tiles_of(state: "bd.State", pairs):
 
 def pointers(state: "bd.State"):
     c = state.cfg
-    p = state.region(state.layout.off_ptr, c.batch * c.heads * 8).view(torch.int32)
-    return p.view(c.batch, c.heads, 2).cpu()
+    p = state.region(state.layout.off_ptr, c.batch * c.heads * 16).view(torch.int32)
+    return p.view(c.batch, c.heads, 4).cpu()
 
 
 def run_decode(shape, seed, steps, h0_std, pairs, rc=0, check_ckpt=True):
