@@ -366,10 +366,10 @@ def bench_readcopy(dev, rc, steps=128, warm=16, layers=4, pool=16):
             "fold_step_avg_us": sum(flush_ms) / max(len(flush_ms), 1) * 1e3}
 
 
-def gdn_rc_replay_bytes_per_head(dv, dk, k, rc, esz=2):
-    """GDN replay launch reading the low-precision copy instead of the fp32 state."""
+def gdn_rc_replay_bytes_per_head(dv, dk, k, rc, esz=2, gsz=4):
+    """GDN / KDA replay launch reading the low-precision copy instead of the fp32 state."""
     copy = dv * dk + dv * 4 if rc == 1 else dv * dk // 2 + dv * dk // 16 + 4
-    return gdn_replay_bytes_per_head(dv, dk, k, esz) - dv * dk * 4 + copy
+    return gdn_replay_bytes_per_head(dv, dk, k, esz, gsz) - dv * dk * 4 + copy
 
 
 def bench_gdn(dev, steps=128, warm=16, layers=2, pool=16, rc=0, kda=False):
@@ -410,11 +410,12 @@ def bench_gdn(dev, steps=128, warm=16, layers=2, pool=16, rc=0, kda=False):
             fold.append(m)
             continue
         rep_b += heads * (gdn_replay_bytes_per_head(dv, dk, k, gsz=gsz) if rc == 0 else
-                          gdn_rc_replay_bytes_per_head(dv, dk, k, rc))
+                          gdn_rc_replay_bytes_per_head(dv, dk, k, rc, gsz=gsz))
         rep_ms += m
     gbs = rep_b / (rep_ms * 1e-3) / 1e9
     if rc != 0:
-        return {"workload": "gdn_readcopy_%s_b256" % ("fp8row" if rc == 1 else "fp4b16"),
+        return {"workload": "%s_readcopy_%s_b256" % ("kda" if kda else "gdn",
+                                                      "fp8row" if rc == 1 else "fp4b16"),
                 "tokens_per_s": Bn * n / wall, "unit": "tokens/s/layer", "layers_rotated": layers,
                 "ms_per_step": wall / n * 1e3, "replay_avg_us": rep_ms / (n - len(fold)) * 1e3,
                 "replay_achieved_gbs": gbs, "replay_frac": gbs / HBM_PEAK_GBS,
@@ -583,7 +584,7 @@ def main():
     ap.add_argument("--workloads", default="all",
                     help="comma list of extra workloads: spec, fp8, fp4, gdn, gdn_spec, "
                          "gdn_fp8, gdn_fp4, kda, g8 (8 B/C groups), lsweep (window 4..32), "
-                         "branch (fork and restore); 'all' or 'none'")
+                         "branch (fork and restore), kda_fp8, kda_fp4; 'all' or 'none'")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -715,7 +716,7 @@ def main():
                            "avg_us": e0.elapsed_time(e1) / 5 * 1e3}
 
     extra = ({"spec", "fp8", "fp4", "gdn", "gdn_spec", "gdn_fp8", "gdn_fp4", "kda", "g8", "lsweep",
-              "branch"}
+              "branch", "kda_fp8", "kda_fp4"}
              if args.workloads == "all" else
              set() if args.workloads == "none" else set(args.workloads.split(",")))
     if extra:
@@ -757,6 +758,12 @@ def main():
             torch.cuda.empty_cache()
         if "gdn_fp4" in extra:
             out["workloads"]["gdn_readcopy_fp4"] = bench_gdn(dev, layers=4, rc=2)
+            torch.cuda.empty_cache()
+        if "kda_fp8" in extra:
+            out["workloads"]["kda_readcopy_fp8"] = bench_gdn(dev, layers=4, rc=1, kda=True)
+            torch.cuda.empty_cache()
+        if "kda_fp4" in extra:
+            out["workloads"]["kda_readcopy_fp4"] = bench_gdn(dev, layers=4, rc=2, kda=True)
             torch.cuda.empty_cache()
         if "gdn_spec" in extra:
             out["workloads"]["gdn_spec"] = bench_gdn_spec(dev)

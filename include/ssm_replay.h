@@ -50,8 +50,7 @@
  * - Supported shapes: Mamba-2 P in {16, 32, 64} and N in {16, 32, 64, 128} with N >= 4 * 64 / P
  *   (P = 64 takes every N); GDN dv and dk in {64, 128}; window L in [1, 32]; max_draft in
  *   [1, min(L, 8)], and for GDN / KDA L + max_draft - 1 <= 32 (SSM_E_UNSUPPORTED otherwise).
- *   KDA takes the GDN shapes. The read copies need N (dk) in {64, 128}, and P = 64 for Mamba-2;
- *   KDA has none (SSM_E_UNSUPPORTED).
+ *   KDA takes the GDN shapes. The read copies need N (dk) in {64, 128}, and P = 64 for Mamba-2.
  */
 #ifndef SSM_REPLAY_H
 #define SSM_REPLAY_H

@@ -15,10 +15,7 @@ static hipError_t launch_decode_vg(const GdnArgs& a, int maxe, hipStream_t s) {
 }
 template <int DV, int DK, typename TIN, int RC>
 static hipError_t launch_decode_dd(const GdnArgs& a, int maxe, hipStream_t s) {
-    if (a.kda) {  // per-channel gate: no read copy
-        if constexpr (RC == 0) return launch_decode_vg<DV, DK, TIN, 0, true>(a, maxe, s);
-        else return hipErrorNotSupported;
-    }
+    if (a.kda) return launch_decode_vg<DV, DK, TIN, RC, true>(a, maxe, s);  // per-channel gate
     return launch_decode_vg<DV, DK, TIN, RC, false>(a, maxe, s);
 }
 

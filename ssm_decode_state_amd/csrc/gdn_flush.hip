@@ -20,10 +20,7 @@ static hipError_t launch_flush_vg(const GdnArgs& a, int mode_all, int rewrite_on
 }
 template <int DV, int DK, typename TIN, int RC>
 static hipError_t launch_flush_dd(const GdnArgs& a, int mode_all, int rewrite_only, hipStream_t s) {
-    if (a.kda) {  // per-channel gate: no read copy
-        if constexpr (RC == 0) return launch_flush_vg<DV, DK, TIN, 0, true>(a, mode_all, rewrite_only, s);
-        else return hipErrorNotSupported;
-    }
+    if (a.kda) return launch_flush_vg<DV, DK, TIN, RC, true>(a, mode_all, rewrite_only, s);  // per-channel gate
     return launch_flush_vg<DV, DK, TIN, RC, false>(a, mode_all, rewrite_only, s);
 }
 

@@ -15,10 +15,7 @@ static hipError_t launch_verify_vg(const GdnArgs& a, hipStream_t s) {
 }
 template <int DV, int DK, typename TIN, int RC>
 static hipError_t launch_verify_dd(const GdnArgs& a, hipStream_t s) {
-    if (a.kda) {  // per-channel gate: no read copy
-        if constexpr (RC == 0) return launch_verify_vg<DV, DK, TIN, 0, true>(a, s);
-        else return hipErrorNotSupported;
-    }
+    if (a.kda) return launch_verify_vg<DV, DK, TIN, RC, true>(a, s);  // per-channel gate
     return launch_verify_vg<DV, DK, TIN, RC, false>(a, s);
 }
 

@@ -40,7 +40,6 @@ ssm_status check_config(const ssm_config* c) {
         if (!isfinite(c->gdn_scale)) return SSM_E_ARG;
         // a call sees at most 32 entries (the replay kernel's sweep bound)
         if (c->window + c->max_draft - 1 > 32) return SSM_E_UNSUPPORTED;
-        if (c->kind == SSM_KDA && c->readcopy != SSM_RC_NONE) return SSM_E_UNSUPPORTED;
     }
     return SSM_OK;
 }

@@ -133,7 +133,7 @@ def test_every_accepted_mamba2_shape(P, N):
     (dict(kind=bd.SSM_GDN, window=32, max_draft=2), bd.SSM_E_UNSUPPORTED),
     (dict(kind=bd.SSM_KDA, groups=64), bd.SSM_E_SHAPE),
     (dict(kind=bd.SSM_KDA, dim_p=32), bd.SSM_E_SHAPE),
-    (dict(kind=bd.SSM_KDA, readcopy=bd.SSM_RC_FP8_ROW), bd.SSM_E_UNSUPPORTED),
+    (dict(kind=bd.SSM_KDA, readcopy=bd.SSM_RC_FP8_ROW, dim_n=32), bd.SSM_E_SHAPE),
     (dict(kind=3), bd.SSM_E_ARG),
     (dict(share_ckpt=2), bd.SSM_E_ARG),
 ])

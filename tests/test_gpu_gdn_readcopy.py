@@ -1,4 +1,5 @@
-"""GPU checks of the low-precision read copy on Gated DeltaNet layers (dv x dk state tiles).
+"""GPU checks of the low-precision read copy on Gated DeltaNet and Kimi Delta Attention layers
+(dv x dk state tiles).
 
 The copy is written from the fp32 state at init and at every flush and read only by the output
 path (replay and speculative verify); the recurrence never sees it. Checks:
@@ -9,7 +10,8 @@ path (replay and speculative verify); the recurrence never sees it. Checks:
   * every output stays within a closed-form bound around the exact (fp64, unquantized) output:
     |o - o_exact| <= scale * ||bound of row p||_2 * ||q||_2, because the replayed query r is q
     mapped through alpha_i (I - beta_i k_i k_i^T) with alpha, beta in (0, 1] and unit keys, so
-    ||r||_2 <= ||q||_2 (1% slack for the bf16 rounding of the unit keys);
+    ||r||_2 <= ||q||_2 (1% slack for the bf16 rounding of the unit keys); with KDA's per-channel
+    decay diag(alpha_i) in place of the scalar every factor still has norm <= 1;
   * every flushed fp32 state still matches the oracle to 1e-4, and the error does not drift;
   * speculative rounds through the read-copy verify stay within the same bound.
 """
@@ -18,7 +20,7 @@ import pytest
 import torch
 
 import oracle
-from harness import GdnTokens, assert_close, gdn_oracle, sample_pairs, to_dev
+from harness import GdnTokens, assert_close, sample_pairs, to_dev
 from oracle import quant
 from ssm_decode_state_amd import synth
 
@@ -67,9 +69,19 @@ def decoded_and_bound(S64, rc):
     return quant.fp4_decode(c, sb, st), quant.fp4_bound(S, quant.fp4_scales(sb, st))
 
 
+KINDS = [synth.GDN, synth.KDA]
+
+
+def fns(kind):
+    """The oracle's (sequential, replay-form, speculative-rounds) functions for the layer type."""
+    if kind == synth.KDA:
+        return oracle.kda_sequential, oracle.kda_replay_output, oracle.kda_spec_rounds
+    return oracle.gdn_sequential, oracle.gdn_replay_output, oracle.gdn_spec_rounds
+
+
 def make(shape, seed, rc, scale=1.0, max_draft=1):
     S0 = synth.initial_state(shape, seed, 0.3162)
-    cfg = bd.make_config(bd.SSM_GDN, shape.batch, shape.heads, shape.heads, shape.dim_p,
+    cfg = bd.make_config(shape.kind, shape.batch, shape.heads, shape.heads, shape.dim_p,
                          shape.dim_n, shape.window, max_draft,
                          bd.SSM_IN_BF16 if shape.in_bf16 else bd.SSM_IN_F32, rc, scale)
     return bd.State(cfg, S0.to(DEV), None, None), S0
@@ -84,10 +96,11 @@ def tiles_of(st, pairs):
     return ck.index_select(0, idx).permute(0, 2, 1, 3).reshape(len(pairs), P, N).cpu().double().numpy()
 
 
+@pytest.mark.parametrize("kind", KINDS)
 @pytest.mark.parametrize("rc", [1, 2])
 @pytest.mark.parametrize("B,H,dv,dk", [(2, 3, 64, 64), (2, 2, 128, 128), (1, 3, 128, 64)])
-def test_gdn_init_copy_is_bit_exact(rc, B, H, dv, dk):
-    shape = synth.Shape(synth.GDN, B, H, H, dv, dk, 8, 1)
+def test_gdn_init_copy_is_bit_exact(rc, B, H, dv, dk, kind):
+    shape = synth.Shape(kind, B, H, H, dv, dk, 8, 1)
     st, S0 = make(shape, 80 + dv + dk, rc)
     pairs = [(b, h) for b in range(B) for h in range(H)]
     torch.cuda.synchronize()
@@ -102,15 +115,17 @@ def _bound(bnd, q, scale):
     return abs(scale) * np.sqrt((bnd ** 2).sum(-1)) * np.linalg.norm(q, axis=-1)[:, None] * 1.01
 
 
+@pytest.mark.parametrize("kind", KINDS)
 @pytest.mark.parametrize("rc", [1, 2])
 @pytest.mark.parametrize("case", ["small", "serving"])
-def test_gdn_readcopy_decode(rc, case):
+def test_gdn_readcopy_decode(rc, case, kind):
+    seq_fn, replay_fn, _ = fns(kind)
     if case == "small":
-        shape = synth.Shape(synth.GDN, 2, 3, 3, 128, 128, 8, 1)
-        seed, T, scale = 90 + rc, 40, 0.5
+        shape = synth.Shape(kind, 2, 3, 3, 128, 128, 8, 1)
+        seed, T, scale = 90 + rc + 7 * kind, 40, 0.5
         pairs = [(b, h) for b in range(2) for h in range(3)]
     else:
-        w = synth.WORKLOADS["gdn_b256"]
+        w = synth.WORKLOADS["kda_b256" if kind == synth.KDA else "gdn_b256"]
         shape, seed, T, scale = w["shape"], w["seed"] + 10 * rc, 64, 1.0
         pairs = sample_pairs(shape.batch, shape.heads, 12)
     L = shape.window
@@ -130,8 +145,9 @@ def test_gdn_readcopy_decode(rc, case):
     torch.cuda.synchronize()
     go = torch.stack(os_, 1).cpu().double().numpy()
     snaps = list(range(L, T + 1, L))
-    oo, _, osn = gdn_oracle(S0, tok, pairs, scale, snaps)
     q, k, v, beta, g = tok.head_inputs(pairs)
+    S0p = np.stack([S0[b, h].double().numpy() for (b, h) in pairs])
+    oo, _, osn = seq_fn(S0p, q, k, v, beta, g, scale=scale, snap_after=snaps)
     # (a) the fp32 recurrence is untouched by the copy
     assert_close(np.stack(cks, 1), osn, (-2, -1), "flushed fp32 states")
     # (b) first window: the oracle's replay form on the decoded initial copy
@@ -141,9 +157,8 @@ def test_gdn_readcopy_decode(rc, case):
     else:
         dec0 = quant.fp4_decode(*init_copy)
     for t in range(L):  # every token of the window replays from the initial copy
-        exp = np.stack([oracle.gdn_replay_output(dec0[i].astype(np.float64), q[i, t], k[i, :t + 1],
-                                                 v[i, :t + 1], beta[i, :t + 1], g[i, :t + 1],
-                                                 scale) for i in range(len(pairs))])
+        exp = np.stack([replay_fn(dec0[i].astype(np.float64), q[i, t], k[i, :t + 1], v[i, :t + 1],
+                                  beta[i, :t + 1], g[i, :t + 1], scale) for i in range(len(pairs))])
         assert_close(go[:, t], exp, (-1,), "first-window outputs on the decoded copy (t=%d)" % t)
     # (c) every output within the bound around the exact output; no drift across windows
     ratios = []
@@ -168,12 +183,14 @@ def test_gdn_readcopy_decode(rc, case):
         assert mism.mean() < 0.01, mism.mean()
 
 
+@pytest.mark.parametrize("kind", KINDS)
 @pytest.mark.parametrize("rc", [1, 2])
-def test_gdn_readcopy_speculative_rounds(rc):
+def test_gdn_readcopy_speculative_rounds(rc, kind):
     """Drafts verified through the read copy: every draft output within the bound around the
     exact output of the oracle's speculative rounds; the fp32 state exact."""
-    shape = synth.Shape(synth.GDN, 2, 3, 3, 128, 128, 8, 4)
-    seed, R, S = 95 + rc, 10, 4
+    _, _, spec_fn = fns(kind)
+    shape = synth.Shape(kind, 2, 3, 3, 128, 128, 8, 4)
+    seed, R, S = 95 + rc + 7 * kind, 10, 4
     st, S0 = make(shape, seed, rc, 1.0, max_draft=S)
     pairs = [(b, h) for b in range(2) for h in range(3)]
     bi = torch.tensor([b for (b, _) in pairs], device=DEV)
@@ -205,8 +222,8 @@ def test_gdn_readcopy_speculative_rounds(rc):
     snap = np.full((len(pairs), ns), -1, dtype=np.int32)
     for i, f in enumerate(folds):
         snap[i, :len(f)] = f
-    oo, ST, sn = oracle.gdn_spec_rounds(S0p, ins["q"], ins["k"], ins["v"], ins["beta"], ins["g"],
-                                        acc, scale=1.0, snap_after=snap)
+    oo, ST, sn = spec_fn(S0p, ins["q"], ins["k"], ins["v"], ins["beta"], ins["g"], acc, scale=1.0,
+                         snap_after=snap)
     got = np.stack([nat[b, h].cpu().double().numpy() for (b, h) in pairs])
     assert_close(got, ST, (-2, -1), "fp32 state after the speculative rounds")
     for i in range(len(pairs)):
