@@ -107,11 +107,11 @@ def gdn_replay_bytes_per_head(dv, dk, k, esz=2, gsz=4):
     return dv * dk * 4 + (k - 1) * entry_rd + 2 * token + dv * 4 + 12
 
 
-def gdn_verify_bytes_per_head(dv, dk, kc, S, esz=2):
-    """GDN speculative verify for one head: state read once, kc committed entries (k, v, beta,
-    g), S drafts read and appended (q, k, v, beta, g), S outputs, pointers."""
-    entry_rd = dk * esz + dv * esz + 8
-    token = 2 * dk * esz + dv * esz + 8
+def gdn_verify_bytes_per_head(dv, dk, kc, S, esz=2, gsz=4):
+    """GDN (KDA: gsz = 4 dk) speculative verify for one head: state read once, kc committed
+    entries (k, v, beta, g), S drafts read and appended (q, k, v, beta, g), S outputs, pointers."""
+    entry_rd = dk * esz + dv * esz + 4 + gsz
+    token = 2 * dk * esz + dv * esz + 4 + gsz
     return dv * dk * 4 + kc * entry_rd + 2 * S * token + S * dv * 4 + 8
 
 
@@ -436,17 +436,20 @@ def bench_gdn(dev, steps=128, warm=16, layers=2, pool=16, rc=0, kda=False):
             "speedup_vs_conventional": (Bn * n / wall) / (Bn * n / cwall)}
 
 
-def bench_gdn_spec(dev, rounds=64, warm=16, pool=16, layers=2):
-    """Gated DeltaNet speculative decoding at B=256, H=32, dv=dk=128: 4 drafts per round
-    verified in one replay call, U{0..4} accepted, pointer rollback (a fold fires whenever a
-    sequence reaches L); `layers` rotated layer instances."""
+def bench_gdn_spec(dev, rounds=64, warm=16, pool=16, layers=2, kda=False):
+    """Gated DeltaNet (kda=True: Kimi Delta Attention) speculative decoding at B=256, H=32,
+    dv=dk=128: 4 drafts per round verified in one replay call, U{0..4} accepted, pointer
+    rollback (a fold fires whenever a sequence reaches L); `layers` rotated layer instances."""
     import torch
     from ssm_decode_state_amd import binding as bd
     from ssm_decode_state_amd import synth
     w = synth.WORKLOADS["gdn_b256_spec"]
     shape = w["shape"]
     Bn, H, dv, dk, L, S = shape.batch, shape.heads, shape.dim_p, shape.dim_n, shape.window, w["ndraft"]
-    cfg = bd.make_config(bd.SSM_GDN, Bn, H, H, dv, dk, L, S, bd.SSM_IN_BF16)
+    if kda:  # the same shapes and draws with one decay per key channel
+        shape = dataclasses.replace(shape, kind=synth.KDA)
+    gsz = 4 * dk if kda else 4
+    cfg = bd.make_config(bd.SSM_KDA if kda else bd.SSM_GDN, Bn, H, H, dv, dk, L, S, bd.SSM_IN_BF16)
     sts = []
     for layer in range(layers):
         s0 = synth.initial_state_device(shape, w["seed"], w["h0_std"], layer)
@@ -474,7 +477,7 @@ def bench_gdn_spec(dev, rounds=64, warm=16, pool=16, layers=2):
     ver_bytes = 0.0
     for i in range(n_warm, n_warm + n):
         r, layer = i // layers, i % layers
-        ver_bytes += H * sum(gdn_verify_bytes_per_head(dv, dk, c, S) for c in counts[layer])
+        ver_bytes += H * sum(gdn_verify_bytes_per_head(dv, dk, c, S, gsz=gsz) for c in counts[layer])
         advance(r, layer)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n)]
     torch.cuda.synchronize()
@@ -492,7 +495,8 @@ def bench_gdn_spec(dev, rounds=64, warm=16, pool=16, layers=2):
     rb = sum(e[1].elapsed_time(e[2]) for e in ev)
     accepted = sum(int(accs[(n_warm + i) // layers].sum()) for i in range(n))
     gbs = ver_bytes / (ver * 1e-3) / 1e9
-    return {"workload": "gdn_spec_b256_4drafts", "accepted_tokens_per_s": accepted / wall,
+    return {"workload": ("kda" if kda else "gdn") + "_spec_b256_4drafts",
+            "accepted_tokens_per_s": accepted / wall,
             "unit": "accepted tokens/s/layer", "rounds": n, "layers_rotated": layers,
             "mean_accept": accepted / (Bn * n), "verify_avg_us": ver / n * 1e3,
             "verify_achieved_gbs": gbs, "verify_frac": gbs / HBM_PEAK_GBS,
@@ -584,7 +588,7 @@ def main():
     ap.add_argument("--workloads", default="all",
                     help="comma list of extra workloads: spec, fp8, fp4, gdn, gdn_spec, "
                          "gdn_fp8, gdn_fp4, kda, g8 (8 B/C groups), lsweep (window 4..32), "
-                         "branch (fork and restore), kda_fp8, kda_fp4; 'all' or 'none'")
+                         "branch (fork and restore), kda_fp8, kda_fp4, kda_spec; 'all' or 'none'")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -716,7 +720,7 @@ def main():
                            "avg_us": e0.elapsed_time(e1) / 5 * 1e3}
 
     extra = ({"spec", "fp8", "fp4", "gdn", "gdn_spec", "gdn_fp8", "gdn_fp4", "kda", "g8", "lsweep",
-              "branch", "kda_fp8", "kda_fp4"}
+              "branch", "kda_fp8", "kda_fp4", "kda_spec"}
              if args.workloads == "all" else
              set() if args.workloads == "none" else set(args.workloads.split(",")))
     if extra:
@@ -767,6 +771,9 @@ def main():
             torch.cuda.empty_cache()
         if "gdn_spec" in extra:
             out["workloads"]["gdn_spec"] = bench_gdn_spec(dev)
+            torch.cuda.empty_cache()
+        if "kda_spec" in extra:
+            out["workloads"]["kda_spec"] = bench_gdn_spec(dev, kda=True)
             torch.cuda.empty_cache()
 
     if not args.no_cpu:

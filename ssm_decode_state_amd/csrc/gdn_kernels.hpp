@@ -67,11 +67,19 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_replay_kernel(GdnArgs a) {
     constexpr int kVC = kRows / kEPC;             // 16-byte chunks of a wave's v slice
     constexpr int kVL = (MAXW * kVC + 63) / 64;
     constexpr int kRS = DK + 4;  // r row stride: the 4 rows an MFMA operand read takes hit distinct banks
-    __shared__ __attribute__((aligned(16))) float s_r[kW][MAXQ][kRS];
+    // The waves of a head split the staging of the entries (entry e by wave e % kW) into shared
+    // keys and decays. With several queries they also split the sweeps (query j by wave j % kW)
+    // and share the swept r_j and coefficients; a single query is swept by every wave.
+    static_assert(MAXW % kW == 0, "entries split over the head's waves");
+    constexpr bool kSplit = kW > 1 && MAXQ > 1;
+    constexpr int kQS = kSplit ? (MAXQ + kW - 1) / kW : MAXQ;  // queries this wave sweeps
+    constexpr int kSW = kSplit ? 1 : kW;                       // copies of r and c
+    constexpr int kEW = MAXW / kW;                             // entries this wave stages
+    __shared__ __attribute__((aligned(16))) float s_r[kSW][MAXQ][kRS];
     __shared__ __attribute__((aligned(16))) u32x4_t s_v[kW][MAXW * kVC];
-    __shared__ __attribute__((aligned(16))) float s_c[kW][MAXW][MAXQ];
-    __shared__ __attribute__((aligned(16))) TIN s_k[kW][MAXW][DK];  // keys, as loaded
-    __shared__ __attribute__((aligned(16))) float s_al[kW][VG ? MAXW : 1][VG ? DK : 4];  // VG: alpha
+    __shared__ __attribute__((aligned(16))) float s_c[kSW][MAXW][MAXQ];
+    __shared__ __attribute__((aligned(16))) TIN s_k[MAXW][DK];  // keys, as loaded
+    __shared__ __attribute__((aligned(16))) float s_al[VG ? MAXW : 1][VG ? DK : 4];  // VG: alpha
 
     const int wave = uniform(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
@@ -107,29 +115,33 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_replay_kernel(GdnArgs a) {
             ge = lane < kmax ? ge : 0.f;
         }
     }
-    TIN kraw[MAXW][kE];  // keys of the entries (entries >= count are this call's tokens)
+    // keys of this wave's entries e = ee kW + wave (entries >= count are this call's tokens)
+    TIN kraw[kEW][kE];
 #pragma unroll
-    for (int e = 0; e < MAXW; ++e) {
+    for (int ee = 0; ee < kEW; ++ee) {
+        const int e = ee * kW + wave;
         const TIN* src = e < count ? rk + ((long)head * cap + ring_slot(start, min(e, cap - 1), cap)) * DK
                                    : ink + tok(e - count) * DK;
-        load_raw<TIN, kE>(src + el * kE, kraw[e]);
+        load_raw<TIN, kE>(src + el * kE, kraw[ee]);
     }
-    float graw[VG ? MAXW : 1][kE];  // VG: the lane's log-decays of every entry
+    float graw[VG ? kEW : 1][kE];  // VG: the lane's log-decays of this wave's entries
     // (issued before the state stream for up to 16 entries; after it for more, where holding
     // them across the stream would exceed the register budget)
     constexpr bool kLateG = VG && MAXW > 16;
     auto load_g = [&]() {
 #pragma unroll
-        for (int e = 0; e < MAXW; ++e) {
+        for (int ee = 0; ee < kEW; ++ee) {
+            const int e = ee * kW + wave;
             const float* src = e < count ? a.ring_g + ((long)head * cap + ring_slot(start, min(e, cap - 1), cap)) * DK
                                          : a.in_g + tok(e - count) * DK;
-            load_raw<float, kE>(src + el * kE, graw[e]);
+            load_raw<float, kE>(src + el * kE, graw[ee]);
         }
     };
     if constexpr (VG && !kLateG) load_g();
-    TIN qraw[MAXQ][kE];
+    auto qidx = [&](int jj) { return kSplit ? jj * kW + wave : jj; };  // query of sweep slot jj
+    TIN qraw[kQS][kE];
 #pragma unroll
-    for (int j = 0; j < MAXQ; ++j) load_raw<TIN, kE>(inq + tok(j) * DK + el * kE, qraw[j]);
+    for (int jj = 0; jj < kQS; ++jj) load_raw<TIN, kE>(inq + tok(qidx(jj)) * DK + el * kE, qraw[jj]);
     u32x4_t vraw[kVL];
 #pragma unroll
     for (int i = 0; i < kVL; ++i) {
@@ -155,33 +167,34 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_replay_kernel(GdnArgs a) {
 
     // ---- stage keys and v rows, append this call's tokens to the rings ------------------------
 #pragma unroll
-    for (int e = 0; e < MAXW; ++e)
+    for (int ee = 0; ee < kEW; ++ee)
 #pragma unroll
-        for (int i = 0; i < kE; ++i) s_k[wave][e][el * kE + i] = kraw[e][i];
+        for (int i = 0; i < kE; ++i) s_k[ee * kW + wave][el * kE + i] = kraw[ee][i];
     if constexpr (VG && !kLateG) {
 #pragma unroll
-        for (int e = 0; e < MAXW; ++e)
+        for (int ee = 0; ee < kEW; ++ee)
 #pragma unroll
-            for (int i = 0; i < kE; ++i) s_al[wave][e][el * kE + i] = expf(graw[e][i]);
+            for (int i = 0; i < kE; ++i) s_al[ee * kW + wave][el * kE + i] = expf(graw[ee][i]);
     } else if constexpr (VG) {  // eight entries at a time: few registers live beside the rows
+        static_assert(kEW % 8 == 0, "late decays in groups of eight");
 #pragma unroll
-        for (int e0 = 0; e0 < MAXW; e0 += 8) {
+        for (int e0 = 0; e0 < kEW; e0 += 8) {
             float gb[8][kE];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int ee = e0 + e;
-                const float* src = ee < count ? a.ring_g + ((long)head * cap + ring_slot(start, min(ee, cap - 1), cap)) * DK
-                                              : a.in_g + tok(ee - count) * DK;
-                load_raw<float, kE>(src + el * kE, gb[e]);
+            for (int u = 0; u < 8; ++u) {
+                const int e = (e0 + u) * kW + wave;
+                const float* src = e < count ? a.ring_g + ((long)head * cap + ring_slot(start, min(e, cap - 1), cap)) * DK
+                                             : a.in_g + tok(e - count) * DK;
+                load_raw<float, kE>(src + el * kE, gb[u]);
             }
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int ee = e0 + e;
+            for (int u = 0; u < 8; ++u) {
+                const int e = (e0 + u) * kW + wave;
 #pragma unroll
-                for (int i = 0; i < kE; ++i) s_al[wave][ee][el * kE + i] = expf(gb[e][i]);
-                if (wave == 0 && ee >= count && ee < kmax)  // this call's tokens: append g
-                    store_raw<float, kE>(a.ring_g + ((long)head * cap + ring_slot(start, ee, cap)) * DK +
-                                             el * kE, gb[e]);
+                for (int i = 0; i < kE; ++i) s_al[e][el * kE + i] = expf(gb[u][i]);
+                if (e >= count && e < kmax)  // this call's tokens: append g
+                    store_raw<float, kE>(a.ring_g + ((long)head * cap + ring_slot(start, e, cap)) * DK +
+                                             el * kE, gb[u]);
             }
         }
     }
@@ -201,75 +214,78 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_replay_kernel(GdnArgs a) {
                                             (rb + ring_slot(start, e, cap)) * DV + wave * kRows +
                                             part * kEPC) = vraw[i];
         }
-        if (wave == 0) {
+        // each wave appends the keys (and decays) it staged and the queries it sweeps
 #pragma unroll
-            for (int j = 0; j < MAXQ; ++j) {
-                if (j >= nq) break;
-                const long rs = rb + ring_slot(start, count + j, cap);
-                store_raw<TIN, kE>(static_cast<TIN*>(a.ring_q) + rs * DK + el * kE, qraw[j]);
-            }
+        for (int jj = 0; jj < kQS; ++jj) {
+            const int j = qidx(jj);
+            if (j >= nq || (!kSplit && wave != 0)) continue;
+            const long rs = rb + ring_slot(start, count + j, cap);
+            store_raw<TIN, kE>(static_cast<TIN*>(a.ring_q) + rs * DK + el * kE, qraw[jj]);
+        }
 #pragma unroll
-            for (int e = 0; e < MAXW; ++e) {
-                if (e >= count && e < kmax)
-                    store_raw<TIN, kE>(static_cast<TIN*>(a.ring_k) +
-                                           (rb + ring_slot(start, e, cap)) * DK + el * kE,
-                                       kraw[e]);
+        for (int ee = 0; ee < kEW; ++ee) {
+            const int e = ee * kW + wave;
+            if (e >= count && e < kmax) {
+                store_raw<TIN, kE>(static_cast<TIN*>(a.ring_k) + (rb + ring_slot(start, e, cap)) * DK +
+                                       el * kE, kraw[ee]);
+                if constexpr (VG && !kLateG)
+                    store_raw<float, kE>(a.ring_g + (rb + ring_slot(start, e, cap)) * DK + el * kE,
+                                         graw[ee]);
             }
-            if (lane >= count && lane < kmax) {
-                const long rs = rb + ring_slot(start, lane, cap);
-                a.ring_beta[rs] = be;
-                if constexpr (!VG) a.ring_g[rs] = ge;
-            }
-            if constexpr (VG && !kLateG) {
-#pragma unroll
-                for (int e = 0; e < MAXW; ++e) {
-                    if (e >= count && e < kmax)
-                        store_raw<float, kE>(a.ring_g + (rb + ring_slot(start, e, cap)) * DK + el * kE,
-                                             graw[e]);
-                }
-            }
+        }
+        if (wave == 0 && lane >= count && lane < kmax) {
+            const long rs = rb + ring_slot(start, lane, cap);
+            a.ring_beta[rs] = be;
+            if constexpr (!VG) a.ring_g[rs] = ge;
         }
     }
 
-    // ---- backward sweeps of every query over the entries it sees --------------------------------
-    float r[MAXQ][kE];
+    // ---- backward sweeps of this wave's queries over the entries they see -----------------------
+    const int sw = kSplit ? 0 : wave;  // this wave's copy of r and c
+    float r[kQS][kE];
 #pragma unroll
-    for (int j = 0; j < MAXQ; ++j)
+    for (int jj = 0; jj < kQS; ++jj)
 #pragma unroll
-        for (int i = 0; i < kE; ++i) r[j][i] = to_f32<TIN>(qraw[j][i]);
-    wave_sync();
+        for (int i = 0; i < kE; ++i) r[jj][i] = to_f32<TIN>(qraw[jj][i]);
+    if constexpr (kW > 1) __syncthreads();  // every wave's entries are staged
+    else wave_sync();
     for (int e = kmax - 1; e >= 0; --e) {  // uniform trip count
         float kv[kE];
 #pragma unroll
-        for (int i = 0; i < kE; ++i) kv[i] = to_f32<TIN>(s_k[wave][e][el * kE + i]);
+        for (int i = 0; i < kE; ++i) kv[i] = to_f32<TIN>(s_k[e][el * kE + i]);
         const float bt = readlane(be, e);
         float al[kE];  // the decay of the lane's key elements
         if constexpr (VG) {
 #pragma unroll
-            for (int i = 0; i < kE; ++i) al[i] = s_al[wave][e][el * kE + i];
+            for (int i = 0; i < kE; ++i) al[i] = s_al[e][el * kE + i];
         } else {
             const float as = expf(readlane(ge, e));
 #pragma unroll
             for (int i = 0; i < kE; ++i) al[i] = as;
         }
 #pragma unroll
-        for (int j = 0; j < MAXQ; ++j) {
+        for (int jj = 0; jj < kQS; ++jj) {
+            const int j = qidx(jj);
             if (j >= nq) break;
             if (e > count + j) continue;  // entry after query j's own token (uniform)
             float d = 0.f;
 #pragma unroll
-            for (int i = 0; i < kE; ++i) d += kv[i] * r[j][i];
+            for (int i = 0; i < kE; ++i) d += kv[i] * r[jj][i];
             const float c = bt * wave_sum(d);
 #pragma unroll
-            for (int i = 0; i < kE; ++i) r[j][i] = al[i] * (r[j][i] - c * kv[i]);
-            if (lane == 0) s_c[wave][e][j] = c;
+            for (int i = 0; i < kE; ++i) r[jj][i] = al[i] * (r[jj][i] - c * kv[i]);
+            if (lane == 0) s_c[sw][e][j] = c;
         }
     }
 #pragma unroll
-    for (int j = 0; j < MAXQ; ++j)
+    for (int jj = 0; jj < kQS; ++jj) {
+        const int j = qidx(jj);
+        if (j >= MAXQ) break;
 #pragma unroll
-        for (int i = 0; i < kE; ++i) s_r[wave][j][el * kE + i] = r[j][i];
-    wave_sync();
+        for (int i = 0; i < kE; ++i) s_r[sw][j][el * kE + i] = r[jj][i];
+    }
+    if constexpr (kSplit) __syncthreads();  // the other waves' r and c
+    else wave_sync();
 
     // ---- value terms and the checkpoint row products --------------------------------------------
     const TIN* sv = reinterpret_cast<const TIN*>(&s_v[wave][0]);
@@ -281,14 +297,14 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_replay_kernel(GdnArgs a) {
 #pragma unroll
         for (int j = 0; j < MAXQ; ++j) {
             if (j >= nq) break;
-            if (e <= count + j) acc[j] += s_c[wave][e][j] * ve;
+            if (e <= count + j) acc[j] += s_c[sw][e][j] * ve;
         }
     }
     float dot[MAXQ];
     if constexpr (RC != 0) {  // the decoded copy's rows against every r_j (news, para 4)
 #pragma unroll
         for (int j = 0; j < MAXQ; ++j) dot[j] = 0.f;
-        rc.template dots<kRS, MAXQ>(nq, &s_r[wave][0][0], dot);
+        rc.template dots<kRS, MAXQ>(nq, &s_r[sw][0][0], dot);
     } else if constexpr (MAXQ >= 4) {
         // four queries per 4x4x1 MFMA (lane = row; query 4g + lane%4 supplies its r column),
         // two accumulator chains per group of four
@@ -300,7 +316,7 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_replay_kernel(GdnArgs a) {
         for (int q = 0; q < kNQ; ++q) {
 #pragma unroll
             for (int g = 0; g < kG; ++g) {
-                const float4 r4 = *reinterpret_cast<const float4*>(&s_r[wave][4 * g + (lane & 3)][4 * q]);
+                const float4 r4 = *reinterpret_cast<const float4*>(&s_r[sw][4 * g + (lane & 3)][4 * q]);
                 f32x4& d = dq[g][q & 1];
                 d = mfma4x4(r4.x, hv[q].x, d);
                 d = mfma4x4(r4.y, hv[q].y, d);
@@ -316,7 +332,7 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_replay_kernel(GdnArgs a) {
             dot[j] = 0.f;
 #pragma unroll
             for (int q = 0; q < kNQ; ++q) {
-                const float4 r4 = *reinterpret_cast<const float4*>(&s_r[wave][j][4 * q]);
+                const float4 r4 = *reinterpret_cast<const float4*>(&s_r[sw][j][4 * q]);
                 dot[j] += hv[q].x * r4.x + hv[q].y * r4.y + hv[q].z * r4.z + hv[q].w * r4.w;
             }
         }
