@@ -339,3 +339,23 @@ def test_restore_serving_batch_sampled(name):
     for _ in range(14):
         br.decode(pairs)
     br.check(pairs, name + " restore")
+
+
+@pytest.mark.parametrize("kind", [synth.MAMBA2, synth.GDN])
+def test_large_batch_past_4gib(kind):
+    """Checkpoint regions past 4 GiB (and twice that with shared slots): every offset must be
+    formed in 64 bits. Corner and sampled heads against the oracle, across a fork from the last
+    sequence into the first and the folds that move the sharers."""
+    if kind == synth.MAMBA2:
+        shape = synth.Shape(kind, 1024, 128, 128, 64, 128, 16, 1)   # 4 GiB per slot set
+    else:
+        shape = synth.Shape(kind, 2048, 32, 32, 128, 128, 16, 1)    # 4 GiB per slot set
+    B, H = shape.batch, shape.heads
+    br = Branches(shape, 500 + kind, 0.3, share=1)
+    pairs = sorted(set(sample_pairs(B, H, 10)) | {(1, 0), (B - 2, H - 1)})
+    for _ in range(18):  # a fold, then two buffered entries
+        br.decode(pairs)
+    br.fork([B - 1, 1], [0, B - 2])
+    for _ in range(16):  # the next fold moves the sharers to their own slots
+        br.decode(pairs)
+    br.check(pairs, "large batch")
