@@ -590,6 +590,7 @@ def cpu_baseline(seconds_target: float = 10.0):
     oracle.m2_sequential(*args1)
     el1 = time.perf_counter() - t0
     oracle.set_threads(None)
+    gdn = cpu_baseline_gdn(seconds_target / 2)
     model = ""
     try:
         model = [l.split(":", 1)[1].strip() for l in open("/proc/cpuinfo")
@@ -602,7 +603,45 @@ def cpu_baseline(seconds_target: float = 10.0):
                       "time(s); fp64 sequential recurrence (C, OpenMP over heads), %.1f s"
                       % (nseq, T, reps, el),
             "single_core": {"value": n1 * T / el1, "sample": "%d sequences, %.1f s" % (n1, el1)},
-            "cpu_model": model}
+            "gdn": gdn, "cpu_model": model}
+
+
+def cpu_baseline_gdn(seconds_target: float = 5.0):
+    """The fp64 oracle's gated delta rule on a bounded sample of the GDN serving workload (B=256,
+    H=32, dv=dk=128): S sequences x all 32 heads x 16 tokens, sized like cpu_baseline."""
+    import dataclasses
+
+    import numpy as np
+    import oracle
+    from ssm_decode_state_amd import synth
+
+    w = synth.WORKLOADS["gdn_b256"]
+    full = w["shape"]
+    H, dv, dk, T = full.heads, full.dim_p, full.dim_n, 16
+
+    def sample(nseq):
+        shape = dataclasses.replace(full, batch=nseq)
+        toks = [synth.token_inputs(shape, w["seed"], "cpu", t) for t in range(T)]
+        cat = {key: torch_cat([d[key] for d in toks]) for key in ("q", "k", "v", "beta", "g")}
+        q, k, v = [cat[key].permute(0, 2, 1, 3).reshape(nseq * H, T, -1) for key in ("q", "k", "v")]
+        beta, g = [cat[key].permute(0, 2, 1).reshape(nseq * H, T) for key in ("beta", "g")]
+        S0 = synth.initial_state(shape, w["seed"], w["h0_std"])
+        return (synth.to_f64(S0.reshape(nseq * H, dv, dk)), synth.to_f64(q), synth.to_f64(k),
+                synth.to_f64(v), synth.to_f64(beta), synth.to_f64(g))
+
+    cal = 2
+    args = sample(cal)
+    t0 = time.perf_counter()
+    oracle.gdn_sequential(*args)
+    t_cal = time.perf_counter() - t0
+    nseq = int(max(1, min(full.batch, round(cal * seconds_target / max(t_cal, 1e-3)))))
+    args = sample(nseq)
+    t0 = time.perf_counter()
+    oracle.gdn_sequential(*args)
+    el = time.perf_counter() - t0
+    return {"value": nseq * T / el, "unit": "tokens/s/layer", "cores": oracle.num_threads(),
+            "sample": "%d of 256 sequences x 32 heads x %d tokens of the GDN serving workload; "
+                      "fp64 sequential gated delta rule, %.1f s" % (nseq, T, el)}
 
 
 def torch_cat(ts):
