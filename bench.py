@@ -357,6 +357,41 @@ def bench_branch(dev, reps=20, pairs=64, share=0):
             "restore_avg_us": sum(ms) / reps * 1e3}
 
 
+def bench_best_of_n(dev, n=4):
+    """Best-of-n decode on the serving state: 256 / n prompts, each forked into n continuations
+    right after a fold, then the L - 1 replay steps of the next window. With shared checkpoints
+    the n continuations read one checkpoint; with copies each reads its own."""
+    import torch
+    from ssm_decode_state_amd import binding as bd
+    from ssm_decode_state_amd import synth
+    w = synth.WORKLOADS["m2_b256"]
+    shape = w["shape"]
+    Bn, H, P, N, L = shape.batch, shape.heads, shape.dim_p, shape.dim_n, shape.window
+    A, D = synth.head_constants(shape, w["seed"])
+    out = {"workload": "mamba2_best_of_%d_b256" % n}
+    inputs = [synth.token_inputs_device(shape, w["seed"], "bench-bon", i) for i in range(2 * L)]
+    for share in (0, 1):
+        h0 = synth.initial_state_device(shape, w["seed"], w["h0_std"])
+        cfg = bd.make_config(bd.SSM_MAMBA2, Bn, H, shape.groups, P, N, L, 1, bd.SSM_IN_BF16,
+                             share_ckpt=share)
+        st = bd.State(cfg, h0, A.to(dev), D.to(dev))
+        del h0
+        y = torch.empty(Bn, H, P, device=dev)
+        for i in range(L):  # one window: ends on the fold
+            bd.ssm_replay_decode(st, inputs[i], y)
+        src = [b for b in range(0, Bn, n) for _ in range(n - 1)]
+        dst = [b + j for b in range(0, Bn, n) for j in range(1, n)]
+        _, fms = timed_calls(1, lambda i: bd.ssm_fork(st, src, dst))
+        wall, ms = timed_calls(L - 1, lambda i: bd.ssm_replay_decode(st, inputs[L + i], y))
+        out["shared" if share else "copied"] = {
+            "fork_us": fms[0] * 1e3, "replay_avg_us": sum(ms) / len(ms) * 1e3,
+            "tokens_per_s": Bn * (L - 1) / wall,
+            "checkpoint_bytes_read_per_step": (Bn // n if share else Bn) * H * P * N * 4}
+        del st
+        torch.cuda.empty_cache()
+    return out
+
+
 def bench_readcopy(dev, rc, steps=128, warm=16, layers=4, pool=16):
     """Decode with the fp8 or fp4 read copy on `layers` rotated layer instances (the fp4 copy of
     one layer fits the 256 MB last-level cache, so each step reads a different layer)."""
@@ -839,6 +874,8 @@ def main():
         if "branch" in extra:
             out["workloads"]["branch"] = bench_branch(dev)
             out["workloads"]["branch_shared"] = bench_branch(dev, share=1)
+            torch.cuda.empty_cache()
+            out["workloads"]["best_of_4"] = bench_best_of_n(dev, 4)
             torch.cuda.empty_cache()
         if "lsweep" in extra:
             out["workloads"]["window_sweep"] = bench_lsweep(dev)
