@@ -357,24 +357,25 @@ def bench_branch(dev, reps=20, pairs=64, share=0):
             "restore_avg_us": sum(ms) / reps * 1e3}
 
 
-def bench_best_of_n(dev, n=4):
-    """Best-of-n decode on the serving state: 256 / n prompts, each forked into n continuations
-    right after a fold, then the L - 1 replay steps of the next window. With shared checkpoints
-    the n continuations read one checkpoint; with copies each reads its own."""
+def bench_best_of_n(dev, n=4, kind=0):
+    """Best-of-n decode on the serving state (kind 0: Mamba-2, 1: GDN): 256 / n prompts, each
+    forked into n continuations right after a fold, then the L - 1 replay steps of the next
+    window. With shared checkpoints the n continuations read one checkpoint; with copies each
+    reads its own."""
     import torch
     from ssm_decode_state_amd import binding as bd
     from ssm_decode_state_amd import synth
-    w = synth.WORKLOADS["m2_b256"]
+    w = synth.WORKLOADS["gdn_b256" if kind else "m2_b256"]
     shape = w["shape"]
     Bn, H, P, N, L = shape.batch, shape.heads, shape.dim_p, shape.dim_n, shape.window
     A, D = synth.head_constants(shape, w["seed"])
-    out = {"workload": "mamba2_best_of_%d_b256" % n}
+    out = {"workload": "%s_best_of_%d_b256" % ("gdn" if kind else "mamba2", n)}
     inputs = [synth.token_inputs_device(shape, w["seed"], "bench-bon", i) for i in range(2 * L)]
     for share in (0, 1):
         h0 = synth.initial_state_device(shape, w["seed"], w["h0_std"])
-        cfg = bd.make_config(bd.SSM_MAMBA2, Bn, H, shape.groups, P, N, L, 1, bd.SSM_IN_BF16,
+        cfg = bd.make_config(shape.kind, Bn, H, shape.groups, P, N, L, 1, bd.SSM_IN_BF16,
                              share_ckpt=share)
-        st = bd.State(cfg, h0, A.to(dev), D.to(dev))
+        st = bd.State(cfg, h0, None if A is None else A.to(dev), None if D is None else D.to(dev))
         del h0
         y = torch.empty(Bn, H, P, device=dev)
         for i in range(L):  # one window: ends on the fold
@@ -876,6 +877,8 @@ def main():
             out["workloads"]["branch_shared"] = bench_branch(dev, share=1)
             torch.cuda.empty_cache()
             out["workloads"]["best_of_4"] = bench_best_of_n(dev, 4)
+            torch.cuda.empty_cache()
+            out["workloads"]["gdn_best_of_4"] = bench_best_of_n(dev, 4, kind=1)
             torch.cuda.empty_cache()
         if "lsweep" in extra:
             out["workloads"]["window_sweep"] = bench_lsweep(dev)
