@@ -188,6 +188,8 @@ ssm_status ssm_replay_decode(ssm_state *st, const void *in, float *y, void *stre
 /* Fold buffered entries into the checkpoint (news, para 3) and rewrite the read copy.
  * SSM_FLUSH_IF_FULL: every sequence whose committed count is >= L folds its oldest L entries
  * (a device-side predicate per sequence). SSM_FLUSH_ALL: fold every committed entry (export).
+ * With share_ckpt every fold launch (here, and the ones decode and rollback make) also moves each
+ * sequence that shares a checkpoint slot to a slot of its own, folding what it holds (ssm_fork).
  * Errors: SSM_E_STATE if drafts are pending. */
 ssm_status ssm_flush(ssm_state *st, int32_t mode, void *stream);
 
