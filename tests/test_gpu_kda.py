@@ -132,12 +132,14 @@ def test_kda_conventional_step(B, H, dv, dk, bf16):
     assert_close(got, ST, (-2, -1), "KDA conventional state")
 
 
-@pytest.mark.parametrize("case", ["small", "odd", "serving"])
+@pytest.mark.parametrize("case", ["small", "odd", "wide", "serving"])
 def test_kda_spec_rounds_match_oracle(case):
     if case == "small":
         shape, seed, R, s0 = _kshape(2, 3, 64, 64, 4, False, 4), 151, 20, 0.3
     elif case == "odd":
         shape, seed, R, s0 = _kshape(3, 2, 128, 64, 8, True, 3), 152, 16, 0.3
+    elif case == "wide":  # eight drafts: the eight-query verify
+        shape, seed, R, s0 = _kshape(2, 3, 128, 128, 16, True, 8), 154, 16, 0.3
     else:
         shape, seed, R, s0 = _kshape(256, 32, 128, 128, 16, True, 4), 153, 16, 0.3162
     S = shape.max_draft

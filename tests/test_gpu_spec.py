@@ -104,7 +104,7 @@ def oracle_spec(A, D, h0, drafts, acc, pairs, shape, S):
     return y, hT, sn, accp
 
 
-@pytest.mark.parametrize("case", ["small", "odd", "serving"])
+@pytest.mark.parametrize("case", ["small", "odd", "six", "wide", "serving"])
 def test_spec_rounds_match_oracle(case):
     if case == "small":
         w = synth.WORKLOADS["m2_small"]
@@ -112,6 +112,12 @@ def test_spec_rounds_match_oracle(case):
     elif case == "odd":
         shape = synth.Shape(synth.MAMBA2, 3, 6, 3, 64, 64, 8, 3, in_bf16=True)
         seed, R, h0s = 21, 30, 0.3
+    elif case == "six":  # six drafts: the eight-query verify with two unused queries, P = 32
+        shape = synth.Shape(synth.MAMBA2, 2, 5, 5, 32, 64, 8, 6, in_bf16=True)
+        seed, R, h0s = 22, 20, 0.3
+    elif case == "wide":  # eight drafts over a 32-entry window: up to 39 entries per call
+        shape = synth.Shape(synth.MAMBA2, 3, 4, 2, 64, 128, 32, 8, in_bf16=True)
+        seed, R, h0s = 23, 24, 0.3
     else:
         w = synth.WORKLOADS["m2_b256_spec"]
         shape, seed, R, h0s = w["shape"], w["seed"], w["rounds"], w["h0_std"]
