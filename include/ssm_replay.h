@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 3
+#define SSM_ABI_VERSION 4
 
 typedef int32_t ssm_status;
 enum {
@@ -141,6 +141,10 @@ typedef struct ssm_state {
     void *mem;                /* device memory of lay.total_bytes, owned by the caller */
     const float *A;           /* Mamba-2: device [H] (A < 0), borrowed; NULL for GDN */
     const float *D;           /* Mamba-2: device [H], borrowed; NULL for GDN */
+    int32_t ring_start;       /* every sequence's ring start while all sequences sit at one start
+                                 and one count (lock-step decoding, checkpoints not shared), else
+                                 -1. The replay and fold launches then take start and count as
+                                 arguments instead of reading them from the device. */
 } ssm_state;
 
 /* Mamba-2 token inputs (device pointers, layouts above). */

@@ -52,7 +52,7 @@ class ssm_state(ctypes.Structure):
     _fields_ = [("magic", ctypes.c_uint32), ("pending", ctypes.c_int32),
                 ("count_lo", ctypes.c_int32), ("count_hi", ctypes.c_int32),
                 ("cfg", ssm_config), ("lay", ssm_layout), ("mem", ctypes.c_void_p),
-                ("A", ctypes.c_void_p), ("D", ctypes.c_void_p)]
+                ("A", ctypes.c_void_p), ("D", ctypes.c_void_p), ("ring_start", ctypes.c_int32)]
 
 
 class ssm_m2_in(ctypes.Structure):

@@ -87,9 +87,9 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_replay_kernel(GdnArgs a) {
     const int H = a.heads;
     const int head = b * H + h;
     const int cap = a.cap, nq = a.ntok;
-    const int4 pt = *reinterpret_cast<const int4*>(a.ptr + kPtrInts * head);
-    const int start = uniform(pt.x), count = uniform(pt.y);
-    const long th = a.share ? (long)uniform(pt.z) * H + h : head;  // this head's checkpoint tile
+    const HeadPtr pt = head_ptr(a.ptr, a.hstart, a.hcount, head, b);
+    const int start = pt.start, count = pt.count;
+    const long th = a.share ? (long)pt.slot * H + h : head;  // this head's checkpoint tile
     const int kmax = count + nq;
     // row of token j (clamped to the call's tokens) in the [batch][ntok][H] inputs
     auto tok = [&](int j) -> long { return ((long)b * nq + min(max(j, 0), nq - 1)) * H + h; };
@@ -479,8 +479,8 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_flush_kernel(GdnArgs a, int mod
     const int h = blockIdx.x, b = blockIdx.y;
     const int head = b * a.heads + h;
     const int cap = a.cap;
-    const int4 pt = *reinterpret_cast<const int4*>(a.ptr + kPtrInts * head);
-    const int start = uniform(pt.x), count = uniform(pt.y), slot = uniform(pt.z);
+    const HeadPtr pt = head_ptr(a.ptr, a.hstart, a.hcount, head, b);
+    const int start = pt.start, count = pt.count, slot = pt.slot;
     // copy-on-write of a shared checkpoint: a sequence that must move folds whatever it holds
     const FoldTarget ft = fold_target(a.refcnt, a.share, a.batch, b, slot);
     // FUSED: the buffered entries and this token; otherwise the oldest L (or all) entries

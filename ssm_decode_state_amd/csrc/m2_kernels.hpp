@@ -77,10 +77,10 @@ __global__ __launch_bounds__(256) void m2_replay_kernel(M2Args a) {
     const int cap = a.cap, nq = a.ntok;
     const int H = a.heads, Gn = a.groups;
 
-    const int4 pt = *reinterpret_cast<const int4*>(a.ptr + kPtrInts * head);
-    const int start = uniform(pt.x);
-    const int count = uniform(pt.y);
-    const long th = a.share ? (long)uniform(pt.z) * H + h : head;  // this head's checkpoint tile
+    const HeadPtr pt = head_ptr(a.ptr, a.hstart, a.hcount, head, b);
+    const int start = pt.start;
+    const int count = pt.count;
+    const long th = a.share ? (long)pt.slot * H + h : head;  // this head's checkpoint tile
     const int kmax = count + nq;
     const float A = a.A[h];
     const float D = a.D[h];
@@ -335,10 +335,10 @@ __attribute__((amdgpu_waves_per_eu(2))) void m2_fold_kernel(M2Args a, int mode_a
     const int grp = h / (H / a.groups);
     const int bg = b * a.groups + grp;
     const int cap = a.cap;
-    const int4 pt = *reinterpret_cast<const int4*>(a.ptr + kPtrInts * head);
-    const int start = uniform(pt.x);
-    const int count = uniform(pt.y);
-    const int slot = uniform(pt.z);
+    const HeadPtr pt = head_ptr(a.ptr, a.hstart, a.hcount, head, b);
+    const int start = pt.start;
+    const int count = pt.count;
+    const int slot = pt.slot;
     // copy-on-write of a shared checkpoint: a sequence that must move folds whatever it holds
     const FoldTarget ft = fold_target(a.refcnt, a.share, a.batch, b, slot);
     int nfold, nring;

@@ -97,6 +97,22 @@ template <typename T> T* at(const ssm_state* st, uint64_t off) {
     return reinterpret_cast<T*>(static_cast<char*>(st->mem) + off);
 }
 
+// Start and count of every sequence's ring when the host knows them (see ssm_state.ring_start):
+// the kernels then skip their dependent read of the pointer entries. hstart = -1 otherwise.
+void known_ptr(const ssm_state* st, int* hstart, int* hcount) {
+    const bool known = !st->cfg.share_ckpt && st->ring_start >= 0 && st->count_lo == st->count_hi;
+    *hstart = known ? st->ring_start : -1;
+    *hcount = known ? st->count_lo : 0;
+}
+
+// The host's copy of the ring start after a fold of nfold entries from every sequence.
+void advance_start(ssm_state* st, int nfold) {
+    if (st->ring_start >= 0 && st->count_lo == st->count_hi)
+        st->ring_start = (st->ring_start + nfold) % st->lay.ring_cap;
+    else
+        st->ring_start = -1;
+}
+
 ssm::M2Args m2_args(const ssm_state* st) {
     ssm::M2Args a;
     memset(&a, 0, sizeof(a));
@@ -119,6 +135,7 @@ ssm::M2Args m2_args(const ssm_state* st) {
     a.groups = st->cfg.groups;
     a.cap = L.ring_cap;
     a.window = st->cfg.window;
+    known_ptr(st, &a.hstart, &a.hcount);
     return a;
 }
 
@@ -144,6 +161,7 @@ ssm::GdnArgs gdn_args(const ssm_state* st) {
     a.cap = L.ring_cap;
     a.window = st->cfg.window;
     a.kda = st->cfg.kind == SSM_KDA;
+    known_ptr(st, &a.hstart, &a.hcount);
     return a;
 }
 
@@ -187,7 +205,12 @@ hipError_t recount(ssm_state* st, hipStream_t s) {
 }
 
 ssm_status launch_flush(ssm_state* st, int mode_all, hipStream_t s) {
-    if (st->cfg.batch == 0) return SSM_OK;
+    // lock step: every sequence folds all its entries (ALL) or the oldest L when full (IF_FULL)
+    const int nfold = mode_all ? st->count_lo : (st->count_lo >= st->cfg.window ? st->cfg.window : 0);
+    if (st->cfg.batch == 0) {
+        advance_start(st, nfold);
+        return SSM_OK;
+    }
     hipError_t e;
     if (st->cfg.kind == SSM_MAMBA2) {
         ssm::M2Args a = m2_args(st);
@@ -200,6 +223,7 @@ ssm_status launch_flush(ssm_state* st, int mode_all, hipStream_t s) {
     }
     if (e == hipErrorNotSupported) return SSM_E_UNSUPPORTED;
     if (e != hipSuccess) return SSM_E_HIP;
+    advance_start(st, nfold);
     // a sequence that shared its checkpoint folded everything it held: its count may now be 0
     if (st->cfg.share_ckpt) st->count_lo = 0;
     return hip_status(recount(st, s));
@@ -248,6 +272,7 @@ ssm_status ssm_ckpt_init(ssm_state* st, const ssm_config* cfg, void* mem, uint64
         if (!aligned16(A) || !aligned16(D)) return SSM_E_ALIGN;
     }
     memset(st, 0, sizeof(*st));
+    st->ring_start = cfg->share_ckpt ? -1 : 0;  // every pointer entry starts at {0, 0}
     st->cfg = *cfg;
     st->lay = lay;
     st->mem = mem;
@@ -311,6 +336,7 @@ ssm_status ssm_replay_decode(ssm_state* st, const void* in, float* y, void* stre
                                      st->cfg.readcopy, 2, 0, hs);
             if (e == hipSuccess) e = recount(st, hs);
             if (e != hipSuccess) return SSM_E_HIP;
+            advance_start(st, L);  // the L - 1 buffered entries and this token
             st->count_lo = st->count_hi = 0;
             return SSM_OK;
         }
@@ -329,6 +355,7 @@ ssm_status ssm_replay_decode(ssm_state* st, const void* in, float* y, void* stre
                                       st->cfg.readcopy, 2, 0, hs);
             if (e == hipSuccess) e = recount(st, hs);
             if (e != hipSuccess) return SSM_E_HIP;
+            advance_start(st, L);  // the L - 1 buffered entries and this token
             st->count_lo = st->count_hi = 0;
             return SSM_OK;
         }
@@ -415,6 +442,7 @@ ssm_status ssm_spec_rollback(ssm_state* st, const int32_t* n_accept, void* strea
                                             st->cfg.heads, st->pending, at<int>(st, st->lay.off_flags),
                                             hs);
     if (e != hipSuccess) return SSM_E_HIP;
+    st->ring_start = -1;  // the accepted counts are known only on the device
     st->count_hi += st->pending;
     st->pending = 0;
     // a flush fires whenever a sequence's committed count reaches L
@@ -436,6 +464,7 @@ ssm_status ssm_restore(ssm_state* st, const int32_t* n_back, void* stream) {
                                              st->cfg.heads, as_stream(stream));
     if (e != hipSuccess) return SSM_E_HIP;
     st->count_lo = 0;  // the rewound counts are known only on the device
+    st->ring_start = -1;
     return SSM_OK;
 }
 
@@ -501,7 +530,9 @@ ssm_status ssm_fork(ssm_state* st, const int32_t* src, const int32_t* dst, int32
         if (e != hipSuccess) return SSM_E_HIP;
     }
     if (recount(st, hs) != hipSuccess) return SSM_E_HIP;
-    return SSM_OK;  // the copies' counts are sources' counts: the host bounds still hold
+    // the copies' pointers are their sources': the host bounds (and a start that every
+    // sequence shares) still hold
+    return SSM_OK;
 }
 
 ssm_status ssm_ckpt_export(const ssm_state* st, float* h_out, void* stream) {

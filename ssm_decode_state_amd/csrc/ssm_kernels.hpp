@@ -26,6 +26,20 @@ __device__ __forceinline__ FoldTarget fold_target(const int* refcnt, int share, 
     return {refcnt[own0] == 0 ? own0 : own1, true};
 }
 
+// Ring pointers of one head. When the host knows them (every sequence at the same start and
+// count, checkpoints not shared, so slot == sequence) they come in as kernel arguments and the
+// wave starts its loads without a dependent round trip to the pointer entry; hstart < 0 means
+// read the entry.
+struct HeadPtr {
+    int start, count, slot;
+};
+__device__ __forceinline__ HeadPtr head_ptr(const int* ptr, int hstart, int hcount, long head, int b) {
+    if (hstart >= 0) return {hstart, hcount, b};
+    const int4 pt = *reinterpret_cast<const int4*>(ptr + kPtrInts * head);
+    return {__builtin_amdgcn_readfirstlane(pt.x), __builtin_amdgcn_readfirstlane(pt.y),
+            __builtin_amdgcn_readfirstlane(pt.z)};
+}
+
 // Everything a Mamba-2 replay / verify / flush launch touches. Device pointers into one state's
 // memory (see the layout in ssm_replay.h) plus this call's inputs and outputs.
 struct M2Args {
@@ -48,6 +62,7 @@ struct M2Args {
     float* y;           // [batch][ntok][H][P]
     int batch, heads, groups, cap, ntok, window;
     int share;          // shared checkpoints enabled (slots 0 .. 2 batch - 1)
+    int hstart, hcount; // every head's {start, count} when known on the host, else hstart = -1
 };
 
 struct M2ConvArgs {
@@ -87,6 +102,7 @@ struct GdnArgs {
     int batch, heads, cap, ntok, window;
     int kda;  // Kimi Delta Attention: g holds dk decays per entry (per-channel gate)
     int share;
+    int hstart, hcount;  // as M2Args
 };
 
 struct GdnConvArgs {

@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert bd.ssm_abi_version() == 3
+    assert bd.ssm_abi_version() == 4
     for s in range(-7, 1):
         assert bd.ssm_status_string(s) not in ("", "unknown status")
     assert bd.ssm_status_string(-99) == "unknown status"
@@ -312,3 +312,42 @@ def test_restore_and_fork_validation():
                None) == bd.SSM_OK
     assert raw("ssm_restore", ctypes.byref(st), v(FAKE), None) == bd.SSM_E_STATE
     assert raw("ssm_fork", ctypes.byref(st), I(), I(), 0, None) == bd.SSM_E_STATE
+
+
+def test_host_ring_start_follows_the_ring_model():
+    """The host's copy of the ring start (used to launch without reading the device pointers)
+    moves exactly as the oracle's ring model moves every sequence's start in lock step, and is
+    dropped once the counts are known only on the device."""
+    from oracle.ring import Ring
+
+    for window, max_draft in ((16, 1), (4, 4), (5, 3)):
+        st = empty_state(max_draft=max_draft, window=window)
+        ring = Ring(cap=st.lay.ring_cap, L=window)
+        y = ctypes.c_void_p(FAKE)
+        assert st.ring_start == 0
+        for t in range(3 * window + 2):
+            assert raw("ssm_replay_decode", ctypes.byref(st), ctypes.byref(m2_in()), y, None) == bd.SSM_OK
+            ring.decode()
+            ring.flush_if_full()
+            assert (st.ring_start, st.count_lo, st.count_hi) == (ring.start, ring.count, ring.count), t
+        assert raw("ssm_flush", ctypes.byref(st), bd.SSM_FLUSH_ALL, None) == bd.SSM_OK
+        ring.flush_all()
+        assert (st.ring_start, st.count_hi) == (ring.start, 0)
+        for _ in range(window - 1):
+            assert raw("ssm_replay_decode", ctypes.byref(st), ctypes.byref(m2_in()), y, None) == bd.SSM_OK
+            ring.decode()
+        assert st.ring_start == ring.start
+        # drafts keep the start (only a rollback makes the counts device-side)
+        assert raw("ssm_spec_append", ctypes.byref(st), 1, ctypes.byref(m2_in()), y, None) == bd.SSM_OK
+        assert st.ring_start == ring.start
+        assert raw("ssm_spec_rollback", ctypes.byref(st), y, None) == bd.SSM_OK
+        assert st.ring_start == -1
+        # and it stays unknown: the launches read the device pointers from here on
+        assert raw("ssm_flush", ctypes.byref(st), bd.SSM_FLUSH_ALL, None) == bd.SSM_OK
+        assert st.ring_start == -1
+
+    st = empty_state(window=4)
+    assert raw("ssm_restore", ctypes.byref(st), ctypes.c_void_p(FAKE), None) == bd.SSM_OK
+    assert st.ring_start == -1
+    st = empty_state(window=4, share_ckpt=1)
+    assert st.ring_start == -1  # shared checkpoints: the slot comes from the device

@@ -29,7 +29,7 @@ def tiles_of(st, pairs):
 def run_gdn(shape, seed, T, s0_std, pairs, scale=1.0):
     S0 = synth.initial_state(shape, seed, s0_std) if s0_std else None
     cfg = bd.make_config(bd.SSM_GDN, shape.batch, shape.heads, shape.heads, shape.dim_p,
-                         shape.dim_n, shape.window, 1,
+                         shape.dim_n, shape.window, shape.max_draft,
                          bd.SSM_IN_BF16 if shape.in_bf16 else bd.SSM_IN_F32, 0, scale)
     st = bd.State(cfg, None if S0 is None else S0.to(DEV), None, None)
     tok = GdnTokens(shape, seed)
@@ -50,24 +50,35 @@ def run_gdn(shape, seed, T, s0_std, pairs, scale=1.0):
     return go, (np.stack(cks, 1) if cks else None), oo, osn, st, S0, tok
 
 
-def _gshape(B, H, dv, dk, L, bf16=True):
-    return synth.Shape(synth.GDN, B, H, H, dv, dk, L, 1, in_bf16=bf16)
+def _gshape(B, H, dv, dk, L, bf16=True, S=1):
+    return synth.Shape(synth.GDN, B, H, H, dv, dk, L, S, in_bf16=bf16)
 
 
-@pytest.mark.parametrize("B,H,dv,dk,L,bf16,T", [
-    (2, 3, 64, 64, 4, True, 21),
-    (1, 2, 128, 128, 16, False, 37),
-    (2, 2, 128, 64, 8, True, 19),
-    (1, 3, 64, 128, 32, True, 70),
-    (2, 2, 128, 128, 1, True, 5),
+def check_lockstep_pointers(st, T, L):
+    """Lock step: the start and count the launches took from the host are the device's."""
+    c = st.cfg
+    assert st.st.ring_start == (T // L) * L % st.layout.ring_cap
+    p = st.region(st.layout.off_ptr, c.batch * c.heads * 16).view(torch.int32)
+    p = p.view(c.batch, c.heads, 4).cpu()
+    assert torch.all(p[..., 0] == st.st.ring_start) and torch.all(p[..., 1] == st.st.count_lo)
+
+
+@pytest.mark.parametrize("B,H,dv,dk,L,bf16,T,S", [
+    (2, 3, 64, 64, 4, True, 21, 1),
+    (1, 2, 128, 128, 16, False, 37, 1),
+    (2, 2, 128, 64, 8, True, 19, 1),
+    (1, 3, 64, 128, 32, True, 70, 1),
+    (2, 2, 128, 128, 1, True, 5, 1),
+    (2, 2, 128, 128, 16, True, 150, 4),  # cap 19: lock-step windows start at every slot in turn
 ])
-def test_gdn_decode_shapes(B, H, dv, dk, L, bf16, T):
-    shape = _gshape(B, H, dv, dk, L, bf16)
+def test_gdn_decode_shapes(B, H, dv, dk, L, bf16, T, S):
+    shape = _gshape(B, H, dv, dk, L, bf16, S)
     pairs = [(b, h) for b in range(B) for h in range(H)]
-    go, gck, oo, osn, *_ = run_gdn(shape, 70 + T, T, 0.3162, pairs, scale=0.5 if L == 8 else 1.0)
+    go, gck, oo, osn, st, *_ = run_gdn(shape, 70 + T, T, 0.3162, pairs, scale=0.5 if L == 8 else 1.0)
     assert_close(go, oo, (-1,), "GDN replay outputs")
     if gck is not None:
         assert_close(gck, osn, (-2, -1), "GDN flushed checkpoints")
+    check_lockstep_pointers(st, T, L)
 
 
 def test_gdn_serving_batch_sampled_heads():

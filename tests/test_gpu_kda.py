@@ -64,20 +64,25 @@ def run_kda(shape, seed, T, s0_std, pairs, scale=1.0):
     return go, (np.stack(cks, 1) if cks else None), oo, osn, st, S0, tok
 
 
-@pytest.mark.parametrize("B,H,dv,dk,L,bf16,T", [
-    (2, 3, 64, 64, 4, True, 21),
-    (1, 2, 128, 128, 16, False, 37),
-    (2, 2, 128, 64, 8, True, 19),
-    (1, 3, 64, 128, 32, True, 70),      # more than 16 entries per call, two fold chunks
-    (2, 2, 128, 128, 1, True, 5),       # L = 1: every token through the fused fold
+@pytest.mark.parametrize("B,H,dv,dk,L,bf16,T,S", [
+    (2, 3, 64, 64, 4, True, 21, 1),
+    (1, 2, 128, 128, 16, False, 37, 1),
+    (2, 2, 128, 64, 8, True, 19, 1),
+    (1, 3, 64, 128, 32, True, 70, 1),      # more than 16 entries per call, two fold chunks
+    (2, 2, 128, 128, 1, True, 5, 1),       # L = 1: every token through the fused fold
+    (1, 2, 128, 128, 8, True, 75, 3),      # cap 10: lock-step windows start at every slot
 ])
-def test_kda_decode_shapes(B, H, dv, dk, L, bf16, T):
-    shape = _kshape(B, H, dv, dk, L, bf16)
+def test_kda_decode_shapes(B, H, dv, dk, L, bf16, T, S):
+    shape = _kshape(B, H, dv, dk, L, bf16, S)
     pairs = [(b, h) for b in range(B) for h in range(H)]
-    go, gck, oo, osn, *_ = run_kda(shape, 170 + T, T, 0.3162, pairs, scale=0.5 if L == 8 else 1.0)
+    go, gck, oo, osn, st, *_ = run_kda(shape, 170 + T, T, 0.3162, pairs, scale=0.5 if L == 8 else 1.0)
     assert_close(go, oo, (-1,), "KDA replay outputs")
     if gck is not None:
         assert_close(gck, osn, (-2, -1), "KDA flushed checkpoints")
+    c = st.cfg
+    assert st.st.ring_start == (T // L) * L % st.layout.ring_cap
+    p = st.region(st.layout.off_ptr, c.batch * c.heads * 16).view(torch.int32).view(c.batch, c.heads, 4).cpu()
+    assert torch.all(p[..., 0] == st.st.ring_start) and torch.all(p[..., 1] == st.st.count_lo)
 
 
 def test_kda_serving_batch_sampled_heads():

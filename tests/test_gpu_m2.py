@@ -84,22 +84,30 @@ def test_small_workload_every_output_and_checkpoint():
     assert torch.all(p[..., 1] == 0) and torch.all(p[..., 0] == (w["steps"] % st.layout.ring_cap))
 
 
-@pytest.mark.parametrize("B,H,G,P,N,L,bf16,T", [
-    (3, 6, 3, 64, 128, 16, True, 37),    # ragged head blocks, B/C shared by pairs of heads
-    (2, 5, 5, 32, 64, 8, False, 19),
-    (1, 4, 2, 16, 128, 5, True, 13),
-    (2, 8, 8, 64, 16, 1, False, 5),      # L = 1: every token is folded at once
-    (2, 4, 1, 64, 64, 32, True, 70),     # L = 32, one B/C group for all heads
-    (1, 3, 3, 64, 32, 7, True, 22),
-    (2, 6, 3, 32, 16, 4, True, 11),      # two row copies per wave, one quad per lane
+@pytest.mark.parametrize("B,H,G,P,N,L,bf16,T,S", [
+    (3, 6, 3, 64, 128, 16, True, 37, 1),    # ragged head blocks, B/C shared by pairs of heads
+    (2, 5, 5, 32, 64, 8, False, 19, 1),
+    (1, 4, 2, 16, 128, 5, True, 13, 1),
+    (2, 8, 8, 64, 16, 1, False, 5, 1),      # L = 1: every token is folded at once
+    (2, 4, 1, 64, 64, 32, True, 70, 1),     # L = 32, one B/C group for all heads
+    (1, 3, 3, 64, 32, 7, True, 22, 1),
+    (2, 6, 3, 32, 16, 4, True, 11, 1),      # two row copies per wave, one quad per lane
+    # rings with draft room (cap = L + S - 1): lock-step windows start at every slot in turn
+    (2, 4, 4, 64, 128, 16, True, 150, 4),
+    (1, 3, 3, 64, 32, 7, True, 60, 3),
 ])
-def test_decode_shapes(B, H, G, P, N, L, bf16, T):
-    shape = _shape(B, H, G, P, N, L, bf16)
+def test_decode_shapes(B, H, G, P, N, L, bf16, T, S):
+    shape = _shape(B, H, G, P, N, L, bf16, S)
     pairs = [(b, h) for b in range(B) for h in range(H)]
-    gy, gck, oy, osn, _ = run_decode(shape, 11 + T, T, 0.3, pairs)
+    gy, gck, oy, osn, st = run_decode(shape, 11 + T, T, 0.3, pairs)
     assert_close(gy, oy, (-1,), "replay outputs")
     if gck is not None:
         assert_close(gck, osn, (-2, -1), "flushed checkpoints")
+    # lock step: the start and count the launches took from the host are the device's
+    cap = st.layout.ring_cap
+    assert st.st.ring_start == (T // L) * L % cap
+    p = pointers(st)
+    assert torch.all(p[..., 0] == st.st.ring_start) and torch.all(p[..., 1] == st.st.count_lo)
 
 
 def test_serving_batch_sampled_heads():
