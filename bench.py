@@ -268,6 +268,67 @@ def bench_lsweep(dev, steps=96, warm=32):
     return out
 
 
+def bench_bsweep(dev, batches=(1, 4, 16, 64, 256), min_bytes=512 << 20, max_layers=256, reps=4):
+    """Per-token latency against batch size: the time of one decode step of one layer, replay
+    against the conventional step, on the Mamba-2 and GDN serving head shapes (L = 16). Each point
+    cycles through enough layer instances that their states (at least min_bytes, twice the 256 MB
+    last-level cache) are read from HBM, as the layers of a model are between their visits. One
+    HIP graph holds a window's steps, every layer in turn, for each path."""
+    import dataclasses
+    import torch
+    from ssm_decode_state_amd import binding as bd
+    from ssm_decode_state_amd import synth
+    out = []
+    for kind, wname in ((bd.SSM_MAMBA2, "m2_b256"), (bd.SSM_GDN, "gdn_b256")):
+        w = synth.WORKLOADS[wname]
+        for Bn in batches:
+            shape = dataclasses.replace(w["shape"], batch=Bn)
+            H, G, P, N, L = shape.heads, shape.groups, shape.dim_p, shape.dim_n, shape.window
+            state = Bn * H * P * N * 4
+            layers = min(max_layers, max(2, -(-min_bytes // state)))
+            if kind == bd.SSM_MAMBA2:
+                A, D = synth.head_constants(shape, w["seed"])
+                A, D = A.to(dev), D.to(dev)
+            else:
+                A = D = None
+            cfg = bd.make_config(kind, Bn, H, G, P, N, L, 1, bd.SSM_IN_BF16)
+            inputs = [synth.token_inputs_device(shape, w["seed"], "bsweep", t) for t in range(L)]
+            y = torch.empty(Bn, H, P, device=dev)
+            res = {"layer": "mamba2" if kind == bd.SSM_MAMBA2 else "gdn", "batch": Bn,
+                   "layers_rotated": layers}
+            for path in ("replay", "conventional"):
+                if path == "replay":
+                    objs = [bd.State(cfg, None, A, D) for _ in range(layers)]
+                    step = lambda o, t: bd.ssm_replay_decode(o, inputs[t], y)  # noqa: E731
+                else:
+                    objs = [torch.zeros(Bn * H * P * N, device=dev) for _ in range(layers)]
+                    step = lambda o, t: bd.ssm_conventional_step(cfg, o, inputs[t], A, D, y)  # noqa: E731
+                for t in range(L):  # one eager window: every state back at a window boundary
+                    for o in objs:
+                        step(o, t)
+                torch.cuda.synchronize()
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    for t in range(L):
+                        for o in objs:
+                            step(o, t)
+                g.replay()
+                torch.cuda.synchronize()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for _ in range(reps):
+                    g.replay()
+                e1.record()
+                torch.cuda.synchronize()
+                res[path + "_us_per_step"] = e0.elapsed_time(e1) * 1e3 / (reps * L * layers)
+                del g, objs
+                torch.cuda.empty_cache()
+            res["replay_tokens_per_s"] = Bn / (res["replay_us_per_step"] * 1e-6)
+            res["speedup_vs_conventional"] = res["conventional_us_per_step"] / res["replay_us_per_step"]
+            out.append(res)
+    return out
+
+
 def graph_decode(st, inputs, y, L, K, W):
     """Time K lock-step decode steps as K / L replays of a HIP graph holding one window. Returns
     None (and the eager figures stand) if the graph cannot be captured."""
@@ -696,7 +757,8 @@ def main():
     ap.add_argument("--workloads", default="all",
                     help="comma list of extra workloads: spec, fp8, fp4, gdn, gdn_spec, "
                          "gdn_fp8, gdn_fp4, kda, g8 (8 B/C groups), lsweep (window 4..32), "
-                         "branch (fork and restore), kda_fp8, kda_fp4, kda_spec; 'all' or 'none'")
+                         "bsweep (batch 1..256), branch (fork and restore), kda_fp8, kda_fp4, "
+                         "kda_spec; 'all' or 'none'")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -854,7 +916,7 @@ def main():
                            "avg_us": e0.elapsed_time(e1) / 5 * 1e3}
 
     extra = ({"spec", "fp8", "fp4", "gdn", "gdn_spec", "gdn_fp8", "gdn_fp4", "kda", "g8", "lsweep",
-              "branch", "kda_fp8", "kda_fp4", "kda_spec"}
+              "bsweep", "branch", "kda_fp8", "kda_fp4", "kda_spec"}
              if args.workloads == "all" else
              set() if args.workloads == "none" else set(args.workloads.split(",")))
     if extra:
@@ -882,6 +944,9 @@ def main():
             torch.cuda.empty_cache()
         if "lsweep" in extra:
             out["workloads"]["window_sweep"] = bench_lsweep(dev)
+            torch.cuda.empty_cache()
+        if "bsweep" in extra:
+            out["workloads"]["batch_sweep"] = bench_bsweep(dev)
             torch.cuda.empty_cache()
         if "fp8" in extra:
             out["workloads"]["readcopy_fp8"] = bench_readcopy(dev, 1)
