@@ -137,8 +137,14 @@ __global__ __launch_bounds__(256) void m2_replay_kernel(M2Args a) {
     float4 hv[G::kQPL];
     const float4* tile = reinterpret_cast<const float4*>(a.ckpt) + th * (P * N / 4);
     if constexpr (RC == 0) {
+        // issued in the order the row dots use them (the scheduler would otherwise reorder the
+        // loads, and the first dot would wait for the whole tile): the dots then run while the
+        // rest of the tile is still arriving
 #pragma unroll
-        for (int j = 0; j < G::kQPL; ++j) hv[j] = ld_stream(tile + (gq + G::kGrp * j) * P + row);
+        for (int j = 0; j < G::kQPL; ++j) {
+            hv[j] = ld_stream(tile + (gq + G::kGrp * j) * P + row);
+            __builtin_amdgcn_sched_barrier(0);
+        }
     }
     asm volatile("" ::: "memory");  // keep every staging store below the stream issue
     __builtin_amdgcn_sched_barrier(0);
