@@ -61,10 +61,11 @@ def pmc_traffic():
 def m2_replay_bytes_per_head(P, N, k, esz=2):
     """Algorithmic bytes of one replay launch for one head at committed count k (after append):
     checkpoint read + the k-1 older ring entries read (x, B, dt) + the token's inputs read and
-    appended (x, B, C, dt) + y written + the pointer pair read and the count written."""
+    appended (x, B, C, dt) + y written + the count written (lock-step launches take start and
+    count from the host; a launch that reads the pointer entry adds 16 bytes)."""
     entry_rd = P * esz + N * esz + 4
     token = P * esz + 2 * N * esz + 4
-    return P * N * 4 + (k - 1) * entry_rd + 2 * token + P * 4 + 12
+    return P * N * 4 + (k - 1) * entry_rd + 2 * token + P * 4 + 4
 
 
 def m2_flush_bytes_per_head(P, N, L, esz=2):
@@ -99,11 +100,11 @@ def m2_rc_replay_bytes_per_head(P, N, k, rc, esz=2):
 
 def gdn_replay_bytes_per_head(dv, dk, k, esz=2, gsz=4):
     """GDN replay for one head at count k: state read + k-1 older entries (k, v, beta, g) + this
-    token read and appended (q, k, v, beta, g) + o written + pointers. gsz: bytes of g per entry
-    (4; Kimi Delta Attention: 4 dk)."""
+    token read and appended (q, k, v, beta, g) + o written + the count written (as for
+    Mamba-2). gsz: bytes of g per entry (4; Kimi Delta Attention: 4 dk)."""
     entry_rd = dk * esz + dv * esz + 4 + gsz
     token = 2 * dk * esz + dv * esz + 4 + gsz
-    return dv * dk * 4 + (k - 1) * entry_rd + 2 * token + dv * 4 + 12
+    return dv * dk * 4 + (k - 1) * entry_rd + 2 * token + dv * 4 + 4
 
 
 def gdn_verify_bytes_per_head(dv, dk, kc, S, esz=2, gsz=4):
