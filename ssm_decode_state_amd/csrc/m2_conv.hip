@@ -6,13 +6,13 @@ namespace ssm {
 
 template <int P, int N, typename TIN>
 static hipError_t launch_conv_pn(const M2ConvArgs& a, hipStream_t s) {
-    hipLaunchKernelGGL((m2_conv_kernel<P, N, TIN>), head_grid(a.batch, a.heads), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((m2_conv_kernel<P, N, TIN>), head_grid(a.batch, a.heads), head_block(a.batch, a.heads), 0, s, a);
     return hipGetLastError();
 }
 
 template <int P, int N, typename TIN>
 static hipError_t launch_snap_pn(const M2ConvArgs& a, hipStream_t s) {
-    const dim3 grid = head_grid(a.batch, a.heads), block(256);
+    const dim3 grid = head_grid(a.batch, a.heads), block = head_block(a.batch, a.heads);
     if (a.ntok <= 4)
         hipLaunchKernelGGL((m2_snap_kernel<P, N, TIN, 4>), grid, block, 0, s, a);
     else

@@ -6,7 +6,7 @@ namespace ssm {
 
 template <int P, int N, typename TIN, int RC>
 static hipError_t launch_decode_pn(const M2Args& a, int maxe, hipStream_t s) {
-    const dim3 grid = head_grid(a.batch, a.heads), block(256);
+    const dim3 grid = head_grid(a.batch, a.heads), block = head_block(a.batch, a.heads);
     if (maxe <= 16)
         hipLaunchKernelGGL((m2_replay_kernel<P, N, TIN, RC, 1, 16, true>), grid, block, 0, s, a);
     else

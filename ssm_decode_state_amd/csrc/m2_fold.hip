@@ -8,10 +8,10 @@ template <int P, int N, typename TIN, int RC>
 static hipError_t launch_flush_pn(const M2Args& a, int mode_all, int rewrite_only, hipStream_t s) {
     if (mode_all == 2)  // fused decode + fold of the L-th lock-step token
         hipLaunchKernelGGL((m2_fold_kernel<P, N, TIN, RC, true>), head_grid(a.batch, a.heads),
-                           dim3(256), 0, s, a, 0, 0);
+                           head_block(a.batch, a.heads), 0, s, a, 0, 0);
     else
         hipLaunchKernelGGL((m2_fold_kernel<P, N, TIN, RC, false>), head_grid(a.batch, a.heads),
-                           dim3(256), 0, s, a, mode_all, rewrite_only);
+                           head_block(a.batch, a.heads), 0, s, a, mode_all, rewrite_only);
     return hipGetLastError();
 }
 

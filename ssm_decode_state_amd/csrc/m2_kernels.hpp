@@ -67,7 +67,7 @@ __global__ __launch_bounds__(256) void m2_replay_kernel(M2Args a) {
 
     const int wave = uniform(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
-    const int h = blockIdx.x * kHeadsPerBlock + wave;
+    const int h = blockIdx.x * (int)(blockDim.x >> 6) + wave;  // one head per wave
     if (h >= a.heads) return;  // whole wave; no block-level barriers below
     const int b = blockIdx.y;
     const int head = b * a.heads + h;
@@ -333,7 +333,7 @@ __attribute__((amdgpu_waves_per_eu(2))) void m2_fold_kernel(M2Args a, int mode_a
 
     const int wave = uniform(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
-    const int h = blockIdx.x * kHeadsPerBlock + wave;
+    const int h = blockIdx.x * (int)(blockDim.x >> 6) + wave;  // one head per wave
     if (h >= a.heads) return;
     const int b = blockIdx.y;
     const int H = a.heads;
@@ -528,7 +528,7 @@ __global__ __launch_bounds__(256) void m2_conv_kernel(M2ConvArgs a) {
     __shared__ __attribute__((aligned(16))) float s_bc[kHeadsPerBlock][2][N];
     const int wave = uniform(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
-    const int h = blockIdx.x * kHeadsPerBlock + wave;
+    const int h = blockIdx.x * (int)(blockDim.x >> 6) + wave;  // one head per wave
     if (h >= a.heads) return;
     const int b = blockIdx.y;
     const int head = b * a.heads + h;
@@ -597,7 +597,7 @@ __global__ __launch_bounds__(256) void m2_snap_kernel(M2ConvArgs a) {
     __shared__ __attribute__((aligned(16))) float s_bc[kHeadsPerBlock][MAXQ][2][N];
     const int wave = uniform(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
-    const int h = blockIdx.x * kHeadsPerBlock + wave;
+    const int h = blockIdx.x * (int)(blockDim.x >> 6) + wave;  // one head per wave
     if (h >= a.heads) return;
     const int b = blockIdx.y;
     const int H = a.heads, Gn = a.groups, nq = a.ntok;
@@ -669,11 +669,21 @@ __global__ __launch_bounds__(256) void m2_snap_kernel(M2ConvArgs a) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// Launch helpers shared by the instantiating translation units. Grid: (ceil(H / 4), batch); one
-// wavefront per head.
+// Launch helpers shared by the instantiating translation units. One wavefront per head; four
+// heads per workgroup, or one when the launch has at most two heads per CU (B * H <= 512 on 256
+// CUs): then the heads spread over the CUs instead of sharing the load paths of a quarter of
+// them. Grid: (ceil(H / heads per workgroup), batch).
 // ---------------------------------------------------------------------------------------------
+constexpr long kSmallLaunchHeads = 512;
+static inline int heads_per_block(int batch, int heads) {
+    return (long)batch * heads <= kSmallLaunchHeads ? 1 : kHeadsPerBlock;
+}
 static inline dim3 head_grid(int batch, int heads) {
-    return dim3((unsigned)((heads + kHeadsPerBlock - 1) / kHeadsPerBlock), (unsigned)batch);
+    const int hpb = heads_per_block(batch, heads);
+    return dim3((unsigned)((heads + hpb - 1) / hpb), (unsigned)batch);
+}
+static inline dim3 head_block(int batch, int heads) {
+    return dim3((unsigned)(64 * heads_per_block(batch, heads)));
 }
 
 #ifdef SSM_SINGLE_SHAPE  // faster builds when inspecting the serving-shape kernels

@@ -6,7 +6,7 @@ namespace ssm {
 
 template <int P, int N, typename TIN, int RC, int MAXQ>
 static hipError_t launch_verify_q(const M2Args& a, int maxe, hipStream_t s) {
-    const dim3 grid = head_grid(a.batch, a.heads), block(256);
+    const dim3 grid = head_grid(a.batch, a.heads), block = head_block(a.batch, a.heads);
     if (maxe <= 32)
         hipLaunchKernelGGL((m2_replay_kernel<P, N, TIN, RC, MAXQ, 32, false>), grid, block, 0, s, a);
     else
