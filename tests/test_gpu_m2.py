@@ -110,6 +110,18 @@ def test_decode_shapes(B, H, G, P, N, L, bf16, T, S):
     assert torch.all(p[..., 0] == st.st.ring_start) and torch.all(p[..., 1] == st.st.count_lo)
 
 
+@pytest.mark.parametrize("B,H", [(4, 128), (5, 103)])
+def test_decode_at_the_launch_geometry_switch(B, H):
+    """Serving head dimensions (P=64, N=128, L=16, bf16) on both sides of the launch geometry
+    switch: 512 heads run one head per workgroup, 515 (a ragged last workgroup) four. Every
+    output and flushed checkpoint against the oracle."""
+    shape = _shape(B, H, H, 64, 128, 16, True)
+    pairs = [(b, h) for b in range(B) for h in range(H)]
+    gy, gck, oy, osn, _ = run_decode(shape, 900 + B, 34, 0.3162, pairs)
+    assert_close(gy, oy, (-1,), "replay outputs")
+    assert_close(gck, osn, (-2, -1), "flushed checkpoints")
+
+
 def test_serving_batch_sampled_heads():
     """The serving-batch workload at full size (B=256, H=128, P=64, N=128, L=16, bf16 inputs,
     256 steps) in the launch configuration the benchmark times; outputs and flushed checkpoints
@@ -149,6 +161,8 @@ def test_flush_all_and_export():
 
 @pytest.mark.parametrize("B,H,G,P,N,bf16", [(2, 4, 4, 16, 16, False), (3, 6, 2, 64, 128, True),
                                             (2, 5, 5, 32, 16, True),
+                                            (4, 128, 128, 64, 128, True),   # 512 heads: one per workgroup
+                                            (5, 103, 103, 64, 128, True),   # 515: four, ragged
                                             (256, 128, 128, 64, 128, True)])
 def test_conventional_step(B, H, G, P, N, bf16):
     shape = _shape(B, H, G, P, N, 16, bf16)
