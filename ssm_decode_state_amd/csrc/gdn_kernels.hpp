@@ -153,12 +153,19 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_replay_kernel(GdnArgs a) {
     }
 
     // ---- the checkpoint rows of this wave ------------------------------------------------------
+    // Several queries (verify): half of the row is issued here and half after the sweeps, so
+    // that the sweeps do not hold all 128 row registers and more waves fit on a SIMD. Loads are
+    // issued in the order the row products use them.
+    constexpr int kEarlyQ = (RC == 0 && MAXQ > 1) ? kNQ / 2 : kNQ;
     float4 hv[kNQ];  // the fp32 rows (no read copy)
     RcRow<DV, DK, RC> rc;  // or the read copy's row, issued at the same point (news, para 4)
+    const float4* tile = reinterpret_cast<const float4*>(a.ckpt) + th * (DV * DK / 4);
     if constexpr (RC == 0) {
-        const float4* tile = reinterpret_cast<const float4*>(a.ckpt) + th * (DV * DK / 4);
 #pragma unroll
-        for (int q = 0; q < kNQ; ++q) hv[q] = ld_stream(tile + q * DV + row);
+        for (int q = 0; q < kEarlyQ; ++q) {
+            hv[q] = ld_stream(tile + q * DV + row);
+            __builtin_amdgcn_sched_barrier(0);
+        }
     } else {
         rc.load(RcView{a.rc_codes, a.rc_scale, a.rc_tscale}, th, row);
     }
@@ -275,6 +282,13 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_replay_kernel(GdnArgs a) {
 #pragma unroll
             for (int i = 0; i < kE; ++i) r[jj][i] = al[i] * (r[jj][i] - c * kv[i]);
             if (lane == 0) s_c[sw][e][j] = c;
+        }
+    }
+    if constexpr (RC == 0 && kEarlyQ < kNQ) {
+#pragma unroll
+        for (int q = kEarlyQ; q < kNQ; ++q) {
+            hv[q] = ld_stream(tile + q * DV + row);
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
 #pragma unroll
