@@ -134,6 +134,10 @@ __global__ __launch_bounds__(256) void m2_replay_kernel(M2Args a) {
 
     // ---- 2. the checkpoint stream (explainer, "Why Decoding, Not Prefill, Is the Hard Part":
     //         decode time goes to reading the state) ----------------------------------------
+    // Several queries (verify): half of the tile is issued here and half before the row dots,
+    // so that the coefficient work does not hold all the tile registers and more waves fit on a
+    // SIMD.
+    constexpr int kEarlyQ = (RC == 0 && MAXQ > 1) ? G::kQPL / 2 : G::kQPL;
     float4 hv[G::kQPL];
     const float4* tile = reinterpret_cast<const float4*>(a.ckpt) + th * (P * N / 4);
     if constexpr (RC == 0) {
@@ -141,7 +145,7 @@ __global__ __launch_bounds__(256) void m2_replay_kernel(M2Args a) {
         // loads, and the first dot would wait for the whole tile): the dots then run while the
         // rest of the tile is still arriving
 #pragma unroll
-        for (int j = 0; j < G::kQPL; ++j) {
+        for (int j = 0; j < kEarlyQ; ++j) {
             hv[j] = ld_stream(tile + (gq + G::kGrp * j) * P + row);
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -242,6 +246,14 @@ __global__ __launch_bounds__(256) void m2_replay_kernel(M2Args a) {
             if (j >= nq) break;
             out[j] += s_w[wave][e][j] * xe;
             if (e == count + j) out[j] += D * xe;
+        }
+    }
+
+    if constexpr (RC == 0 && kEarlyQ < G::kQPL) {
+#pragma unroll
+        for (int j = kEarlyQ; j < G::kQPL; ++j) {
+            hv[j] = ld_stream(tile + (gq + G::kGrp * j) * P + row);
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
 
