@@ -153,10 +153,10 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_replay_kernel(GdnArgs a) {
     }
 
     // ---- the checkpoint rows of this wave ------------------------------------------------------
-    // Several queries (verify): half of the row is issued here and half after the sweeps, so
-    // that the sweeps do not hold all 128 row registers and more waves fit on a SIMD. Loads are
-    // issued in the order the row products use them.
-    constexpr int kEarlyQ = (RC == 0 && MAXQ > 1) ? kNQ / 2 : kNQ;
+    // Half of the row is issued here and half after the sweeps, so that the sweeps do not hold
+    // all 128 row registers and more waves fit on a SIMD. Loads are issued in the order the row
+    // products use them.
+    constexpr int kEarlyQ = RC == 0 ? kNQ / 2 : kNQ;
     float4 hv[kNQ];  // the fp32 rows (no read copy)
     RcRow<DV, DK, RC> rc;  // or the read copy's row, issued at the same point (news, para 4)
     const float4* tile = reinterpret_cast<const float4*>(a.ckpt) + th * (DV * DK / 4);
