@@ -182,20 +182,20 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_replay_kernel(GdnArgs a) {
         for (int ee = 0; ee < kEW; ++ee)
 #pragma unroll
             for (int i = 0; i < kE; ++i) s_al[ee * kW + wave][el * kE + i] = expf(graw[ee][i]);
-    } else if constexpr (VG) {  // eight entries at a time: few registers live beside the rows
-        static_assert(kEW % 8 == 0, "late decays in groups of eight");
+    } else if constexpr (VG) {  // up to eight entries at a time: few registers live beside the rows
+        constexpr int kGB = kEW % 8 == 0 ? 8 : kEW % 6 == 0 ? 6 : kEW % 4 == 0 ? 4 : kEW % 2 == 0 ? 2 : 1;
 #pragma unroll
-        for (int e0 = 0; e0 < kEW; e0 += 8) {
-            float gb[8][kE];
+        for (int e0 = 0; e0 < kEW; e0 += kGB) {
+            float gb[kGB][kE];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
+            for (int u = 0; u < kGB; ++u) {
                 const int e = (e0 + u) * kW + wave;
                 const float* src = e < count ? a.ring_g + ((long)head * cap + ring_slot(start, min(e, cap - 1), cap)) * DK
                                              : a.in_g + tok(e - count) * DK;
                 load_raw<float, kE>(src + el * kE, gb[u]);
             }
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
+            for (int u = 0; u < kGB; ++u) {
                 const int e = (e0 + u) * kW + wave;
 #pragma unroll
                 for (int i = 0; i < kE; ++i) s_al[e][el * kE + i] = expf(gb[u][i]);

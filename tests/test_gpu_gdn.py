@@ -128,7 +128,7 @@ def test_gdn_conventional_step(B, H, dv, dk, bf16):
     assert_close(nat[bi, hi].cpu().double().numpy(), ST, (-2, -1), "GDN conventional state")
 
 
-@pytest.mark.parametrize("case", ["small", "odd", "wide", "serving"])
+@pytest.mark.parametrize("case", ["small", "odd", "wide", "long", "serving"])
 def test_gdn_spec_rounds_match_oracle(case):
     """Speculative rounds (drafts appended and verified in one pass, U{0..S} accepted, pointer
     rollback, fold when a sequence reaches L) against the oracle's speculative rounds."""
@@ -138,6 +138,8 @@ def test_gdn_spec_rounds_match_oracle(case):
         shape, seed, R, s0 = synth.Shape(synth.GDN, 3, 2, 2, 128, 64, 8, 3, in_bf16=True), 52, 16, 0.3
     elif case == "wide":  # eight drafts: the eight-query verify, up to 23 entries per call
         shape, seed, R, s0 = synth.Shape(synth.GDN, 2, 3, 3, 128, 128, 16, 8, in_bf16=True), 53, 16, 0.3
+    elif case == "long":  # four drafts on a 24-entry window: calls that see 25..27 entries
+        shape, seed, R, s0 = synth.Shape(synth.GDN, 2, 2, 2, 128, 128, 24, 4, in_bf16=True), 54, 24, 0.3
     else:
         w = synth.WORKLOADS["gdn_b256_spec"]
         shape, seed, R, s0 = w["shape"], w["seed"], 24, w["h0_std"]

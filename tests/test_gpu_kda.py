@@ -137,7 +137,7 @@ def test_kda_conventional_step(B, H, dv, dk, bf16):
     assert_close(got, ST, (-2, -1), "KDA conventional state")
 
 
-@pytest.mark.parametrize("case", ["small", "odd", "wide", "serving"])
+@pytest.mark.parametrize("case", ["small", "odd", "wide", "long", "serving"])
 def test_kda_spec_rounds_match_oracle(case):
     if case == "small":
         shape, seed, R, s0 = _kshape(2, 3, 64, 64, 4, False, 4), 151, 20, 0.3
@@ -145,6 +145,8 @@ def test_kda_spec_rounds_match_oracle(case):
         shape, seed, R, s0 = _kshape(3, 2, 128, 64, 8, True, 3), 152, 16, 0.3
     elif case == "wide":  # eight drafts: the eight-query verify
         shape, seed, R, s0 = _kshape(2, 3, 128, 128, 16, True, 8), 154, 16, 0.3
+    elif case == "long":  # four drafts on a 24-entry window: calls that see 25..27 entries
+        shape, seed, R, s0 = _kshape(2, 2, 128, 128, 24, True, 4), 155, 24, 0.3
     else:
         shape, seed, R, s0 = _kshape(256, 32, 128, 128, 16, True, 4), 153, 16, 0.3162
     S = shape.max_draft
