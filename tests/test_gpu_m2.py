@@ -157,6 +157,21 @@ def test_flush_all_and_export():
     assert_close(g, hT, (-2, -1), "checkpoint after flush(ALL)")
     p = pointers(st)
     assert torch.all(p[..., 1] == 0) and torch.all(p[..., 0] == 11 % 8)
+    # decoding goes on from the moved start (the launches take it from the host in lock step)
+    assert st.st.ring_start == 11 % 8
+    bi = torch.tensor([b for (b, _) in pairs], device=DEV)
+    hi = torch.tensor([h for (_, h) in pairs], device=DEV)
+    ys = []
+    for t in range(11, 24):  # a fold at 8 more entries, five left
+        bd.ssm_replay_decode(st.st, to_dev(tok.draw(t), DEV), y)
+        ys.append(y[bi, hi].clone())
+    torch.cuda.synchronize()
+    oy, _, _ = m2_oracle(A, D, h0, tok, pairs)
+    assert_close(torch.stack(ys, 1).cpu().double().numpy(), oy[:, 11:], (-1,),
+                 "replay outputs after flush(ALL)")
+    p = pointers(st)
+    assert st.st.count_lo == st.st.count_hi == 5
+    assert torch.all(p[..., 0] == st.st.ring_start) and torch.all(p[..., 1] == 5)
 
 
 @pytest.mark.parametrize("B,H,G,P,N,bf16", [(2, 4, 4, 16, 16, False), (3, 6, 2, 64, 128, True),
