@@ -137,7 +137,7 @@ __global__ __launch_bounds__(256) void m2_replay_kernel(M2Args a) {
     // Several queries (verify): half of the tile is issued here and half before the row dots,
     // so that the coefficient work does not hold all the tile registers and more waves fit on a
     // SIMD.
-    constexpr int kEarlyQ = (RC == 0 && MAXQ > 1) ? G::kQPL / 2 : G::kQPL;
+    constexpr int kEarlyQ = RC == 0 ? G::kQPL / 2 : G::kQPL;
     float4 hv[G::kQPL];
     const float4* tile = reinterpret_cast<const float4*>(a.ckpt) + th * (P * N / 4);
     if constexpr (RC == 0) {
