@@ -564,8 +564,12 @@ __global__ __launch_bounds__(256) void m2_conv_kernel(M2ConvArgs a) {
     // float4 (gq + kGrp j) * P + row of the head's tile
     const TileIO tio{reinterpret_cast<char*>(a.h) + (long)head * (P * N * 4),
                      (uint32_t)((gq * P + row) * 16)};
+    // issued in the order the update uses them, so that it runs while the tile arrives
 #pragma unroll
-    for (int j = 0; j < G::kQPL; ++j) hv[j] = tio.load((uint32_t)(G::kGrp * j * P * 16));
+    for (int j = 0; j < G::kQPL; ++j) {
+        hv[j] = tio.load((uint32_t)(G::kGrp * j * P * 16));
+        __builtin_amdgcn_sched_barrier(0);
+    }
     asm volatile("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
 
