@@ -397,8 +397,12 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_conv_kernel(GdnConvArgs a) {
     float4 hv[kNQ];
     // float4 q * DV + row of the head's tile
     const TileIO tio{reinterpret_cast<char*>(a.S) + (long)head * (DV * DK * 4), (uint32_t)(row * 16)};
+    // issued in the order the row dot uses them, so that it runs while the row arrives
 #pragma unroll
-    for (int q = 0; q < kNQ; ++q) hv[q] = tio.load((uint32_t)(q * DV * 16));
+    for (int q = 0; q < kNQ; ++q) {
+        hv[q] = tio.load((uint32_t)(q * DV * 16));
+        __builtin_amdgcn_sched_barrier(0);
+    }
     asm volatile("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
