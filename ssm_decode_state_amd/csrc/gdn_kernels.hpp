@@ -460,7 +460,7 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_conv_kernel(GdnConvArgs a) {
 // VG (Kimi Delta Attention): the decay is a dk-vector per entry. With G_t[n] the within-chunk
 // cumulative log-decay of key channel n, the same UT/WY steps hold with
 //   Lm[t][i] = beta_t sum_n k_t[n] k_i[n] exp(G_t[n] - G_i[n])   (a gated Gram matrix, on MFMA
-//     as (K * exp(G - G_ref)) (K * exp(G_ref - G))^T around the mid-chunk reference G_ref),
+//     as four products over a binary split of the chunk, every exponent <= 0: see below),
 //   W_t = beta_t (exp(G_t) * k_t) - sum_{i<t} Lm[t][i] W_i,
 //   S <- S diag(exp(G_L)) + sum_t Delta_t (k_t * exp(G_L - G_t))^T.
 // ---------------------------------------------------------------------------------------------
@@ -667,29 +667,59 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_flush_kernel(GdnArgs a, int mod
             const float t = __shfl_up(G, o, 16);
             G += li >= o ? t : 0.f;
         }
-        if (wave == 0) {
-            // K K^T on MFMA: lane l supplies K[l%16][n0 + l/16] as both operands (VG: scaled by
-            // exp(G - G_ref) as the left and exp(G_ref - G) as the right operand)
+        if constexpr (VG) {
+            // Gated Gram matrix sum_n k_t[n] k_i[n] exp(G_t[n] - G_i[n]) for i < t, over a binary
+            // split of the chunk: the pair (t, i) belongs to level b, the highest bit in which t and
+            // i differ, and there both lie in one aligned block of 2^(b+1) entries with i in its
+            // lower half and t in its upper half. With c the last entry of the lower half,
+            // exp(G_t - G_i) = exp(G_t - G_c) exp(G_c - G_i) and both factors are <= 1 (G only
+            // falls), so neither overflows however fast a channel decays; a factor that underflows
+            // bounds the true product below it. Each level is one Gram product on MFMA: lane l
+            // supplies row l%16 scaled by its factor as the left operand if it lies in the upper
+            // half of its block, as the right one if in the lower half (the other operand 0).
+            // The head's waves split the four levels (level b on wave b % kW).
+            constexpr int kLv = 4 / kW;  // levels of this wave
+#pragma unroll
+            for (int v = 0; v < kLv; ++v) {
+                __builtin_amdgcn_sched_barrier(0);  // one level's operands live at a time
+                const int lev = v * kW + wave;
+                const int half = 1 << lev;
+                const int cut = (li & ~(2 * half - 1)) | (half - 1);
+                const bool upper = (li & half) != 0;
+                f32x4 gram = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int n0 = 0; n0 < DK; n0 += 4) {
+                    const float kk = s_k[li][n0 + lg];
+                    const float Gr = s_w[li][n0 + lg], Gc = s_w[cut][n0 + lg];
+                    const float x = kk * expf(upper ? Gr - Gc : Gc - Gr);
+                    gram = mfma4(upper ? x : 0.f, upper ? 0.f : x, gram);
+                }
+                // Lm[t][i] = beta_t Gram[t][i] for t = 4lg + r, i = li, for the pairs of this level
+                // (t and i differ first in bit lev); wave 0 also writes the zeros of i >= t
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int t = 4 * lg + r, i = li;
+                    const float bt = __shfl(be, t, 64);
+                    if (i < t && 31 - __clz(t ^ i) == lev) s_l[t][i] = bt * gram[r];
+                    if (v == 0 && wave == 0 && i >= t) s_l[t][i] = 0.f;
+                }
+            }
+        } else if (wave == 0) {
+            // K K^T on MFMA: lane l supplies K[l%16][n0 + l/16] as both operands
             f32x4 gram = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int n0 = 0; n0 < DK; n0 += 4) {
                 const float kk = s_k[li][n0 + lg];
-                if constexpr (VG) {
-                    const float d = s_w[li][n0 + lg] - s_w[7][n0 + lg];
-                    gram = mfma4(kk * expf(d), kk * expf(-d), gram);
-                } else {
-                    gram = mfma4(kk, kk, gram);
-                }
+                gram = mfma4(kk, kk, gram);
             }
             // Lm[t][i] for t = 4lg + r, i = li (t varies across lanes: per-lane shuffles);
-            // the decay from entry i to t is exp(G_t - G_i) (VG: inside the Gram matrix)
+            // the decay from entry i to t is exp(G_t - G_i) <= 1 (only taken where i < t)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int t = 4 * lg + r, i = li;
                 const float bt = __shfl(be, t, 64);
                 const float Gt = __shfl(G, t, 64);
-                const float dec = VG ? 1.f : expf(Gt - G);
-                s_l[t][i] = (i < t) ? bt * dec * gram[r] : 0.f;
+                s_l[t][i] = (i < t) ? bt * expf(Gt - G) * gram[r] : 0.f;
             }
         }
         __syncthreads();

@@ -110,7 +110,7 @@ def initial_state(shape: Shape, seed: int, std: float, layer: int = 0,
 
 
 def token_inputs(shape: Shape, seed: int, tag: str, index: int, ntok: int = 1,
-                 layer: int = 0) -> Dict[str, torch.Tensor]:
+                 layer: int = 0, fast_decay: bool = False) -> Dict[str, torch.Tensor]:
     """Inputs of `ntok` consecutive tokens for every sequence, as one block keyed by (tag, index).
 
     Mamba-2: x [batch][ntok][H][P], B and C [batch][ntok][G][N] in the storage dtype;
@@ -118,6 +118,9 @@ def token_inputs(shape: Shape, seed: int, tag: str, index: int, ntok: int = 1,
     GDN:     q, k [batch][ntok][H][dk], v [batch][ntok][H][dv] in the storage dtype;
              beta, g [batch][ntok][H] fp32.
     KDA:     as GDN with g [batch][ntok][H][dk] (one log-decay per key channel).
+    fast_decay (GDN, KDA): a third of the decays are redrawn as g = -U(10, 40) per token -- the
+    key channels n % 3 == 0 (KDA) or the heads h % 3 == 0 (GDN) -- from a stream of their own,
+    so every other value is unchanged: gates that forget a channel within a token or two.
     """
     g = _gen(seed, tag, layer, index)
     bsz, H = shape.batch, shape.heads
@@ -140,6 +143,12 @@ def token_inputs(shape: Shape, seed: int, tag: str, index: int, ntok: int = 1,
     beta = torch.sigmoid(torch.randn(bsz, ntok, H, generator=g, dtype=torch.float64))
     gshape = (bsz, ntok, H, dk) if shape.kind == KDA else (bsz, ntok, H)
     gl = -_softplus64(torch.randn(*gshape, generator=g, dtype=torch.float64))
+    if fast_decay:
+        fast = -(10.0 + 30.0 * torch.rand(*gshape, generator=_gen(seed, tag, layer, index, "fast"),
+                                          dtype=torch.float64))
+        sel = torch.zeros(gshape[-1], dtype=torch.bool)
+        sel[::3] = True
+        gl = torch.where(sel, fast, gl)
     return {"q": q.to(torch.float32).to(dt_), "k": k.to(torch.float32).to(dt_), "v": v.to(dt_),
             "beta": beta.to(torch.float32), "g": gl.to(torch.float32)}
 
