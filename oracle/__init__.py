@@ -283,6 +283,21 @@ def gdn_replay_output(Sc, qk, k, v, beta, g, scale: float = 1.0):
     return o
 
 
+def replay_query(qk, k, v, beta, g, kda: bool = False):
+    """The query vector r [dk] of the GDN (KDA: per-channel decay) replay form for one head: qk
+    [dk], entries k [kk][dk], v [kk][dv], beta [kk], g [kk] (KDA [kk][dk]). The output is
+    scale (Sc r + acc), so replacing the checkpoint Sc by Sc + E changes output p by exactly
+    scale * (E r)[p]."""
+    lib = _load()
+    qk, k, v, beta, g = _f64(qk), _f64(k), _f64(v), _f64(beta), _f64(g)
+    kk, dk = k.shape
+    dv = v.shape[1]
+    r = np.zeros(dk)
+    lib.orc_replay_query(dv, dk, kk, 1 if kda else 0, _d(qk), _d(k), _d(v), _d(beta), _d(g),
+                         _d(r))
+    return r
+
+
 def gdn_flush(Sc, k, v, beta, g):
     """GDN flush (UT/WY form) for one head: fold entries k [L][dk], v [L][dv], beta/g [L]."""
     lib = _load()
@@ -309,10 +324,12 @@ def _declare(lib):
                                               [_ip, _dp, _dp, i, _ip, _dp])
     lib.orc_kda_sequential_batch.argtypes = [i, i, i, i, d] + [_dp] * 8 + [i, _ip, _dp]
     lib.orc_kda_replay_output.argtypes = [i, i, i, d] + [_dp] * 7
+    lib.orc_replay_query.argtypes = [i, i, i, i] + [_dp] * 6
     lib.orc_kda_spec_rounds_batch.argtypes = ([i, i, i, i, i, d] + [_dp] * 6 +
                                               [_ip, _dp, _dp, i, _ip, _dp])
     for f in ("orc_m2_sequential", "orc_m2_sequential_batch", "orc_m2_replay_output",
               "orc_m2_flush", "orc_m2_spec_rounds_batch", "orc_gdn_sequential_batch",
               "orc_gdn_replay_output", "orc_gdn_flush", "orc_gdn_spec_rounds_batch",
-              "orc_kda_sequential_batch", "orc_kda_replay_output", "orc_kda_spec_rounds_batch"):
+              "orc_kda_sequential_batch", "orc_kda_replay_output", "orc_kda_spec_rounds_batch",
+              "orc_replay_query"):
         getattr(lib, f).restype = None

@@ -334,6 +334,25 @@ void orc_kda_sequential_batch(int nh, int dv, int dk, int T, double scale, const
     }
 }
 
+/* The backward walk shared by the GDN and KDA replay forms: r <- q_k, acc <- 0; for i = k..1:
+ * c_i = beta_i (k_i . r), acc += c_i v_i, r <- alpha_i (r - c_i k_i), with alpha_i = exp(g_i) one
+ * scalar (GDN, gdim = 1) or one value per key channel (KDA, gdim = dk, elementwise). On return r is
+ * the query mapped back to the checkpoint's position and acc the buffered entries' value terms,
+ * so the output is o = scale (Sc r + acc). */
+static void replay_walk(int dv, int dk, int kk, int gdim, const double *qk, const double *k,
+                        const double *v, const double *beta, const double *g, double *r,
+                        double *acc) {
+    memcpy(r, qk, (size_t)dk * sizeof(double));
+    memset(acc, 0, (size_t)dv * sizeof(double));
+    for (int i = kk - 1; i >= 0; --i) {
+        const double *ki = k + (size_t)i * dk, *vi = v + (size_t)i * dv;
+        const double c = beta[i] * dotd(ki, r, dk);
+        for (int p = 0; p < dv; ++p) acc[p] += c * vi[p];
+        for (int n = 0; n < dk; ++n)
+            r[n] = exp(g[(size_t)i * gdim + (gdim > 1 ? n : 0)]) * (r[n] - c * ki[n]);
+    }
+}
+
 /* KDA replay form of one output (the GDN walk with a per-channel decay): r <- q_k, acc <- 0;
  * for i = k..1: c_i = beta_i (k_i . r), acc += c_i v_i, r <- alpha_i * (r - c_i k_i)
  * (elementwise); o = scale (Sc r + acc). */
@@ -341,17 +360,21 @@ void orc_kda_replay_output(int dv, int dk, int kk, double scale, const double *S
                            const double *qk, const double *k, const double *v,
                            const double *beta, const double *g, double *o) {
     double *r = (double *)malloc((size_t)dk * sizeof(double));
-    double *acc = (double *)calloc((size_t)dv, sizeof(double));
-    memcpy(r, qk, (size_t)dk * sizeof(double));
-    for (int i = kk - 1; i >= 0; --i) {
-        const double *ki = k + (size_t)i * dk;
-        const double c = beta[i] * dotd(ki, r, dk);
-        for (int p = 0; p < dv; ++p) acc[p] += c * v[(size_t)i * dv + p];
-        for (int n = 0; n < dk; ++n) r[n] = exp(g[(size_t)i * dk + n]) * (r[n] - c * ki[n]);
-    }
+    double *acc = (double *)malloc((size_t)dv * sizeof(double));
+    replay_walk(dv, dk, kk, dk, qk, k, v, beta, g, r, acc);
     for (int p = 0; p < dv; ++p) o[p] = scale * (dotd(Sc + (size_t)p * dk, r, dk) + acc[p]);
     free(acc);
     free(r);
+}
+
+/* The query vector r of the replay forms above (GDN: kda = 0, g [kk]; KDA: kda = 1, g [kk][dk]):
+ * the checkpoint enters the output only through scale * Sc r, so a change E of the checkpoint
+ * (e.g. its read copy's rounding) changes output p by exactly scale * sum_n E[p][n] r[n]. */
+void orc_replay_query(int dv, int dk, int kk, int kda, const double *qk, const double *k,
+                      const double *v, const double *beta, const double *g, double *r) {
+    double *acc = (double *)malloc((size_t)dv * sizeof(double));
+    replay_walk(dv, dk, kk, kda ? dk : 1, qk, k, v, beta, g, r, acc);
+    free(acc);
 }
 
 /* KDA speculative rounds: as orc_gdn_spec_rounds, with the per-channel recurrence. */
@@ -407,15 +430,8 @@ void orc_gdn_replay_output(int dv, int dk, int kk, double scale, const double *S
                            const double *qk, const double *k, const double *v,
                            const double *beta, const double *g, double *o) {
     double *r = (double *)malloc((size_t)dk * sizeof(double));
-    double *acc = (double *)calloc((size_t)dv, sizeof(double));
-    memcpy(r, qk, (size_t)dk * sizeof(double));
-    for (int i = kk - 1; i >= 0; --i) {
-        const double *ki = k + (size_t)i * dk, *vi = v + (size_t)i * dv;
-        const double c = beta[i] * dotd(ki, r, dk);
-        for (int p = 0; p < dv; ++p) acc[p] += c * vi[p];
-        const double a = exp(g[i]);
-        for (int n = 0; n < dk; ++n) r[n] = a * (r[n] - c * ki[n]);
-    }
+    double *acc = (double *)malloc((size_t)dv * sizeof(double));
+    replay_walk(dv, dk, kk, 1, qk, k, v, beta, g, r, acc);
     for (int p = 0; p < dv; ++p) o[p] = scale * (dotd(Sc + (size_t)p * dk, r, dk) + acc[p]);
     free(acc);
     free(r);

@@ -3,10 +3,14 @@
 // checkpoint), shared by the Mamba-2 and Gated DeltaNet kernels.
 //
 // A head's tile has ROWS rows (Mamba-2 P = 64, GDN dv) of N elements (Mamba-2 N, GDN dk):
-//   fp8 row copy: s = amax_row / 448 (1 if zero), code = RNE_sat_e4m3(h * (1/s)), value*s.
-//   fp4 copy (NVFP4 reading): s_t = amax_tile / 2688 (1 if zero); per 16-element block
-//     s_b = value(RNE_sat_e4m3(amax_blk / (6 s_t))), S = s_b s_t,
+//   fp8 row copy: s = max(amax_row / 448, 2^-126) (1 if zero), code = RNE_sat_e4m3(h * (1/s)),
+//     value*s.
+//   fp4 copy (NVFP4 reading): s_t = max(amax_tile / 2688, 2^-117) (1 if zero); per 16-element
+//     block s_b = value(RNE_sat_e4m3(amax_blk / (6 s_t))), S = s_b s_t,
 //     code = RNE_sat_e2m1(h * (1/S)) (all zero when S == 0), value*S.
+//   The floors keep every scale normal with a finite reciprocal (a nonzero E4M3 block scale is at
+//   least 2^-9, so S >= 2^-126): a row or tile of tiny values, e.g. a sequence that decayed with
+//   no input, would otherwise get an infinite reciprocal and encode 0 * inf = NaN.
 // Codes: fp8 byte at ((n/16)*ROWS + p)*16 + n%16 of the head's code block; fp4 nibble of byte
 // ((n/32)*ROWS + p)*16 + (n%32)/2, low nibble = even n. Block scales [p][N/16]; row and tile
 // scales fp32.
@@ -14,6 +18,9 @@
 #include "ssm_device.hpp"
 
 namespace ssm {
+
+constexpr float kRcScaleFloorFp8 = 0x1p-126f;      // smallest normal fp32
+constexpr float kRcScaleFloorFp4Tile = 0x1p-117f;  // 2^-126 / 2^-9 (smallest E4M3 subnormal)
 
 // Device pointers of one layer's read copy.
 struct RcView {
@@ -150,7 +157,7 @@ __device__ __forceinline__ void rc_write_blocks(const RcView& v, long head, int 
 #pragma unroll
                 for (int r = 0; r < 4; ++r) amax = fmaxf(amax, fabsf(hb[pb][nb][r]));
             amax = xor_reduce_max<16, 32>(amax);  // the row is spread over lanes li + 16 lg
-            const float sc = amax > 0.f ? amax / 448.f : 1.f;
+            const float sc = amax > 0.f ? fmaxf(amax / 448.f, kRcScaleFloorFp8) : 1.f;
             const float inv = 1.f / sc;
             const int p = row0 + 16 * pb + li;
 #pragma unroll
@@ -162,7 +169,7 @@ __device__ __forceinline__ void rc_write_blocks(const RcView& v, long head, int 
             if (lg == 0) static_cast<float*>(v.scale)[head * ROWS + p] = sc;
         }
     } else {
-        const float st = amax_tile > 0.f ? amax_tile / 2688.f : 1.f;
+        const float st = amax_tile > 0.f ? fmaxf(amax_tile / 2688.f, kRcScaleFloorFp4Tile) : 1.f;
         const float d6 = 6.f * st;
         uint8_t* codes = v.codes + head * (long)(ROWS * N / 2);
         uint8_t* sbp = static_cast<uint8_t*>(v.scale) + head * (long)ROWS * (N / 16);

@@ -127,3 +127,27 @@ def test_spec_rounds_match_sequential_on_accepted_stream():
         od, _, _ = oracle.gdn_sequential(Sprev, q[:, sl], k[:, sl], v[:, sl], beta[:, sl],
                                          g[:, sl], scale=0.7)
         np.testing.assert_allclose(o[0, r], od[0], rtol=1e-13, atol=1e-14)
+
+
+@pytest.mark.parametrize("kda", [False, True])
+def test_replay_query_is_the_checkpoint_read_vector(kda):
+    """replay_query returns the r of o = scale (Sc r + acc): the output's change under a change E
+    of the checkpoint is scale * E r (checked through replay_output, itself pinned to stepping);
+    with no entries r = q; with beta = 0 it is q times the product of the decays."""
+    rng = np.random.default_rng(7)
+    dv, dk, kk = 12, 10, 6
+    Sc = rng.standard_normal((dv, dk))
+    q = rng.standard_normal(dk)
+    k = rng.standard_normal((kk, dk))
+    v = rng.standard_normal((kk, dv))
+    beta = rng.random(kk)
+    g = -rng.random((kk, dk)) if kda else -rng.random(kk)
+    fo = oracle.kda_replay_output if kda else oracle.gdn_replay_output
+    r = oracle.replay_query(q, k, v, beta, g, kda)
+    E = rng.standard_normal((dv, dk)) * 1e-2
+    d = fo(Sc + E, q, k, v, beta, g, 0.7) - fo(Sc, q, k, v, beta, g, 0.7)
+    np.testing.assert_allclose(d, 0.7 * E @ r, rtol=0, atol=1e-14)
+    np.testing.assert_array_equal(oracle.replay_query(q, k[:0], v[:0], beta[:0], g[:0], kda), q)
+    r0 = oracle.replay_query(q, k, v, np.zeros(kk), g, kda)
+    decay = np.exp(g.sum(axis=0)) if kda else np.exp(g.sum())
+    np.testing.assert_allclose(r0, q * decay, rtol=1e-14)
