@@ -247,9 +247,10 @@ ssm_status ssm_conventional_step(const ssm_config *cfg, float *h, const void *in
 /* Conventional speculative decoding, the comparison point for ssm_spec_append (news, para 3:
  * per-token snapshots; explainer, "Usage examples", example 3: snapshot and restore). Runs the
  * recurrence of ssm_conventional_step over `ndraft` draft tokens (`in` with ntok = ndraft,
- * 1 <= ndraft <= 8) starting from h, which is only read, and writes the state after each draft
- * j = 0..ndraft-1 to h_snap [ndraft][batch][H] tiles (tile layout of ssm_layout) and the outputs
- * y [batch][ndraft][H][P]. Mamba-2 only (SSM_E_UNSUPPORTED for GDN). h and h_snap must not
+ * 1 <= ndraft <= 8, SSM_E_CAPACITY otherwise) starting from h, which is only read, and writes the
+ * state after each draft j = 0..ndraft-1 to h_snap [ndraft][batch][H] tiles (tile layout of
+ * ssm_layout) and the outputs y [batch][ndraft][H][P] (GDN / KDA: [batch][ndraft][H][dv], `in`
+ * an ssm_gdn_in, A and D ignored and may be NULL). All three layer types. h and h_snap must not
  * overlap. */
 ssm_status ssm_conventional_spec_snapshot(const ssm_config *cfg, const float *h, float *h_snap,
                                           int32_t ndraft, const void *in, const float *A,
@@ -257,7 +258,7 @@ ssm_status ssm_conventional_spec_snapshot(const ssm_config *cfg, const float *h,
 
 /* The restore half of the snapshot scheme: sequence b takes the state after its n_accept[b]-th
  * draft, h[b] <- h_snap[n_accept[b] - 1][b] (device int32 [batch], clamped to [0, ndraft]; 0
- * keeps h[b]). Moves one state per sequence that accepted a draft. Mamba-2 only. */
+ * keeps h[b]). Moves one state per sequence that accepted a draft. All three layer types. */
 ssm_status ssm_conventional_spec_select(const ssm_config *cfg, float *h, const float *h_snap,
                                         int32_t ndraft, const int32_t *n_accept, void *stream);
 
@@ -274,6 +275,16 @@ ssm_status ssm_tiles_unpack(const ssm_config *cfg, const float *tiles, float *na
  * as listed); `in` and `out` must hold n items each -- they are not checked. Lets tests check the
  * read-copy codecs bit for bit against the format definitions. */
 ssm_status ssm_debug_codec(int32_t op, const void *in, void *out, int64_t n, void *stream);
+
+/* Measurement hook: one pass of plain streaming reads over `bytes` of device memory at src (a
+ * multiple of 16; 16-byte aligned) by `blocks` workgroups of 256 threads: each wavefront reads
+ * contiguous 32 KiB chunks with 32 16-byte non-temporal loads in flight per lane, the way the
+ * decode kernels stream a state tile; the practical read ceiling that the decode kernels' achieved
+ * bandwidth is compared with. out: device uint32 [blocks * 4] (one word per wavefront, derived from the data
+ * so that no read is dead; its value means nothing). SSM_E_ARG for blocks outside [1, 2^20], a
+ * size not a multiple of 16, or a null pointer with bytes > 0. */
+ssm_status ssm_debug_stream_read(const void *src, uint64_t bytes, uint32_t *out, int32_t blocks,
+                                 void *stream);
 
 /* Test hook: read the state's flag word (SSM_FLAG_* bits) into *host_flags, clearing it on the
  * device when `clear` is non-zero. Synchronizes `stream`. */

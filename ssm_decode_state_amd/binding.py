@@ -91,6 +91,7 @@ def _load() -> ctypes.CDLL:
         "ssm_debug_flags": ([P(ssm_state), P(ctypes.c_int32), i32, vp], st),
         "ssm_restore": ([P(ssm_state), vp, vp], st),
         "ssm_fork": ([P(ssm_state), P(ctypes.c_int32), P(ctypes.c_int32), i32, vp], st),
+        "ssm_debug_stream_read": ([vp, ctypes.c_uint64, vp, i32, vp], st),
     }
     for name, (args, res) in sig.items():
         f = getattr(lib, name)
@@ -104,7 +105,7 @@ EXPORTS = ("ssm_abi_version", "ssm_status_string", "ssm_layout_query", "ssm_ckpt
            "ssm_replay_decode", "ssm_flush", "ssm_spec_append", "ssm_spec_rollback",
            "ssm_ckpt_export", "ssm_conventional_step", "ssm_tiles_pack", "ssm_tiles_unpack",
            "ssm_debug_codec", "ssm_conventional_spec_snapshot", "ssm_conventional_spec_select",
-           "ssm_debug_flags", "ssm_restore", "ssm_fork")
+           "ssm_debug_flags", "ssm_restore", "ssm_fork", "ssm_debug_stream_read")
 
 
 def _st(st):
@@ -249,6 +250,13 @@ def ssm_conventional_spec_select(cfg: ssm_config, h: torch.Tensor, h_snap: torch
         raise ValueError("n_accept must be int32")
     _check("ssm_conventional_spec_select", _lib.ssm_conventional_spec_select(
         ctypes.byref(cfg), _ptr(h), _ptr(h_snap), ndraft, _ptr(n_accept), _stream(stream)))
+
+
+def ssm_debug_stream_read(src: torch.Tensor, out: torch.Tensor, blocks: int, stream=None) -> None:
+    """One pass of streaming reads over the bytes of src (measurement reference); out: int32
+    [>= 4 * blocks] on the device."""
+    _check("ssm_debug_stream_read", _lib.ssm_debug_stream_read(
+        _ptr(src), src.numel() * src.element_size(), _ptr(out), blocks, _stream(stream)))
 
 
 def ssm_debug_flags(st, clear: bool = False, stream=None) -> int:

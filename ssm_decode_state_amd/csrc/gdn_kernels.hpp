@@ -443,6 +443,104 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_conv_kernel(GdnConvArgs a) {
 }
 
 // ---------------------------------------------------------------------------------------------
+// Snapshot-based speculative step (the comparison point for the speculative verify; news para 3:
+// conventional speculation keeps per-token state snapshots; explainer, "Usage examples": snapshot
+// and restore): the recurrence of gdn_conv_kernel over ntok <= MAXQ draft tokens from the
+// read-only state a.S, writing the state after each draft j to its own snapshot tile
+// a.snap + (j * batch * H + head) * DV * DK and o [batch][ntok][H][DV].
+// ---------------------------------------------------------------------------------------------
+template <int DV, int DK, typename TIN, int MAXQ, bool VG = false>
+__global__ __launch_bounds__(DV)
+__attribute__((amdgpu_waves_per_eu(2))) void gdn_snap_kernel(GdnConvArgs a) {
+    static_assert(DV % 64 == 0 && DK % 64 == 0, "snapshot tile shape");
+    constexpr int kW = DV / 64;
+    constexpr int kNQ = DK / 4;
+    constexpr int kCE = DK / 64;
+    __shared__ __attribute__((aligned(16))) float s_kq[kW][MAXQ][VG ? 3 : 2][DK];  // k, q (, alpha)
+    const int wave = uniform(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int h = blockIdx.x, b = blockIdx.y;
+    const int H = a.heads, nq = a.ntok;
+    const long head = (long)b * H + h;
+    const int row = wave * 64 + lane;
+    const TIN* ink = static_cast<const TIN*>(a.in_k);
+    const TIN* inq = static_cast<const TIN*>(a.in_q);
+    const TIN* inv = static_cast<const TIN*>(a.in_v);
+    // every draft's inputs, issued before the state stream (rows past ntok repeat the last one)
+    TIN kraw[MAXQ][kCE], qraw[MAXQ][kCE], vraw[MAXQ];
+    float graw[VG ? MAXQ : 1][kCE], betaj[MAXQ], gj[MAXQ];
+#pragma unroll
+    for (int j = 0; j < MAXQ; ++j) {
+        const long tok = ((long)b * nq + min(j, nq - 1)) * H + h;
+#pragma unroll
+        for (int i = 0; i < kCE; ++i) {
+            const int n = lane + 64 * i;
+            kraw[j][i] = ink[tok * DK + n];
+            qraw[j][i] = inq[tok * DK + n];
+            if constexpr (VG) graw[j][i] = a.in_g[tok * DK + n];
+        }
+        vraw[j] = inv[tok * DV + row];
+        betaj[j] = a.in_beta[tok];
+        gj[j] = VG ? 0.f : a.in_g[tok];
+    }
+    float4 hv[kNQ];
+    const uint32_t lane_off = (uint32_t)(row * 16);
+    const TileIO tin{reinterpret_cast<char*>(a.S) + head * (DV * DK * 4), lane_off};
+#pragma unroll
+    for (int q = 0; q < kNQ; ++q) {
+        hv[q] = tin.load((uint32_t)(q * DV * 16));
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < MAXQ; ++j)
+#pragma unroll
+        for (int i = 0; i < kCE; ++i) {
+            const int n = lane + 64 * i;
+            s_kq[wave][j][0][n] = to_f32<TIN>(kraw[j][i]);
+            s_kq[wave][j][1][n] = to_f32<TIN>(qraw[j][i]);
+            if constexpr (VG) s_kq[wave][j][2][n] = expf(graw[j][i]);
+        }
+    wave_sync();
+    const long nheads = (long)a.batch * H;
+#pragma unroll
+    for (int t = 0; t < MAXQ; ++t) {
+        if (t >= nq) break;
+        const float alpha = VG ? 1.f : expf(gj[t]);
+        float sk = 0.f;  // (S k) for a scalar decay; (S diag(alpha) k) with VG
+#pragma unroll
+        for (int q = 0; q < kNQ; ++q) {
+            float4 k4 = *reinterpret_cast<const float4*>(&s_kq[wave][t][0][4 * q]);
+            if constexpr (VG) {
+                const float4 a4 = *reinterpret_cast<const float4*>(&s_kq[wave][t][2][4 * q]);
+                k4 = make_float4(k4.x * a4.x, k4.y * a4.y, k4.z * a4.z, k4.w * a4.w);
+            }
+            sk += hv[q].x * k4.x + hv[q].y * k4.y + hv[q].z * k4.z + hv[q].w * k4.w;
+        }
+        const float u = betaj[t] * (to_f32<TIN>(vraw[t]) - alpha * sk);
+        asm volatile("" ::: "memory");  // re-read k below rather than keeping 32 quads of it live
+        const TileIO tout{reinterpret_cast<char*>(a.snap) + ((long)t * nheads + head) * (DV * DK * 4),
+                          lane_off};
+        float o = 0.f;
+#pragma unroll
+        for (int q = 0; q < kNQ; ++q) {
+            const float4 k4 = *reinterpret_cast<const float4*>(&s_kq[wave][t][0][4 * q]);
+            const float4 q4 = *reinterpret_cast<const float4*>(&s_kq[wave][t][1][4 * q]);
+            float4 a4 = make_float4(alpha, alpha, alpha, alpha);
+            if constexpr (VG) a4 = *reinterpret_cast<const float4*>(&s_kq[wave][t][2][4 * q]);
+            hv[q].x = a4.x * hv[q].x + u * k4.x;
+            hv[q].y = a4.y * hv[q].y + u * k4.y;
+            hv[q].z = a4.z * hv[q].z + u * k4.z;
+            hv[q].w = a4.w * hv[q].w + u * k4.w;
+            o += hv[q].x * q4.x + hv[q].y * q4.y + hv[q].z * q4.z + hv[q].w * q4.w;
+            tout.store((uint32_t)(q * DV * 16), hv[q]);
+        }
+        a.o[(((long)b * nq + t) * H + h) * DV + row] = a.scale * o;
+    }
+}
+
+// ---------------------------------------------------------------------------------------------
 // Flush in UT/WY form (news para 3: fold the buffer into the checkpoint in one pass). For a chunk
 // of (up to) 16 entries, with G_t the running sum of g (log of the cumulative decay gamma_t):
 //   Lm[t][i] = beta_t exp(G_t - G_i) (k_t . k_i)   (i < t; decay as a partial sum of g)
@@ -866,6 +964,7 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_flush_kernel(GdnArgs a, int mod
 #define SSM_GDN_SHAPES(X, T) X(64, 64, T) X(64, 128, T) X(128, 64, T) X(128, 128, T)
 
 // Speculative verify launches (gdn_verify.hip); gdn_launch_replay forwards multi-token calls here.
+// Snapshot-based speculation (gdn_conv.hip) is declared with the other launchers.
 hipError_t gdn_launch_verify(const GdnArgs& a, int dv, int dk, int bf16, int rc, int maxe,
                              hipStream_t s);
 

@@ -577,13 +577,12 @@ ssm_status ssm_conventional_step(const ssm_config* cfg, float* h, const void* in
     return hip_status(e);
 }
 
-static ssm_status check_m2_spec_baseline(const ssm_config* cfg, ssm_config* c, int32_t ndraft) {
+static ssm_status check_spec_baseline(const ssm_config* cfg, ssm_config* c, int32_t ndraft) {
     if (!cfg) return SSM_E_ARG;
     *c = *cfg;
     c->readcopy = SSM_RC_NONE;
     const ssm_status s = check_config(c);
     if (s != SSM_OK) return s;
-    if (c->kind != SSM_MAMBA2) return SSM_E_UNSUPPORTED;
     if (ndraft < 1 || ndraft > 8) return SSM_E_CAPACITY;
     return SSM_OK;
 }
@@ -592,18 +591,29 @@ ssm_status ssm_conventional_spec_snapshot(const ssm_config* cfg, const float* h,
                                           int32_t ndraft, const void* in, const float* A,
                                           const float* D, float* y, void* stream) {
     ssm_config c;
-    ssm_status s = check_m2_spec_baseline(cfg, &c, ndraft);
+    ssm_status s = check_spec_baseline(cfg, &c, ndraft);
     if (s != SSM_OK) return s;
-    if (!h || !h_snap || !y || !A || !D) return SSM_E_ARG;
-    if (!aligned16(h) || !aligned16(h_snap) || !aligned16(y) || !aligned16(A) || !aligned16(D))
-        return SSM_E_ALIGN;
+    if (!h || !h_snap || !y) return SSM_E_ARG;
+    if (!aligned16(h) || !aligned16(h_snap) || !aligned16(y)) return SSM_E_ALIGN;
+    if (c.kind == SSM_MAMBA2) {
+        if (!A || !D) return SSM_E_ARG;
+        if (!aligned16(A) || !aligned16(D)) return SSM_E_ALIGN;
+    }
     s = check_inputs(c, in);
     if (s != SSM_OK) return s;
     if (c.batch == 0) return SSM_OK;
-    const ssm_m2_in* m = static_cast<const ssm_m2_in*>(in);
-    ssm::M2ConvArgs a{const_cast<float*>(h), m->x, m->B, m->C, m->dt, A, D, y,
-                      c.batch, c.heads, c.groups, h_snap, ndraft};
-    const hipError_t e = ssm::m2_launch_snapshot(a, c.dim_p, c.dim_n, c.in_dtype, as_stream(stream));
+    hipError_t e;
+    if (c.kind == SSM_MAMBA2) {
+        const ssm_m2_in* m = static_cast<const ssm_m2_in*>(in);
+        ssm::M2ConvArgs a{const_cast<float*>(h), m->x, m->B, m->C, m->dt, A, D, y,
+                          c.batch, c.heads, c.groups, h_snap, ndraft};
+        e = ssm::m2_launch_snapshot(a, c.dim_p, c.dim_n, c.in_dtype, as_stream(stream));
+    } else {
+        const ssm_gdn_in* g = static_cast<const ssm_gdn_in*>(in);
+        ssm::GdnConvArgs a{const_cast<float*>(h), g->q, g->k, g->v, g->beta, g->g, y,
+                           c.gdn_scale, c.batch, c.heads, c.kind == SSM_KDA, h_snap, ndraft};
+        e = ssm::gdn_launch_snapshot(a, c.dim_p, c.dim_n, c.in_dtype, as_stream(stream));
+    }
     if (e == hipErrorNotSupported) return SSM_E_UNSUPPORTED;
     return hip_status(e);
 }
@@ -611,7 +621,7 @@ ssm_status ssm_conventional_spec_snapshot(const ssm_config* cfg, const float* h,
 ssm_status ssm_conventional_spec_select(const ssm_config* cfg, float* h, const float* h_snap,
                                         int32_t ndraft, const int32_t* n_accept, void* stream) {
     ssm_config c;
-    const ssm_status s = check_m2_spec_baseline(cfg, &c, ndraft);
+    const ssm_status s = check_spec_baseline(cfg, &c, ndraft);
     if (s != SSM_OK) return s;
     if (!h || !h_snap || !n_accept) return SSM_E_ARG;
     if (!aligned16(h) || !aligned16(h_snap) || ((uintptr_t)n_accept & 3u) != 0) return SSM_E_ALIGN;
@@ -660,6 +670,14 @@ ssm_status ssm_debug_codec(int32_t op, const void* in, void* out, int64_t n, voi
     if (op < 0 || op > 11 || n < 0) return SSM_E_ARG;
     if (n > 0 && (!in || !out)) return SSM_E_ARG;
     return hip_status(ssm::launch_codec(op, in, out, (long)n, as_stream(stream)));
+}
+
+ssm_status ssm_debug_stream_read(const void* src, uint64_t bytes, uint32_t* out, int32_t blocks,
+                                 void* stream) {
+    if (blocks < 1 || blocks > (1 << 20) || (bytes % 16) != 0) return SSM_E_ARG;
+    if (bytes > 0 && (!src || !out)) return SSM_E_ARG;
+    if (!aligned16(src) || ((uintptr_t)out & 3u) != 0) return SSM_E_ALIGN;
+    return hip_status(ssm::launch_stream_read(src, (long)bytes, out, blocks, as_stream(stream)));
 }
 
 }  // extern "C"

@@ -116,6 +116,8 @@ struct GdnConvArgs {
     float scale;
     int batch, heads;
     int kda;  // per-channel gate (g [batch][H][dk])
+    float* snap = nullptr;  // speculative snapshots [ntok][batch * heads] tiles (S read only)
+    int ntok = 1;
 };
 
 // maxe: upper bound on count + ntok over all sequences (<= 64).
@@ -133,6 +135,7 @@ hipError_t gdn_launch_replay(const GdnArgs& a, int dv, int dk, int bf16, int rc,
 hipError_t gdn_launch_flush(const GdnArgs& a, int dv, int dk, int bf16, int rc, int mode_all,
                             int rewrite_only, hipStream_t s);
 hipError_t gdn_launch_conv(const GdnConvArgs& a, int dv, int dk, int bf16, hipStream_t s);
+hipError_t gdn_launch_snapshot(const GdnConvArgs& a, int dv, int dk, int bf16, hipStream_t s);
 
 // Pointer commit after a speculative round: count += min(n_accept[b], pending) for every head.
 hipError_t launch_snap_select(float* h, const float* snap, const int32_t* n_accept, int batch,
@@ -166,5 +169,7 @@ hipError_t launch_ptr_init(int* ptr, int batch, int heads, hipStream_t s);
 hipError_t launch_recount(int* refcnt, const int* ptr, int batch, int heads, int nslot,
                           hipStream_t s);
 hipError_t launch_codec(int op, const void* in, void* out, long n, hipStream_t s);
+// One pass of streaming 16-byte reads over `bytes` (a multiple of 16); out: 4 words per block.
+hipError_t launch_stream_read(const void* src, long bytes, uint32_t* out, int blocks, hipStream_t s);
 
 }  // namespace ssm

@@ -244,6 +244,46 @@ hipError_t launch_recount(int* refcnt, const int* ptr, int batch, int heads, int
     return hipGetLastError();
 }
 
+// Measurement reference: one pass of plain streaming reads over n16 16-byte units, the practical
+// read ceiling the decode kernels are compared with. Read the way the decode kernels read a state
+// tile: every wavefront takes a contiguous chunk of 64 * kU units (32 KiB), its lanes issue kU
+// non-temporal 16-byte loads at once (each instruction covering 1 KiB), and the wavefronts of the
+// grid stride over the chunks; units past the last whole chunk are read one per lane. Every value
+// read feeds a per-wave XOR that lane 0 stores, so no load is dead.
+__global__ __launch_bounds__(256) void stream_read_kernel(const u32x4_t* __restrict__ src, long n16,
+                                                         uint32_t* __restrict__ out) {
+    constexpr int kU = 32;
+    constexpr long kChunk = 64L * kU;
+    const int lane = threadIdx.x & 63;
+    const long wave = (long)blockIdx.x * (blockDim.x / 64) + threadIdx.x / 64;
+    const long nwaves = (long)gridDim.x * (blockDim.x / 64);
+    const long nchunks = n16 / kChunk;
+    uint32_t acc = 0;
+    for (long c = wave; c < nchunks; c += nwaves) {
+        const u32x4_t* p = src + c * kChunk + lane;
+        u32x4_t v[kU];
+#pragma unroll
+        for (int u = 0; u < kU; ++u) v[u] = __builtin_nontemporal_load(p + 64 * u);
+        __builtin_amdgcn_sched_barrier(0);  // all kU loads in flight before the first use
+#pragma unroll
+        for (int u = 0; u < kU; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+    }
+    for (long i = nchunks * kChunk + wave * 64 + lane; i < n16; i += nwaves * 64) {
+        const u32x4_t v = __builtin_nontemporal_load(src + i);
+        acc ^= v.x ^ v.y ^ v.z ^ v.w;
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) acc ^= (uint32_t)__shfl_xor((int)acc, o, 64);
+    if (lane == 0) out[wave] = acc;
+}
+
+hipError_t launch_stream_read(const void* src, long bytes, uint32_t* out, int blocks, hipStream_t s) {
+    if (bytes == 0) return hipSuccess;
+    hipLaunchKernelGGL(stream_read_kernel, dim3(blocks), dim3(256), 0, s,
+                       static_cast<const u32x4_t*>(src), bytes / 16, out);
+    return hipGetLastError();
+}
+
 hipError_t launch_codec(int op, const void* in, void* out, long n, hipStream_t s) {
     if (n == 0) return hipSuccess;
     hipLaunchKernelGGL(codec_kernel, dim3(blocks_for(n, 256)), dim3(256), 0, s, op, in, out, n);

@@ -160,6 +160,10 @@ def m2_in(addr=FAKE):
     return bd.ssm_m2_in(addr, addr, addr, addr)
 
 
+def gdn_in(addr=FAKE):
+    return bd.ssm_gdn_in(addr, addr, addr, addr, addr)
+
+
 def test_init_validation():
     c = cfg()
     st = bd.ssm_state()
@@ -262,8 +266,21 @@ def test_snapshot_baseline_validation():
     assert snap(c, 2, h=FAKE + 4) == bd.SSM_E_ALIGN
     assert snap(c, 2, y=FAKE + 8) == bd.SSM_E_ALIGN
     assert snap(c, 2, inp=m2_in(FAKE + 2)) == bd.SSM_E_ALIGN
-    assert snap(cfg(kind=bd.SSM_GDN, groups=128), 2) == bd.SSM_E_UNSUPPORTED
     assert snap(cfg(batch=0), 4) == bd.SSM_OK  # nothing to do
+    # GDN / KDA: gdn inputs, A and D ignored (NULL allowed); the same validation otherwise
+    for kind in (bd.SSM_GDN, bd.SSM_KDA):
+        g = cfg(kind=kind, groups=128, max_draft=4)
+        gsnap = lambda cc, nd, h=FAKE, inp=None: raw(
+            "ssm_conventional_spec_snapshot", ctypes.byref(cc), v(h), v(FAKE), nd,
+            ctypes.byref(inp if inp is not None else gdn_in()), None, None, v(FAKE), None)
+        assert gsnap(g, 9) == bd.SSM_E_CAPACITY
+        assert gsnap(g, 2, h=FAKE + 4) == bd.SSM_E_ALIGN
+        assert gsnap(g, 2, inp=gdn_in(FAKE + 8)) == bd.SSM_E_ALIGN
+        assert gsnap(cfg(kind=kind, groups=128, batch=0), 4) == bd.SSM_OK
+        assert raw("ssm_conventional_spec_snapshot", ctypes.byref(g), v(FAKE), v(FAKE), 2, None,
+                   None, None, v(FAKE), None) == bd.SSM_E_ARG
+        assert raw("ssm_conventional_spec_select", ctypes.byref(cfg(kind=kind, groups=128, batch=0)),
+                   v(FAKE), v(FAKE), 2, v(FAKE), None) == bd.SSM_OK
     assert raw("ssm_conventional_spec_snapshot", ctypes.byref(c), None, v(FAKE), 2,
                ctypes.byref(m2_in()), v(FAKE), v(FAKE), v(FAKE), None) == bd.SSM_E_ARG
     sel = lambda cc, nd, acc=FAKE: raw("ssm_conventional_spec_select", ctypes.byref(cc), v(FAKE),
@@ -351,3 +368,16 @@ def test_host_ring_start_follows_the_ring_model():
     assert st.ring_start == -1
     st = empty_state(window=4, share_ckpt=1)
     assert st.ring_start == -1  # shared checkpoints: the slot comes from the device
+
+
+def test_stream_read_validation():
+    v = ctypes.c_void_p
+    sr = lambda src, nbytes, out, blocks: raw("ssm_debug_stream_read", v(src), ctypes.c_uint64(nbytes),
+                                              v(out), blocks, None)
+    assert sr(FAKE, 1 << 20, FAKE, 0) == bd.SSM_E_ARG          # no workgroups
+    assert sr(FAKE, 1 << 20, FAKE, (1 << 20) + 1) == bd.SSM_E_ARG
+    assert sr(FAKE, (1 << 20) + 8, FAKE, 64) == bd.SSM_E_ARG   # not whole 16-byte units
+    assert sr(None, 1 << 20, FAKE, 64) == bd.SSM_E_ARG
+    assert sr(FAKE + 8, 1 << 20, FAKE, 64) == bd.SSM_E_ALIGN
+    assert sr(FAKE, 1 << 20, FAKE + 2, 64) == bd.SSM_E_ALIGN
+    assert sr(FAKE, 0, FAKE, 64) == bd.SSM_OK                  # empty: nothing launched

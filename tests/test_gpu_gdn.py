@@ -176,3 +176,62 @@ def test_gdn_spec_rounds_match_oracle(case):
     assert_close(go, oo, (-1,), "GDN draft outputs")
     got = np.stack([nat[b, h].cpu().double().numpy() for (b, h) in pairs])
     assert_close(got, ST, (-2, -1), "GDN state after the speculative rounds")
+
+
+@pytest.mark.parametrize("kind", [synth.GDN, synth.KDA])
+@pytest.mark.parametrize("case", ["small", "odd", "wide", "serving"])
+def test_gdn_snapshot_baseline_matches_oracle(kind, case):
+    """Conventional speculation for GDN and KDA (the state after every draft written as a
+    snapshot, then each sequence's accepted one restored) computes the same draft outputs and
+    final state as the oracle's speculative rounds; the restore moves exactly the accepted
+    snapshot (bitwise)."""
+    if case == "small":
+        shape, seed, R = synth.Shape(kind, 2, 3, 3, 64, 64, 4, 4, in_bf16=False), 61, 12
+    elif case == "odd":
+        shape, seed, R = synth.Shape(kind, 3, 2, 2, 128, 64, 8, 3), 62, 10
+    elif case == "wide":  # eight drafts: the eight-token snapshot kernel
+        shape, seed, R = synth.Shape(kind, 2, 3, 3, 128, 128, 16, 8), 63, 6
+    else:
+        shape, seed, R = synth.Shape(kind, 256, 32, 32, 128, 128, 16, 4), 64, 6
+    S = shape.max_draft
+    Bn, H, dv, dk = shape.batch, shape.heads, shape.dim_p, shape.dim_n
+    pairs = sample_pairs(Bn, H, 16) if Bn * H > 64 else [(b, h) for b in range(Bn) for h in range(H)]
+    S0 = synth.initial_state(shape, seed, 0.3)
+    cfg = bd.make_config(kind, Bn, H, H, dv, dk, shape.window, S,
+                         bd.SSM_IN_BF16 if shape.in_bf16 else bd.SSM_IN_F32, 0, 0.75)
+    h = torch.empty(Bn * H * dv * dk, device=DEV)
+    bd.ssm_tiles_pack(cfg, S0.to(DEV).contiguous(), h)
+    snap = torch.empty(S, Bn * H * dv * dk, device=DEV)
+    o = torch.empty(Bn, S, H, dv, device=DEV)
+    bi = torch.tensor([b for (b, _) in pairs], device=DEV)
+    hi = torch.tensor([hh for (_, hh) in pairs], device=DEV)
+    outs, accs, drafts = [], [], []
+    for r in range(R):
+        d = synth.token_inputs(shape, seed, "draft", r, ntok=S)
+        drafts.append(d)
+        bd.ssm_conventional_spec_snapshot(cfg, h, snap, S, to_dev(d, DEV), None, None, o)
+        outs.append(o[bi, :, hi].clone())
+        acc = synth.accept_counts(Bn, S, 1002, r)
+        accs.append(acc)
+        if r == 0:
+            before = h.clone()
+        bd.ssm_conventional_spec_select(cfg, h, snap, S, acc.to(DEV))
+        if r == 0:
+            torch.cuda.synchronize()
+            hv, bv, sv = h.view(Bn, -1), before.view(Bn, -1), snap.view(S, Bn, -1)
+            for b in range(Bn):
+                a = int(acc[b])
+                assert torch.equal(hv[b], sv[a - 1, b] if a > 0 else bv[b]), b
+    nat = torch.empty(Bn, H, dv, dk, device=DEV)
+    bd.ssm_tiles_unpack(cfg, h, nat)
+    torch.cuda.synchronize()
+    go = torch.stack(outs, 1).cpu().double().numpy()
+    ins = {key: np.stack([np.stack([synth.to_f64(d[key][b, :, hh]) for d in drafts])
+                          for (b, hh) in pairs]) for key in ("q", "k", "v", "beta", "g")}
+    acc = np.stack([torch.stack(accs, 1)[b].numpy() for (b, _) in pairs]).astype(np.int32)
+    S0p = np.stack([S0[b, hh].double().numpy() for (b, hh) in pairs])
+    spec = oracle.kda_spec_rounds if kind == synth.KDA else oracle.gdn_spec_rounds
+    oo, ST, _ = spec(S0p, ins["q"], ins["k"], ins["v"], ins["beta"], ins["g"], acc, scale=0.75)
+    assert_close(go, oo, (-1,), "snapshot-baseline draft outputs")
+    got = np.stack([nat[b, hh].cpu().double().numpy() for (b, hh) in pairs])
+    assert_close(got, ST, (-2, -1), "state after the snapshot rounds")

@@ -311,3 +311,16 @@ def test_packed_word_codecs_match_format_definitions():
     got[0::2] = b & 0xF
     got[1::2] = b >> 4
     np.testing.assert_array_equal(got, quant.e2m1_encode(v2))
+
+
+@pytest.mark.parametrize("nbytes,blocks", [(1 << 20, 64), ((1 << 20) + 16 * 37, 7), (16 * 5, 3)])
+def test_stream_read_reads_every_unit_once(nbytes, blocks):
+    """The streaming-read reference touches every 16-byte unit exactly once: the XOR of its
+    per-wave outputs equals the XOR of every word of the input (ragged sizes and tails too)."""
+    src = torch.randint(-2 ** 31, 2 ** 31 - 1, (nbytes // 4,), dtype=torch.int32, device=DEV)
+    out = torch.zeros(4 * blocks, dtype=torch.int32, device=DEV)
+    bd.ssm_debug_stream_read(src, out, blocks)
+    torch.cuda.synchronize()
+    exp = np.bitwise_xor.reduce(src.cpu().numpy().view(np.uint32))
+    got = np.bitwise_xor.reduce(out.cpu().numpy().view(np.uint32))
+    assert got == exp
