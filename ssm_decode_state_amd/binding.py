@@ -13,7 +13,9 @@ from typing import Mapping, Optional
 
 import torch
 
-_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libssm_replay.so")
+# the in-tree build; SSM_REPLAY_LIB names another build of the same library (same ABI) instead
+_LIB_PATH = (os.environ.get("SSM_REPLAY_LIB")
+             or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libssm_replay.so"))
 
 SSM_OK, SSM_E_ARG, SSM_E_SHAPE, SSM_E_ALIGN, SSM_E_STATE, SSM_E_CAPACITY, SSM_E_UNSUPPORTED, \
     SSM_E_HIP = 0, -1, -2, -3, -4, -5, -6, -7
