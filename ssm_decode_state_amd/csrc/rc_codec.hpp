@@ -123,6 +123,25 @@ struct RcRow<ROWS, N, 0> {
     __device__ __forceinline__ void load(const RcView&, long, int) {}
 };
 
+// E4M3 code of the fp4 block scale, RNE_sat_e4m3(RN(ab / d6)) for ab >= 0 and d6 > 0, without a
+// division in the common case. q = ab * rd6 with rd6 = RN(1/d6) is within about 2^-23 (relative)
+// of ab / d6, so the interval [q (1 - 2^-21), q (1 + 2^-21)] holds both ab / d6 and its rounding
+// RN(ab / d6). Rounding to E4M3 is monotonic: when both ends of the interval give the same code,
+// that is the code of RN(ab / d6); otherwise (an E4M3 rounding boundary within a few fp32 ulps of
+// the quotient) the quotient is divided out exactly. Quotients in the subnormal fp32 range, where
+// the relative bound does not hold, lie far below 2^-10 and every candidate encodes to 0. The
+// encodes are the gfx950 conversion instruction, two values per instruction, on values clamped
+// to the format's largest finite magnitude.
+__device__ __forceinline__ uint32_t block_scale_code(float ab, float d6, float rd6) {
+    const float q = ab * rd6;
+    const uint32_t lohi = e4m3x2_encode_hw<false>(sat(q * (1.f - 0x1p-21f), 448.f),
+                                                  sat(q * (1.f + 0x1p-21f), 448.f), 0u);
+    uint32_t code = lohi & 0xffu;
+    if (code != ((lohi >> 8) & 0xffu))  // rare: a rounding boundary is within reach
+        code = e4m3x2_encode_hw<false>(sat(ab / d6, 448.f), 0.f, 0u) & 0xffu;
+    return code;
+}
+
 // Largest magnitude among this lane's values of a tile held in MFMA accumulator order (hb[pb][nb]
 // holds row row0 + 16 pb + l%16, columns 16 nb + 4 (l/16) .. + 3). The caller reduces it over the
 // lanes (and waves) that hold the head's tile: the fp4 tile scale.
@@ -171,25 +190,33 @@ __device__ __forceinline__ void rc_write_blocks(const RcView& v, long head, int 
     } else {
         const float st = amax_tile > 0.f ? fmaxf(amax_tile / 2688.f, kRcScaleFloorFp4Tile) : 1.f;
         const float d6 = 6.f * st;
+        const float rd6 = 1.f / d6;  // correctly rounded, once per tile
         uint8_t* codes = v.codes + head * (long)(ROWS * N / 2);
         uint8_t* sbp = static_cast<uint8_t*>(v.scale) + head * (long)ROWS * (N / 16);
 #pragma unroll
         for (int pb = 0; pb < 4; ++pb) {
             const int p = row0 + 16 * pb + li;
+            uint32_t sbw[(kNB + 3) / 4] = {};  // the row's block-scale codes, byte nb
 #pragma unroll
             for (int nb = 0; nb < kNB; ++nb) {
                 float ab = fmaxf(fmaxf(fabsf(hb[pb][nb][0]), fabsf(hb[pb][nb][1])),
                                  fmaxf(fabsf(hb[pb][nb][2]), fabsf(hb[pb][nb][3])));
                 ab = xor_reduce_max<16, 32>(ab);  // the 16-element block spans lanes li + 16 lg
-                const uint32_t sb = e4m3_encode(ab / d6);
-                const float S = e4m3_decode(sb) * st;
+                const uint32_t sb = block_scale_code(ab, d6, rd6);
+                const float S = e4m3x2_decode_hw<false>(sb).x * st;
                 const float inv = S > 0.f ? 1.f / S : 0.f;
                 const uint32_t c = S > 0.f ? e2m1_half_encode(hb[pb][nb][0] * inv, hb[pb][nb][1] * inv,
                                                               hb[pb][nb][2] * inv, hb[pb][nb][3] * inv)
                                            : 0u;
                 *reinterpret_cast<uint16_t*>(codes + ((long)(nb / 2) * ROWS + p) * 16 + 8 * (nb % 2) +
                                              2 * lg) = (uint16_t)c;
-                if (lg == 0) sbp[(long)p * (N / 16) + nb] = (uint8_t)sb;
+                sbw[nb / 4] |= sb << (8 * (nb % 4));
+            }
+            if (lg == 0) {  // one store of the row's N/16 block-scale codes
+                if constexpr (kNB == 8)
+                    *reinterpret_cast<uint2*>(sbp + (long)p * (N / 16)) = make_uint2(sbw[0], sbw[1]);
+                else
+                    *reinterpret_cast<uint32_t*>(sbp + (long)p * (N / 16)) = sbw[0];
             }
         }
         if (tile_writer) v.tscale[head] = st;
