@@ -270,18 +270,39 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_replay_kernel(GdnArgs a) {
 #pragma unroll
             for (int i = 0; i < kE; ++i) al[i] = as;
         }
+        if constexpr (kQS == 1) {
+            const int j = qidx(0);
+            if (j < nq && e <= count + j) {  // (entries after query j's own token: uniform skip)
+                float d = 0.f;
 #pragma unroll
-        for (int jj = 0; jj < kQS; ++jj) {
-            const int j = qidx(jj);
-            if (j >= nq) break;
-            if (e > count + j) continue;  // entry after query j's own token (uniform)
-            float d = 0.f;
+                for (int i = 0; i < kE; ++i) d += kv[i] * r[0][i];
+                const float c = bt * wave_sum(d);
 #pragma unroll
-            for (int i = 0; i < kE; ++i) d += kv[i] * r[jj][i];
-            const float c = bt * wave_sum(d);
+                for (int i = 0; i < kE; ++i) r[0][i] = al[i] * (r[0][i] - c * kv[i]);
+                if (lane == 0) s_c[sw][e][j] = c;
+            }
+        } else {
+            // several queries: their reductions are independent chains, so the loop body has no
+            // branch and they interleave; a query that does not see entry e (e after its own
+            // token, or a padding query) keeps its r, and its coefficient slot is never read
+            float d[kQS];
 #pragma unroll
-            for (int i = 0; i < kE; ++i) r[jj][i] = al[i] * (r[jj][i] - c * kv[i]);
-            if (lane == 0) s_c[sw][e][j] = c;
+            for (int jj = 0; jj < kQS; ++jj) {
+                d[jj] = 0.f;
+#pragma unroll
+                for (int i = 0; i < kE; ++i) d[jj] += kv[i] * r[jj][i];
+            }
+#pragma unroll
+            for (int jj = 0; jj < kQS; ++jj) d[jj] = bt * wave_sum(d[jj]);
+#pragma unroll
+            for (int jj = 0; jj < kQS; ++jj) {
+                const int j = qidx(jj);
+                const bool sees = j < nq && e <= count + j;
+#pragma unroll
+                for (int i = 0; i < kE; ++i)
+                    r[jj][i] = sees ? al[i] * (r[jj][i] - d[jj] * kv[i]) : r[jj][i];
+                if (lane == 0 && j < MAXQ) s_c[sw][e][j] = d[jj];
+            }
         }
     }
     if constexpr (RC == 0 && kEarlyQ < kNQ) {
