@@ -383,7 +383,7 @@ def bench_bsweep(dev, batches=(1, 4, 16, 64, 256), min_bytes=512 << 20, max_laye
     return out
 
 
-def graph_steps(step, K, mem, restore_mem=True):
+def graph_steps(step, K, mem):
     """Time exactly K steps as one HIP graph: step(i) for i < K is captured from the current
     state, replayed once untimed (warm-up), the state bytes `mem` (a tensor holding all device
     state the steps touch) are restored to the captured start, and the graph is replayed once
@@ -867,6 +867,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=32)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--skip-conv", action="store_true", help="skip the conventional comparison")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="time the headline eagerly only (for counter-collection runs, which do "
+                         "not follow graph replays)")
     ap.add_argument("--copy-ref", type=int, default=0,
                     help="also run a plain copy of this many MiB (reference for HBM counters)")
     ap.add_argument("--workloads", default="all",
@@ -905,19 +908,17 @@ def main():
     st = bd.State(cfg, h0, Ad, Dd)
     y = torch.empty(Bn, H, P, device=dev)
 
-    # ---- first launches: one window on a separate one-sequence state loads every kernel the
-    #      timed steps use (replay at each count, the fused fold, the conventional step), so a
-    #      warm-up shorter than a window does not leave a first launch inside the timed region
-    cfg1 = bd.make_config(bd.SSM_MAMBA2, 1, H, G, P, N, L, 1, bd.SSM_IN_BF16)
-    st1 = bd.State(cfg1, None, Ad, Dd)
-    in1 = synth.token_inputs_device(dataclasses.replace(shape, batch=1), seed, "bench-first", 0)
-    y1 = torch.empty(1, H, P, device=dev)
+    # ---- first launches: one window on a separate state of the same shape loads every kernel
+    #      the timed steps use (replay at each count, the fused fold, the conventional step), so
+    #      a warm-up shorter than a window leaves no first launch inside the timed region (and
+    #      every launch of these kernels in this process has the serving shape)
+    st1 = bd.State(cfg, None, Ad, Dd)
     for t in range(L):
-        bd.ssm_replay_decode(st1, in1, y1)
-    t1 = torch.zeros(H * P * N, device=dev)
-    bd.ssm_conventional_step(cfg1, t1, in1, Ad, Dd, y1)
+        bd.ssm_replay_decode(st1, inputs[0], y)
+    t1 = torch.zeros(Bn * H * P * N, device=dev)
+    bd.ssm_conventional_step(cfg, t1, inputs[0], Ad, Dd, y)
     torch.cuda.synchronize()
-    del st1, in1, y1, t1
+    del st1, t1
 
     # ---- replay path, eager: one launch per step, HIP events around each (per-kernel figures) -
     for t in range(W):
@@ -962,7 +963,8 @@ def main():
 
     # ---- the headline: exactly the K steps, launched from one captured graph ------------------
     # (from the state the eager pass left; the state is restored after the warm-up replay)
-    graph = graph_steps(lambda i: bd.ssm_replay_decode(st, inputs[W + i], y), K, st.mem)
+    graph = (None if args.no_graph else
+             graph_steps(lambda i: bd.ssm_replay_decode(st, inputs[W + i], y), K, st.mem))
     if graph is not None:
         value, ms_step = Bn * K / graph["wall_s"], graph["ms_per_step"]
         timing = "one HIP graph of exactly the K steps, replayed once after an untimed replay"
@@ -1028,8 +1030,9 @@ def main():
                                "ms_per_step": t_conv / K * 1e3, "avg_launch_us": conv_ms * 1e3,
                                "achieved_gbs": conv_gbs, "frac": conv_gbs / HBM_PEAK_GBS,
                                "timing": "eager"}
-        gconv = graph_steps(lambda i: bd.ssm_conventional_step(cfg, tiles, inputs[W + i], Ad, Dd, y),
-                            K, tiles)
+        gconv = (None if args.no_graph else
+                 graph_steps(lambda i: bd.ssm_conventional_step(cfg, tiles, inputs[W + i], Ad, Dd, y),
+                             K, tiles))
         if gconv is not None:
             out["conventional"].update(value=Bn * K / gconv["wall_s"],
                                        ms_per_step=gconv["ms_per_step"],
