@@ -51,6 +51,8 @@
  *   (P = 64 takes every N); GDN dv and dk in {64, 128}; window L in [1, 32]; max_draft in
  *   [1, min(L, 8)], and for GDN / KDA L + max_draft - 1 <= 32 (SSM_E_UNSUPPORTED otherwise).
  *   KDA takes the GDN shapes. The read copies need N (dk) in {64, 128}, and P = 64 for Mamba-2.
+ *   batch * heads <= 2^30 and heads * max(P, N) * max_draft < 2^31 (SSM_E_SHAPE otherwise: the
+ *   kernels address a call's token rows with 32-bit offsets from each sequence's first token).
  */
 #ifndef SSM_REPLAY_H
 #define SSM_REPLAY_H

@@ -68,10 +68,14 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_replay_kernel(GdnArgs a) {
     constexpr int kVL = (MAXW * kVC + 63) / 64;
     constexpr int kRS = DK + 4;  // r row stride: the 4 rows an MFMA operand read takes hit distinct banks
     // The waves of a head split the staging of the entries (entry e by wave e % kW) into shared
-    // keys and decays. With several queries they also split the sweeps (query j by wave j % kW)
-    // and share the swept r_j and coefficients; a single query is swept by every wave.
+    // keys and decays. With several queries, or with a read copy, they also split the sweeps
+    // (query j by wave j % kW) and share the swept r_j and coefficients: a single query is then
+    // swept by wave 0 while the others wait at the barrier, which saves the repeated sweep's
+    // instructions where the copy's short row stream leaves the kernel bound by instruction issue.
+    // Without a copy the state stream bounds the kernel, and every wave sweeps a single query
+    // itself rather than wait for another.
     static_assert(MAXW % kW == 0, "entries split over the head's waves");
-    constexpr bool kSplit = kW > 1 && MAXQ > 1;
+    constexpr bool kSplit = kW > 1 && (MAXQ > 1 || RC != 0);
     constexpr int kQS = kSplit ? (MAXQ + kW - 1) / kW : MAXQ;  // queries this wave sweeps
     constexpr int kSW = kSplit ? 1 : kW;                       // copies of r and c
     constexpr int kEW = MAXW / kW;                             // entries this wave stages
@@ -91,8 +95,26 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_replay_kernel(GdnArgs a) {
     const int start = pt.start, count = pt.count;
     const long th = a.share ? (long)pt.slot * H + h : head;  // this head's checkpoint tile
     const int kmax = count + nq;
+    const long rh = uniform64((long)head * cap);      // this head's first ring row
+    const long t0 = uniform64((long)b * nq * H + h);  // this call's token 0 in the inputs
     // row of token j (clamped to the call's tokens) in the [batch][ntok][H] inputs
-    auto tok = [&](int j) -> long { return ((long)b * nq + min(max(j, 0), nq - 1)) * H + h; };
+    auto tok = [&](int j) -> long { return t0 + (long)min(max(j, 0), nq - 1) * H; };
+    // first element of entry e's row (wave-uniform e) in a ring or in this call's inputs, held in
+    // scalar registers so that each lane adds only its own element offset
+    // (offsets, not the pointers, go through uniform64: the pointers keep their global address
+    // space, so the loads stay global loads with a scalar base)
+    auto erow = [&](auto* ring, auto* in, int e, int w) {
+        return e < count ? ring + uniform64((rh + ring_slot(start, min(e, cap - 1), cap)) * w)
+                         : in + uniform64(tok(e - count) * w);
+    };
+    // the same for a per-lane entry e: a scalar base on each side (this head's ring rows, this
+    // call's token 0) and a 32-bit element offset per lane (the host bounds heads * w * ntok)
+    auto lrow = [&](auto* ring, auto* in, int e, int w) {
+        const bool r = e < count;
+        const unsigned o = r ? (unsigned)(ring_slot(start, min(e, cap - 1), cap) * w)
+                             : (unsigned)min(max(e - count, 0), nq - 1) * (unsigned)(H * w);
+        return (r ? ring + uniform64(rh * w) : in + uniform64(t0 * w)) + o;
+    };
     const TIN* rk = static_cast<const TIN*>(a.ring_k);
     const TIN* rv = static_cast<const TIN*>(a.ring_v);
     const TIN* inq = static_cast<const TIN*>(a.in_q);
@@ -104,14 +126,10 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_replay_kernel(GdnArgs a) {
     const int el = lane;  // lane's key elements: [el*kE, el*kE + kE)
     float be = 0.f, ge = 0.f;  // beta, g of entry e = lane
     {
-        const bool ring = lane < count;
-        const int s = ring_slot(start, min(lane, cap - 1), cap);
-        const float* pb = ring ? a.ring_beta + (long)head * cap + s : a.in_beta + tok(lane - count);
-        be = *pb;
+        be = *lrow(a.ring_beta, a.in_beta, lane, 1);
         be = lane < kmax ? be : 0.f;
         if constexpr (!VG) {
-            const float* pg = ring ? a.ring_g + (long)head * cap + s : a.in_g + tok(lane - count);
-            ge = *pg;
+            ge = *lrow(a.ring_g, a.in_g, lane, 1);
             ge = lane < kmax ? ge : 0.f;
         }
     }
@@ -120,9 +138,7 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_replay_kernel(GdnArgs a) {
 #pragma unroll
     for (int ee = 0; ee < kEW; ++ee) {
         const int e = ee * kW + wave;
-        const TIN* src = e < count ? rk + ((long)head * cap + ring_slot(start, min(e, cap - 1), cap)) * DK
-                                   : ink + tok(e - count) * DK;
-        load_raw<TIN, kE>(src + el * kE, kraw[ee]);
+        load_raw<TIN, kE>(erow(rk, ink, e, DK) + el * kE, kraw[ee]);
     }
     float graw[VG ? kEW : 1][kE];  // VG: the lane's log-decays of this wave's entries
     // (issued before the state stream for up to 16 entries; after it for more, where holding
@@ -132,24 +148,21 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_replay_kernel(GdnArgs a) {
 #pragma unroll
         for (int ee = 0; ee < kEW; ++ee) {
             const int e = ee * kW + wave;
-            const float* src = e < count ? a.ring_g + ((long)head * cap + ring_slot(start, min(e, cap - 1), cap)) * DK
-                                         : a.in_g + tok(e - count) * DK;
-            load_raw<float, kE>(src + el * kE, graw[ee]);
+            load_raw<float, kE>(erow(a.ring_g, a.in_g, e, DK) + el * kE, graw[ee]);
         }
     };
     if constexpr (VG && !kLateG) load_g();
     auto qidx = [&](int jj) { return kSplit ? jj * kW + wave : jj; };  // query of sweep slot jj
     TIN qraw[kQS][kE];
 #pragma unroll
-    for (int jj = 0; jj < kQS; ++jj) load_raw<TIN, kE>(inq + tok(qidx(jj)) * DK + el * kE, qraw[jj]);
+    for (int jj = 0; jj < kQS; ++jj)
+        load_raw<TIN, kE>(inq + uniform64(tok(qidx(jj)) * DK) + el * kE, qraw[jj]);
     u32x4_t vraw[kVL];
 #pragma unroll
     for (int i = 0; i < kVL; ++i) {
         const int idx = (lane + 64 * i) % (MAXW * kVC);
         const int e = idx / kVC, part = idx % kVC;
-        const TIN* src = e < count ? rv + ((long)head * cap + ring_slot(start, min(e, cap - 1), cap)) * DV
-                                   : inv + tok(e - count) * DV;
-        vraw[i] = *reinterpret_cast<const u32x4_t*>(src + wave * kRows + part * kEPC);
+        vraw[i] = *reinterpret_cast<const u32x4_t*>(lrow(rv, inv, e, DV) + wave * kRows + part * kEPC);
     }
 
     // ---- the checkpoint rows of this wave ------------------------------------------------------
@@ -190,9 +203,7 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_replay_kernel(GdnArgs a) {
 #pragma unroll
             for (int u = 0; u < kGB; ++u) {
                 const int e = (e0 + u) * kW + wave;
-                const float* src = e < count ? a.ring_g + ((long)head * cap + ring_slot(start, min(e, cap - 1), cap)) * DK
-                                             : a.in_g + tok(e - count) * DK;
-                load_raw<float, kE>(src + el * kE, gb[u]);
+                load_raw<float, kE>(erow(a.ring_g, a.in_g, e, DK) + el * kE, gb[u]);
             }
 #pragma unroll
             for (int u = 0; u < kGB; ++u) {
@@ -200,7 +211,7 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_replay_kernel(GdnArgs a) {
 #pragma unroll
                 for (int i = 0; i < kE; ++i) s_al[e][el * kE + i] = expf(gb[u][i]);
                 if (e >= count && e < kmax)  // this call's tokens: append g
-                    store_raw<float, kE>(a.ring_g + ((long)head * cap + ring_slot(start, e, cap)) * DK +
+                    store_raw<float, kE>(a.ring_g + uniform64((rh + ring_slot(start, e, cap)) * DK) +
                                              el * kE, gb[u]);
             }
         }
@@ -211,14 +222,13 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_replay_kernel(GdnArgs a) {
         if (idx < MAXW * kVC) s_v[wave][idx] = vraw[i];
     }
     {
-        const long rb = (long)head * cap;
 #pragma unroll
         for (int i = 0; i < kVL; ++i) {
             const int idx = lane + 64 * i;
             const int e = idx / kVC, part = idx % kVC;
             if (e >= count && e < kmax && idx < MAXW * kVC)
-                *reinterpret_cast<u32x4_t*>(static_cast<TIN*>(a.ring_v) +
-                                            (rb + ring_slot(start, e, cap)) * DV + wave * kRows +
+                *reinterpret_cast<u32x4_t*>(static_cast<TIN*>(a.ring_v) + uniform64(rh * DV) +
+                                            (unsigned)(ring_slot(start, e, cap) * DV) + wave * kRows +
                                             part * kEPC) = vraw[i];
         }
         // each wave appends the keys (and decays) it staged and the queries it sweeps
@@ -226,24 +236,23 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_replay_kernel(GdnArgs a) {
         for (int jj = 0; jj < kQS; ++jj) {
             const int j = qidx(jj);
             if (j >= nq || (!kSplit && wave != 0)) continue;
-            const long rs = rb + ring_slot(start, count + j, cap);
-            store_raw<TIN, kE>(static_cast<TIN*>(a.ring_q) + rs * DK + el * kE, qraw[jj]);
+            const long rs = rh + ring_slot(start, count + j, cap);
+            store_raw<TIN, kE>(static_cast<TIN*>(a.ring_q) + uniform64(rs * DK) + el * kE, qraw[jj]);
         }
 #pragma unroll
         for (int ee = 0; ee < kEW; ++ee) {
             const int e = ee * kW + wave;
             if (e >= count && e < kmax) {
-                store_raw<TIN, kE>(static_cast<TIN*>(a.ring_k) + (rb + ring_slot(start, e, cap)) * DK +
-                                       el * kE, kraw[ee]);
+                const long rs = rh + ring_slot(start, e, cap);
+                store_raw<TIN, kE>(static_cast<TIN*>(a.ring_k) + uniform64(rs * DK) + el * kE, kraw[ee]);
                 if constexpr (VG && !kLateG)
-                    store_raw<float, kE>(a.ring_g + (rb + ring_slot(start, e, cap)) * DK + el * kE,
-                                         graw[ee]);
+                    store_raw<float, kE>(a.ring_g + uniform64(rs * DK) + el * kE, graw[ee]);
             }
         }
         if (wave == 0 && lane >= count && lane < kmax) {
-            const long rs = rb + ring_slot(start, lane, cap);
-            a.ring_beta[rs] = be;
-            if constexpr (!VG) a.ring_g[rs] = ge;
+            const unsigned rs = ring_slot(start, lane, cap);
+            a.ring_beta[rh + rs] = be;
+            if constexpr (!VG) a.ring_g[rh + rs] = ge;
         }
     }
 
@@ -256,7 +265,8 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_replay_kernel(GdnArgs a) {
         for (int i = 0; i < kE; ++i) r[jj][i] = to_f32<TIN>(qraw[jj][i]);
     if constexpr (kW > 1) __syncthreads();  // every wave's entries are staged
     else wave_sync();
-    for (int e = kmax - 1; e >= 0; --e) {  // uniform trip count
+    const bool sweeps = qidx(0) < nq;  // uniform: a wave left without a query skips the sweep
+    for (int e = sweeps ? kmax - 1 : -1; e >= 0; --e) {  // uniform trip count
         float kv[kE];
 #pragma unroll
         for (int i = 0; i < kE; ++i) kv[i] = to_f32<TIN>(s_k[e][el * kE + i]);
@@ -628,6 +638,7 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_flush_kernel(GdnArgs a, int mod
     if (nfold == 0 && !rewrite_only && !ft.move) return;
     const long th = a.share ? (long)slot * a.heads + h : head;   // tile read
     const long tw = a.share ? (long)ft.wr * a.heads + h : head;  // tile written
+    const long rh = uniform64((long)head * cap);                  // this head's first ring row
     const TIN* rk = static_cast<const TIN*>(a.ring_k);
     const TIN* rv = static_cast<const TIN*>(a.ring_v);
     const int li = lane & 15, lg = lane >> 4;
@@ -637,15 +648,15 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_flush_kernel(GdnArgs a, int mod
     // entry e (already clamped to a folded entry): ring slot, or the caller's token (FUSED)
     auto krow = [&](int e) -> const TIN* {
         if (FUSED && e >= nring) return static_cast<const TIN*>(a.in_k) + (long)head * DK;
-        return rk + ((long)head * cap + ring_slot(start, e, cap)) * DK;
+        return rk + (rh + ring_slot(start, e, cap)) * DK;
     };
     auto vrow = [&](int e) -> const TIN* {
         if (FUSED && e >= nring) return static_cast<const TIN*>(a.in_v) + (long)head * DV;
-        return rv + ((long)head * cap + ring_slot(start, e, cap)) * DV;
+        return rv + (rh + ring_slot(start, e, cap)) * DV;
     };
     auto grow = [&](int e) -> const float* {  // VG: the entry's dk log-decays
         if (FUSED && e >= nring) return a.in_g + (long)head * DK;
-        return a.ring_g + ((long)head * cap + ring_slot(start, e, cap)) * DK;
+        return a.ring_g + (rh + ring_slot(start, e, cap)) * DK;
     };
     // chunk loader (branch-free: entries past nfold read the last folded entry, zeroed later);
     // wave w loads key pieces w * 16 kKC / kW .. of the chunk
@@ -665,7 +676,7 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_flush_kernel(GdnArgs a, int mod
             vraw[i] = *reinterpret_cast<const u32x4_t*>(vrow(e) + p_base + part * kEPC);
         }
         const int e = min(c0 + li, max(nfold - 1, 0));
-        const long s = (long)head * cap + ring_slot(start, min(e, cap - 1), cap);
+        const long s = rh + ring_slot(start, min(e, cap - 1), cap);
         const bool tok = FUSED && e >= nring;
         be = tok ? a.in_beta[head] : a.ring_beta[s];
         be = (c0 + li < nfold) ? be : 0.f;  // lanes 16..63 mirror lanes 0..15

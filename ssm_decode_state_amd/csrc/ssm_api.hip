@@ -25,6 +25,10 @@ ssm_status check_config(const ssm_config* c) {
     if (c->share_ckpt != 0 && c->share_ckpt != 1) return SSM_E_ARG;
     if (c->batch < 0 || c->heads < 1 || c->groups < 1) return SSM_E_SHAPE;
     if ((int64_t)c->batch * c->heads > (int64_t)1 << 30) return SSM_E_SHAPE;
+    // the kernels reach a call's token j of a sequence by a 32-bit element offset j * H * width
+    const int64_t width = c->dim_p > c->dim_n ? c->dim_p : c->dim_n;
+    if ((int64_t)c->heads * width * (c->max_draft > 1 ? c->max_draft : 1) >= (int64_t)1 << 31)
+        return SSM_E_SHAPE;
     if (c->heads % c->groups != 0) return SSM_E_SHAPE;
     if (c->window < 1 || c->window > 32) return SSM_E_SHAPE;
     if (c->max_draft < 1 || c->max_draft > 8 || c->max_draft > c->window) return SSM_E_SHAPE;

@@ -242,6 +242,15 @@ __device__ __forceinline__ float readlane(float v, int lane) {
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
 }
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+// A 64-bit wave-uniform value moved to scalar registers: the compiler forms 64-bit products
+// such as a row index times a stride in vector registers, and everything derived from them
+// (ring and input addresses) would then stay there too.
+__device__ __forceinline__ long uniform64(long v) {
+    const unsigned long long u = (unsigned long long)v;
+    const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)u);
+    const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(u >> 32));
+    return (long)(((unsigned long long)hi << 32) | lo);
+}
 
 // fp32 MFMA 16x16x4 (v_mfma_f32_16x16x4f32): D = A (16x4) * B (4x16) + C. Operand lanes:
 // A[m][k] from lane m + 16k, B[k][c] from lane c + 16k, D[m][c] in lane c + 16(m/4), register m%4.

@@ -124,6 +124,8 @@ def test_every_accepted_mamba2_shape(P, N):
     (dict(max_draft=9, window=16), bd.SSM_E_SHAPE),
     (dict(max_draft=5, window=4), bd.SSM_E_SHAPE),
     (dict(batch=-1), bd.SSM_E_SHAPE),
+    (dict(batch=1, heads=1 << 21, groups=1 << 21, max_draft=8), bd.SSM_E_SHAPE),
+    (dict(kind=bd.SSM_GDN, batch=1, heads=1 << 22, groups=1 << 22, max_draft=4), bd.SSM_E_SHAPE),
     (dict(readcopy=bd.SSM_RC_FP8_ROW, dim_p=32, dim_n=64), bd.SSM_E_UNSUPPORTED),
     (dict(readcopy=bd.SSM_RC_FP8_ROW, dim_n=32), bd.SSM_E_UNSUPPORTED),
     (dict(readcopy=bd.SSM_RC_FP4_B16, dim_n=32), bd.SSM_E_UNSUPPORTED),
