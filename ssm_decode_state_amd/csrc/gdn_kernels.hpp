@@ -981,7 +981,7 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_flush_kernel(GdnArgs a, int mod
             }
         }
         rc_write_blocks<DV, DK, RC>(RcView{a.rc_codes, a.rc_scale, a.rc_tscale}, tw, p_base, li, lg,
-                                    S, amax_t, wave == 0 && lane == 0);
+                                    S, amax_t, wave == 0 && lane == 0, &s_v[wave][0][0]);
     }
     if constexpr (kW > 1) __builtin_amdgcn_s_barrier();  // every wave has read the pointers
     if ((nfold > 0 || ft.move) && wave == 0 && lane == 0)

@@ -530,7 +530,7 @@ __attribute__((amdgpu_waves_per_eu(2))) void m2_fold_kernel(M2Args a, int mode_a
         static_assert(P == 64, "read copy needs P == 64");
         const float amax_t = RC == 2 ? xor_reduce_max<1, 32>(rc_local_amax<N>(hb)) : 0.f;
         rc_write_blocks<P, N, RC>(RcView{a.rc_codes, a.rc_scale, a.rc_tscale}, tw, 0, li, lg, hb,
-                                  amax_t, lane == 0);
+                                  amax_t, lane == 0, &s_b[wave][0][0]);  // (staging is done)
     }
     if ((nfold > 0 || ft.move) && lane == 0)
         *reinterpret_cast<int4*>(a.ptr + kPtrInts * head) =

@@ -160,10 +160,11 @@ __device__ __forceinline__ float rc_local_amax(const f32x4 (&hb)[4][N / 16]) {
 // Write the copy of rows row0 .. row0 + 63 of a head's tile from its fp32 values in MFMA
 // accumulator order (see rc_local_amax). fp4 needs amax_tile, the largest magnitude over the whole
 // head tile; `tile_writer` is true in exactly one lane of the head, which stores the tile scale.
+// s_tab: 128 floats of LDS private to the calling wavefront (fp4 only; may hold anything).
 template <int ROWS, int N, int RC>
 __device__ __forceinline__ void rc_write_blocks(const RcView& v, long head, int row0, int li, int lg,
                                                 const f32x4 (&hb)[4][N / 16], float amax_tile,
-                                                bool tile_writer) {
+                                                bool tile_writer, float* s_tab) {
     static_assert(N == 64 || N == 128, "read copy: N in {64, 128}");
     constexpr int kNB = N / 16;
     if constexpr (RC == 1) {
@@ -191,26 +192,44 @@ __device__ __forceinline__ void rc_write_blocks(const RcView& v, long head, int 
         const float st = amax_tile > 0.f ? fmaxf(amax_tile / 2688.f, kRcScaleFloorFp4Tile) : 1.f;
         const float d6 = 6.f * st;
         const float rd6 = 1.f / d6;  // correctly rounded, once per tile
+        // The element codes take h * RN(1/S) with S = RN(value(sb) * st): with st fixed for the
+        // tile, S and its reciprocal depend on the block-scale code alone, so the wave divides
+        // once per code (two codes per lane) and every block looks its reciprocal up. Code 0
+        // (S = 0) maps to 0; code 127 is NaN and never produced (block codes saturate at 448).
+        wave_sync();  // this wave may have read the table's LDS just before
+#pragma unroll
+        for (int c = li + 16 * lg; c < 128; c += 64) {
+            const float S = e4m3x2_decode_hw<false>((uint32_t)c).x * st;
+            s_tab[c] = (c != 0 && c < 127) ? 1.f / S : 0.f;
+        }
+        wave_sync();
         uint8_t* codes = v.codes + head * (long)(ROWS * N / 2);
         uint8_t* sbp = static_cast<uint8_t*>(v.scale) + head * (long)ROWS * (N / 16);
 #pragma unroll
         for (int pb = 0; pb < 4; ++pb) {
             const int p = row0 + 16 * pb + li;
-            uint32_t sbw[(kNB + 3) / 4] = {};  // the row's block-scale codes, byte nb
+            // every block's scale code first, then the table reads back to back, then the codes:
+            // no branch between a table read and its use, so the reads share one wait
+            uint32_t sb[kNB];
 #pragma unroll
             for (int nb = 0; nb < kNB; ++nb) {
                 float ab = fmaxf(fmaxf(fabsf(hb[pb][nb][0]), fabsf(hb[pb][nb][1])),
                                  fmaxf(fabsf(hb[pb][nb][2]), fabsf(hb[pb][nb][3])));
                 ab = xor_reduce_max<16, 32>(ab);  // the 16-element block spans lanes li + 16 lg
-                const uint32_t sb = block_scale_code(ab, d6, rd6);
-                const float S = e4m3x2_decode_hw<false>(sb).x * st;
-                const float inv = S > 0.f ? 1.f / S : 0.f;
-                const uint32_t c = S > 0.f ? e2m1_half_encode(hb[pb][nb][0] * inv, hb[pb][nb][1] * inv,
-                                                              hb[pb][nb][2] * inv, hb[pb][nb][3] * inv)
-                                           : 0u;
+                sb[nb] = block_scale_code(ab, d6, rd6);
+            }
+            float inv[kNB];
+#pragma unroll
+            for (int nb = 0; nb < kNB; ++nb) inv[nb] = s_tab[sb[nb]];  // RN(1/S), 0 for sb == 0
+            uint32_t sbw[(kNB + 3) / 4] = {};  // the row's block-scale codes, byte nb
+#pragma unroll
+            for (int nb = 0; nb < kNB; ++nb) {
+                // S > 0 exactly when sb != 0; a zero block's codes are 0 (not the -0 of h * 0)
+                const uint32_t c = e2m1_half_encode(hb[pb][nb][0] * inv[nb], hb[pb][nb][1] * inv[nb],
+                                                    hb[pb][nb][2] * inv[nb], hb[pb][nb][3] * inv[nb]);
                 *reinterpret_cast<uint16_t*>(codes + ((long)(nb / 2) * ROWS + p) * 16 + 8 * (nb % 2) +
-                                             2 * lg) = (uint16_t)c;
-                sbw[nb / 4] |= sb << (8 * (nb % 4));
+                                             2 * lg) = (uint16_t)(sb[nb] != 0u ? c : 0u);
+                sbw[nb / 4] |= sb[nb] << (8 * (nb % 4));
             }
             if (lg == 0) {  // one store of the row's N/16 block-scale codes
                 if constexpr (kNB == 8)
