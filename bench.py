@@ -8,15 +8,18 @@ H = 128 heads, head dim P = 64, state dim N = 128 (fp32 checkpoint, 4 MiB per se
 L = 16, bf16 x/B/C and fp32 dt. One step = one decode token for every sequence through the whole
 replay path: append to the ring, replay output from the checkpoint, and (every L-th step) the
 flush that folds the window into the checkpoint. After W eager warm-up steps, the K steps run once
-eagerly with HIP events around every launch (the per-kernel figures), and then as one HIP graph of
+eagerly, launched back to back with HIP events between runs of one kernel (a window's replays, the
+fold: the per-kernel figures), once more with an event pair around each launch (the per-count
+figures), and then as one HIP graph of
 exactly those K steps: captured, replayed once untimed, the state bytes restored, and replayed
 once more inside the timed region. `value` is B * K over that timed replay's wall time, for any
 K; the window-amortized step ((L - 1) replays + the fused fold) / L is reported beside it, so a K
 that is not a multiple of L neither flatters nor penalizes the fold's share.
 
 Reported: tokens/s per layer, the in-house conventional read-modify-write step on the same shapes
-and inputs (timed the same way), the replay kernel's achieved HBM bandwidth from per-launch HIP
-events against the algorithmic bytes (also against a measured streaming-read ceiling), and the
+and inputs (timed the same way), the replay kernel's achieved HBM bandwidth from those HIP events
+against the algorithmic bytes (also against a streaming-read ceiling measured at the same bytes
+per launch), and the
 fp64 CPU oracle timed on a bounded sample of the same workload on this host.
 
 Inputs are seeded synthetic draws made on the device (ssm_decode_state_amd.synth) and resident in
@@ -145,21 +148,42 @@ def gpu_preroll(launches=12):
         bd.ssm_debug_stream_read(_PREROLL["buf"], _PREROLL["out"], 2048)
 
 
-def timed_calls(n, fn):
-    """Run fn(i) for i < n with a HIP-event pair around each call on the current stream, behind a
-    GPU pre-roll (see gpu_preroll); returns (seconds of GPU time from the first call's start to
+def timed_calls(n, fn, kind=None):
+    """Run fn(i) for i < n on the current stream behind a GPU pre-roll (see gpu_preroll).
+    Without `kind`, a HIP-event pair brackets each call. With kind(i), a label per call (say
+    replay or fold), events mark only the boundaries between runs of calls of one kind and each
+    call of a run is charged the run's span over its length: the launches of a run go back to
+    back with no event between them, as a serving loop issues them, and no per-launch event
+    overhead lands on short kernels. Returns (seconds of GPU time from the first call's start to
     the last call's end, per-call milliseconds)."""
     import torch
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(n)]
     torch.cuda.synchronize()
+    if kind is None:
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(n)]
+        gpu_preroll()
+        for i in range(n):
+            ev[i][0].record()
+            fn(i)
+            ev[i][1].record()
+        torch.cuda.synchronize()
+        return ev[0][0].elapsed_time(ev[-1][1]) * 1e-3, [a.elapsed_time(b) for a, b in ev]
+    starts = [0] + [i for i in range(1, n) if kind(i) != kind(i - 1)]
+    ends = starts[1:] + [n]
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(starts) + 1)]
     gpu_preroll()
+    r = 0
     for i in range(n):
-        ev[i][0].record()
+        if r < len(starts) and i == starts[r]:
+            ev[r].record()
+            r += 1
         fn(i)
-        ev[i][1].record()
+    ev[-1].record()
     torch.cuda.synchronize()
-    return ev[0][0].elapsed_time(ev[-1][1]) * 1e-3, [a.elapsed_time(b) for a, b in ev]
+    ms = []
+    for j, (a, b) in enumerate(zip(starts, ends)):
+        ms += [ev[j].elapsed_time(ev[j + 1]) / (b - a)] * (b - a)
+    return ev[0].elapsed_time(ev[-1]) * 1e-3, ms
 
 
 CEILING_SIZES_MIB = (64, 128, 256, 512, 1024)
@@ -169,8 +193,9 @@ def bench_read_ceiling(dev, sizes_mib=CEILING_SIZES_MIB, launches=12, pool_bytes
     """The practical read ceiling against bytes per launch: one pass of plain streaming reads
     (16-byte non-temporal loads, ssm_debug_stream_read) over S bytes for S from 64 MiB to 1 GiB,
     each launch on the next S-byte slice of a 2 GiB pool (eight times the last-level cache), so
-    that every launch reads HBM. Timed like the decode kernels' per-launch figures: a HIP-event
-    pair around each launch behind a GPU pre-roll. Per size, the better of two grid shapes (one
+    that every launch reads HBM. Timed like the decode kernels' per-launch figures: launches back
+    to back behind a GPU pre-roll, their span over their number. Per size, the better of two grid
+    shapes (one
     or four 32 KiB chunks per wavefront). A short launch pays the grid's ramp-up and drain, so a
     kernel is compared with this curve at its own bytes per launch (ceiling_at)."""
     import torch
@@ -193,7 +218,7 @@ def bench_read_ceiling(dev, sizes_mib=CEILING_SIZES_MIB, launches=12, pool_bytes
 
             for i in (-2, -1):
                 fn(i)
-            _, ms = timed_calls(launches, fn)
+            _, ms = timed_calls(launches, fn, kind=lambda i: 0)  # back to back, like the workloads
             us = sum(ms) / len(ms) * 1e3
             r = {"avg_us": us, "gbs": nb / (us * 1e-6) / 1e9, "workgroups": blocks}
             if best is None or r["gbs"] > best["gbs"]:
@@ -349,7 +374,8 @@ def bench_m2_decode(dev, shape, seed, h0_std, steps, warm, pool=16):
     y = torch.empty(Bn, H, P, device=dev)
     for i in range(warm):
         bd.ssm_replay_decode(st, inputs[i % pool], y)
-    wall, ms = timed_calls(steps, lambda i: bd.ssm_replay_decode(st, inputs[(warm + i) % pool], y))
+    wall, ms = timed_calls(steps, lambda i: bd.ssm_replay_decode(st, inputs[(warm + i) % pool], y),
+                           kind=lambda i: (warm + i) % L == L - 1)
     fold = [m for i, m in enumerate(ms) if (warm + i) % L == L - 1]
     rep = [m for i, m in enumerate(ms) if (warm + i) % L != L - 1]
     rep_b = sum(Bn * H * m2_replay_bytes_per_head(P, N, (warm + i) % L + 1, 2)
@@ -583,7 +609,8 @@ def bench_readcopy(dev, rc, steps=128, warm=16, layers=4, pool=16):
     for i in range(n_warm):
         bd.ssm_replay_decode(sts[i % layers], inputs[i % pool], y)
     wall, ms = timed_calls(n, lambda i: bd.ssm_replay_decode(sts[i % layers],
-                                                             inputs[(n_warm + i) % pool], y))
+                                                             inputs[(n_warm + i) % pool], y),
+                           kind=lambda i: ((n_warm + i) // layers) % L == L - 1)
     heads = Bn * H
     rep_b = rep_ms = 0.0
     flush_ms = []
@@ -636,7 +663,8 @@ def bench_gdn(dev, steps=128, warm=16, layers=2, pool=16, rc=0, kda=False):
     for i in range(n_warm):
         bd.ssm_replay_decode(sts[i % layers], inputs[i % pool], o)
     wall, ms = timed_calls(n, lambda i: bd.ssm_replay_decode(sts[i % layers],
-                                                             inputs[(n_warm + i) % pool], o))
+                                                             inputs[(n_warm + i) % pool], o),
+                           kind=lambda i: ((n_warm + i) // layers) % L == L - 1)
     heads = Bn * H
     rep_b = rep_ms = 0.0
     fold = []
@@ -659,7 +687,7 @@ def bench_gdn(dev, steps=128, warm=16, layers=2, pool=16, rc=0, kda=False):
     for i in range(n_warm):
         bd.ssm_conventional_step(cfg, convs[i % layers], inputs[i % pool], None, None, o)
     cwall, cms = timed_calls(n, lambda i: bd.ssm_conventional_step(
-        cfg, convs[i % layers], inputs[(n_warm + i) % pool], None, None, o))
+        cfg, convs[i % layers], inputs[(n_warm + i) % pool], None, None, o), kind=lambda i: 0)
     cgbs = heads * gdn_conv_bytes_per_head(dv, dk, gsz=gsz) / (sum(cms) / n * 1e-3) / 1e9
     return {"workload": "kda_replay_decode_b256" if kda else "gdn_replay_decode_b256",
             "tokens_per_s": Bn * n / wall,
@@ -972,23 +1000,16 @@ def main():
     torch.cuda.synchronize()
     del st1, t1
 
-    # ---- replay path, eager: one launch per step, HIP events around each (per-kernel figures) -
+    # ---- replay path, eager: one launch per step from Python behind a GPU pre-roll. Per-kernel
+    #      figures come from runs of back-to-back launches of one kernel (a window's L-1 replays,
+    #      then the fused fold) with events only at the run boundaries -----------------------
     for t in range(W):
         bd.ssm_replay_decode(st, inputs[t], y)
-    torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(K)]
-    gpu_preroll()  # the launches below queue up behind it: the events bracket the kernels alone
-    for t in range(K):
-        ev[t][0].record()
-        bd.ssm_replay_decode(st, inputs[W + t], y)
-        ev[t][1].record()
-    torch.cuda.synchronize()
+    ks = [((W + t) % L) + 1 for t in range(K)]  # committed count after the append
     # the eager figure: GPU time from the first step's start to the last step's end (the pre-roll
     # keeps host launch latency out of it)
-    t_eager = ev[0][0].elapsed_time(ev[-1][1]) * 1e-3
-    step_ms = [a.elapsed_time(b) for a, b in ev]
-    ks = [((W + t) % L) + 1 for t in range(K)]  # committed count after the append
+    t_eager, step_ms = timed_calls(K, lambda t: bd.ssm_replay_decode(st, inputs[W + t], y),
+                                   kind=lambda t: ks[t] == L)
 
     heads = Bn * H
     rep_bytes = rep_ms = 0.0
@@ -1010,9 +1031,12 @@ def main():
     fold_gbs = fold_bytes / (fold_ms * 1e-3) / 1e9 if fold_ms else None
     # the replay launches timed above run at counts 1..L-1 (the L-th step is the fused fold)
     mean_bytes_per_head = rep_bytes / heads / max(n_rep, 1)
+    # per-count launch times (a diagnostic: the replay grows with the entries it reads): the same
+    # K steps once more, an event pair around each launch
+    _, each_ms = timed_calls(K, lambda t: bd.ssm_replay_decode(st, inputs[W + t], y))
     per_k = {}
-    for k, ms in zip(ks, step_ms):
-        per_k.setdefault(k, []).append(ms)
+    for t, ms in enumerate(each_ms):
+        per_k.setdefault(((W + K + t) % L) + 1, []).append(ms)
 
     # ---- the headline: exactly the K steps, launched from one captured graph ------------------
     # (from the state the eager pass left; the state is restored after the warm-up replay)
@@ -1047,8 +1071,9 @@ def main():
         "step_us_by_count": {str(k): sum(v) / len(v) * 1e3 for k, v in sorted(per_k.items())},
         "eager": {"value": Bn * K / t_eager, "ms_per_step": t_eager / K * 1e3,
                   "note": "the same K steps launched one by one from Python behind a GPU pre-roll, "
-                          "HIP events around each (the per-kernel figures above come from this "
-                          "pass); GPU time from the first step's start to the last one's end"},
+                          "HIP events only between runs of one kernel (a window's replays, the "
+                          "fold); the per-kernel figures above come from this pass; GPU time "
+                          "from the first step's start to the last one's end"},
     }
     if graph is not None:
         out["graph"] = graph
@@ -1068,16 +1093,10 @@ def main():
         for t in range(W):
             bd.ssm_conventional_step(cfg, tiles, inputs[t], Ad, Dd, y)
         torch.cuda.synchronize()
-        evc = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(K)]
-        gpu_preroll()
-        for t in range(K):
-            evc[t][0].record()
-            bd.ssm_conventional_step(cfg, tiles, inputs[W + t], Ad, Dd, y)
-            evc[t][1].record()
-        torch.cuda.synchronize()
-        t_conv = evc[0][0].elapsed_time(evc[-1][1]) * 1e-3
-        conv_ms = sum(a.elapsed_time(b) for a, b in evc) / K
+        t_conv, cms = timed_calls(K, lambda t: bd.ssm_conventional_step(cfg, tiles, inputs[W + t],
+                                                                         Ad, Dd, y),
+                                  kind=lambda t: 0)
+        conv_ms = sum(cms) / K
         conv_gbs = heads * m2_conv_bytes_per_head(P, N) / (conv_ms * 1e-3) / 1e9
         out["conventional"] = {"value": Bn * K / t_conv, "unit": "tokens/s/layer",
                                "ms_per_step": t_conv / K * 1e3, "avg_launch_us": conv_ms * 1e3,
