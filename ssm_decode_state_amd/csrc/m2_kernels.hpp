@@ -95,20 +95,6 @@ __global__ __launch_bounds__(256) void m2_replay_kernel(M2Args a) {
 
     // ---- 1. small loads (branch-free: invalid entries read a valid row and are masked later) -
     const long tok0 = (long)b * nq;  // this sequence's first token in the call's inputs
-    const long rh = uniform64((long)head * cap);   // this head's first ring row (x, dt)
-    const long rg = uniform64((long)bg * cap);     // its group's first ring row (B, C)
-    const long tx = uniform64(tok0 * H + h);       // token 0's x and dt rows in the inputs
-    const long tb = uniform64(tok0 * Gn + grp);    // token 0's B and C rows
-    // entry e (per lane) of a ring or of this call's tokens: a scalar base on each side (ring
-    // row rbase, input row ibase; istride rows between tokens) and a 32-bit element offset per
-    // lane (the host bounds heads * width * ntok); offsets, not pointers, go through uniform64 so
-    // that the pointers keep their global address space
-    auto lrow = [&](auto* ring, auto* in, long rbase, long ibase, int istride, int e, int w) {
-        const bool r = e < count;
-        const unsigned o = r ? (unsigned)(ring_slot(start, min(e, cap - 1), cap) * w)
-                             : (unsigned)min(max(e - count, 0), nq - 1) * (unsigned)(istride * w);
-        return (r ? ring + uniform64(rbase * w) : in + uniform64(ibase * w)) + o;
-    };
     // C of each query: lane holds elements n = lane + 64 i (N >= 64) or n = lane (N < 64)
     TIN craw[MAXQ][kCE];
 #pragma unroll
@@ -117,11 +103,13 @@ __global__ __launch_bounds__(256) void m2_replay_kernel(M2Args a) {
 #pragma unroll
         for (int i = 0; i < kCE; ++i) {
             const int n = (lane + 64 * i) % N;
-            craw[j][i] = (inC + uniform64((tb + (long)jj * Gn) * N))[n];
+            craw[j][i] = inC[((tok0 + jj) * Gn + grp) * N + n];
         }
     }
     // dt of entry e = lane
-    float dte = *lrow(a.ring_dt, a.in_dt, rh, tx, H, lane, 1);
+    const float* dsrc = lane < count ? a.ring_dt + head * cap + ring_slot(start, min(lane, cap - 1), cap)
+                                     : a.in_dt + (tok0 + min(max(lane - count, 0), nq - 1)) * H + h;
+    float dte = *dsrc;
     dte = lane < kmax ? dte : 0.f;
     // B rows of every entry in 16-byte chunks, chunk idx = lane + 64 i -> (entry idx / kBCE,
     // part idx % kBCE): each load instruction covers whole rows, 1 KiB per ring run
@@ -129,7 +117,9 @@ __global__ __launch_bounds__(256) void m2_replay_kernel(M2Args a) {
 #pragma unroll
     for (int i = 0; i < kBL; ++i) {
         const int e = (lane + 64 * i) / kBCE, part = lane % kBCE;
-        braw[i] = *reinterpret_cast<const u32x4_t*>(lrow(rB, inB, rg, tb, Gn, e, N) + part * kEPC);
+        const TIN* src = e < count ? rB + ((long)bg * cap + ring_slot(start, min(e, cap - 1), cap)) * N
+                                   : inB + ((tok0 + min(max(e - count, 0), nq - 1)) * Gn + grp) * N;
+        braw[i] = *reinterpret_cast<const u32x4_t*>(src + part * kEPC);
     }
     // x rows of every entry, in 16-byte chunks: chunk idx -> (row e = idx / kCPR, part idx % kCPR)
     u32x4_t xraw[kXL];
@@ -137,7 +127,9 @@ __global__ __launch_bounds__(256) void m2_replay_kernel(M2Args a) {
     for (int i = 0; i < kXL; ++i) {
         const int idx = lane + 64 * i;
         const int e = idx / kCPR, part = idx % kCPR;
-        xraw[i] = *reinterpret_cast<const u32x4_t*>(lrow(rx, inx, rh, tx, H, e, P) + part * kEPC);
+        const TIN* src = e < count ? rx + ((long)head * cap + ring_slot(start, min(e, cap - 1), cap)) * P
+                                   : inx + ((tok0 + min(max(e - count, 0), nq - 1)) * H + h) * P;
+        xraw[i] = *reinterpret_cast<const u32x4_t*>(src + part * kEPC);
     }
 
     // ---- 2. the checkpoint stream (explainer, "Why Decoding, Not Prefill, Is the Hard Part":
@@ -179,17 +171,17 @@ __global__ __launch_bounds__(256) void m2_replay_kernel(M2Args a) {
         const int idx = lane + 64 * i;
         const int e = idx / kCPR, part = idx % kCPR;
         if (e >= count && e < kmax)  // this call's token: append its x row
-            *reinterpret_cast<u32x4_t*>(rx + uniform64(rh * P) + (unsigned)(ring_slot(start, e, cap) * P) +
-                                        part * kEPC) = xraw[i];
+            *reinterpret_cast<u32x4_t*>(rx + ((long)head * cap + ring_slot(start, e, cap)) * P + part * kEPC) =
+                xraw[i];
     }
-    if (lane >= count && lane < kmax) a.ring_dt[rh + (unsigned)ring_slot(start, lane, cap)] = dte;
+    if (lane >= count && lane < kmax) a.ring_dt[head * cap + ring_slot(start, lane, cap)] = dte;
     if (h % hpg == 0) {  // the group's first head writes the shared B and C entries
 #pragma unroll
         for (int i = 0; i < kBL; ++i) {
             const int e = (lane + 64 * i) / kBCE, part = lane % kBCE;
             if (e >= count && e < kmax)
-                *reinterpret_cast<u32x4_t*>(rB + uniform64(rg * N) + (unsigned)(ring_slot(start, e, cap) * N) +
-                                            part * kEPC) = braw[i];
+                *reinterpret_cast<u32x4_t*>(rB + ((long)bg * cap + ring_slot(start, e, cap)) * N + part * kEPC) =
+                    braw[i];
         }
 #pragma unroll
         for (int j = 0; j < MAXQ; ++j) {
@@ -198,7 +190,7 @@ __global__ __launch_bounds__(256) void m2_replay_kernel(M2Args a) {
 #pragma unroll
             for (int i = 0; i < kCE; ++i) {
                 const int n = lane + 64 * i;
-                if (n < N) (rC + uniform64((rg + slot) * N))[n] = craw[j][i];
+                if (n < N) rC[((long)bg * cap + slot) * N + n] = craw[j][i];
             }
         }
     }
@@ -314,7 +306,7 @@ __global__ __launch_bounds__(256) void m2_replay_kernel(M2Args a) {
 #pragma unroll
         for (int j = 0; j < MAXQ; ++j) {
             if (j >= nq) break;
-            (a.y + uniform64((tx + (long)j * H) * P))[row] = s0[j] * acc[j] + out[j];
+            a.y[(((long)b * nq + j) * H + h) * P + row] = s0[j] * acc[j] + out[j];
         }
     }
     if constexpr (COMMIT) {

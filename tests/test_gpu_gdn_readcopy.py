@@ -139,7 +139,7 @@ def test_gdn_readcopy_decode(rc, case, kind):
         pairs = [(b, h) for b in range(2) for h in range(3)]
     else:
         w = synth.WORKLOADS["kda_b256" if kind == synth.KDA else "gdn_b256"]
-        shape, seed, T, scale = w["shape"], w["seed"] + 10 * rc, 256, 1.0
+        shape, seed, T, scale = w["shape"], w["seed"] + 10 * rc, 512, 1.0  # 32 windows
         pairs = sample_pairs(shape.batch, shape.heads, 8)
     per_window = run_decode(shape, seed, rc, T, scale, pairs)
     slope, se = drift_slope(per_window)
