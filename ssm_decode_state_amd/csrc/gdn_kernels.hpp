@@ -194,7 +194,7 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_replay_kernel(GdnArgs a) {
 #pragma unroll
         for (int ee = 0; ee < kEW; ++ee)
 #pragma unroll
-            for (int i = 0; i < kE; ++i) s_al[ee * kW + wave][el * kE + i] = expf(graw[ee][i]);
+            for (int i = 0; i < kE; ++i) s_al[ee * kW + wave][el * kE + i] = __expf(graw[ee][i]);
     } else if constexpr (VG) {  // up to eight entries at a time: few registers live beside the rows
         constexpr int kGB = kEW % 8 == 0 ? 8 : kEW % 6 == 0 ? 6 : kEW % 4 == 0 ? 4 : kEW % 2 == 0 ? 2 : 1;
 #pragma unroll
@@ -209,7 +209,7 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_replay_kernel(GdnArgs a) {
             for (int u = 0; u < kGB; ++u) {
                 const int e = (e0 + u) * kW + wave;
 #pragma unroll
-                for (int i = 0; i < kE; ++i) s_al[e][el * kE + i] = expf(gb[u][i]);
+                for (int i = 0; i < kE; ++i) s_al[e][el * kE + i] = __expf(gb[u][i]);
                 if (e >= count && e < kmax)  // this call's tokens: append g
                     store_raw<float, kE>(a.ring_g + uniform64((rh + ring_slot(start, e, cap)) * DK) +
                                              el * kE, gb[u]);
@@ -266,6 +266,7 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_replay_kernel(GdnArgs a) {
     if constexpr (kW > 1) __syncthreads();  // every wave's entries are staged
     else wave_sync();
     const bool sweeps = qidx(0) < nq;  // uniform: a wave left without a query skips the sweep
+    const float ae = VG ? 0.f : expf(ge);  // GDN: the decay of entry e = lane, one exp per lane
     for (int e = sweeps ? kmax - 1 : -1; e >= 0; --e) {  // uniform trip count
         float kv[kE];
 #pragma unroll
@@ -276,7 +277,7 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_replay_kernel(GdnArgs a) {
 #pragma unroll
             for (int i = 0; i < kE; ++i) al[i] = s_al[e][el * kE + i];
         } else {
-            const float as = expf(readlane(ge, e));
+            const float as = readlane(ae, e);
 #pragma unroll
             for (int i = 0; i < kE; ++i) al[i] = as;
         }
