@@ -88,13 +88,24 @@ struct RcRow {
                 }
             }
         } else {
+            // the row's block scales S = value(code) * s_t, two codes per conversion instruction
+            // (the codes are finite and non-negative: the writer saturates them at 448)
+            float S_blk[N / 16];
+#pragma unroll
+            for (int w = 0; w < kSB; ++w) {
+                const float2 lo = e4m3x2_decode_hw<false>(sbw[w]), hi = e4m3x2_decode_hw<true>(sbw[w]);
+                const float sv[4] = {lo.x, lo.y, hi.x, hi.y};
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (4 * w + i < N / 16) S_blk[4 * w + i] = sv[i] * st;
+            }
 #pragma unroll
             for (int k = 0; k < kU; ++k) {
                 const uint32_t w[4] = {u[k].x, u[k].y, u[k].z, u[k].w};
 #pragma unroll
                 for (int half = 0; half < 2; ++half) {
                     const int blk = 2 * k + half;
-                    const float S = e4m3_decode((sbw[blk / 4] >> (8 * (blk % 4))) & 0xff) * st;
+                    const float S = S_blk[blk];
                     float val[16];  // elements 16 half .. 16 half + 15 of the 32-element unit
 #pragma unroll
                     for (int q = 0; q < 2; ++q) {
