@@ -68,12 +68,12 @@ def pmc_traffic():
 
 def m2_replay_bytes_per_head(P, N, k, esz=2):
     """Algorithmic bytes of one replay launch for one head at committed count k (after append):
-    checkpoint read + the k-1 older ring entries read (x, B, dt) + the token's inputs read and
-    appended (x, B, C, dt) + y written + the count written (lock-step launches take start and
-    count from the host; a launch that reads the pointer entry adds 16 bytes)."""
-    entry_rd = P * esz + N * esz + 4
+    checkpoint read + the k-1 older ring entries read (x, B, dt) + the token's inputs read (x, B,
+    C, dt) + its x, B and dt appended + y written + the count written (lock-step launches take
+    start and count from the host; a launch that reads the pointer entry adds 16 bytes)."""
+    entry = P * esz + N * esz + 4
     token = P * esz + 2 * N * esz + 4
-    return P * N * 4 + (k - 1) * entry_rd + 2 * token + P * 4 + 4
+    return P * N * 4 + (k - 1) * entry + token + entry + P * 4 + 4
 
 
 def m2_flush_bytes_per_head(P, N, L, esz=2):
@@ -88,10 +88,10 @@ def m2_conv_bytes_per_head(P, N, esz=2):
 
 def m2_verify_bytes_per_head(P, N, kc, S, esz=2):
     """One speculative verify launch for one head: checkpoint read once, kc committed entries
-    (x, B, dt), S drafts read and appended (x, B, C, dt), S outputs, pointers."""
-    entry_rd = P * esz + N * esz + 4
+    (x, B, dt), S drafts read (x, B, C, dt) and appended (x, B, dt), S outputs, pointers."""
+    entry = P * esz + N * esz + 4
     token = P * esz + 2 * N * esz + 4
-    return P * N * 4 + kc * entry_rd + 2 * S * token + S * P * 4 + 8
+    return P * N * 4 + kc * entry + S * (token + entry) + S * P * 4 + 8
 
 
 def m2_snapshot_bytes_per_head(P, N, S, esz=2):
@@ -108,19 +108,20 @@ def m2_rc_replay_bytes_per_head(P, N, k, rc, esz=2):
 
 def gdn_replay_bytes_per_head(dv, dk, k, esz=2, gsz=4):
     """GDN replay for one head at count k: state read + k-1 older entries (k, v, beta, g) + this
-    token read and appended (q, k, v, beta, g) + o written + the count written (as for
-    Mamba-2). gsz: bytes of g per entry (4; Kimi Delta Attention: 4 dk)."""
-    entry_rd = dk * esz + dv * esz + 4 + gsz
+    token read (q, k, v, beta, g) and appended (k, v, beta, g) + o written + the count written
+    (as for Mamba-2). gsz: bytes of g per entry (4; Kimi Delta Attention: 4 dk)."""
+    entry = dk * esz + dv * esz + 4 + gsz
     token = 2 * dk * esz + dv * esz + 4 + gsz
-    return dv * dk * 4 + (k - 1) * entry_rd + 2 * token + dv * 4 + 4
+    return dv * dk * 4 + (k - 1) * entry + token + entry + dv * 4 + 4
 
 
 def gdn_verify_bytes_per_head(dv, dk, kc, S, esz=2, gsz=4):
     """GDN (KDA: gsz = 4 dk) speculative verify for one head: state read once, kc committed
-    entries (k, v, beta, g), S drafts read and appended (q, k, v, beta, g), S outputs, pointers."""
-    entry_rd = dk * esz + dv * esz + 4 + gsz
+    entries (k, v, beta, g), S drafts read (q, k, v, beta, g) and appended (k, v, beta, g), S
+    outputs, pointers."""
+    entry = dk * esz + dv * esz + 4 + gsz
     token = 2 * dk * esz + dv * esz + 4 + gsz
-    return dv * dk * 4 + kc * entry_rd + 2 * S * token + S * dv * 4 + 8
+    return dv * dk * 4 + kc * entry + S * (token + entry) + S * dv * 4 + 8
 
 
 def gdn_snapshot_bytes_per_head(dv, dk, S, esz=2, gsz=4):

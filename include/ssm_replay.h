@@ -64,7 +64,7 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 4
+#define SSM_ABI_VERSION 5
 
 typedef int32_t ssm_status;
 enum {
@@ -112,9 +112,11 @@ typedef struct ssm_config {
  * byte t*P*N + ((n/16)*P + p)*16 + n%16, row scales fp32 [t][P]; fp4 codes (two per byte, low
  * nibble = even n) at byte t*P*N/2 + ((n/32)*P + p)*16 + (n%32)/2, block-scale E4M3 codes
  * [t][P][N/16], tile scale fp32 [t].
- * Rings (slot s of cap): Mamba-2 x [b][h][s][P], B and C [b][g][s][N] (input dtype),
- * dt [b][h][s] fp32; GDN q, k [b][h][s][dk], v [b][h][s][dv] (input dtype), beta, g [b][h][s];
- * KDA as GDN with g [b][h][s][dk].
+ * Rings (slot s of cap) hold the inputs the state update consumes: Mamba-2 x [b][h][s][P],
+ * B [b][g][s][N] (input dtype), dt [b][h][s] fp32; GDN k [b][h][s][dk], v [b][h][s][dv] (input
+ * dtype), beta, g [b][h][s]; KDA as GDN with g [b][h][s][dk]. C (GDN: q) enters only its own
+ * token's output and is not buffered: its off_ring entry (Mamba-2 [2], GDN [0]) names an empty
+ * region.
  * Pointers: int32 [b][h][4] = {start slot, committed count, checkpoint slot, 0}. Flags: one int32
  * word of SSM_FLAG_* bits set by device-side checks. Reader counts: int32 [ckpt_slots], the
  * number of sequences reading each checkpoint slot (kept by the library). */
@@ -126,7 +128,7 @@ typedef struct ssm_layout {
     uint64_t off_rc_codes;  /* read-copy codes (0 bytes when readcopy == SSM_RC_NONE) */
     uint64_t off_rc_scale;  /* fp8: row scales fp32; fp4: block-scale codes u8 */
     uint64_t off_rc_tscale; /* fp4: tile scales fp32 */
-    uint64_t off_ring[5];   /* Mamba-2: x, B, C, dt, (unused); GDN: q, k, v, beta, g */
+    uint64_t off_ring[5];   /* Mamba-2: x, B, (empty), dt, (empty); GDN: (empty), k, v, beta, g */
     uint64_t off_ptr;       /* int32 [batch][heads][4] */
     uint64_t off_flags;     /* int32 flag word */
     uint64_t off_refcnt;    /* int32 [ckpt_slots] reader counts */

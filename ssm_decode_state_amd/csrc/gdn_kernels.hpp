@@ -58,7 +58,7 @@ template <int DV, int DK, typename TIN, int RC, int MAXW, int MAXQ, bool COMMIT,
 __global__ __launch_bounds__(64 * (DV >= 64 ? DV / 64 : 1))
 __attribute__((amdgpu_waves_per_eu(2))) void gdn_replay_kernel(GdnArgs a) {
     static_assert(DV >= 64 && DK >= 64, "replay tile: dv, dk >= 64");
-    static_assert(MAXW <= 64, "entries per call");
+    static_assert(MAXW <= 64 && MAXW % 4 == 0, "entries per call");
     constexpr int kW = DV / 64;                   // wavefronts per head
     constexpr int kRows = 64;                     // rows per wave
     constexpr int kNQ = DK / 4;
@@ -231,14 +231,7 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_replay_kernel(GdnArgs a) {
                                             (unsigned)(ring_slot(start, e, cap) * DV) + wave * kRows +
                                             part * kEPC) = vraw[i];
         }
-        // each wave appends the keys (and decays) it staged and the queries it sweeps
-#pragma unroll
-        for (int jj = 0; jj < kQS; ++jj) {
-            const int j = qidx(jj);
-            if (j >= nq || (!kSplit && wave != 0)) continue;
-            const long rs = rh + ring_slot(start, count + j, cap);
-            store_raw<TIN, kE>(static_cast<TIN*>(a.ring_q) + uniform64(rs * DK) + el * kE, qraw[jj]);
-        }
+        // each wave appends the keys (and decays) it staged
 #pragma unroll
         for (int ee = 0; ee < kEW; ++ee) {
             const int e = ee * kW + wave;
@@ -267,30 +260,47 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_replay_kernel(GdnArgs a) {
     else wave_sync();
     const bool sweeps = qidx(0) < nq;  // uniform: a wave left without a query skips the sweep
     const float ae = VG ? 0.f : expf(ge);  // GDN: the decay of entry e = lane, one exp per lane
-    for (int e = sweeps ? kmax - 1 : -1; e >= 0; --e) {  // uniform trip count
-        float kv[kE];
+    // The sweep is a serial chain through r. Entry e - 1's key (and decays) are read from LDS
+    // while entry e is processed, the lane sums stay in vector registers, and coefficient c_e
+    // is kept by lane e (cv) and stored once after the sweep.
+    float cv[kQS];
 #pragma unroll
-        for (int i = 0; i < kE; ++i) kv[i] = to_f32<TIN>(s_k[e][el * kE + i]);
-        const float bt = readlane(be, e);
-        float al[kE];  // the decay of the lane's key elements
+    for (int jj = 0; jj < kQS; ++jj) cv[jj] = 0.f;
+    float kn[kE], an[VG ? kE : 1];
+    auto fetch = [&](int e) {
+#pragma unroll
+        for (int i = 0; i < kE; ++i) kn[i] = to_f32<TIN>(s_k[e][el * kE + i]);
         if constexpr (VG) {
 #pragma unroll
-            for (int i = 0; i < kE; ++i) al[i] = s_al[e][el * kE + i];
+            for (int i = 0; i < kE; ++i) an[i] = s_al[e][el * kE + i];
+        }
+    };
+    fetch(max(kmax - 1, 0));
+    for (int e = sweeps ? kmax - 1 : -1; e >= 0; --e) {  // uniform trip count
+        float kv[kE], al[kE];  // entry e's key and the decay of the lane's key elements
+#pragma unroll
+        for (int i = 0; i < kE; ++i) kv[i] = kn[i];
+        if constexpr (VG) {
+#pragma unroll
+            for (int i = 0; i < kE; ++i) al[i] = an[i];
         } else {
             const float as = readlane(ae, e);
 #pragma unroll
             for (int i = 0; i < kE; ++i) al[i] = as;
         }
+        fetch(max(e - 1, 0));
+        const float bt = readlane(be, e);
+        const bool mine = lane == e;
         if constexpr (kQS == 1) {
             const int j = qidx(0);
             if (j < nq && e <= count + j) {  // (entries after query j's own token: uniform skip)
                 float d = 0.f;
 #pragma unroll
                 for (int i = 0; i < kE; ++i) d += kv[i] * r[0][i];
-                const float c = bt * wave_sum(d);
+                const float c = bt * group_sum<64>(d);
 #pragma unroll
                 for (int i = 0; i < kE; ++i) r[0][i] = al[i] * (r[0][i] - c * kv[i]);
-                if (lane == 0) s_c[sw][e][j] = c;
+                cv[0] = mine ? c : cv[0];
             }
         } else {
             // several queries: their reductions are independent chains, so the loop body has no
@@ -304,7 +314,7 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_replay_kernel(GdnArgs a) {
                 for (int i = 0; i < kE; ++i) d[jj] += kv[i] * r[jj][i];
             }
 #pragma unroll
-            for (int jj = 0; jj < kQS; ++jj) d[jj] = bt * wave_sum(d[jj]);
+            for (int jj = 0; jj < kQS; ++jj) d[jj] = bt * group_sum<64>(d[jj]);
 #pragma unroll
             for (int jj = 0; jj < kQS; ++jj) {
                 const int j = qidx(jj);
@@ -312,9 +322,15 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_replay_kernel(GdnArgs a) {
 #pragma unroll
                 for (int i = 0; i < kE; ++i)
                     r[jj][i] = sees ? al[i] * (r[jj][i] - d[jj] * kv[i]) : r[jj][i];
-                if (lane == 0 && j < MAXQ) s_c[sw][e][j] = d[jj];
+                cv[jj] = mine ? d[jj] : cv[jj];
             }
         }
+    }
+    // coefficients c_e of the entries each query sees (lanes e < kmax; the rest are never read)
+#pragma unroll
+    for (int jj = 0; jj < kQS; ++jj) {
+        const int j = qidx(jj);
+        if (j < MAXQ && lane < MAXW) s_c[sw][lane][j] = cv[jj];
     }
     if constexpr (RC == 0 && kEarlyQ < kNQ) {
 #pragma unroll
@@ -338,12 +354,21 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_replay_kernel(GdnArgs a) {
     float acc[MAXQ];
 #pragma unroll
     for (int j = 0; j < MAXQ; ++j) acc[j] = 0.f;
-    for (int e = 0; e < kmax; ++e) {
-        const float ve = to_f32<TIN>(sv[e * kRows + lane]);
+    // value terms four entries at a time, so that the LDS reads of a group go out together. Every
+    // slot e < MAXW of s_v holds a staged row (entries past the call's last token repeat it) and
+    // s_c holds 0 for the entries a query does not see; the select keeps a non-finite v of an
+    // unseen entry out of the sum.
+    for (int e0 = 0; e0 < kmax; e0 += 4) {  // uniform; MAXW is a multiple of 4
+        float ve[4];
 #pragma unroll
-        for (int j = 0; j < MAXQ; ++j) {
-            if (j >= nq) break;
-            if (e <= count + j) acc[j] += s_c[sw][e][j] * ve;
+        for (int u = 0; u < 4; ++u) ve[u] = to_f32<TIN>(sv[(e0 + u) * kRows + lane]);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int e = e0 + u;
+#pragma unroll
+            for (int j = 0; j < MAXQ; ++j) {
+                acc[j] = fmaf(s_c[sw][e][j], e <= count + j ? ve[u] : 0.f, acc[j]);
+            }
         }
     }
     float dot[MAXQ];

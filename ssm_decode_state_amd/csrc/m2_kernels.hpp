@@ -41,7 +41,8 @@ constexpr int kMaxEntries = 64;  // ring entries a wave can address (cap <= 63)
 // with s_{e,j} = A * sum_{m = e+1 .. kq_j - 1} dt_m and s0_j = A * sum_{m < kq_j} dt_m
 // (news, para 2: outputs from checkpoint + buffered inputs, no state write).
 // Entries e < count come from the ring; entries count .. count+ntok-1 are this call's tokens,
-// read from the caller's input and appended to the ring (news, para 3).
+// read from the caller's input; their x, B and dt rows are appended to the ring (news, para 3).
+// C enters only its own token's output, so the ring does not keep it.
 // COMMIT: decode (count += ntok at the end); otherwise the tokens stay pending drafts.
 //
 // Memory order matters here: the vector-memory counter retires in order, so every small load
@@ -91,7 +92,6 @@ __global__ __launch_bounds__(256) void m2_replay_kernel(M2Args a) {
     const TIN* inC = static_cast<const TIN*>(a.in_C);
     TIN* rx = static_cast<TIN*>(a.ring_x);
     TIN* rB = static_cast<TIN*>(a.ring_B);
-    TIN* rC = static_cast<TIN*>(a.ring_C);
 
     // ---- 1. small loads (branch-free: invalid entries read a valid row and are masked later) -
     const long tok0 = (long)b * nq;  // this sequence's first token in the call's inputs
@@ -175,23 +175,13 @@ __global__ __launch_bounds__(256) void m2_replay_kernel(M2Args a) {
                 xraw[i];
     }
     if (lane >= count && lane < kmax) a.ring_dt[head * cap + ring_slot(start, lane, cap)] = dte;
-    if (h % hpg == 0) {  // the group's first head writes the shared B and C entries
+    if (h % hpg == 0) {  // the group's first head writes the shared B entries
 #pragma unroll
         for (int i = 0; i < kBL; ++i) {
             const int e = (lane + 64 * i) / kBCE, part = lane % kBCE;
             if (e >= count && e < kmax)
                 *reinterpret_cast<u32x4_t*>(rB + ((long)bg * cap + ring_slot(start, e, cap)) * N + part * kEPC) =
                     braw[i];
-        }
-#pragma unroll
-        for (int j = 0; j < MAXQ; ++j) {
-            if (j >= nq) break;
-            const int slot = ring_slot(start, count + j, cap);
-#pragma unroll
-            for (int i = 0; i < kCE; ++i) {
-                const int n = lane + 64 * i;
-                if (n < N) rC[((long)bg * cap + slot) * N + n] = craw[j][i];
-            }
         }
     }
     wave_sync();
@@ -239,15 +229,25 @@ __global__ __launch_bounds__(256) void m2_replay_kernel(M2Args a) {
 #pragma unroll
     for (int j = 0; j < MAXQ; ++j) out[j] = 0.f;
     const TIN* sx = reinterpret_cast<const TIN*>(&s_x[wave][0]);
-    for (int e = 0; e < kmax; ++e) {
-        const float xe = to_f32<TIN>(sx[e * P + row]);
+    // four entries at a time, so that the LDS reads of a group go out together; the weights of
+    // entries past kmax are not written, and the select keeps them out of the sum
+    for (int e0 = 0; e0 < kmax; e0 += 4) {  // uniform; MAXE is a multiple of 16
+        float xe[4];
 #pragma unroll
-        for (int j = 0; j < MAXQ; ++j) {
-            if (j >= nq) break;
-            out[j] += s_w[wave][e][j] * xe;
-            if (e == count + j) out[j] += D * xe;
+        for (int u = 0; u < 4; ++u) xe[u] = to_f32<TIN>(sx[(e0 + u) * P + row]);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int e = e0 + u;
+#pragma unroll
+            for (int j = 0; j < MAXQ; ++j) {
+                const float t = s_w[wave][e][j] * xe[u];
+                out[j] += e <= count + j ? t : 0.f;
+            }
         }
     }
+#pragma unroll
+    for (int j = 0; j < MAXQ; ++j)  // skip term of the query's own token
+        out[j] += D * to_f32<TIN>(sx[min(count + j, MAXE - 1) * P + row]);
 
     if constexpr (RC == 0 && kEarlyQ < G::kQPL) {
 #pragma unroll

@@ -74,11 +74,11 @@ void compute_layout(const ssm_config* c, ssm_layout* L) {
     if (c->kind == SSM_MAMBA2) {
         L->off_ring[0] = take(B * H * cap * P * esz);  // x
         L->off_ring[1] = take(B * G * cap * N * esz);  // B
-        L->off_ring[2] = take(B * G * cap * N * esz);  // C
+        L->off_ring[2] = take(0);  // C is not buffered: it enters only its own token's output
         L->off_ring[3] = take(B * H * cap * 4);        // dt
         L->off_ring[4] = take(0);
     } else {
-        L->off_ring[0] = take(B * H * cap * N * esz);  // q  (dk)
+        L->off_ring[0] = take(0);  // q is not buffered: it enters only its own token's output
         L->off_ring[1] = take(B * H * cap * N * esz);  // k  (dk)
         L->off_ring[2] = take(B * H * cap * P * esz);  // v  (dv)
         L->off_ring[3] = take(B * H * cap * 4);        // beta
@@ -127,7 +127,6 @@ ssm::M2Args m2_args(const ssm_state* st) {
     a.rc_tscale = at<float>(st, L.off_rc_tscale);
     a.ring_x = at<void>(st, L.off_ring[0]);
     a.ring_B = at<void>(st, L.off_ring[1]);
-    a.ring_C = at<void>(st, L.off_ring[2]);
     a.ring_dt = at<float>(st, L.off_ring[3]);
     a.ptr = at<int>(st, L.off_ptr);
     a.refcnt = at<int>(st, L.off_refcnt);
@@ -151,7 +150,6 @@ ssm::GdnArgs gdn_args(const ssm_state* st) {
     a.rc_codes = at<uint8_t>(st, L.off_rc_codes);
     a.rc_scale = at<void>(st, L.off_rc_scale);
     a.rc_tscale = at<float>(st, L.off_rc_tscale);
-    a.ring_q = at<void>(st, L.off_ring[0]);
     a.ring_k = at<void>(st, L.off_ring[1]);
     a.ring_v = at<void>(st, L.off_ring[2]);
     a.ring_beta = at<float>(st, L.off_ring[3]);
@@ -511,10 +509,8 @@ ssm_status ssm_fork(ssm_state* st, const int32_t* src, const int32_t* dst, int32
     if (c.kind == SSM_MAMBA2) {
         add(L.off_ring[0], H * cap * P * esz);
         add(L.off_ring[1], G * cap * N * esz);
-        add(L.off_ring[2], G * cap * N * esz);
         add(L.off_ring[3], H * cap * 4);
     } else {
-        add(L.off_ring[0], H * cap * N * esz);
         add(L.off_ring[1], H * cap * N * esz);
         add(L.off_ring[2], H * cap * P * esz);
         add(L.off_ring[3], H * cap * 4);

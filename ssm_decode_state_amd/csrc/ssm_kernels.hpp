@@ -47,9 +47,8 @@ struct M2Args {
     uint8_t* rc_codes;  // read-copy codes
     void* rc_scale;     // fp8: fp32 row scales; fp4: E4M3 block-scale codes
     float* rc_tscale;   // fp4: fp32 tile scales
-    void* ring_x;
+    void* ring_x;       // buffered inputs: x, B and dt (C enters only its own token's output)
     void* ring_B;
-    void* ring_C;
     float* ring_dt;
     int* ptr;           // int32 [batch][heads][4] = {start, count, checkpoint slot, 0}
     const int* refcnt;  // shared checkpoints: readers of each slot [2 batch]
@@ -85,8 +84,7 @@ struct GdnArgs {
     uint8_t* rc_codes;  // read-copy codes (null without a read copy)
     void* rc_scale;     // fp8: fp32 row scales; fp4: E4M3 block-scale codes
     float* rc_tscale;   // fp4: fp32 tile scales
-    void* ring_q;
-    void* ring_k;
+    void* ring_k;       // buffered inputs: k, v, beta and g (q enters only its own token's output)
     void* ring_v;
     float* ring_beta;
     float* ring_g;

@@ -54,10 +54,10 @@ static void check_layout(const ssm_config& c, const ssm_layout& L) {
     if (c.kind == SSM_MAMBA2) {
         r[n++] = {L.off_ring[0], B * H * cap * P * esz};
         r[n++] = {L.off_ring[1], B * G * cap * N * esz};
-        r[n++] = {L.off_ring[2], B * G * cap * N * esz};
+        r[n++] = {L.off_ring[2], 0};  // C is not buffered
         r[n++] = {L.off_ring[3], B * H * cap * 4};
     } else {
-        r[n++] = {L.off_ring[0], B * H * cap * N * esz};
+        r[n++] = {L.off_ring[0], 0};  // q is not buffered
         r[n++] = {L.off_ring[1], B * H * cap * N * esz};
         r[n++] = {L.off_ring[2], B * H * cap * P * esz};
         r[n++] = {L.off_ring[3], B * H * cap * 4};

@@ -37,7 +37,6 @@ static void check_m2(const ssm::M2Args& a, const char* fn) {
     in_state(a.ckpt, S * H * P * N * 4, fn, "checkpoint");
     in_state(a.ring_x, B * H * cap * P * esz, fn, "x ring");
     in_state(a.ring_B, B * G * cap * N * esz, fn, "B ring");
-    in_state(a.ring_C, B * G * cap * N * esz, fn, "C ring");
     in_state(a.ring_dt, B * H * cap * 4, fn, "dt ring");
     in_state(a.ptr, B * H * 16, fn, "pointers");
     if (a.share) in_state(a.refcnt, S * 4, fn, "reader counts");
@@ -57,7 +56,6 @@ static void check_gdn(const ssm::GdnArgs& a, const char* fn) {
     const uint64_t S = g_world.slots, B = a.batch, H = a.heads;
     const uint64_t dv = g_world.P, dk = g_world.N, cap = a.cap, esz = g_world.esz;
     in_state(a.ckpt, S * H * dv * dk * 4, fn, "checkpoint");
-    in_state(a.ring_q, B * H * cap * dk * esz, fn, "q ring");
     in_state(a.ring_k, B * H * cap * dk * esz, fn, "k ring");
     in_state(a.ring_v, B * H * cap * dv * esz, fn, "v ring");
     in_state(a.ring_beta, B * H * cap * 4, fn, "beta ring");

@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert bd.ssm_abi_version() == 4
+    assert bd.ssm_abi_version() == 5
     for s in range(-7, 1):
         assert bd.ssm_status_string(s) not in ("", "unknown status")
     assert bd.ssm_status_string(-99) == "unknown status"
@@ -59,6 +59,11 @@ def test_layout_serving_shape():
             lay.off_ring[3], lay.off_ptr]
     assert all(o % 256 == 0 for o in offs)
     assert offs == sorted(offs)
+    # the ring keeps x, B and dt; C enters only its own token's output and has no ring
+    assert lay.off_ring[1] - lay.off_ring[0] == 256 * 128 * 16 * 64 * 2
+    assert lay.off_ring[2] - lay.off_ring[1] == 256 * 128 * 16 * 128 * 2
+    assert lay.off_ring[3] == lay.off_ring[2]
+    assert lay.off_ptr - lay.off_ring[3] == 256 * 128 * 16 * 4
     assert lay.off_flags >= lay.off_ptr + 256 * 128 * 16 and lay.off_flags % 256 == 0
     assert lay.ckpt_slots == 256 and lay.off_refcnt >= lay.off_flags + 4
     assert lay.total_bytes >= lay.off_refcnt + 256 * 4
@@ -94,6 +99,10 @@ def test_layout_kda_gate_ring():
     # KDA keeps dk log-decays per entry: the g ring is dk times the GDN one
     assert kda.off_ptr - kda.off_ring[4] == 256 * 32 * 16 * 128 * 4
     assert gdn.off_ptr - gdn.off_ring[4] == 256 * 32 * 16 * 4
+    # k, v, beta and g are buffered; q enters only its own token's output and has no ring
+    for lay in (kda, gdn):
+        assert lay.off_ring[0] == lay.off_ring[1]
+        assert lay.off_ring[2] - lay.off_ring[1] == 256 * 32 * 16 * 128 * 2
 
 
 def test_layout_read_copies():

@@ -257,9 +257,9 @@ def _seq_regions(st):
               (L.off_rc_tscale, H * 4)]
     if c.kind == bd.SSM_MAMBA2:
         r += [(L.off_ring[0], H * cap * P * e), (L.off_ring[1], G * cap * N * e),
-              (L.off_ring[2], G * cap * N * e), (L.off_ring[3], H * cap * 4)]
+              (L.off_ring[3], H * cap * 4)]
     else:
-        r += [(L.off_ring[0], H * cap * N * e), (L.off_ring[1], H * cap * N * e),
+        r += [(L.off_ring[1], H * cap * N * e),
               (L.off_ring[2], H * cap * P * e), (L.off_ring[3], H * cap * 4),
               (L.off_ring[4], H * cap * (N if c.kind == bd.SSM_KDA else 1) * 4)]
     r.append((L.off_ptr, H * 16))

@@ -29,7 +29,7 @@ def make_state(shape, seed, h0_std):
 
 
 def regions(st):
-    """Raw byte regions of a state: ckpt, ring x/B/C/dt, pointers (device tensors)."""
+    """Raw byte regions of a state: ckpt, ring x/B/dt, pointers (device tensors)."""
     c, L = st.cfg, st.layout
     esz = 2 if c.in_dtype == bd.SSM_IN_BF16 else 4
     cap = L.ring_cap
@@ -38,7 +38,6 @@ def regions(st):
         "ckpt": st.region(L.off_ckpt, B * H * P * N * 4),
         "x": st.region(L.off_ring[0], B * H * cap * P * esz).view(B, H, cap, P * esz),
         "B": st.region(L.off_ring[1], B * G * cap * N * esz).view(B, G, cap, N * esz),
-        "C": st.region(L.off_ring[2], B * G * cap * N * esz).view(B, G, cap, N * esz),
         "dt": st.region(L.off_ring[3], B * H * cap * 4).view(B, H, cap, 4),
         "ptr": st.region(L.off_ptr, B * H * 16).view(torch.int32).view(B, H, 4),
     }
@@ -52,14 +51,14 @@ def committed_ring(st, b_list=None):
     hpg = c.heads // c.groups
     cap = st.layout.ring_cap
     out = {}
-    xs, Bs, Cs, ds = r["x"].cpu(), r["B"].cpu(), r["C"].cpu(), r["dt"].cpu()
+    xs, Bs, ds = r["x"].cpu(), r["B"].cpu(), r["dt"].cpu()
     for b in (b_list if b_list is not None else range(c.batch)):
         for h in range(c.heads):
             start, count = int(ptr[b, h, 0]), int(ptr[b, h, 1])
             for e in range(count):
                 s = (start + e) % cap
                 out[(b, h, e)] = (bytes(xs[b, h, s].numpy()), bytes(Bs[b, h // hpg, s].numpy()),
-                                  bytes(Cs[b, h // hpg, s].numpy()), bytes(ds[b, h, s].numpy()))
+                                  bytes(ds[b, h, s].numpy()))
     return out
 
 
