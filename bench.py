@@ -515,10 +515,10 @@ def seq_state_bytes(cfg, lay):
             n += H * P * N + H * P * 4
         elif cfg.readcopy == 2:
             n += H * P * N // 2 + H * P * (N // 16) + H * 4
-    if cfg.kind == 0:
-        n += H * cap * P * e + 2 * G * cap * N * e + H * cap * 4
-    else:
-        n += 2 * H * cap * N * e + H * cap * P * e + H * cap * 4
+    if cfg.kind == 0:  # rings x, B, dt
+        n += H * cap * P * e + G * cap * N * e + H * cap * 4
+    else:  # rings k, v, beta, g
+        n += H * cap * N * e + H * cap * P * e + H * cap * 4
         n += H * cap * (N if cfg.kind == 2 else 1) * 4
     return n
 

@@ -20,24 +20,6 @@
 
 namespace ssm {
 
-namespace {
-
-// Sum over all 64 lanes, the same value in every lane. Four DPP steps sum each row of 16 lanes
-// (lane i^1, lane i^2, the mirror within 8, the mirror within 16), then the four row sums are
-// read as scalars. No LDS round trips: the sweep below is a serial chain of these sums.
-template <int CTRL> __device__ __forceinline__ float dpp_add(float v) {
-    return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
-}
-__device__ __forceinline__ float wave_sum(float v) {
-    v = dpp_add<0xB1>(v);   // quad_perm [1,0,3,2]
-    v = dpp_add<0x4E>(v);   // quad_perm [2,3,0,1]
-    v = dpp_add<0x141>(v);  // row_half_mirror
-    v = dpp_add<0x140>(v);  // row_mirror
-    return (readlane(v, 0) + readlane(v, 16)) + (readlane(v, 32) + readlane(v, 48));
-}
-
-}  // namespace
-
 constexpr int kGdnMaxWin = 32;  // most entries a replay call can see
 
 // ---------------------------------------------------------------------------------------------
