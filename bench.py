@@ -10,8 +10,9 @@ replay path: append to the ring, replay output from the checkpoint, and (every L
 flush that folds the window into the checkpoint. After W warm-up steps, the K steps run launched
 back to back from Python behind a GPU pre-roll (about 2 ms of unrelated streaming reads, so the
 host's launches get ahead of the GPU), synchronized before and after; `value` is B * K over the
-GPU time from the first step's start to the last step's end, bracketed by HIP events, and HIP
-events between runs of one kernel (a window's replays, the fold) give the per-kernel figures. The
+GPU time from the first step's start to the last step's end, bracketed by HIP events, for the
+median of three such passes in a row, and HIP events between runs of one kernel (a window's
+replays, the fold) give the per-kernel figures over all three passes. The
 same K steps then run once more with an event pair around each launch (per-count figures) and
 as one HIP graph (reported beside the headline). The window-amortized step ((L - 1) replays +
 the fused fold) / L is reported too, so a K that is not a multiple of L neither flatters nor
@@ -39,6 +40,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, 8 TB/s
+REPS = 3  # timed passes of the K headline steps; the median is reported
 
 
 # Sources the one-token replay kernel is compiled from; the counter profile records their hash.
@@ -1013,22 +1015,28 @@ def main():
     #      then the fused fold) with events only at the run boundaries -----------------------
     for t in range(W):
         bd.ssm_replay_decode(st, inputs[t], y)
-    ks = [((W + t) % L) + 1 for t in range(K)]  # committed count after the append
     # the eager figure: GPU time from the first step's start to the last step's end (the pre-roll
-    # keeps host launch latency out of it)
-    t_eager, step_ms = timed_calls(K, lambda t: bd.ssm_replay_decode(st, inputs[W + t], y),
-                                   kind=lambda t: ks[t] == L)
-
+    # keeps host launch latency out of it), for REPS passes of the K steps in a row (the state
+    # moves on; each pass reuses the K inputs): the headline is the median pass, the per-kernel
+    # figures sum all passes
     heads = Bn * H
     rep_bytes = rep_ms = 0.0
     flush_steps = []
-    for k, ms in zip(ks, step_ms):
-        if k == L:
-            flush_steps.append(ms)
-            continue
-        rep_bytes += heads * m2_replay_bytes_per_head(P, N, k)
-        rep_ms += ms
-    n_rep = K - len(flush_steps)
+    passes = []
+    n_rep = 0
+    for r in range(REPS):
+        ks = [((W + r * K + t) % L) + 1 for t in range(K)]  # committed count after the append
+        t_pass, step_ms = timed_calls(K, lambda t: bd.ssm_replay_decode(st, inputs[W + t], y),
+                                      kind=lambda t, ks=ks: ks[t] == L)
+        passes.append(t_pass)
+        for k, ms in zip(ks, step_ms):
+            if k == L:
+                flush_steps.append(ms)
+                continue
+            rep_bytes += heads * m2_replay_bytes_per_head(P, N, k)
+            rep_ms += ms
+            n_rep += 1
+    t_eager = sorted(passes)[REPS // 2]
     rep_avg_ms = rep_ms / max(n_rep, 1)
     rep_gbs = rep_bytes / (rep_ms * 1e-3) / 1e9 if rep_ms > 0 else float("nan")
     # the L-th step of each window is one fused pass: fold the window and emit the output from
@@ -1044,7 +1052,7 @@ def main():
     _, each_ms = timed_calls(K, lambda t: bd.ssm_replay_decode(st, inputs[W + t], y))
     per_k = {}
     for t, ms in enumerate(each_ms):
-        per_k.setdefault(((W + K + t) % L) + 1, []).append(ms)
+        per_k.setdefault(((W + REPS * K + t) % L) + 1, []).append(ms)
 
     # ---- the headline: the back-to-back pass above -- HIP events bracket exactly the K steps
     #      (GPU time from the first step's start to the last step's end), behind a pre-roll that
@@ -1052,7 +1060,8 @@ def main():
     #      beside it (from the state the passes left; restored after the graph's warm-up replay).
     value, ms_step = Bn * K / t_eager, t_eager / K * 1e3
     timing = ("the K steps launched back to back from Python behind a GPU pre-roll; HIP events "
-              "bracket exactly the K steps, synchronized before and after")
+              "bracket exactly the K steps, synchronized before and after; the median of %d such "
+              "passes in a row" % REPS)
     graph = (None if args.no_graph else
              graph_steps(lambda i: bd.ssm_replay_decode(st, inputs[W + i], y), K, st.mem))
     if graph is not None:
@@ -1067,6 +1076,7 @@ def main():
                    "groups": G, "head_dim": P, "state_dim": N, "window": L,
                    "inputs": "bf16 x/B/C, fp32 dt", "checkpoint": "fp32"},
         "timing": timing,
+        "passes_tokens_per_s": [Bn * K / t for t in passes],
         "roofline": {"bound": "hbm", "achieved": rep_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": rep_gbs / HBM_PEAK_GBS, "traffic": pmc_traffic(),
                      "algorithmic_bytes_per_launch": rep_bytes / max(n_rep, 1),
@@ -1090,7 +1100,7 @@ def main():
         # fused fold, whatever fraction of folds the K timed steps happened to hold
         amort_us = ((L - 1) * rep_avg_ms + fold_ms) / L * 1e3
         out["window_amortized"] = {"step_us": amort_us, "tokens_per_s": Bn / (amort_us * 1e-6),
-                                   "folds_in_timed_steps": len(flush_steps),
+                                   "folds_in_timed_passes": len(flush_steps),
                                    "note": "((L-1) * replay + fused fold) / L from the per-launch "
                                            "event times"}
 
@@ -1101,15 +1111,21 @@ def main():
         for t in range(W):
             bd.ssm_conventional_step(cfg, tiles, inputs[t], Ad, Dd, y)
         torch.cuda.synchronize()
-        t_conv, cms = timed_calls(K, lambda t: bd.ssm_conventional_step(cfg, tiles, inputs[W + t],
-                                                                         Ad, Dd, y),
-                                  kind=lambda t: 0)
-        conv_ms = sum(cms) / K
+        conv_passes, cms = [], []
+        for r in range(REPS):
+            t_c, c_ms = timed_calls(K, lambda t: bd.ssm_conventional_step(cfg, tiles, inputs[W + t],
+                                                                          Ad, Dd, y),
+                                    kind=lambda t: 0)
+            conv_passes.append(t_c)
+            cms += c_ms
+        t_conv = sorted(conv_passes)[REPS // 2]
+        conv_ms = sum(cms) / len(cms)
         conv_gbs = heads * m2_conv_bytes_per_head(P, N) / (conv_ms * 1e-3) / 1e9
         out["conventional"] = {"value": Bn * K / t_conv, "unit": "tokens/s/layer",
                                "ms_per_step": t_conv / K * 1e3, "avg_launch_us": conv_ms * 1e3,
                                "achieved_gbs": conv_gbs, "frac": conv_gbs / HBM_PEAK_GBS,
-                               "timing": "the K steps back to back, as the headline"}
+                               "timing": "the K steps back to back, median of %d passes, as the "
+                                         "headline" % REPS}
         gconv = (None if args.no_graph else
                  graph_steps(lambda i: bd.ssm_conventional_step(cfg, tiles, inputs[W + i], Ad, Dd, y),
                              K, tiles))
