@@ -304,11 +304,12 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_replay_kernel(GdnArgs a) {
 #pragma unroll
                 for (int i = 0; i < kE; ++i)
                     r[jj][i] = sees ? al[i] * (r[jj][i] - d[jj] * kv[i]) : r[jj][i];
-                cv[jj] = mine ? d[jj] : cv[jj];
+                cv[jj] = mine && sees ? d[jj] : cv[jj];  // 0 for an entry the query does not see
             }
         }
     }
-    // coefficients c_e of the entries each query sees (lanes e < kmax; the rest are never read)
+    // coefficients c_e of the entries each query sees (0 for the others, so a later draft's
+    // inputs, finite or not, never reach an earlier draft's output)
 #pragma unroll
     for (int jj = 0; jj < kQS; ++jj) {
         const int j = qidx(jj);
@@ -338,8 +339,8 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_replay_kernel(GdnArgs a) {
     for (int j = 0; j < MAXQ; ++j) acc[j] = 0.f;
     // value terms four entries at a time, so that the LDS reads of a group go out together. Every
     // slot e < MAXW of s_v holds a staged row (entries past the call's last token repeat it) and
-    // s_c holds 0 for the entries a query does not see; the select keeps a non-finite v of an
-    // unseen entry out of the sum.
+    // s_c holds 0 for the entries a query does not see; the select keeps a non-finite v of such
+    // an entry out of the sum.
     for (int e0 = 0; e0 < kmax; e0 += 4) {  // uniform; MAXW is a multiple of 4
         float ve[4];
 #pragma unroll

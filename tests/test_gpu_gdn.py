@@ -235,3 +235,34 @@ def test_gdn_snapshot_baseline_matches_oracle(kind, case):
     assert_close(go, oo, (-1,), "snapshot-baseline draft outputs")
     got = np.stack([nat[b, hh].cpu().double().numpy() for (b, hh) in pairs])
     assert_close(got, ST, (-2, -1), "state after the snapshot rounds")
+
+
+@pytest.mark.parametrize("kind", [synth.GDN, synth.KDA])
+@pytest.mark.parametrize("rc", [0, 2])
+def test_gdn_draft_outputs_ignore_later_drafts(kind, rc):
+    """As for Mamba-2: with NaN in every input of the last draft, the earlier drafts' outputs
+    (GDN and KDA verify, fp32 state or fp4 read copy) are bit-identical to those of a run with
+    finite inputs there. An entry a query does not see contributes no coefficient and no value
+    row to that query."""
+    shape = synth.Shape(kind, 2, 3, 3, 128, 128, 16, 4, in_bf16=True)
+    S = shape.max_draft
+    outs = []
+    for poison in (False, True):
+        S0 = synth.initial_state(shape, 61, 0.3)
+        cfg = bd.make_config(bd.SSM_GDN if kind == synth.GDN else bd.SSM_KDA, 2, 3, 3, 128, 128,
+                             16, S, bd.SSM_IN_BF16, rc, 0.75)
+        st = bd.State(cfg, S0.to(DEV), None, None)
+        o1 = torch.empty(2, 3, 128, device=DEV)
+        for t in range(5):
+            bd.ssm_replay_decode(st, to_dev(synth.token_inputs(shape, 61, "decode", t), DEV), o1)
+        d = synth.token_inputs(shape, 61, "draft", 0, ntok=S)
+        if poison:
+            for key in ("q", "k", "v", "beta", "g"):
+                d[key][:, S - 1] = float("nan")
+        o = torch.empty(2, S, 3, 128, device=DEV)
+        bd.ssm_spec_append(st, S, to_dev(d, DEV), o)
+        torch.cuda.synchronize()
+        outs.append(o.cpu())
+    assert torch.isfinite(outs[0]).all()
+    assert torch.equal(outs[0][:, :S - 1], outs[1][:, :S - 1])
+    assert torch.isnan(outs[1][:, S - 1]).all()

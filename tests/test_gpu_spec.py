@@ -266,3 +266,33 @@ def test_spec_state_equals_sequential_decode_bitwise():
         ring_seq = committed_ring(sb)
         ring_spec = {(0, h, e): v for (bb, h, e), v in committed_ring(st, [b]).items()}
         assert ring_seq == ring_spec, b
+
+
+@pytest.mark.parametrize("rc", [0, 2])
+def test_draft_outputs_ignore_later_drafts(rc):
+    """Draft j's output depends on the committed entries and drafts 1..j only (news, para 3:
+    drafts are appended to the buffer and verified in one pass). With NaN in every input of the
+    last draft, the earlier drafts' outputs are bit-identical to those of a run with finite
+    inputs there: the entries a query does not see are selected away, not multiplied by zero."""
+    shape = synth.Shape(synth.MAMBA2, 4, 8, 4, 64, 128, 16, 4, in_bf16=True)
+    S = shape.max_draft
+    outs = []
+    for poison in (False, True):
+        A, D = synth.head_constants(shape, 41)
+        h0 = synth.initial_state(shape, 41, 0.3)
+        cfg = bd.make_config(bd.SSM_MAMBA2, 4, 8, 4, 64, 128, 16, S, bd.SSM_IN_BF16, rc)
+        st = bd.State(cfg, h0.to(DEV), A.to(DEV), D.to(DEV))
+        y1 = torch.empty(4, 8, 64, device=DEV)
+        for t in range(5):
+            bd.ssm_replay_decode(st, to_dev(synth.token_inputs(shape, 41, "decode", t), DEV), y1)
+        d = synth.token_inputs(shape, 41, "draft", 0, ntok=S)
+        if poison:
+            for key in ("x", "B", "C", "dt"):
+                d[key][:, S - 1] = float("nan")
+        y = torch.empty(4, S, 8, 64, device=DEV)
+        bd.ssm_spec_append(st, S, to_dev(d, DEV), y)
+        torch.cuda.synchronize()
+        outs.append(y.cpu())
+    assert torch.isfinite(outs[0]).all()
+    assert torch.equal(outs[0][:, :S - 1], outs[1][:, :S - 1])
+    assert torch.isnan(outs[1][:, S - 1]).all()
