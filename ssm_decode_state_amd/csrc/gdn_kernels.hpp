@@ -97,6 +97,11 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_replay_kernel(GdnArgs a) {
                              : (unsigned)min(max(e - count, 0), nq - 1) * (unsigned)(H * w);
         return (r ? ring + uniform64(rh * w) : in + uniform64(t0 * w)) + o;
     };
+    // appends and outputs go through write-through stores (the appends also streaming beside a
+    // read copy), each through a resource over this head's ring rows or one output row
+    constexpr int kPol = RC == 0 ? kStoreWT : kStoreWTNT;
+    const PolicyStore kring(static_cast<TIN*>(a.ring_k) + uniform64(rh * DK), (uint32_t)(cap * DK * sizeof(TIN)));
+    const PolicyStore gring(a.ring_g + uniform64(rh * (VG ? DK : 1)), (uint32_t)(cap * (VG ? DK : 1) * 4));
     const TIN* rk = static_cast<const TIN*>(a.ring_k);
     const TIN* rv = static_cast<const TIN*>(a.ring_v);
     const TIN* inq = static_cast<const TIN*>(a.in_q);
@@ -193,8 +198,8 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_replay_kernel(GdnArgs a) {
 #pragma unroll
                 for (int i = 0; i < kE; ++i) s_al[e][el * kE + i] = __expf(gb[u][i]);
                 if (e >= count && e < kmax)  // this call's tokens: append g
-                    store_raw<float, kE>(a.ring_g + uniform64((rh + ring_slot(start, e, cap)) * DK) +
-                                             el * kE, gb[u]);
+                    gring.template bytes<kPol, kE * 4>((uint32_t)((ring_slot(start, e, cap) * DK + el * kE) * 4),
+                                                       gb[u]);
             }
         }
     }
@@ -204,24 +209,23 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_replay_kernel(GdnArgs a) {
         if (idx < MAXW * kVC) s_v[wave][idx] = vraw[i];
     }
     {
+        const PolicyStore vring(static_cast<TIN*>(a.ring_v) + uniform64(rh * DV), (uint32_t)(cap * DV * sizeof(TIN)));
 #pragma unroll
         for (int i = 0; i < kVL; ++i) {
             const int idx = lane + 64 * i;
             const int e = idx / kVC, part = idx % kVC;
             if (e >= count && e < kmax && idx < MAXW * kVC)
-                *reinterpret_cast<u32x4_t*>(static_cast<TIN*>(a.ring_v) + uniform64(rh * DV) +
-                                            (unsigned)(ring_slot(start, e, cap) * DV) + wave * kRows +
-                                            part * kEPC) = vraw[i];
+                vring.template bytes<kPol, 16>(
+                    (uint32_t)((ring_slot(start, e, cap) * DV + wave * kRows + part * kEPC) * sizeof(TIN)), &vraw[i]);
         }
         // each wave appends the keys (and decays) it staged
 #pragma unroll
         for (int ee = 0; ee < kEW; ++ee) {
             const int e = ee * kW + wave;
             if (e >= count && e < kmax) {
-                const long rs = rh + ring_slot(start, e, cap);
-                store_raw<TIN, kE>(static_cast<TIN*>(a.ring_k) + uniform64(rs * DK) + el * kE, kraw[ee]);
-                if constexpr (VG && !kLateG)
-                    store_raw<float, kE>(a.ring_g + uniform64(rs * DK) + el * kE, graw[ee]);
+                const uint32_t ro = (uint32_t)(ring_slot(start, e, cap) * DK + el * kE);
+                kring.template bytes<kPol, kE * (int)sizeof(TIN)>(ro * (uint32_t)sizeof(TIN), kraw[ee]);
+                if constexpr (VG && !kLateG) gring.template bytes<kPol, kE * 4>(ro * 4u, graw[ee]);
             }
         }
         if (wave == 0 && lane >= count && lane < kmax) {
@@ -394,7 +398,9 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_replay_kernel(GdnArgs a) {
 #pragma unroll
     for (int j = 0; j < MAXQ; ++j) {
         if (j >= nq) break;
-        a.o[tok(j) * DV + row] = a.scale * (dot[j] + acc[j]);
+        const PolicyStore orow(a.o + uniform64(tok(j) * DV), DV * 4);
+        const float ov = a.scale * (dot[j] + acc[j]);
+        orow.template bytes<kStoreWT, 4>((uint32_t)(row * 4), &ov);
     }
     if constexpr (COMMIT) {
         if constexpr (kW > 1) __builtin_amdgcn_s_barrier();  // every wave has read the pointers

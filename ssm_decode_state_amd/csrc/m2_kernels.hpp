@@ -166,22 +166,27 @@ __global__ __launch_bounds__(256) void m2_replay_kernel(M2Args a) {
         if (kXL * 64 == MAXE * kCPR || idx < MAXE * kCPR) s_x[wave][idx] = xraw[i];
     }
     __builtin_amdgcn_sched_barrier(0);
+    // appends and outputs go through write-through stores (the appends also streaming beside a
+    // read copy)
+    constexpr int kPol = RC == 0 ? kStoreWT : kStoreWTNT;
+    const PolicyStore xring(rx + uniform64((long)head * cap * P), (uint32_t)(cap * P * sizeof(TIN)));
 #pragma unroll
     for (int i = 0; i < kXL; ++i) {
         const int idx = lane + 64 * i;
         const int e = idx / kCPR, part = idx % kCPR;
         if (e >= count && e < kmax)  // this call's token: append its x row
-            *reinterpret_cast<u32x4_t*>(rx + ((long)head * cap + ring_slot(start, e, cap)) * P + part * kEPC) =
-                xraw[i];
+            xring.template bytes<kPol, 16>((uint32_t)((ring_slot(start, e, cap) * P + part * kEPC) * sizeof(TIN)),
+                                           &xraw[i]);
     }
     if (lane >= count && lane < kmax) a.ring_dt[head * cap + ring_slot(start, lane, cap)] = dte;
     if (h % hpg == 0) {  // the group's first head writes the shared B entries
+        const PolicyStore bring(rB + uniform64((long)bg * cap * N), (uint32_t)(cap * N * sizeof(TIN)));
 #pragma unroll
         for (int i = 0; i < kBL; ++i) {
             const int e = (lane + 64 * i) / kBCE, part = lane % kBCE;
             if (e >= count && e < kmax)
-                *reinterpret_cast<u32x4_t*>(rB + ((long)bg * cap + ring_slot(start, e, cap)) * N + part * kEPC) =
-                    braw[i];
+                bring.template bytes<kPol, 16>((uint32_t)((ring_slot(start, e, cap) * N + part * kEPC) * sizeof(TIN)),
+                                               &braw[i]);
         }
     }
     wave_sync();
@@ -306,7 +311,9 @@ __global__ __launch_bounds__(256) void m2_replay_kernel(M2Args a) {
 #pragma unroll
         for (int j = 0; j < MAXQ; ++j) {
             if (j >= nq) break;
-            a.y[(((long)b * nq + j) * H + h) * P + row] = s0[j] * acc[j] + out[j];
+            const PolicyStore yrow(a.y + uniform64((((long)b * nq + j) * H + h) * P), P * 4);
+            const float yv = s0[j] * acc[j] + out[j];
+            yrow.template bytes<kStoreWT, 4>((uint32_t)(row * 4), &yv);
         }
     }
     if constexpr (COMMIT) {

@@ -147,6 +147,48 @@ __device__ __forceinline__ void store_raw(T* __restrict__ dst, const T (&d)[E]) 
     }
 }
 
+// Stores with an explicit cache policy, for the per-token ring appends and outputs of the replay
+// kernels: gfx950 buffer stores through a resource whose base is wave-uniform (one head's ring
+// rows, one output row) and a per-lane byte offset, checked by the hardware against the
+// resource's size. The policy is the store's cache-policy operand: sc0 | sc1 (system scope, so
+// the L2 writes the line through rather than holding it dirty) and nt (streaming). Those few
+// thin writes inside a saturated read stream cost far more than their bytes; written through
+// they cost less (measured on the replay and verify kernels; the folds' bulk writes keep the
+// default policy, which measured faster for them).
+enum : int { kStoreWT = 1 | 16, kStoreWTNT = 1 | 2 | 16 };
+// Third dword of a raw buffer resource: untyped access, 32-bit data format.
+constexpr int kRawBufferWord3 = 0x00020000;
+
+struct PolicyStore {
+    __amdgpu_buffer_rsrc_t rsrc;
+    __device__ __forceinline__ PolicyStore(const void* base, uint32_t bytes)
+        : rsrc(__builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes,
+                                                 kRawBufferWord3)) {}
+    // B bytes (16, 8, 4 or 2) from src at byte offset off
+    template <int POL, int B>
+    __device__ __forceinline__ void bytes(uint32_t off, const void* src) const {
+        static_assert(B == 16 || B == 8 || B == 4 || B == 2, "store width");
+        if constexpr (B == 16) {
+            u32x4_t v;
+            __builtin_memcpy(&v, src, 16);
+            __builtin_amdgcn_raw_buffer_store_b128(v, rsrc, (int)off, 0, POL);
+        } else if constexpr (B == 8) {
+            typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+            u32x2_t v;
+            __builtin_memcpy(&v, src, 8);
+            __builtin_amdgcn_raw_buffer_store_b64(v, rsrc, (int)off, 0, POL);
+        } else if constexpr (B == 4) {
+            uint32_t v;
+            __builtin_memcpy(&v, src, 4);
+            __builtin_amdgcn_raw_buffer_store_b32(v, rsrc, (int)off, 0, POL);
+        } else {
+            unsigned short v;
+            __builtin_memcpy(&v, src, 2);
+            __builtin_amdgcn_raw_buffer_store_b16(v, rsrc, (int)off, 0, POL);
+        }
+    }
+};
+
 // Copy E contiguous elements of T (raw bits) from src to dst with the widest access possible.
 template <typename T, int E>
 __device__ __forceinline__ void copy_row(T* __restrict__ dst, const T* __restrict__ src) {
