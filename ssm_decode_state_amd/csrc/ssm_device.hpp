@@ -73,21 +73,6 @@ template <typename T> __device__ __forceinline__ float to_f32(T v);
 template <> __device__ __forceinline__ float to_f32<float>(float v) { return v; }
 template <> __device__ __forceinline__ float to_f32<bf16_t>(bf16_t v) { return bf16_to_f32(v); }
 
-// Load E contiguous elements of T starting at src (aligned to the access width) as floats, using
-// the widest access the byte count allows.
-template <typename T, int E>
-__device__ __forceinline__ void load_row(const T* __restrict__ src, float (&d)[E]) {
-    constexpr int kBytes = E * (int)sizeof(T);
-    if constexpr (kBytes % 16 == 0) {
-        const uint4* s = reinterpret_cast<const uint4*>(src);
-#pragma unroll
-        for (int u = 0; u < kBytes / 16; ++u) Unit<T>::unpack(s[u], d + u * Unit<T>::kElems);
-    } else {
-#pragma unroll
-        for (int i = 0; i < E; ++i) d[i] = to_f32<T>(src[i]);
-    }
-}
-
 // Load E contiguous elements of T as raw bits (no conversion) with the widest access possible.
 template <typename T, int E>
 __device__ __forceinline__ void load_raw(const T* __restrict__ src, T (&d)[E]) {
@@ -113,37 +98,6 @@ __device__ __forceinline__ void load_raw(const T* __restrict__ src, T (&d)[E]) {
     } else {
 #pragma unroll
         for (int i = 0; i < E; ++i) d[i] = src[i];
-    }
-}
-
-// Store E raw elements of T with the widest access possible.
-template <typename T, int E>
-__device__ __forceinline__ void store_raw(T* __restrict__ dst, const T (&d)[E]) {
-    constexpr int kBytes = E * (int)sizeof(T);
-    if constexpr (kBytes % 16 == 0) {
-#pragma unroll
-        for (int u = 0; u < kBytes / 16; ++u) {
-            uint4 t;
-            __builtin_memcpy(&t, &d[u * (16 / sizeof(T))], 16);
-            reinterpret_cast<uint4*>(dst)[u] = t;
-        }
-    } else if constexpr (kBytes % 8 == 0) {
-#pragma unroll
-        for (int u = 0; u < kBytes / 8; ++u) {
-            uint2 t;
-            __builtin_memcpy(&t, &d[u * (8 / sizeof(T))], 8);
-            reinterpret_cast<uint2*>(dst)[u] = t;
-        }
-    } else if constexpr (kBytes % 4 == 0) {
-#pragma unroll
-        for (int u = 0; u < kBytes / 4; ++u) {
-            uint32_t t;
-            __builtin_memcpy(&t, &d[u * (4 / sizeof(T))], 4);
-            reinterpret_cast<uint32_t*>(dst)[u] = t;
-        }
-    } else {
-#pragma unroll
-        for (int i = 0; i < E; ++i) dst[i] = d[i];
     }
 }
 
@@ -188,20 +142,6 @@ struct PolicyStore {
         }
     }
 };
-
-// Copy E contiguous elements of T (raw bits) from src to dst with the widest access possible.
-template <typename T, int E>
-__device__ __forceinline__ void copy_row(T* __restrict__ dst, const T* __restrict__ src) {
-    constexpr int kBytes = E * (int)sizeof(T);
-    if constexpr (kBytes % 16 == 0) {
-#pragma unroll
-        for (int u = 0; u < kBytes / 16; ++u)
-            reinterpret_cast<uint4*>(dst)[u] = reinterpret_cast<const uint4*>(src)[u];
-    } else {
-#pragma unroll
-        for (int i = 0; i < E; ++i) dst[i] = src[i];
-    }
-}
 
 // Wave-local ordering point for LDS written by some lanes and read by others of the same wave:
 // the LDS unit executes one wave's operations in order, so a compiler-level barrier with
