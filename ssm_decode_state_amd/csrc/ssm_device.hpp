@@ -34,6 +34,12 @@ __device__ __forceinline__ int ring_slot(int start, int e, int cap) {
     return s >= cap ? s - cap : s;
 }
 
+// Cache-policy operands of gfx950 buffer stores (sc0 = 1, nt = 2, sc1 = 16): write-through at
+// system scope, and the same with the streaming hint.
+enum : int { kStoreWT = 1 | 16, kStoreWTNT = 1 | 2 | 16 };
+// Third dword of a raw buffer resource: untyped access, 32-bit data format.
+constexpr int kRawBufferWord3 = 0x00020000;
+
 // Streaming access to a state tile through a wave-uniform base and a 32-bit per-lane byte
 // offset: each access is an SGPR base plus one shared VGPR offset, so a tile that is loaded at
 // the start of a kernel and stored at its end keeps no per-access 64-bit addresses alive.
@@ -43,8 +49,19 @@ struct TileIO {
     __device__ __forceinline__ float4 load(uint32_t off) const {
         return ld_stream(reinterpret_cast<const float4*>((base + off) + lane));
     }
+    // POL = 0: a non-temporal global store; otherwise a buffer store with that cache-policy
+    // operand through a resource based at the tile
+    template <int POL = 0>
     __device__ __forceinline__ void store(uint32_t off, float4 v) const {
-        st_stream(v, reinterpret_cast<float4*>((base + off) + lane));
+        if constexpr (POL == 0) {
+            st_stream(v, reinterpret_cast<float4*>((base + off) + lane));
+        } else {
+            const u32x4_t t = {__float_as_uint(v.x), __float_as_uint(v.y), __float_as_uint(v.z),
+                               __float_as_uint(v.w)};
+            __builtin_amdgcn_raw_buffer_store_b128(
+                t, __builtin_amdgcn_make_buffer_rsrc(base, 0, 0x7fffffff, kRawBufferWord3),
+                (int)(off + lane), 0, POL);
+        }
     }
 };
 
@@ -107,11 +124,10 @@ __device__ __forceinline__ void load_raw(const T* __restrict__ src, T (&d)[E]) {
 // resource's size. The policy is the store's cache-policy operand: sc0 | sc1 (system scope, so
 // the L2 writes the line through rather than holding it dirty) and nt (streaming). Those few
 // thin writes inside a saturated read stream cost far more than their bytes; written through
-// they cost less (measured on the replay and verify kernels; the folds' bulk writes keep the
-// default policy, which measured faster for them).
-enum : int { kStoreWT = 1 | 16, kStoreWTNT = 1 | 2 | 16 };
-// Third dword of a raw buffer resource: untyped access, 32-bit data format.
-constexpr int kRawBufferWord3 = 0x00020000;
+// they cost less (measured on the replay and verify kernels). Of the bulk tile writes, the
+// Gated DeltaNet flush and conventional kernels take write-through streaming stores too
+// (TileIO::store's policy argument); the Mamba-2 fold's copy writes measured faster with the
+// default policy.
 
 struct PolicyStore {
     __amdgpu_buffer_rsrc_t rsrc;
