@@ -157,3 +157,88 @@ def test_adversarial_tiles(rc, N):
     pairs = [(b, h) for b in range(2) for h in range(H)]
     per_window = run_readcopy(shape, 75 + N + rc, rc, 12, pairs, h0=h0)
     assert len(per_window) == 2
+
+
+@pytest.mark.parametrize("rc", [1, 2])
+def test_readcopy_speculative_rounds(rc):
+    """Drafts verified through the read copy (several queries per call). After every round
+    (rollback and any fold) the copy is bit-exact against the GPU's own fp32 checkpoint; every
+    draft output equals, to 1e-4, the oracle's replay form on the decoded copy in effect for that
+    round, over the committed entries since the last fold and drafts 1..j, and lies within the
+    bound around the exact speculative output; the fp32 checkpoint after the rounds is exact."""
+    shape = synth.Shape(synth.MAMBA2, 2, 6, 3, 64, 128, 8, 4)
+    seed, R, S = 70 + rc, 12, shape.max_draft
+    L, hpg = shape.window, shape.heads // shape.groups
+    A, D = synth.head_constants(shape, seed)
+    h0 = synth.initial_state(shape, seed, 0.3162)
+    cfg = bd.make_config(bd.SSM_MAMBA2, shape.batch, shape.heads, shape.groups, shape.dim_p,
+                         shape.dim_n, L, S, bd.SSM_IN_BF16, rc)
+    st = bd.State(cfg, h0.to(DEV), A.to(DEV), D.to(DEV))
+    pairs = [(b, h) for b in range(shape.batch) for h in range(shape.heads)]
+    n = len(pairs)
+    bi = torch.tensor([b for (b, _) in pairs], device=DEV)
+    hi = torch.tensor([h for (_, h) in pairs], device=DEV)
+    y = torch.empty(shape.batch, S, shape.heads, shape.dim_p, device=DEV)
+    torch.cuda.synchronize()
+    cks, copies = [ckpt_of(st, pairs)], [copy_of(st, pairs, rc)]  # in effect for round r: index r
+    outs, drafts, accs = [], [], []
+    for r in range(R):
+        d = synth.token_inputs(shape, seed, "draft", r, ntok=S)
+        drafts.append(d)
+        bd.ssm_spec_append(st, S, to_dev(d, DEV), y)
+        outs.append(y[bi, :, hi].clone())
+        acc = synth.accept_counts(shape.batch, S, 1003, r)
+        accs.append(acc)
+        bd.ssm_spec_rollback(st, acc.to(DEV))
+        cks.append(ckpt_of(st, pairs))
+        copies.append(copy_of(st, pairs, rc))
+    torch.cuda.synchronize()
+    for r, (hg32, cp) in enumerate(zip(cks, copies)):
+        assert_copy_exact(hg32, cp, rc, "copy after round %d" % (r - 1))
+    gy = torch.stack(outs, 1).cpu().double().numpy()  # [n][R][S][P]
+    x = np.stack([np.stack([synth.to_f64(d["x"][b, :, h]) for d in drafts]) for (b, h) in pairs])
+    Bm = np.stack([np.stack([synth.to_f64(d["B"][b, :, h // hpg]) for d in drafts]) for (b, h) in pairs])
+    Cm = np.stack([np.stack([synth.to_f64(d["C"][b, :, h // hpg]) for d in drafts]) for (b, h) in pairs])
+    dt = np.stack([np.stack([synth.to_f64(d["dt"][b, :, h]) for d in drafts]) for (b, h) in pairs])
+    acc = np.stack([torch.stack(accs, 1)[b].numpy() for (b, _) in pairs]).astype(np.int32)
+    hs = np.array([h for (_, h) in pairs])
+    Ah, Dh = A.double().numpy()[hs], D.double().numpy()[hs]
+    h0n = np.stack([h0[b, h].double().numpy() for (b, h) in pairs])
+    tot = np.cumsum(acc, axis=1)
+    folds = [list(range(L, int(tot[i, -1]) + 1, L)) for i in range(n)]
+    snap = np.full((n, max(1, max(len(f) for f in folds))), -1, dtype=np.int32)
+    for i, f in enumerate(folds):
+        snap[i, :len(f)] = f
+    oy, _, sn = oracle.m2_spec_rounds(Ah, Dh, h0n, x, Bm, Cm, dt, acc, snap_after=snap)
+    assert max(len(f) for f in folds) >= 2  # the rounds cross several folds
+    for i in range(n):
+        com = {"x": [], "B": [], "dt": []}  # the accepted drafts, in order
+        for r in range(R):
+            nf = len(com["dt"]) // L  # folds so far
+            he = h0n[i] if nf == 0 else sn[i, nf - 1]
+            hg32, cp = cks[r][i:i + 1], tuple(c[i:i + 1] for c in copies[r])
+            dec = decode_copy(cp, rc)[0]
+            lim_el = (elem_bound(hg32, cp, rc) + np.abs(hg32.astype(np.float64) - he))[0]
+            for j in range(S):
+                ent = {"x": np.concatenate([np.asarray(com["x"][nf * L:]).reshape(-1, shape.dim_p), x[i, r, :j + 1]]),
+                       "B": np.concatenate([np.asarray(com["B"][nf * L:]).reshape(-1, shape.dim_n), Bm[i, r, :j + 1]]),
+                       "dt": np.concatenate([np.asarray(com["dt"][nf * L:]).reshape(-1), dt[i, r, :j + 1]])}
+                yc = oracle.m2_replay_output(float(Ah[i]), float(Dh[i]), dec, ent["x"], ent["B"],
+                                             Cm[i, r, j], ent["dt"])
+                what = "pair %d round %d draft %d" % (i, r, j)
+                assert_close(gy[i, r, j], yc, (-1,), "output on the decoded copy, " + what)
+                s0 = np.exp(Ah[i] * ent["dt"].sum())
+                lim = quant.output_bound(lim_el, Cm[i, r, j], s0)
+                rms = np.sqrt((yc ** 2).mean())
+                slack = TOL * np.maximum(np.abs(yc), rms)
+                err = np.abs(gy[i, r, j] - oy[i, r, j])
+                assert np.all(err <= lim + slack), (what, float((err - lim - slack).max()))
+            for key, src in (("x", x), ("B", Bm), ("dt", dt)):
+                com[key].extend(list(src[i, r, :int(acc[i, r])]))
+    nat = torch.empty(shape.batch, shape.heads, shape.dim_p, shape.dim_n, device=DEV)
+    bd.ssm_flush(st, bd.SSM_FLUSH_ALL)
+    bd.ssm_ckpt_export(st, nat)
+    torch.cuda.synchronize()
+    _, hT, _ = oracle.m2_spec_rounds(Ah, Dh, h0n, x, Bm, Cm, dt, acc)
+    got = np.stack([nat[b, h].cpu().double().numpy() for (b, h) in pairs])
+    assert_close(got, hT, (-2, -1), "fp32 checkpoint after the speculative rounds")
