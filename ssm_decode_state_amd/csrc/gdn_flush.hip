@@ -7,11 +7,8 @@ namespace ssm {
 template <int DV, int DK, typename TIN, int RC, bool VG>
 static hipError_t launch_flush_vg(const GdnArgs& a, int mode_all, int rewrite_only, hipStream_t s) {
     const dim3 grid(a.heads, a.batch), block(DV);
-    if (mode_all == 2) {  // fused decode + fold of the L-th lock-step token
-        // not with a read copy: there the closing step's replay reads only the copy, and the
-        // fused kernel with the copy rewrite does not fit the register budget
-        if constexpr (RC != 0) return hipErrorNotSupported;
-        else hipLaunchKernelGGL((gdn_flush_kernel<DV, DK, TIN, RC, true, VG>), grid, block, 0, s, a, 0, 0);
+    if (mode_all == 2) {  // fused decode + fold of the L-th lock-step token (and copy rewrite)
+        hipLaunchKernelGGL((gdn_flush_kernel<DV, DK, TIN, RC, true, VG>), grid, block, 0, s, a, 0, 0);
     } else {
         hipLaunchKernelGGL((gdn_flush_kernel<DV, DK, TIN, RC, false, VG>), grid, block, 0, s, a,
                            mode_all, rewrite_only);

@@ -987,6 +987,10 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_flush_kernel(GdnArgs a, int mod
         const float* r = s_d[lane];
         a.o[(long)head * DV + p_base + lane] = a.scale * ((r[0] + r[1]) + (r[2] + r[3]));
     }
+    // (the copy's encoding stays below this point: scheduled up with the fused output it took
+    // more than 256 registers)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
     if constexpr (RC != 0) {  // rewrite the read copy from the new fp32 tile (news, para 4)
         float amax_t = 0.f;
         if constexpr (RC == 2) {

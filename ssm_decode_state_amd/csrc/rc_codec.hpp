@@ -177,6 +177,9 @@ __device__ __forceinline__ void rc_write_blocks(const RcView& v, long head, int 
                                                 const f32x4 (&hb)[4][N / 16], float amax_tile,
                                                 bool tile_writer, float* s_tab) {
     static_assert(N == 64 || N == 128, "read copy: N in {64, 128}");
+    // the lane indices pass through an empty asm here, so that the compiler cannot compute the
+    // copy's store addresses at the top of the calling kernel and hold them across its loops
+    asm volatile("" : "+v"(li), "+v"(lg));
     constexpr int kNB = N / 16;
     if constexpr (RC == 1) {
         uint8_t* codes = v.codes + head * (long)(ROWS * N);

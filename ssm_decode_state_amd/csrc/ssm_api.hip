@@ -351,8 +351,8 @@ ssm_status ssm_replay_decode(ssm_state* st, const void* in, float* y, void* stre
         a.o = y;
         a.ntok = 1;
         const int L = st->cfg.window;
-        if (st->cfg.readcopy == SSM_RC_NONE && st->count_lo == L - 1 && st->count_hi == L - 1) {
-            // as for Mamba-2 above (with a read copy: replay, then the fold below)
+        if (st->count_lo == L - 1 && st->count_hi == L - 1) {
+            // as for Mamba-2 above (with a read copy, the same pass rewrites the copy)
             e = ssm::gdn_launch_flush(a, st->cfg.dim_p, st->cfg.dim_n, st->cfg.in_dtype,
                                       st->cfg.readcopy, 2, 0, hs);
             if (e == hipSuccess) e = recount(st, hs);

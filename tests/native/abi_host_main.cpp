@@ -107,7 +107,6 @@ static void drive(const ssm_config& c) {
     const void* in = m2 ? (const void*)&mi : (const void*)&gi;
     float* y = (float*)kOut;
     const int Lw = c.window;
-    const bool fused_path = m2 || c.readcopy == SSM_RC_NONE;
 
     // lock-step decode: two whole windows and three more tokens
     const long fused0 = g_world.calls[kFused], fold0 = g_world.calls[kFold];
@@ -120,8 +119,8 @@ static void drive(const ssm_config& c) {
         CHECK(st.count_lo <= rest && rest <= st.count_hi && st.count_hi <= L.ring_cap);
     } else {
         if (c.batch > 0) {
-            CHECK(g_world.calls[kFused] - fused0 == (fused_path ? nwin : 0));
-            CHECK(g_world.calls[kFold] - fold0 == (fused_path ? 0 : nwin));
+            CHECK(g_world.calls[kFused] - fused0 == nwin);  // every window closes in one pass
+            CHECK(g_world.calls[kFold] - fold0 == 0);
         }
         CHECK(st.count_lo == rest && st.count_hi == rest);
         CHECK(st.ring_start == (nwin * Lw) % L.ring_cap);

@@ -8,7 +8,9 @@ Checks, in every window (decode) and every round (speculation):
     own fp32 state (at init: to the initial state);
   * outputs: every output equals, to 1e-4, the oracle's replay form evaluated on the GPU's
     decoded copy with exactly the entries the GPU replayed (for drafts: the committed entries
-    since the last fold and drafts 1..j);
+    since the last fold and drafts 1..j); the window-closing step of a lock-step decode folds in
+    fp32, rewrites the copy and emits its output from the new fp32 state, so that output is
+    compared with the exact one at 1e-4;
   * bound: every output is within
         |o - o_exact| <= |scale| sum_n (bound[p, n] + |S_gpu - S_exact|[p, n]) |r[n]| + 1e-4 m
     of the exact fp64 output, where r is the replayed query (oracle.replay_query: the checkpoint
@@ -117,10 +119,13 @@ def run_decode(shape, seed, rc, T, scale, pairs, S0=None):
         Se = S0p if w == 0 else osn[:, w - 1]
         dec = decode_copy(cp, rc)
         worst = 0.0
-        for j in range(L):  # every token of the window replays from the copy of its start state
+        for j in range(L):  # the window's tokens replay from the copy of its start state
             t = w * L + j
             if t >= T:
                 break
+            if j == L - 1:  # the fused window-closing step: output from the new fp32 state
+                assert_close(go[:, t], oo[:, t], (-1,), "window-closing output (t=%d)" % t)
+                continue
             e = slice(w * L, t + 1)
             worst = max(worst, check_output(shape.kind, scale, go[:, t], dec, Sg32, Se, cp, rc,
                                             q[:, t], k[:, e], v[:, e], beta[:, e], g[:, e],

@@ -30,7 +30,8 @@ def _state(shape, seed, rc):
 
 
 @pytest.mark.parametrize("kind,rc", [(synth.MAMBA2, 0), (synth.MAMBA2, bd.SSM_RC_FP8_ROW),
-                                     (synth.GDN, 0), (synth.KDA, 0)])
+                                     (synth.GDN, 0), (synth.KDA, 0), (synth.GDN, bd.SSM_RC_FP4_B16),
+                                     (synth.KDA, bd.SSM_RC_FP8_ROW)])
 def test_graph_window_replays_match_eager(kind, rc):
     L, R = 8, 3
     if kind == synth.MAMBA2:
