@@ -189,7 +189,9 @@ ssm_status ssm_ckpt_init(ssm_state *st, const ssm_config *cfg, void *mem, uint64
  * to an ssm_m2_in or ssm_gdn_in with ntok = 1) to each ring, compute y [batch][H][P] fp32 from the
  * checkpoint (or its read copy) and the buffered inputs with no state write, and commit the token.
  * When a sequence's committed count reaches L the buffer is folded into the checkpoint (the same
- * work as ssm_flush(SSM_FLUSH_IF_FULL)) before the call returns.
+ * work as ssm_flush(SSM_FLUSH_IF_FULL)) before the call returns. In lock step (every sequence at
+ * count L - 1) that token is handled by the fold pass itself: its output comes from the new fp32
+ * checkpoint, and the read copy, if configured, is rewritten in the same pass.
  * Errors: SSM_E_STATE if drafts are pending; SSM_E_CAPACITY if a ring could overflow. */
 ssm_status ssm_replay_decode(ssm_state *st, const void *in, float *y, void *stream);
 
