@@ -98,6 +98,8 @@ def test_fast_decay_decode_and_flush_all(kind, B, H, dv, dk, L, T, rc):
     assert_close(gend, ST, (-2, -1), "state after flush(ALL), fast gates")
     if rc == 0:  # (read-copy outputs are checked against their bound in the read-copy tests)
         assert_close(go, oo, (-1,), "replay outputs, fast gates")
+    else:  # the window-closing steps emit from the new fp32 state, copy or not
+        assert_close(go[:, L - 1::L], oo[:, L - 1::L], (-1,), "window-closing outputs, fast gates")
 
 
 @pytest.mark.parametrize("kind", KINDS)

@@ -136,11 +136,11 @@ def run_decode(shape, seed, rc, T, scale, pairs, S0=None):
 
 @pytest.mark.parametrize("kind", KINDS)
 @pytest.mark.parametrize("rc", [1, 2])
-@pytest.mark.parametrize("case", ["small", "serving"])
+@pytest.mark.parametrize("case", ["small", "small_f32", "serving"])
 def test_gdn_readcopy_decode(rc, case, kind):
-    if case == "small":
-        shape = synth.Shape(kind, 2, 3, 3, 128, 128, 8, 1)
-        seed, T, scale = 90 + rc + 7 * kind, 64, 0.5
+    if case.startswith("small"):  # small_f32: fp32 inputs
+        shape = synth.Shape(kind, 2, 3, 3, 128, 128, 8, 1, in_bf16=case == "small")
+        seed, T, scale = 90 + rc + 7 * kind + (5 if case == "small_f32" else 0), 64, 0.5
         pairs = [(b, h) for b in range(2) for h in range(3)]
     else:
         w = synth.WORKLOADS["kda_b256" if kind == synth.KDA else "gdn_b256"]
