@@ -47,7 +47,8 @@ def make(shape, seed, rc, h0=None):
     if h0 is None:
         h0 = synth.initial_state(shape, seed, 0.3162)
     cfg = bd.make_config(bd.SSM_MAMBA2, shape.batch, shape.heads, shape.groups, shape.dim_p,
-                         shape.dim_n, shape.window, 1, bd.SSM_IN_BF16, rc)
+                         shape.dim_n, shape.window, 1,
+                         bd.SSM_IN_BF16 if shape.in_bf16 else bd.SSM_IN_F32, rc)
     st = bd.State(cfg, h0.to(DEV), A.to(DEV), D.to(DEV))
     return st, A, D, h0
 
@@ -125,11 +126,11 @@ def run_readcopy(shape, seed, rc, T, pairs, h0=None):
 
 
 @pytest.mark.parametrize("rc", [1, 2])
-@pytest.mark.parametrize("case", ["small", "serving"])
+@pytest.mark.parametrize("case", ["small", "small_f32", "serving"])
 def test_readcopy_decode(rc, case):
-    if case == "small":
-        shape = synth.Shape(synth.MAMBA2, 2, 6, 3, 64, 128, 8, 1)
-        seed, T = 60 + rc, 96
+    if case.startswith("small"):  # small_f32: fp32 inputs
+        shape = synth.Shape(synth.MAMBA2, 2, 6, 3, 64, 128, 8, 1, in_bf16=case == "small")
+        seed, T = 60 + rc + (3 if case == "small_f32" else 0), 96
         pairs = [(b, h) for b in range(2) for h in range(6)]
     else:
         w = synth.WORKLOADS["m2_b256_readcopy"]
