@@ -83,6 +83,23 @@ def m2_flush_bytes_per_head(P, N, L, esz=2):
     return 2 * P * N * 4 + L * (P * esz + N * esz + 4) + 16
 
 
+def rc_copy_bytes_per_head(rows, cols, rc):
+    """One head's read copy: fp8 codes and an fp32 scale per row, or fp4 codes, an E4M3 scale per
+    16 elements and the fp32 tile scale."""
+    if rc == 0:
+        return 0
+    return rows * cols + rows * 4 if rc == 1 else rows * cols // 2 + rows * cols // 16 + 4
+
+
+def m2_fused_step_bytes_per_head(P, N, L, rc=0, esz=2):
+    """The window-closing step (one fused pass): checkpoint read + written, the L-1 buffered
+    entries (x, B, dt), the token read (x, B, C, dt), y, the pointer entry; with a read copy, the
+    copy rewritten."""
+    entry = P * esz + N * esz + 4
+    token = P * esz + 2 * N * esz + 4
+    return 2 * P * N * 4 + (L - 1) * entry + token + P * 4 + 16 + rc_copy_bytes_per_head(P, N, rc)
+
+
 def m2_conv_bytes_per_head(P, N, esz=2):
     """State read + write, the token's inputs read, y written."""
     return 2 * P * N * 4 + P * esz + 2 * N * esz + 4 + P * 4
@@ -104,8 +121,7 @@ def m2_snapshot_bytes_per_head(P, N, S, esz=2):
 
 def m2_rc_replay_bytes_per_head(P, N, k, rc, esz=2):
     """Replay launch reading the low-precision copy instead of the fp32 checkpoint."""
-    copy = P * N + P * 4 if rc == 1 else P * N // 2 + P * (N // 16) + 4
-    return m2_replay_bytes_per_head(P, N, k, esz) - P * N * 4 + copy
+    return m2_replay_bytes_per_head(P, N, k, esz) - P * N * 4 + rc_copy_bytes_per_head(P, N, rc)
 
 
 def gdn_replay_bytes_per_head(dv, dk, k, esz=2, gsz=4):
@@ -130,6 +146,23 @@ def gdn_snapshot_bytes_per_head(dv, dk, S, esz=2, gsz=4):
     """Snapshot-based GDN / KDA speculation: read the state once, write it after each of S drafts,
     read the drafts' inputs, write their outputs."""
     return 4 * dv * dk * (1 + S) + S * (2 * dk * esz + dv * esz + 4 + gsz) + 4 * S * dv
+
+
+def gdn_fused_step_bytes_per_head(dv, dk, L, rc=0, esz=2, gsz=4):
+    """GDN / KDA window-closing step: state read + written, the L-1 buffered entries (k, v, beta,
+    g), the token read (q, k, v, beta, g), o, the pointer entry; with a read copy, the copy
+    rewritten."""
+    entry = dk * esz + dv * esz + 4 + gsz
+    token = 2 * dk * esz + dv * esz + 4 + gsz
+    return 2 * dv * dk * 4 + (L - 1) * entry + token + dv * 4 + 16 + rc_copy_bytes_per_head(dv, dk, rc)
+
+
+def fold_step_rate(nbytes, ms_list):
+    """Achieved GB/s and fraction of the HBM peak of the timed window-closing steps (nbytes each)."""
+    if not ms_list:
+        return {}
+    gbs = nbytes / (sum(ms_list) / len(ms_list) * 1e-3) / 1e9
+    return {"fold_step_achieved_gbs": gbs, "fold_step_frac": gbs / HBM_PEAK_GBS}
 
 
 def gdn_conv_bytes_per_head(dv, dk, esz=2, gsz=4):
@@ -636,13 +669,13 @@ def bench_readcopy(dev, rc, steps=128, warm=16, layers=4, pool=16):
             "tokens_per_s": Bn * n / wall, "unit": "tokens/s/layer", "layers_rotated": layers,
             "ms_per_step": wall / n * 1e3, "replay_avg_us": rep_ms / (n - len(flush_ms)) * 1e3,
             "replay_achieved_gbs": gbs, "replay_frac": gbs / HBM_PEAK_GBS,
-            "fold_step_avg_us": sum(flush_ms) / max(len(flush_ms), 1) * 1e3}
+            "fold_step_avg_us": sum(flush_ms) / max(len(flush_ms), 1) * 1e3,
+            **fold_step_rate(heads * m2_fused_step_bytes_per_head(P, N, L, rc), flush_ms)}
 
 
 def gdn_rc_replay_bytes_per_head(dv, dk, k, rc, esz=2, gsz=4):
     """GDN / KDA replay launch reading the low-precision copy instead of the fp32 state."""
-    copy = dv * dk + dv * 4 if rc == 1 else dv * dk // 2 + dv * dk // 16 + 4
-    return gdn_replay_bytes_per_head(dv, dk, k, esz, gsz) - dv * dk * 4 + copy
+    return gdn_replay_bytes_per_head(dv, dk, k, esz, gsz) - dv * dk * 4 + rc_copy_bytes_per_head(dv, dk, rc)
 
 
 def bench_gdn(dev, steps=128, warm=16, layers=2, pool=16, rc=0, kda=False):
@@ -693,7 +726,8 @@ def bench_gdn(dev, steps=128, warm=16, layers=2, pool=16, rc=0, kda=False):
                 "tokens_per_s": Bn * n / wall, "unit": "tokens/s/layer", "layers_rotated": layers,
                 "ms_per_step": wall / n * 1e3, "replay_avg_us": rep_ms / (n - len(fold)) * 1e3,
                 "replay_achieved_gbs": gbs, "replay_frac": gbs / HBM_PEAK_GBS,
-                "fold_step_avg_us": sum(fold) / max(len(fold), 1) * 1e3}
+                "fold_step_avg_us": sum(fold) / max(len(fold), 1) * 1e3,
+                **fold_step_rate(heads * gdn_fused_step_bytes_per_head(dv, dk, L, rc, gsz=gsz), fold)}
     for i in range(n_warm):
         bd.ssm_conventional_step(cfg, convs[i % layers], inputs[i % pool], None, None, o)
     cwall, cms = timed_calls(n, lambda i: bd.ssm_conventional_step(
@@ -705,6 +739,7 @@ def bench_gdn(dev, steps=128, warm=16, layers=2, pool=16, rc=0, kda=False):
             "replay_avg_us": rep_ms / (n - len(fold)) * 1e3, "replay_achieved_gbs": gbs,
             "replay_frac": gbs / HBM_PEAK_GBS,
             "fold_step_avg_us": sum(fold) / max(len(fold), 1) * 1e3,
+            **fold_step_rate(heads * gdn_fused_step_bytes_per_head(dv, dk, L, gsz=gsz), fold),
             "conventional": {"tokens_per_s": Bn * n / cwall, "avg_us": sum(cms) / n * 1e3,
                              "achieved_gbs": cgbs, "frac": cgbs / HBM_PEAK_GBS},
             "speedup_vs_conventional": (Bn * n / wall) / (Bn * n / cwall)}
@@ -1042,8 +1077,7 @@ def main():
     # the L-th step of each window is one fused pass: fold the window and emit the output from
     # the new checkpoint (checkpoint read + write, L-1 buffered entries, this token, y)
     fold_ms = sum(flush_steps) / len(flush_steps) if flush_steps else None
-    fold_bytes = heads * (m2_flush_bytes_per_head(P, N, L) - (P * 2 + N * 2 + 4)
-                          + (P * 2 + 2 * N * 2 + 4) + P * 4)
+    fold_bytes = heads * m2_fused_step_bytes_per_head(P, N, L)
     fold_gbs = fold_bytes / (fold_ms * 1e-3) / 1e9 if fold_ms else None
     # the replay launches timed above run at counts 1..L-1 (the L-th step is the fused fold)
     mean_bytes_per_head = rep_bytes / heads / max(n_rep, 1)

@@ -97,3 +97,25 @@ def test_read_ceiling_interpolation():
     assert bench.ceiling_at(rc, 128 << 20) == pytest.approx(5500.0)  # halfway in log2(bytes)
     assert bench.ceiling_at(rc, 512 << 20) == pytest.approx(6500.0)
     assert bench.ceiling_at(rc, 4 << 30) == 7000.0       # above the largest
+
+
+def test_fused_window_closing_step_models():
+    # Mamba-2: tile read + written, 15 buffered entries, the token, y, the pointer entry
+    m2 = 2 * TILE_M2 + 15 * 388 + 644 + 256 + 16
+    assert m2 == 72272
+    assert bench.m2_fused_step_bytes_per_head(P, N, 16) == m2
+    assert bench.m2_fused_step_bytes_per_head(P, N, 16, 1) == m2 + 8448  # fp8 copy rewritten
+    assert bench.m2_fused_step_bytes_per_head(P, N, 16, 2) == m2 + 4612  # fp4 copy rewritten
+    for kda in (False, True):
+        g = 4 * DK if kda else 4
+        entry, token = 256 + 256 + 4 + g, 256 * 3 + 4 + g
+        gdn = 2 * TILE_GDN + 15 * entry + token + 512 + 16
+        assert gdn == (148304 if kda else 140176)
+        assert bench.gdn_fused_step_bytes_per_head(DV, DK, 16, gsz=g) == gdn
+        assert bench.gdn_fused_step_bytes_per_head(DV, DK, 16, 1, gsz=g) == gdn + DV * DK + DV * 4
+        assert bench.gdn_fused_step_bytes_per_head(DV, DK, 16, 2, gsz=g) == \
+            gdn + DV * DK // 2 + DV * DK // 16 + 4
+    r = bench.fold_step_rate(2e9, [0.5, 0.5])  # 2 GB in 0.5 ms
+    assert r["fold_step_achieved_gbs"] == pytest.approx(4000.0)
+    assert r["fold_step_frac"] == pytest.approx(0.5)
+    assert bench.fold_step_rate(1.0, []) == {}
