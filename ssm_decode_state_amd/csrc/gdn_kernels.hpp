@@ -803,7 +803,7 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_flush_kernel(GdnArgs a, int mod
                     s_w[t][n] = Gc;
                 }
                 glog[j] = Gc;
-                s_gl[n] = expf(Gc);
+                s_gl[n] = __expf(Gc);
             }
         }
         __syncthreads();
@@ -817,6 +817,10 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_flush_kernel(GdnArgs a, int mod
             const float t = __shfl_up(G, o, 16);
             G += li >= o ? t : 0.f;
         }
+        // The flush's decay factors use the hardware exponential (__expf: the exponent scaled by
+        // log2 e, then v_exp_f32): relative error about 1e-7 |x| for exp(x), far inside the fp32
+        // metric, at a fraction of the instructions of the correctly rounded expf (KDA takes
+        // about a hundred per lane per chunk). With log-decays g <= 0 no exponent here is positive.
         if constexpr (VG) {
             // Gated Gram matrix sum_n k_t[n] k_i[n] exp(G_t[n] - G_i[n]) for i < t, over a binary
             // split of the chunk: the pair (t, i) belongs to level b, the highest bit in which t and
@@ -841,7 +845,7 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_flush_kernel(GdnArgs a, int mod
                 for (int n0 = 0; n0 < DK; n0 += 4) {
                     const float kk = s_k[li][n0 + lg];
                     const float Gr = s_w[li][n0 + lg], Gc = s_w[cut][n0 + lg];
-                    const float x = kk * expf(upper ? Gr - Gc : Gc - Gr);
+                    const float x = kk * __expf(upper ? Gr - Gc : Gc - Gr);
                     gram = mfma4(upper ? x : 0.f, upper ? 0.f : x, gram);
                 }
                 // Lm[t][i] = beta_t Gram[t][i] for t = 4lg + r, i = li, for the pairs of this level
@@ -869,7 +873,7 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_flush_kernel(GdnArgs a, int mod
                 const int t = 4 * lg + r, i = li;
                 const float bt = __shfl(be, t, 64);
                 const float Gt = __shfl(G, t, 64);
-                s_l[t][i] = (i < t) ? bt * expf(Gt - G) * gram[r] : 0.f;
+                s_l[t][i] = (i < t) ? bt * __expf(Gt - G) * gram[r] : 0.f;
             }
         }
         __syncthreads();
@@ -881,7 +885,7 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_flush_kernel(GdnArgs a, int mod
 #pragma unroll
         for (int t = 0; t < 16; ++t) {
             const float bt = readlane(be, t);
-            const float bg = bt * (VG ? 1.f : expf(readlane(G, t)));
+            const float bg = bt * (VG ? 1.f : __expf(readlane(G, t)));
             float lrow[16];
 #pragma unroll
             for (int i = 0; i < t; ++i) lrow[i] = s_l[t][i];
@@ -893,8 +897,8 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_flush_kernel(GdnArgs a, int mod
                 float sw;
                 if constexpr (VG) {  // row t of s_w still holds G_t here
                     const float Gt = s_w[t][n];
-                    sw = -bg * expf(Gt) * kt;
-                    s_k[t][n] = kt * expf(glog[j] - Gt);  // K~ for the update below
+                    sw = -bg * __expf(Gt) * kt;
+                    s_k[t][n] = kt * __expf(glog[j] - Gt);  // K~ for the update below
                 } else {
                     sw = -bg * kt;
                 }
@@ -913,7 +917,7 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_flush_kernel(GdnArgs a, int mod
 
         asm volatile("" ::: "memory");
         // ---- Delta^T[p][t] = U^T[p][t] - sum_n S[p][n] W[t][n]   (D layout: p = 4lg + r, t = li)
-        const float dscale = VG ? 1.f : expf(gL - G);  // gamma_L / gamma_t for t = li (VG: in K~)
+        const float dscale = VG ? 1.f : __expf(gL - G);  // gamma_L / gamma_t for t = li (VG: in K~)
         f32x4 delta[kPB];
 #pragma unroll
         for (int pb = 0; pb < kPB; ++pb)
@@ -940,7 +944,7 @@ __attribute__((amdgpu_waves_per_eu(2))) void gdn_flush_kernel(GdnArgs a, int mod
 
         asm volatile("" ::: "memory");
         // ---- S <- gamma_L S + sum_t K^T[n][t] Delta'^T[t][p]   (D rows = n, columns = p) -----
-        const float gammaL = expf(gL);
+        const float gammaL = __expf(gL);
         if constexpr (VG) {  // column n = 16 nb + 4 lg + r scaled by exp(G_L[n]), one block at a time
 #pragma unroll
             for (int nb = 0; nb < kNB; ++nb) {
